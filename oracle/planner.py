@@ -1,0 +1,364 @@
+"""Integer oracle for admission: budgets, clusters, tiers, pages, tables, plan.
+
+TEST INFRASTRUCTURE (see ``oracle/__init__``).  Everything here is exact
+integer arithmetic in Python ints; it is written from the pages and from the
+readings stated below, never from the C++ planner.
+
+Sources (page, section):
+
+* Tangram page (arXiv 2606.06302 explainer), "Key finding: two-level structural
+  law" -- head importance ranking is input-invariant and each head's retention
+  ratio lies in a narrow band; "Three mechanisms", item 1 (Budget Reservation)
+  -- each head's post-compression footprint is fixed when the request starts;
+  item 2 (Ragged Paging) -- heads with similar budgets share their own page
+  table, and pages need not all be the same size; item 3 (AOT load balancing)
+  -- work is partitioned ahead of time by KV occupancy, with no runtime
+  re-planning.
+* TTKV page (arXiv 2604.19769 explainer), "Tier Content" -- the most recent N%
+  of tokens stay in the high-precision fast tier, the rest go to the
+  block-quantised slow tier; "Tier Interaction" -- the slow tier is quantised
+  in blocks.
+* RadixAttention lesson, "The concept" -- each radix-tree node owns a token
+  range and its KV blocks, and requests on the same branch reuse them.
+
+Readings where the pages are silent (each also listed in the design notes):
+
+R-rank   ratio_ppm(k) = hi - floor((hi - lo) * k / (H - 1)) for rank k
+         (k = 0 most important), hi when H == 1.
+R-round  budget = clamp(ceil(ratio_ppm * n_comp / 1e6), 1, n_comp); a given
+         per-(request, KV-head) override replaces it.  L = n_fixed + budget.
+R-clust  heads sorted by rank are cut into C contiguous groups; group c has
+         ceil(H/C) heads if c < H mod C, else floor(H/C).
+R-tier   n_bf0 = ceil(L * recent_ppm / 1e6); n_i8 = floor((L - n_bf0) / Qb) * Qb;
+         n_bf = L - n_i8.  INT8 rows are the oldest: logical rows [0, n_i8).
+R-page   a page of tier t holds S_t token slots (P for bf16, Qb for INT8) for
+         every head of its cluster.  Row r of cluster c needs
+         ceil(max_h n_bf / P) bf16 pages and max_h n_i8 / Qb INT8 pages.
+R-alloc  each (cluster, tier) pool hands out the lowest free page id.  Order:
+         request, cluster, tier (INT8 then bf16), page.  A page is shared when
+         every head of the cluster starts it at the same logical position s
+         and s + S_t <= n_fixed[r]; its key is (c, t, node holding position
+         s + S_t - 1, s).  A key seen before adds a reference, otherwise a
+         fresh page is taken and the key registered.  A failed call leaves the
+         pool exactly as it was.
+R-plan   items (r, h, tier, t0, t1, slot) in order r, h, tier (INT8 first),
+         t0 = 0, chunk, 2*chunk, ...; slot is the natural index; part_off is the
+         CSR of slots per (r, h).  With lpt, items are stably sorted by
+         descending cost (t1 - t0) * (2 for bf16, 1 for INT8).
+
+Pinned by: tests/test_oracle_planner.py (hand-worked golden tables, the
+worked radix example's consistent block counts, a second allocator written
+over a sorted free list, and the invariants the rules imply).
+"""
+from __future__ import annotations
+
+import heapq
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence, Tuple
+
+TIER_I8 = 0
+TIER_BF = 1
+PPM = 1_000_000
+
+
+class OracleError(Exception):
+    def __init__(self, code: str, msg: str = ""):
+        super().__init__(f"{code}: {msg}")
+        self.code = code
+
+
+def _ceil_div(a: int, b: int) -> int:
+    return -((-a) // b)
+
+
+# ---------------------------------------------------------------- budgets
+def ratio_ppm(k: int, H: int, hi: int, lo: int) -> int:
+    """Retention ratio (ppm) of the head at importance rank ``k`` (R-rank)."""
+    if H == 1:
+        return hi
+    return hi - ((hi - lo) * k) // (H - 1)
+
+
+@dataclass
+class Reservation:
+    budget: List[List[int]]          # [B][H]
+    L: List[List[int]]               # [B][H]
+    n_i8: List[List[int]]            # [B][H]
+    n_bf: List[List[int]]            # [B][H]
+    cluster_of_head: List[int]       # [H]
+    slot_in_cluster: List[int]       # [H]
+    cluster_size: List[int]          # [C]
+
+
+def reserve(head_rank: Sequence[int], ratio_hi_ppm: int, ratio_lo_ppm: int,
+            n_clusters: int, recent_ppm: int, quant_block: int,
+            n_comp: Sequence[int], n_fixed: Optional[Sequence[int]] = None,
+            budget_override: Optional[Sequence[int]] = None) -> Reservation:
+    """Budget reservation, clustering and tier split for a batch (R-rank,
+    R-round, R-clust, R-tier)."""
+    H = len(head_rank)
+    B = len(n_comp)
+    rank = [int(x) for x in head_rank]
+    if sorted(rank) != list(range(H)):
+        raise OracleError("EINVAL", "head_rank is not a permutation")
+    if not (0 < ratio_lo_ppm <= ratio_hi_ppm <= PPM):
+        raise OracleError("EINVAL", "ratio bounds")
+    if not (1 <= n_clusters <= H):
+        raise OracleError("EINVAL", "n_clusters")
+    if not (0 <= recent_ppm <= PPM) or quant_block < 1:
+        raise OracleError("EINVAL", "tier parameters")
+    nf = [0] * B if n_fixed is None else [int(x) for x in n_fixed]
+    budget, L = [], []
+    for r in range(B):
+        n = int(n_comp[r])
+        if n < 1 or nf[r] < 0:
+            raise OracleError("EINVAL", "lengths")
+        row = []
+        for h in range(H):
+            if budget_override is not None:
+                b = int(budget_override[r * H + h])
+                if not (1 <= b <= n):
+                    raise OracleError("EINVAL", "override out of range")
+            else:
+                b = _ceil_div(ratio_ppm(rank[h], H, ratio_hi_ppm, ratio_lo_ppm) * n, PPM)
+                b = min(max(b, 1), n)
+            row.append(b)
+        budget.append(row)
+        L.append([nf[r] + b for b in row])
+
+    order = sorted(range(H), key=lambda h: rank[h])
+    sizes = [(H + n_clusters - 1) // n_clusters if c < H % n_clusters else H // n_clusters
+             for c in range(n_clusters)]
+    coh, sic = [0] * H, [0] * H
+    pos = 0
+    for c, sz in enumerate(sizes):
+        for s in range(sz):
+            coh[order[pos]] = c
+            sic[order[pos]] = s
+            pos += 1
+
+    n_i8, n_bf = [], []
+    for r in range(B):
+        ri, rb = [], []
+        for h in range(H):
+            l = L[r][h]
+            old = l - _ceil_div(l * recent_ppm, PPM)
+            i8 = (old // quant_block) * quant_block
+            ri.append(i8)
+            rb.append(l - i8)
+        n_i8.append(ri)
+        n_bf.append(rb)
+    return Reservation(budget, L, n_i8, n_bf, coh, sic, sizes)
+
+
+# ---------------------------------------------------------------- pages
+def heads_of_cluster(res: Reservation, c: int) -> List[int]:
+    hs = [h for h in range(len(res.cluster_of_head)) if res.cluster_of_head[h] == c]
+    return sorted(hs, key=lambda h: res.slot_in_cluster[h])
+
+
+def page_counts(res: Reservation, page_size: int, quant_block: int) -> List[List[List[int]]]:
+    """np[r][c][t] -- pages of row r in the (cluster c, tier t) table (R-page)."""
+    B = len(res.L)
+    C = len(res.cluster_size)
+    out = []
+    for r in range(B):
+        rc = []
+        for c in range(C):
+            hs = heads_of_cluster(res, c)
+            i8 = max(res.n_i8[r][h] for h in hs)
+            bf = max(res.n_bf[r][h] for h in hs)
+            assert i8 % quant_block == 0
+            rc.append([i8 // quant_block, _ceil_div(bf, page_size)])
+        out.append(rc)
+    return out
+
+
+def _node_at(path: Sequence[int], node_len: Sequence[int], pos: int) -> int:
+    acc = 0
+    for nid in path:
+        acc += int(node_len[nid])
+        if pos < acc:
+            return nid
+    raise AssertionError("position beyond shared path")
+
+
+def share_key(res: Reservation, r: int, c: int, t: int, j: int, page_size: int,
+              quant_block: int, n_fixed: Sequence[int],
+              paths: Optional[Sequence[Sequence[int]]],
+              node_len: Optional[Sequence[int]]):
+    """Registry key of page j of row (r, c, t), or None if the page is private
+    (R-alloc)."""
+    if paths is None:
+        return None
+    S = quant_block if t == TIER_I8 else page_size
+    starts = set()
+    for h in heads_of_cluster(res, c):
+        starts.add(j * S if t == TIER_I8 else res.n_i8[r][h] + j * S)
+    if len(starts) != 1:
+        return None
+    s = starts.pop()
+    if s + S > int(n_fixed[r]):
+        return None
+    return (c, t, _node_at(paths[r], node_len, s + S - 1), s)
+
+
+class Pool:
+    """Refcounted page pools, one per (cluster, tier), lowest free id first.
+
+    Free ids are the freed ids (a min-heap) plus every id at or above the
+    high-water mark ``top``; the lowest free id is the smaller of the two.
+    """
+
+    def __init__(self, pages_bf: Sequence[int], pages_i8: Sequence[int]):
+        C = len(pages_bf)
+        self.cap = [[int(pages_i8[c]), int(pages_bf[c])] for c in range(C)]
+        self.ref = [[{} for _ in range(2)] for _ in range(C)]
+        self.heap = [[[] for _ in range(2)] for _ in range(C)]
+        self.top = [[0, 0] for _ in range(C)]
+        self.registry: Dict[tuple, int] = {}
+        self.key_of: Dict[Tuple[int, int, int], tuple] = {}
+
+    def _snapshot(self):
+        return ([[dict(x) for x in rc] for rc in self.ref],
+                [[list(x) for x in rc] for rc in self.heap],
+                [list(x) for x in self.top],
+                dict(self.registry), dict(self.key_of))
+
+    def _restore(self, snap):
+        self.ref, self.heap, self.top, self.registry, self.key_of = snap
+
+    def alloc(self, c: int, t: int) -> int:
+        h = self.heap[c][t]
+        if h:
+            pid = heapq.heappop(h)
+        elif self.top[c][t] < self.cap[c][t]:
+            pid = self.top[c][t]
+            self.top[c][t] += 1
+        else:
+            raise OracleError("ENOMEM", f"pool (c={c}, t={t}) exhausted")
+        assert self.ref[c][t].get(pid, 0) == 0
+        self.ref[c][t][pid] = 1
+        return pid
+
+    def unref(self, c: int, t: int, pid: int):
+        self.ref[c][t][pid] -= 1
+        if self.ref[c][t][pid] == 0:
+            del self.ref[c][t][pid]
+            heapq.heappush(self.heap[c][t], pid)
+            key = self.key_of.pop((c, t, pid), None)
+            if key is not None:
+                del self.registry[key]
+
+    def refcount(self, c: int, t: int, pid: int) -> int:
+        return self.ref[c][t].get(pid, 0)
+
+    def free_pages(self, c: int, t: int) -> int:
+        return self.cap[c][t] - len(self.ref[c][t])
+
+
+@dataclass
+class Tables:
+    bt: List[List[List[List[int]]]]   # bt[c][t][r][j], padded with -1
+    stride: List[List[int]]           # stride[c][t]
+    lens: List[List[Tuple[int, int]]]  # [r][h] -> (n_i8, n_bf)
+    work: List[Tuple[int, int, int, int, int, int]]
+    part_off: List[int]
+    pages: List[List[List[List[int]]]] = field(default_factory=list)  # [r][c][t] -> ids
+
+
+def allocate(pool: Pool, res: Reservation, page_size: int, quant_block: int,
+             n_fixed: Optional[Sequence[int]] = None,
+             paths: Optional[Sequence[Sequence[int]]] = None,
+             node_len: Optional[Sequence[int]] = None) -> List[List[List[List[int]]]]:
+    """Allocate every page of every row, all or nothing (R-alloc)."""
+    B = len(res.L)
+    C = len(res.cluster_size)
+    nf = [0] * B if n_fixed is None else list(n_fixed)
+    counts = page_counts(res, page_size, quant_block)
+    snap = pool._snapshot()
+    try:
+        out = []
+        for r in range(B):
+            rc = []
+            for c in range(C):
+                rt = [None, None]
+                for t in (TIER_I8, TIER_BF):
+                    ids = []
+                    for j in range(counts[r][c][t]):
+                        key = share_key(res, r, c, t, j, page_size, quant_block, nf, paths, node_len)
+                        if key is not None and key in pool.registry:
+                            pid = pool.registry[key]
+                            pool.ref[c][t][pid] += 1
+                        else:
+                            pid = pool.alloc(c, t)
+                            if key is not None:
+                                pool.registry[key] = pid
+                                pool.key_of[(c, t, pid)] = key
+                        ids.append(pid)
+                    rt[t] = ids
+                rc.append(rt)
+            out.append(rc)
+        return out
+    except OracleError:
+        pool._restore(snap)
+        raise
+
+
+def pages_needed(res: Reservation, page_size: int, quant_block: int,
+                 n_fixed=None, paths=None, node_len=None) -> Tuple[List[int], List[int]]:
+    """Pages an empty pool must hold for this batch: (bf16[C], INT8[C])."""
+    C = len(res.cluster_size)
+    big = [10 ** 9] * C
+    p = Pool(big, big)
+    allocate(p, res, page_size, quant_block, n_fixed, paths, node_len)
+    bf = [p.cap[c][TIER_BF] - p.free_pages(c, TIER_BF) for c in range(C)]
+    i8 = [p.cap[c][TIER_I8] - p.free_pages(c, TIER_I8) for c in range(C)]
+    return bf, i8
+
+
+def release(pool: Pool, pages_of_request: List[List[List[int]]]):
+    """Drop request r's references (R-alloc): pages reaching zero are freed
+    and their registry keys removed."""
+    for c, rt in enumerate(pages_of_request):
+        for t in (TIER_I8, TIER_BF):
+            for pid in rt[t]:
+                pool.unref(c, t, pid)
+
+
+# ---------------------------------------------------------------- tables & plan
+def plan(res: Reservation, chunk_bf: int, chunk_i8: int, lpt: bool):
+    """Split plan and partial CSR (R-plan)."""
+    B = len(res.L)
+    H = len(res.cluster_of_head)
+    work = []
+    part_off = []
+    for r in range(B):
+        for h in range(H):
+            part_off.append(len(work))
+            for t, n, ch in ((TIER_I8, res.n_i8[r][h], chunk_i8), (TIER_BF, res.n_bf[r][h], chunk_bf)):
+                for t0 in range(0, n, ch):
+                    work.append((r, h, t, t0, min(t0 + ch, n), len(work)))
+    part_off.append(len(work))
+    if lpt:
+        work = sorted(work, key=lambda it: -(it[4] - it[3]) * (2 if it[2] == TIER_BF else 1))
+    return work, part_off
+
+
+def build_tables(pool: Pool, res: Reservation, page_size: int, quant_block: int,
+                 chunk_bf: int, chunk_i8: int, lpt: bool,
+                 n_fixed=None, paths=None, node_len=None) -> Tables:
+    """Allocate pages and emit block tables, lengths and the plan (R-alloc,
+    R-page, R-plan)."""
+    if chunk_bf < page_size or chunk_bf % page_size or chunk_i8 < quant_block or chunk_i8 % quant_block:
+        raise OracleError("EINVAL", "chunk sizes")
+    B = len(res.L)
+    C = len(res.cluster_size)
+    H = len(res.cluster_of_head)
+    pages = allocate(pool, res, page_size, quant_block, n_fixed, paths, node_len)
+    stride = [[max(len(pages[r][c][t]) for r in range(B)) for t in range(2)] for c in range(C)]
+    bt = [[[pages[r][c][t] + [-1] * (stride[c][t] - len(pages[r][c][t])) for r in range(B)]
+           for t in range(2)] for c in range(C)]
+    lens = [[(res.n_i8[r][h], res.n_bf[r][h]) for h in range(H)] for r in range(B)]
+    work, part_off = plan(res, chunk_bf, chunk_i8, lpt)
+    return Tables(bt, stride, lens, work, part_off, pages)

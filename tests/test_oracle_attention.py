@@ -1,0 +1,162 @@
+"""Pins for the fp64 attention oracle (oracle/attention.py) against facts the
+mathematics fixes: a library SDPA on dense tensors, closed forms, brute force
+with math.fsum, invariances, INT8/bf16 equivalence, and split invariance of
+the log-sum-exp merge."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from oracle import planner as P
+from oracle import quant
+from workloads import make_workload
+
+
+def _sdpa_dense(w, res):
+    """torch fp64 scaled_dot_product_attention over the full logical rows."""
+    q = torch.from_numpy(A.q_f64(w))
+    G = w.Hq // w.Hkv
+    out = np.zeros((w.B, w.Hq, w.d))
+    for r in range(w.B):
+        Ks, Vs = [], []
+        for h in range(w.Hkv):
+            K16, V16 = w.logical_kv(r, h, res.L[r][h])
+            Ks.append(torch.from_numpy(A.bf16_to_f64(K16)))
+            Vs.append(torch.from_numpy(A.bf16_to_f64(V16)))
+        K = torch.stack(Ks).repeat_interleave(G, dim=0)      # [Hq, L, d]
+        V = torch.stack(Vs).repeat_interleave(G, dim=0)
+        o = torch.nn.functional.scaled_dot_product_attention(q[r][:, None, :], K, V)
+        out[r] = o[:, 0, :].numpy()
+    return out
+
+
+@pytest.mark.parametrize("name,over", [
+    ("tiny", dict(budget=None, n_clusters=1)),
+    ("llama8b", dict(B=2, ctx=("uniform", 200, 500), ratio_ppm=(1_000_000, 1_000_000), n_clusters=1)),
+])
+def test_uniform_budgets_equal_dense_sdpa(name, over):
+    w = make_workload(name, **over)
+    res = A.reserve_for(w)
+    assert all(res.L[r][h] == int(w.n_comp[r]) for r in range(w.B) for h in range(w.Hkv))
+    o = A.decode(w, res)
+    ref = _sdpa_dense(w, res)
+    assert np.max(np.abs(o - ref)) < 1e-12
+
+
+def test_single_row_returns_its_value_row():
+    g = np.random.default_rng(0)
+    q = g.standard_normal((4, 64))
+    K = g.standard_normal((1, 64))
+    V = g.standard_normal((1, 64))
+    o = A.attend(q, K, V, 0.125)
+    assert np.array_equal(o, np.repeat(V, 4, axis=0))
+
+
+def test_closed_forms():
+    g = np.random.default_rng(1)
+    d = 32
+    V = g.standard_normal((50, d))
+    q = g.standard_normal((2, d))
+    # all keys equal -> plain mean of V
+    K = np.repeat(g.standard_normal((1, d)), 50, axis=0)
+    assert np.allclose(A.attend(q, K, V, 0.3), V.mean(axis=0)[None], atol=1e-14, rtol=0)
+    # zero query -> plain mean of V
+    assert np.allclose(A.attend(np.zeros((1, d)), g.standard_normal((50, d)), V, 0.3),
+                       V.mean(axis=0)[None], atol=1e-14, rtol=0)
+    # all values equal -> that value
+    c = g.standard_normal(d)
+    assert np.allclose(A.attend(q, g.standard_normal((50, d)), np.tile(c, (50, 1)), 0.3), c[None], atol=1e-14)
+    # two rows whose scores differ by ln 3 -> weights 3/4 and 1/4
+    qq = np.zeros((1, d)); qq[0, 0] = math.sqrt(d)
+    KK = np.zeros((2, d)); KK[0, 0] = math.log(3.0)
+    VV = g.standard_normal((2, d))
+    assert np.allclose(A.attend(qq, KK, VV, 1 / math.sqrt(d)), 0.75 * VV[0] + 0.25 * VV[1], atol=1e-15)
+
+
+def test_matches_pure_python_brute_force():
+    g = np.random.default_rng(2)
+    for L, d, G in [(1, 4, 1), (7, 8, 2), (64, 16, 4), (33, 5, 3)]:
+        q = g.standard_normal((G, d))
+        K = g.standard_normal((L, d))
+        V = g.standard_normal((L, d))
+        sc = 1 / math.sqrt(d)
+        o = A.attend(q, K, V, sc)
+        for gi in range(G):
+            s = [math.fsum(q[gi, i] * K[t, i] for i in range(d)) * sc for t in range(L)]
+            m = max(s)
+            e = [math.exp(x - m) for x in s]
+            z = math.fsum(e)
+            for i in range(d):
+                ref = math.fsum(e[t] * V[t, i] for t in range(L)) / z
+                assert abs(o[gi, i] - ref) < 1e-12
+
+
+def test_row_order_invariance():
+    g = np.random.default_rng(3)
+    q = g.standard_normal((4, 64))
+    K = g.standard_normal((300, 64))
+    V = g.standard_normal((300, 64))
+    perm = g.permutation(300)
+    assert np.max(np.abs(A.attend(q, K, V, 0.125) - A.attend(q, K[perm], V[perm], 0.125))) < 1e-13
+
+
+def test_lse_merge_split_invariance():
+    g = np.random.default_rng(4)
+    q = g.standard_normal((4, 32))
+    K = 3 * g.standard_normal((500, 32))
+    V = g.standard_normal((500, 32))
+    full = A.attend(q, K, V, 0.2)
+    for cuts in ([250], [1, 2, 3, 499], sorted(g.choice(np.arange(1, 500), 17, replace=False))):
+        b = [0, *cuts, 500]
+        parts = [A.partial(q, K[b[i]:b[i + 1]], V[b[i]:b[i + 1]], 0.2) for i in range(len(b) - 1)]
+        m = np.stack([p[0] for p in parts]); l = np.stack([p[1] for p in parts])
+        acc = np.stack([p[2] for p in parts])
+        assert np.max(np.abs(A.lse_merge(m, l, acc) - full)) < 1e-12
+
+
+def test_int8_rows_equal_attention_over_same_bf16_values():
+    # rows that are integer multiples of 2^-5 with absmax 127*2^-5 per channel
+    # quantise exactly, so the INT8 tier must give the bf16 result
+    g = np.random.default_rng(5)
+    k = g.integers(-127, 128, size=(128, 64)); k[0] = 127; k[64] = -127
+    v = g.integers(-127, 128, size=(128, 64)); v[3] = 127; v[70] = 127
+    Kx = (k * 2.0 ** -5).astype(np.float32)
+    Vx = (v * 2.0 ** -5).astype(np.float32)
+    qk, sk = quant.quantize_rows(Kx, 64)
+    qv, sv = quant.quantize_rows(Vx, 64)
+    q = g.standard_normal((4, 64))
+    a = A.attend(q, quant.dequantize_rows(qk, sk, 64), quant.dequantize_rows(qv, sv, 64), 0.125)
+    b = A.attend(q, Kx.astype(np.float64), Vx.astype(np.float64), 0.125)
+    assert np.max(np.abs(a - b)) < 1e-12
+
+
+def test_workload_tier_rows_oldest_quantised_newest_exact():
+    w = make_workload("tiered", B=1, Hkv=2, Hq=4, ctx=("fixed", 1000))
+    res = A.reserve_for(w)
+    n8 = res.n_i8[0][1]
+    assert n8 == 832 and res.n_bf[0][1] == 168
+    K, V = A.head_rows(w, res, 0, 1)
+    K16, V16 = w.logical_kv(0, 1, res.L[0][1])
+    Kb, Vb = A.bf16_to_f64(K16), A.bf16_to_f64(V16)
+    assert np.array_equal(K[n8:], Kb[n8:]) and np.array_equal(V[n8:], Vb[n8:])
+    for X, Xb in ((K, Kb), (V, Vb)):
+        for blk in range(n8 // 64):
+            sl = slice(64 * blk, 64 * blk + 64)
+            step = np.abs(Xb[sl]).max(axis=0) / 127
+            assert np.all(np.abs(X[sl] - Xb[sl]) <= step * (0.5 + 2.0 ** -10) + 1e-30)
+        assert not np.array_equal(X[:n8], Xb[:n8])
+
+
+def test_gqa_mapping_and_scale_default():
+    # each q-head reads its own KV-head (hq // G), with scale 1/sqrt(d)
+    w = make_workload("llama8b", B=1, ctx=("uniform", 64, 64), ratio_ppm=(1_000_000, 1_000_000), n_clusters=1)
+    res = A.reserve_for(w)
+    q = A.q_f64(w)
+    o = A.decode(w, res)
+    for hq in (0, 3, 4, 31):
+        h = hq // 4
+        K16, V16 = w.logical_kv(0, h, 64)
+        ref = A.attend(q[0, hq:hq + 1], A.bf16_to_f64(K16), A.bf16_to_f64(V16), 1 / math.sqrt(128))
+        assert np.max(np.abs(o[0, hq] - ref[0])) < 1e-14

@@ -1,0 +1,274 @@
+"""Pins for the integer oracle (oracle/planner.py), independent of its code:
+hand-worked golden tables, the radix lesson's printed block counts, a second
+allocator built on a sorted free list, and invariants the rules imply."""
+import bisect
+import json
+import os
+import random
+
+import pytest
+
+from oracle import planner as P
+from workloads import make_workload
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def test_hand_worked_budgets_clusters_tables_plan():
+    g = _gold("planner_hand.json")["case_budgets"]
+    res = P.reserve(g["head_rank"], g["ratio_hi_ppm"], g["ratio_lo_ppm"], g["n_clusters"],
+                    g["recent_ppm"], g["quant_block"], g["n_comp"])
+    assert res.budget == g["expect_budget"]
+    assert res.cluster_of_head == g["expect_cluster_of_head"]
+    assert res.slot_in_cluster == g["expect_slot_in_cluster"]
+    assert res.cluster_size == g["expect_cluster_size"]
+    pool = P.Pool([16, 16], [0, 0])
+    t = P.build_tables(pool, res, g["page_size"], g["quant_block"], g["chunk_bf"], g["chunk_i8"], False)
+    assert t.bt[0][P.TIER_BF] == g["expect_bt_c0_bf"]
+    assert t.bt[1][P.TIER_BF] == g["expect_bt_c1_bf"]
+    assert [list(w) for w in t.work] == g["expect_work"]
+    assert t.part_off == g["expect_part_off"]
+    work_lpt, off2 = P.plan(res, g["chunk_bf"], g["chunk_i8"], True)
+    assert [w[5] for w in work_lpt] == g["expect_lpt_slots"]
+    assert off2 == g["expect_part_off"]
+
+
+def test_hand_worked_tier_split():
+    g = _gold("planner_hand.json")["case_tiers"]
+    res = P.reserve([0], 1_000_000, 1_000_000, 1, g["recent_ppm"], g["quant_block"],
+                    [1] * len(g["L"]), [x - 1 for x in g["L"]])
+    assert [row[0] for row in res.L] == g["L"]
+    assert [row[0] for row in res.n_i8] == g["expect_n_i8"]
+    assert [row[0] for row in res.n_bf] == g["expect_n_bf"]
+
+
+def test_tiered_128k_split_matches_workload_statement():
+    g = _gold("planner_hand.json")["case_ttkv_128k"]
+    res = P.reserve([0], 1_000_000, 1_000_000, 1, g["recent_ppm"], g["quant_block"], [g["L"]])
+    assert res.n_i8[0][0] == g["expect_n_i8"] and res.n_bf[0][0] == g["expect_n_bf"]
+    # newest 12.5% exactly, and the INT8 part is whole 64-token blocks
+    assert res.n_bf[0][0] * 8 == g["L"] and res.n_i8[0][0] % 64 == 0
+
+
+def _share_case():
+    g = _gold("planner_hand.json")["case_share"]
+    B = len(g["paths"])
+    n_fixed = [sum(g["node_len"][n] for n in p) for p in g["paths"]]
+    res = P.reserve([0, 1], 1_000_000, 1_000_000, 1, 1_000_000, g["quant_block"], g["n_comp"],
+                    n_fixed, g["budget_override"])
+    return g, res, n_fixed
+
+
+def test_hand_worked_sharing_and_release():
+    g, res, n_fixed = _share_case()
+    assert res.L == g["expect_L"]
+    need_bf, need_i8 = P.pages_needed(res, g["page_size"], g["quant_block"], n_fixed, g["paths"], g["node_len"])
+    assert need_bf == [g["expect_pages_needed"]] and need_i8 == [0]
+    pool = P.Pool([need_bf[0]], [0])
+    t = P.build_tables(pool, res, g["page_size"], g["quant_block"], 4, 8, False, n_fixed, g["paths"], g["node_len"])
+    assert t.bt[0][P.TIER_BF] == g["expect_bt"]
+    for pid, cnt in g["expect_refcount"].items():
+        assert pool.refcount(0, P.TIER_BF, int(pid)) == cnt
+    P.release(pool, t.pages[0])
+    a = g["after_release_r0_new_request"]
+    res2 = P.reserve([0, 1], 1_000_000, 1_000_000, 1, 1_000_000, g["quant_block"], [a["n_comp"]],
+                     [n_fixed[0]], a["budget"])
+    pages = P.allocate(pool, res2, g["page_size"], g["quant_block"], [n_fixed[0]], [a["path"]], g["node_len"])
+    assert pages[0][0][P.TIER_BF] == a["expect_pages"]
+
+
+def test_enomem_rolls_back_completely():
+    g, res, n_fixed = _share_case()
+    pool = P.Pool([g["expect_pages_needed"] - 1], [0])
+    before = pool._snapshot()
+    with pytest.raises(P.OracleError) as e:
+        P.build_tables(pool, res, g["page_size"], g["quant_block"], 4, 8, False, n_fixed, g["paths"], g["node_len"])
+    assert e.value.code == "ENOMEM"
+    assert pool._snapshot() == before
+
+
+def test_radix_lesson_block_counts():
+    g = _gold("radix_blocks.json")
+    ps = g["page_size"]
+    for e in g["blocks_to_hold"]:
+        if not e["consistent"]:
+            continue
+        res = P.reserve([0], 1_000_000, 1_000_000, 1, 1_000_000, 64, [e["tokens"]])
+        assert P.page_counts(res, ps, 64)[0][0][P.TIER_BF] == e["blocks"], e
+    # whole pages of a page-aligned 500-token branch are the shared ones
+    e = g["full_blocks_reused"][0]
+    node_len = [2000, 500]
+    res = P.reserve([0], 1_000_000, 1_000_000, 1, 1_000_000, 64, [30], [2500])
+    shared = [j for j in range(P.page_counts(res, ps, 64)[0][0][P.TIER_BF])
+              if P.share_key(res, 0, 0, P.TIER_BF, j, ps, 64, [2500], [[0, 1]], node_len) is not None]
+    branch = [j for j in shared
+              if P.share_key(res, 0, 0, P.TIER_BF, j, ps, 64, [2500], [[0, 1]], node_len)[2] == 1]
+    assert len(branch) == e["blocks"]
+    assert len(shared) - len(branch) == 2000 // ps
+
+
+# ---------------------------------------------------------------- brute-force allocator
+class SortedListPool:
+    """Second allocator: a sorted Python list of free ids (bisect), refcount dict."""
+
+    def __init__(self, cap):
+        self.free = list(range(cap))
+        self.ref = {}
+        self.reg = {}
+        self.key_of = {}
+
+    def take(self, key):
+        if key is not None and key in self.reg:
+            pid = self.reg[key]
+            self.ref[pid] += 1
+            return pid
+        pid = self.free.pop(0)
+        self.ref[pid] = 1
+        if key is not None:
+            self.reg[key] = pid
+            self.key_of[pid] = key
+        return pid
+
+    def drop(self, pid):
+        self.ref[pid] -= 1
+        if self.ref[pid] == 0:
+            del self.ref[pid]
+            bisect.insort(self.free, pid)
+            k = self.key_of.pop(pid, None)
+            if k is not None:
+                del self.reg[k]
+
+
+def test_allocator_matches_sorted_list_allocator_under_churn():
+    rnd = random.Random(1234)
+    node_len = [5, 3, 7, 2]
+    ps = 4
+    oracle_pool = P.Pool([400], [0])
+    ref_pool = SortedListPool(400)
+    live = []
+    for step in range(60):
+        if live and rnd.random() < 0.4:
+            idx = rnd.randrange(len(live))
+            pages_o, pages_r = live.pop(idx)
+            P.release(oracle_pool, pages_o)
+            for pid in pages_r:
+                ref_pool.drop(pid)
+            continue
+        path = [0, rnd.choice([1, 2, 3])]
+        nf = sum(node_len[n] for n in path)
+        ncomp = rnd.randint(1, 9)
+        b = [rnd.randint(1, ncomp), rnd.randint(1, ncomp)]
+        res = P.reserve([0, 1], 1_000_000, 1_000_000, 1, 1_000_000, 8, [ncomp], [nf], b)
+        pages = P.allocate(oracle_pool, res, ps, 8, [nf], [path], node_len)
+        npg = -(-max(res.L[0]) // ps)
+        expect = []
+        for j in range(npg):
+            key = None
+            if j * ps + ps <= nf:
+                acc, node = 0, None
+                for n in path:
+                    acc += node_len[n]
+                    if j * ps + ps - 1 < acc:
+                        node = n
+                        break
+                key = (node, j * ps)
+            expect.append(ref_pool.take(key))
+        assert pages[0][0][P.TIER_BF] == expect
+        live.append((pages[0], expect))
+
+
+# ---------------------------------------------------------------- invariants
+def _small(name):
+    over = {"tiny": {}, "llama8b": dict(B=6, ctx=("uniform", 300, 1200)),
+            "ragged": dict(B=8, ctx=("loguniform", 100, 3000)),
+            "tiered": dict(B=2, ctx=("fixed", 4000)),
+            "radix": dict(B=12, share=dict(prefix=200, branch=50, n_branches=4, suffix=(8, 100)))}[name]
+    return make_workload(name, **over)
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama8b", "ragged", "tiered", "radix"])
+def test_invariants(name):
+    w = _small(name)
+    res = P.reserve(w.head_rank, w.ratio_hi_ppm, w.ratio_lo_ppm, w.n_clusters, w.recent_ppm,
+                    w.quant_block, w.n_comp, w.n_fixed, w.budget_override)
+    H, B = w.Hkv, w.B
+    # budgets: bounded by the ratio band, non-increasing in rank
+    for r in range(B):
+        n = int(w.n_comp[r])
+        for h in range(H):
+            b = res.budget[r][h]
+            assert 1 <= b <= n
+            assert res.L[r][h] == b + int(w.n_fixed[r])
+            if w.budget_override is None:
+                assert -(-w.ratio_lo_ppm * n // 10**6) <= b <= -(-w.ratio_hi_ppm * n // 10**6)
+        if w.budget_override is None:
+            by_rank = [res.budget[r][h] for h in sorted(range(H), key=lambda h: w.head_rank[h])]
+            assert by_rank == sorted(by_rank, reverse=True)
+    # clusters: sizes sum to H, contiguous in rank, sizes differ by <= 1
+    assert sum(res.cluster_size) == H and max(res.cluster_size) - min(res.cluster_size) <= 1
+    order = sorted(range(H), key=lambda h: w.head_rank[h])
+    assert [res.cluster_of_head[h] for h in order] == sorted(res.cluster_of_head)
+    # tiers: INT8 part whole blocks, recent share kept in bf16
+    for r in range(B):
+        for h in range(H):
+            assert res.n_i8[r][h] % w.quant_block == 0
+            assert res.n_i8[r][h] + res.n_bf[r][h] == res.L[r][h]
+            assert res.n_bf[r][h] * 10**6 >= res.L[r][h] * w.recent_ppm
+    share = None if w.paths is None else (w.n_fixed, w.paths, w.node_len)
+    need_bf, need_i8 = P.pages_needed(res, w.page_size, w.quant_block, *(share or ()))
+    pool = P.Pool(need_bf, need_i8)
+    t = P.build_tables(pool, res, w.page_size, w.quant_block, 4 * w.page_size, 2 * w.quant_block, True,
+                       *(share or ()))
+    # pool sized exactly: full afterwards; refcounts equal the number of referencing rows
+    for c in range(w.n_clusters):
+        for tt in (0, 1):
+            assert pool.free_pages(c, tt) == 0
+            counts = {}
+            for r in range(B):
+                for pid in t.pages[r][c][tt]:
+                    counts[pid] = counts.get(pid, 0) + 1
+            for pid, cnt in counts.items():
+                assert pool.refcount(c, tt, pid) == cnt
+                if cnt > 1:
+                    assert (c, tt, pid) in pool.key_of
+    # plan tiles every tier range exactly once; part_off is the CSR of slots
+    seen = {}
+    for (r, h, tier, t0, t1, slot) in t.work:
+        assert 0 <= t0 < t1
+        seen.setdefault((r, h, tier), []).append((t0, t1))
+        assert t.part_off[r * H + h] <= slot < t.part_off[r * H + h + 1]
+    assert sorted(s[5] for s in t.work) == list(range(len(t.work)))
+    for r in range(B):
+        for h in range(H):
+            for tier, n in ((0, res.n_i8[r][h]), (1, res.n_bf[r][h])):
+                iv = sorted(seen.get((r, h, tier), []))
+                pos = 0
+                for a, b in iv:
+                    assert a == pos
+                    pos = b
+                assert pos == n
+    # releasing everything restores an empty pool
+    for r in range(B):
+        P.release(pool, t.pages[r])
+    for c in range(w.n_clusters):
+        for tt in (0, 1):
+            assert pool.free_pages(c, tt) == pool.cap[c][tt]
+    assert not pool.registry
+
+
+def test_rejects_bad_admission_inputs():
+    with pytest.raises(P.OracleError):
+        P.reserve([0, 0], 10, 10, 1, 10**6, 64, [5])
+    with pytest.raises(P.OracleError):
+        P.reserve([0, 1], 10, 20, 1, 10**6, 64, [5])
+    with pytest.raises(P.OracleError):
+        P.reserve([0, 1], 10, 10, 3, 10**6, 64, [5])
+    with pytest.raises(P.OracleError):
+        P.reserve([0, 1], 10, 10, 1, 10**6, 64, [0])
+    with pytest.raises(P.OracleError):
+        P.reserve([0, 1], 10, 10, 1, 10**6, 64, [5], None, [1, 6])
