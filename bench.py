@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark: effective KV GB/s of one ragged-paged decode step on one GPU.
+
+    python bench.py [--steps K] [--warmup W] [--config llama8b]
+
+One step = the whole decode hot path over one batch: the split-K kernel over
+every plan item (bf16 pages and INT8 blocks) and the log-sum-exp merge, on a
+cache that is already resident in HBM.  Before every timed step a 1 GiB
+device write evicts L2 and the 256 MB last-level cache (outside the timed
+events).  Each step is bracketed by HIP events on the stream the kernels run
+on; the K steps together are bracketed by device synchronisation.
+
+Prints one JSON line (see the ``result`` dict at the end).  ``--gpus`` above 1
+is refused: this build measures one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+METRIC = "effective KV GB/s (and % of HBM peak) in ragged-paged decode attention"
+DESCRIPTIONS = {
+    "tiny": "tiny: 2 requests, 4/2 heads, d 64, ctx 256, budgets in {32..256}, 2 clusters",
+    "llama8b": "Llama-3-8B-shaped layer: batch 64, 32/8 heads, d 128, ctx U[4096,16384], ratio 0.50->0.10 by head rank, 2 clusters, page 16, bf16",
+    "ragged": "high raggedness: batch 256, 32/8 heads, d 128, ctx log-U[2048,32768], ratio 0.60->0.05, 8 clusters, 1% K outlier channels x8",
+    "tiered": "TTKV tiered: batch 4, ctx 131072, 32/8 heads, d 128, newest 12.5% bf16, rest INT8 64-token blocks",
+    "radix": "prefix-shared radix: batch 256, 2000-token prefix + 1 of 4 500-token branches + 80..1000 suffix, ratio 0.60->0.20 on suffix",
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_traffic.txt")
+KERNEL_SRC = os.path.join(ROOT, "non_uniform_paged_amd", "csrc", "tg_decode.hip")
+
+
+def _kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic_record(config: str):
+    """HBM bytes per split launch from the committed rocprofv3 counter runs,
+    or None when absent or taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    if rec.get("kernel_source_sha256_16") != _kernel_hash() or rec.get("workload") != config:
+        return None
+    try:
+        return float(rec["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, prep, budget_s: float = 12.0):
+    """The oracle, untuned, on this host: fp64 attention of sampled (r, h)
+    pairs from their raw rows (row generation excluded from the time)."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    from oracle import attention as A
+
+    res = A.reserve_for(w)
+    q = A.q_f64(w)
+    G = w.Hq // w.Hkv
+    scale = 1.0 / math.sqrt(w.d)
+    order = np.random.default_rng(7).permutation(w.B * w.Hkv)
+    gpu_out = prep.output()
+    spent = 0.0
+    nbytes = 0
+    done = 0
+    worst = 0.0
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    try:
+        for i in order:
+            r, h = divmod(int(i), w.Hkv)
+            K16, V16 = w.logical_kv(r, h, res.L[r][h])
+            t0 = time.perf_counter()
+            o = A.decode_rows(q[r, h * G:(h + 1) * G], K16, V16, res.n_i8[r][h], w.quant_block, scale)
+            spent += time.perf_counter() - t0
+            n8, nb = res.n_i8[r][h], res.n_bf[r][h]
+            nbytes += nb * 4 * w.d + n8 * 2 * w.d + (n8 // w.quant_block) * 4 * w.d
+            worst = max(worst, float(np.abs(gpu_out[r, h * G:(h + 1) * G] - o).max()))
+            done += 1
+            if spent > budget_s:
+                break
+    finally:
+        if ctx is not None:
+            ctx.unregister() if hasattr(ctx, "unregister") else None
+    return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {w.B * w.Hkv} (request, KV-head) pairs of the same step, fp64 numpy, "
+                      f"1 BLAS thread, {spent:.1f} s", "max_abs_err_vs_gpu": worst}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="llama8b", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--chunk-bf", type=int, default=512)
+    ap.add_argument("--chunk-i8", type=int, default=1024)
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the decode step shards by request with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from non_uniform_paged_amd import api
+    from non_uniform_paged_amd.runner import Prepared
+    from workloads import make_workload
+
+    torch.cuda.set_device(0)
+    w = make_workload(args.config)
+    t_prep = time.perf_counter()
+    prep = Prepared(w, chunk_bf=args.chunk_bf, chunk_i8=args.chunk_i8)
+    t_prep = time.perf_counter() - t_prep
+    tr = prep.traffic()
+    G = w.Hq // w.Hkv
+    stream = torch.cuda.current_stream()
+    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def one_step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        api.tg_decode_split(prep.cache, prep.q, prep.workspace, w.Hq, stream=stream)
+        if evs is not None:
+            evs[1].record(stream)
+        api.tg_merge_partials(prep.workspace, prep.tables.n_items, w.B * w.Hkv, G, w.d,
+                              prep.cache.part_off, prep.out, stream=stream)
+        if evs is not None:
+            evs[2].record(stream)
+
+    for i in range(args.warmup):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        one_step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.fill_((i + 1) & 0xFF)
+        one_step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    split_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    merge_ms = np.array([e[1].elapsed_time(e[2]) for e in events])
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in events])
+    ms = float(step_ms.mean())
+    med = float(np.median(step_ms))
+
+    split_bytes = tr["kv_roofline"] + w.B * w.Hq * w.d * (4 if w.q_dtype == "f32" else 2) + tr["tables"] \
+        + prep.tables.n_items * G * (w.d + 2) * 4
+    achieved = split_bytes / (split_ms.mean() * 1e-3) / 1e9
+    traffic = _traffic_record(args.config)
+    value = tr["effective"] / (ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 K/V/Q; no datasets or weights)",
+        "config": {"workload": DESCRIPTIONS[args.config], "name": args.config, "batch": w.B,
+                   "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "clusters": w.n_clusters,
+                   "page": w.page_size, "chunk_bf": args.chunk_bf, "chunk_i8": args.chunk_i8,
+                   "plan_items": prep.tables.n_items, "retained_head_rows": tr["head_rows"],
+                   "parallelism": "single GPU"},
+        "hbm_frac_roofline_bytes": round(tr["roofline"] / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "effective_bytes": tr["effective"],
+        "roofline_bytes": tr["roofline"],
+        "steps_per_s": round(1e3 / med, 2),
+        "median_ms": round(med, 5),
+        "p10_ms": round(float(np.percentile(step_ms, 10)), 5),
+        "p90_ms": round(float(np.percentile(step_ms, 90)), 5),
+        "split_ms": round(float(split_ms.mean()), 5),
+        "merge_ms": round(float(merge_ms.mean()), 5),
+        "cache_flush_between_steps": flush is not None,
+        "wall_s_timed_region": round(wall, 4),
+        "prepare_s": round(t_prep, 2),
+        "roofline": {
+            "kernel": "split_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": split_bytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, prep)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,299 @@
+/*
+ * tg.h -- C ABI of the ragged-paged decode-attention library (gfx950).
+ *
+ * One decode step of one layer attends, for every request r and q-head hq,
+ * over the rows that KV-head h = hq / G of r retains:
+ *
+ *     o[r][hq] = sum_t softmax_t(q[r][hq] . K_rh[t] * scale) V_rh[t]
+ *
+ * (TTKV page, "What real problem": each new token attends over all cached KV
+ * states.)  The cache is shaped by three ideas from the pages:
+ *
+ *   - Budget Reservation (Tangram page, "Three mechanisms", item 1): every
+ *     (request, KV-head) gets a fixed retained-token footprint at admission,
+ *     from an input-invariant head ranking and a narrow per-head ratio band
+ *     (Tangram page, "Key finding: two-level structural law").
+ *   - Ragged Paging (same section, item 2): heads with similar budgets form a
+ *     cluster with its own page pool and block table; a page holds the same
+ *     token slots for every head of its cluster, so page size varies by
+ *     cluster.
+ *   - Recency tiers (TTKV page, "Tier Layout", "Tier Content", "Tier
+ *     Interaction"): the newest share of each sequence stays bf16; older rows
+ *     sit in 64-token blocks quantised to INT8 with per-channel scales.
+ *   Shared-prefix pages (RadixAttention lesson, "The concept") are
+ *   reference-counted and appear in many block tables.
+ *
+ * Conventions
+ *   - Every call returns an int status (TG_OK or a negative TG_E* code) and
+ *     never throws.  On error, outputs are unspecified and pool state is
+ *     unchanged.
+ *   - The caller owns every buffer.  Host outputs go to caller-allocated
+ *     arrays whose sizes come from a sizing call.  Device memory (pools,
+ *     tables, q, out, workspace) is allocated by the caller; the library never
+ *     allocates device memory.
+ *   - "device" pointers are HIP device pointers on the current device;
+ *     "host" pointers are ordinary host memory.  `stream` is a hipStream_t
+ *     (NULL = the default stream); device work is enqueued asynchronously and
+ *     faults surface at the caller's next synchronisation.
+ *   - Host functions are deterministic and not thread-safe per pool.
+ *
+ * Index conventions: B requests, H KV-heads, Hq = G*H q-heads with q-head hq
+ * reading KV-head hq / G; tier 0 = INT8 (TG_TIER_I8), tier 1 = bf16
+ * (TG_TIER_BF16); logical rows of (r, h) run oldest first, rows
+ * [0, n_i8) in the INT8 tier and [n_i8, L) in the bf16 tier.
+ */
+#ifndef TG_H_
+#define TG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TG_OK 0
+#define TG_EINVAL (-1)       /* malformed argument or inconsistent sizes */
+#define TG_ENOMEM (-2)       /* a page pool is exhausted (nothing changed) */
+#define TG_EOVERFLOW (-3)    /* a size does not fit its integer type */
+#define TG_EDEVICE (-4)      /* a HIP launch or runtime call failed */
+#define TG_EUNSUPPORTED (-5) /* shape the device kernels do not implement */
+
+#define TG_TIER_I8 0
+#define TG_TIER_BF16 1
+#define TG_MAX_CLUSTERS 16
+
+#define TG_Q_F32 0
+#define TG_Q_BF16 1
+
+/* Human-readable text for a status code (static storage). */
+const char* tg_strerror(int status);
+
+/* ------------------------------------------------------------------------
+ * Admission: budget reservation, clustering, tier split  (host only)
+ *
+ * Tangram page, "Key finding" and "Three mechanisms" items 1-2; TTKV page,
+ * "Tier Content".  Rules (exact integers, 64-bit intermediates):
+ *   ratio(k) = hi - floor((hi - lo) * k / (H - 1))   (k = rank, 0 = most
+ *              important; hi when H == 1)
+ *   budget   = clamp(ceil(ratio(rank[h]) * n_comp[r] / 1e6), 1, n_comp[r]),
+ *              or budget_override[r*H + h] when given
+ *   L        = n_fixed[r] + budget
+ *   clusters = heads sorted by rank, cut into n_clusters contiguous groups,
+ *              group c holding ceil(H/C) heads if c < H mod C else floor(H/C);
+ *              slot_in_cluster = position inside the group in rank order
+ *   n_bf0    = ceil(L * recent_ppm / 1e6);  n_i8 = floor((L - n_bf0) / Qb) * Qb;
+ *   n_bf     = L - n_i8
+ * ---------------------------------------------------------------------- */
+typedef struct tg_budget_table {
+  int32_t n_kv_heads;        /* H >= 1 */
+  const int32_t* head_rank;  /* host [H]: a permutation of 0..H-1 */
+  int32_t ratio_hi_ppm;      /* ratio of rank 0, in parts per million */
+  int32_t ratio_lo_ppm;      /* ratio of rank H-1; 0 < lo <= hi <= 1e6 */
+  int32_t n_clusters;        /* 1 <= C <= min(H, TG_MAX_CLUSTERS) */
+  int32_t recent_ppm;        /* share kept bf16, 0..1e6 (1e6 = no INT8 tier) */
+  int32_t quant_block;       /* INT8 block length Qb >= 1 (tokens) */
+} tg_budget_table;
+
+typedef struct tg_reservation {
+  int32_t B, n_kv_heads, n_clusters; /* written by tg_reserve */
+  int32_t* budget;           /* host [B*H] retained compressible tokens */
+  int32_t* length;           /* host [B*H] L = n_fixed + budget */
+  int32_t* n_i8;             /* host [B*H] rows in the INT8 tier */
+  int32_t* n_bf;             /* host [B*H] rows in the bf16 tier */
+  int32_t* cluster_of_head;  /* host [H] */
+  int32_t* slot_in_cluster;  /* host [H] */
+  int32_t* cluster_size;     /* host [C] */
+} tg_reservation;
+
+/* Fill `out` (all arrays caller-allocated, sizes as listed).  n_comp [B]
+ * (>= 1) are the compressible tokens of each request, n_fixed [B] (>= 0,
+ * nullable = all 0) the always-kept shared-path tokens, budget_override
+ * [B*H] (nullable) explicit budgets in [1, n_comp[r]].  TG_EINVAL on a
+ * malformed table or length, TG_EOVERFLOW if L exceeds int32. */
+int tg_reserve(const tg_budget_table* table, int32_t B, const int32_t* n_comp,
+               const int32_t* n_fixed, const int32_t* budget_override,
+               tg_reservation* out);
+
+/* ------------------------------------------------------------------------
+ * Page pools  (host bookkeeping; the bytes live in caller device memory)
+ *
+ * Ragged Paging (Tangram page, "Three mechanisms", item 2): one pool per
+ * (cluster, tier).  A page of cluster c holds S token slots for each of its
+ * n_c heads, S = page_size (bf16) or quant_block (INT8).  Device layout of
+ * one page, head slot s = slot_in_cluster at byte offset s * head_bytes:
+ *   bf16 : K [S][d] bf16, then V [S][d] bf16          head_bytes = 4*S*d
+ *   INT8 : K codes [S][d] int8, V codes [S][d] int8,
+ *          K scales [d] fp16, V scales [d] fp16       head_bytes = 2*S*d + 4*d
+ * Pages are handed out lowest free id first; shared pages are
+ * reference-counted; a failing allocation changes nothing.
+ * ---------------------------------------------------------------------- */
+typedef struct tg_pool tg_pool;
+
+/* cluster_size [C] from tg_reserve; pages_bf / pages_i8 [C] capacities (>= 0).
+ * TG_EINVAL on bad geometry, TG_EOVERFLOW if a pool's byte size overflows. */
+int tg_pool_create(int32_t n_clusters, const int32_t* cluster_size, int32_t head_dim,
+                   int32_t page_size, int32_t quant_block, const int64_t* pages_bf,
+                   const int64_t* pages_i8, tg_pool** out);
+void tg_pool_destroy(tg_pool* pool);
+/* Bytes of one page of (cluster c, tier), or -1 on a bad index. */
+int64_t tg_pool_page_bytes(const tg_pool* pool, int32_t c, int32_t tier);
+/* Capacity in pages, and pages currently free, of (c, tier); -1 on a bad index. */
+int64_t tg_pool_capacity(const tg_pool* pool, int32_t c, int32_t tier);
+int64_t tg_pool_free_pages(const tg_pool* pool, int32_t c, int32_t tier);
+/* Reference count of page `page` of (c, tier); -1 on a bad index. */
+int32_t tg_pool_refcount(const tg_pool* pool, int32_t c, int32_t tier, int64_t page);
+
+/* ------------------------------------------------------------------------
+ * Block tables and the ahead-of-time split plan  (host only)
+ *
+ * Tangram page, "Three mechanisms", items 2-3 (per-cluster tables; work
+ * partitioned ahead of time, no per-step re-planning); RadixAttention lesson,
+ * "The concept" (nodes own token ranges and their KV blocks; requests on a
+ * branch reuse them).
+ *
+ *   pages   row r of (c, t) needs ceil(max_{h in c} n_bf / page_size) bf16 or
+ *           max_{h in c} n_i8 / Qb INT8 pages, allocated in order r, c,
+ *           t (INT8 then bf16), page j.
+ *   sharing page j is shared when every head of c starts it at the same
+ *           logical row s and s + S <= n_fixed[r]; its key is (c, t, node
+ *           holding row s + S - 1, s).  A known key adds a reference; a new
+ *           one takes a fresh page.  Other pages are always fresh.
+ *   tables  bt[c][t] is [B][stride[c][t]] int32 page ids in logical order,
+ *           padded with -1; stride = max_r pages; len [B*H*2] = (n_i8, n_bf).
+ *   plan    items {r, h, tier, t0, t1, slot} for r, h, tier (INT8 first),
+ *           t0 = 0, chunk, 2*chunk, ... (t0, t1 are row indices inside the
+ *           tier); slot = the item's index in that natural order; part_off
+ *           [B*H + 1] = first slot of each (r, h).  With lpt != 0 the items
+ *           are stably sorted by descending (t1 - t0) * (2 bf16 | 1 INT8).
+ * ---------------------------------------------------------------------- */
+typedef struct tg_share_desc {
+  const int32_t* n_nodes;   /* host [B] radix-path length of each request */
+  const int32_t* node_ids;  /* host [sum n_nodes] paths, root first */
+  int32_t n_node_table;     /* number of distinct node ids */
+  const int32_t* node_len;  /* host [n_node_table] tokens owned by each node */
+} tg_share_desc;            /* sum of node_len over r's path must be n_fixed[r] */
+
+typedef struct tg_plan_opts {
+  int32_t chunk_bf;  /* bf16 item length, a positive multiple of page_size */
+  int32_t chunk_i8;  /* INT8 item length, a positive multiple of quant_block */
+  int32_t lpt;       /* nonzero: longest items first */
+} tg_plan_opts;
+
+typedef struct tg_table_sizes {
+  int32_t stride[TG_MAX_CLUSTERS][2];        /* entries per table row */
+  int32_t n_items;                           /* plan length */
+  int64_t pages_needed[TG_MAX_CLUSTERS][2];  /* from an empty pool */
+} tg_table_sizes;
+
+/* Sizes of the arrays tg_build_tables fills; touches no pool.  `share` is
+ * nullable.  TG_EINVAL on malformed input, TG_EOVERFLOW on int32 overflow. */
+int tg_size_tables(const tg_reservation* res, int32_t page_size, int32_t quant_block,
+                   const tg_share_desc* share, const tg_plan_opts* opts,
+                   tg_table_sizes* out);
+
+typedef struct tg_tables {
+  int32_t* bt[TG_MAX_CLUSTERS][2];     /* host [B][stride[c][t]] (may be NULL if stride 0) */
+  int32_t stride[TG_MAX_CLUSTERS][2];  /* in: must equal tg_size_tables' values */
+  int32_t* len;                        /* host [B*H*2] */
+  int32_t* work;                       /* host [n_items*6] */
+  int32_t n_items;                     /* in: must equal tg_size_tables' value */
+  int32_t* part_off;                   /* host [B*H + 1] */
+  int32_t* released;                   /* host [B] zeroed here; set by tg_release */
+} tg_tables;
+
+/* Allocate every page of the batch from `pool` (all or nothing) and fill the
+ * tables.  TG_ENOMEM leaves the pool unchanged. */
+int tg_build_tables(tg_pool* pool, const tg_reservation* res, const tg_share_desc* share,
+                    const tg_plan_opts* opts, tg_tables* out);
+
+/* Drop request r's page references; pages reaching zero become free and their
+ * share keys are forgotten.  TG_EINVAL if r was already released. */
+int tg_release(tg_pool* pool, tg_tables* tables, int32_t r);
+
+/* ------------------------------------------------------------------------
+ * Device view of a populated cache  (all pointers device, except the struct)
+ * ---------------------------------------------------------------------- */
+typedef struct tg_cache {
+  int32_t B, n_kv_heads, head_dim, page_size, quant_block, n_clusters;
+  void* pool[TG_MAX_CLUSTERS][2];            /* pool base of (c, t), 16-byte aligned */
+  int64_t page_bytes[TG_MAX_CLUSTERS][2];    /* from tg_pool_page_bytes */
+  int64_t n_pages[TG_MAX_CLUSTERS][2];       /* pool capacities */
+  const int32_t* bt[TG_MAX_CLUSTERS][2];     /* device [B][stride[c][t]] */
+  int32_t stride[TG_MAX_CLUSTERS][2];
+  const int32_t* cluster_of_head;            /* device [H] */
+  const int32_t* slot_in_cluster;            /* device [H] */
+  const int32_t* len;                        /* device [B*H*2] (n_i8, n_bf) */
+} tg_cache;
+
+/* ------------------------------------------------------------------------
+ * Cache fill  (device)
+ *
+ * Writes logical rows into their pages: row i of (r, h) is
+ * rows[index[offsets[r*H + h] + i]] ([2][d] bf16 bits: K then V).  Rows
+ * [0, n_i8) are quantised per 64-token block and channel (TTKV page, "Tier
+ * Layout" / "Tier Interaction"; symmetric absmax reading):
+ *   s  = fp16_rne(fp32(absmax) / 127), +inf saturating to 65504
+ *   q8 = s > 0 ? clamp(rint_even(x / s), -127, 127) : 0       (fp32 math)
+ * Shared pages may be written by several sequences with identical data.
+ * rows: device uint16 [n_rows][2][d]; index: device int32 [offsets[B*H]];
+ * offsets: device int64 [B*H + 1].  TG_EINVAL on a bad shape.
+ * ---------------------------------------------------------------------- */
+int tg_write_kv(const tg_cache* cache, const uint16_t* rows, const int32_t* index,
+                const int64_t* offsets, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode attention  (device)
+ *
+ * Split-K over the plan: each item (r, h, tier, t0, t1) computes, for the G
+ * q-heads of h, the partial (m, l, acc) of the online normaliser (CAP survey
+ * page, section 2.4.3, online normaliser [88]): m = max score, l = sum
+ * exp(s - m), acc = sum exp(s - m) v, with INT8 rows dequantised in
+ * registers.  A second kernel merges the partials of each (r, h):
+ *   o = sum_s e^{m_s - M} acc_s / sum_s e^{m_s - M} l_s,  M = max_s m_s.
+ *
+ *   q         device [B][Hq][d], fp32 (TG_Q_F32) or bf16 bits (TG_Q_BF16)
+ *   work, part_off, n_items  device copies of tg_build_tables' plan
+ *   workspace device fp32, >= tg_decode_workspace_bytes(n_items, G, d) bytes:
+ *             acc [n_items][G][d] then (m, l) [n_items][G][2] (m in natural
+ *             log units of the scaled score)
+ *   out       device fp32 [B][Hq][d]
+ *   sm_scale  score scale; 0 means 1/sqrt(d)
+ * TG_EUNSUPPORTED unless d in {64, 128}, G in {1, 2, 4, 8}, page_size 16 and
+ * quant_block 64; TG_EINVAL on inconsistent arguments; TG_EDEVICE on a
+ * failed launch.
+ * ---------------------------------------------------------------------- */
+size_t tg_decode_workspace_bytes(int32_t n_items, int32_t G, int32_t d);
+
+typedef struct tg_decode_args {
+  int32_t n_q_heads;
+  int32_t q_dtype;
+  const void* q;
+  const int32_t* work;
+  int32_t n_items;
+  const int32_t* part_off;
+  float* workspace;
+  size_t workspace_bytes;
+  float* out;
+  float sm_scale;
+} tg_decode_args;
+
+int tg_decode_attn(const tg_cache* cache, const tg_decode_args* args, void* stream);
+
+/* Split stage alone: writes the partials of every plan item into
+ * `workspace` (layout above) without merging them; `out` is not used.
+ * tg_decode_attn == tg_decode_split followed by tg_merge_partials over the
+ * B*H pairs of `part_off`.  Same errors as tg_decode_attn. */
+int tg_decode_split(const tg_cache* cache, const tg_decode_args* args, void* stream);
+
+/* Merge stage alone (also the merge of partials computed on different
+ * shards).  For each pair p in [0, n_pairs) and g < G, merges slots
+ * [part_off[p], part_off[p+1]) of `workspace` (layout as above, n_slots
+ * slots) into out[p*G + g][d].  Pairs with no slot are written as 0. */
+int tg_merge_partials(const float* workspace, int32_t n_slots, int32_t n_pairs, int32_t G,
+                      int32_t d, const int32_t* part_off, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TG_H_ */

@@ -1,0 +1,299 @@
+"""Python binding of the C ABI in include/tg.h -- argument marshalling only.
+
+Every computation happens in ``libtg.so``: the host planner (reservation,
+pools, tables, plan) and the HIP kernels (cache fill, split decode, merge).
+PyTorch is used here only to own device memory and to name the stream.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import numpy as np
+
+from . import _lib as L
+from ._lib import TG_Q_BF16, TG_Q_F32, TG_TIER_BF16, TG_TIER_I8, TGError, check, lib
+
+__all__ = [
+    "TGError", "TG_TIER_I8", "TG_TIER_BF16", "TG_Q_F32", "TG_Q_BF16",
+    "Reservation", "Share", "Pool", "Tables", "DeviceCache",
+    "tg_reserve", "tg_size_tables", "tg_build_tables", "tg_release",
+    "tg_write_kv", "tg_decode_workspace_bytes", "tg_decode_attn", "tg_decode_split",
+    "tg_merge_partials",
+]
+
+
+def _i32(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x), dtype=np.int32)
+
+
+def _p32(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(L.P32)
+
+
+# --------------------------------------------------------------------------- host
+class Reservation:
+    """Output of ``tg_reserve`` as numpy arrays (kept alive with the struct)."""
+
+    def __init__(self, B: int, H: int, C: int):
+        self.B, self.H, self.C = B, H, C
+        self.budget = np.zeros((B, H), np.int32)
+        self.length = np.zeros((B, H), np.int32)
+        self.n_i8 = np.zeros((B, H), np.int32)
+        self.n_bf = np.zeros((B, H), np.int32)
+        self.cluster_of_head = np.zeros(H, np.int32)
+        self.slot_in_cluster = np.zeros(H, np.int32)
+        self.cluster_size = np.zeros(C, np.int32)
+        self.struct = L.Reservation(0, 0, 0, _p32(self.budget), _p32(self.length), _p32(self.n_i8),
+                                    _p32(self.n_bf), _p32(self.cluster_of_head),
+                                    _p32(self.slot_in_cluster), _p32(self.cluster_size))
+
+
+def tg_reserve(head_rank: Sequence[int], ratio_hi_ppm: int, ratio_lo_ppm: int, n_clusters: int,
+               recent_ppm: int, quant_block: int, n_comp: Sequence[int],
+               n_fixed: Optional[Sequence[int]] = None,
+               budget_override: Optional[Sequence[int]] = None) -> Reservation:
+    rank = _i32(head_rank)
+    nc = _i32(n_comp)
+    nf = None if n_fixed is None else _i32(n_fixed)
+    ov = None if budget_override is None else _i32(budget_override)
+    H, B = int(rank.size), int(nc.size)
+    if nf is not None and nf.size != B:
+        raise ValueError("n_fixed must have B entries")
+    if ov is not None and ov.size != B * H:
+        raise ValueError("budget_override must have B*H entries")
+    res = Reservation(B, H, max(int(n_clusters), 1))
+    tb = L.BudgetTable(H, _p32(rank), int(ratio_hi_ppm), int(ratio_lo_ppm), int(n_clusters),
+                       int(recent_ppm), int(quant_block))
+    check(lib().tg_reserve(ctypes.byref(tb), B, _p32(nc), _p32(nf), _p32(ov), ctypes.byref(res.struct)),
+          "tg_reserve")
+    return res
+
+
+class Share:
+    """Radix paths of the batch (``tg_share_desc``)."""
+
+    def __init__(self, n_nodes: Sequence[int], node_ids: Sequence[int], node_len: Sequence[int]):
+        self.n_nodes = _i32(n_nodes)
+        self.node_ids = _i32(node_ids)
+        self.node_len = _i32(node_len)
+        self.struct = L.ShareDesc(_p32(self.n_nodes), _p32(self.node_ids), int(self.node_len.size),
+                                  _p32(self.node_len))
+
+
+def _share_ptr(share: Optional[Share]):
+    return None if share is None else ctypes.byref(share.struct)
+
+
+class Pool:
+    """Host bookkeeping of the (cluster, tier) page pools (``tg_pool``)."""
+
+    def __init__(self, cluster_size: Sequence[int], head_dim: int, page_size: int, quant_block: int,
+                 pages_bf: Sequence[int], pages_i8: Sequence[int]):
+        cs = _i32(cluster_size)
+        self.C = int(cs.size)
+        self.head_dim, self.page_size, self.quant_block = int(head_dim), int(page_size), int(quant_block)
+        pb = np.ascontiguousarray(pages_bf, dtype=np.int64)
+        pi = np.ascontiguousarray(pages_i8, dtype=np.int64)
+        h = ctypes.c_void_p()
+        check(lib().tg_pool_create(self.C, _p32(cs), self.head_dim, self.page_size, self.quant_block,
+                                   pb.ctypes.data_as(L.P64), pi.ctypes.data_as(L.P64), ctypes.byref(h)),
+              "tg_pool_create")
+        self.handle = h
+
+    def page_bytes(self, c: int, tier: int) -> int:
+        return int(lib().tg_pool_page_bytes(self.handle, c, tier))
+
+    def capacity(self, c: int, tier: int) -> int:
+        return int(lib().tg_pool_capacity(self.handle, c, tier))
+
+    def free_pages(self, c: int, tier: int) -> int:
+        return int(lib().tg_pool_free_pages(self.handle, c, tier))
+
+    def refcount(self, c: int, tier: int, page: int) -> int:
+        return int(lib().tg_pool_refcount(self.handle, c, tier, page))
+
+    def close(self):
+        if self.handle:
+            lib().tg_pool_destroy(self.handle)
+            self.handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def tg_size_tables(res: Reservation, page_size: int, quant_block: int, share: Optional[Share] = None,
+                   chunk_bf: int = 512, chunk_i8: int = 1024, lpt: bool = True) -> dict:
+    opts = L.PlanOpts(int(chunk_bf), int(chunk_i8), int(bool(lpt)))
+    sz = L.TableSizes()
+    check(lib().tg_size_tables(ctypes.byref(res.struct), int(page_size), int(quant_block),
+                               _share_ptr(share), ctypes.byref(opts), ctypes.byref(sz)), "tg_size_tables")
+    C = res.C
+    return {"stride": [[sz.stride[c][t] for t in range(2)] for c in range(C)],
+            "n_items": int(sz.n_items),
+            "pages_needed": [[int(sz.pages_needed[c][t]) for t in range(2)] for c in range(C)]}
+
+
+class Tables:
+    """Block tables, lengths and plan filled by ``tg_build_tables`` (numpy)."""
+
+    def __init__(self, res: Reservation, sizes: dict):
+        B, H, C = res.B, res.H, res.C
+        self.B, self.H, self.C = B, H, C
+        self.stride = sizes["stride"]
+        self.n_items = sizes["n_items"]
+        self.bt = [[np.full((B, self.stride[c][t]), -1, np.int32) for t in range(2)] for c in range(C)]
+        self.len = np.zeros((B, H, 2), np.int32)
+        self.work = np.zeros((max(self.n_items, 1), 6), np.int32)
+        self.part_off = np.zeros(B * H + 1, np.int32)
+        self.released = np.zeros(B, np.int32)
+        s = L.Tables()
+        for c in range(C):
+            for t in range(2):
+                s.bt[c][t] = _p32(self.bt[c][t]) if self.stride[c][t] else None
+                s.stride[c][t] = self.stride[c][t]
+        s.len = _p32(self.len)
+        s.work = _p32(self.work)
+        s.n_items = self.n_items
+        s.part_off = _p32(self.part_off)
+        s.released = _p32(self.released)
+        self.struct = s
+
+    @property
+    def plan(self) -> np.ndarray:
+        return self.work[:self.n_items]
+
+
+def tg_build_tables(pool: Pool, res: Reservation, share: Optional[Share] = None, chunk_bf: int = 512,
+                    chunk_i8: int = 1024, lpt: bool = True) -> Tables:
+    sizes = tg_size_tables(res, pool.page_size, pool.quant_block, share, chunk_bf, chunk_i8, lpt)
+    t = Tables(res, sizes)
+    opts = L.PlanOpts(int(chunk_bf), int(chunk_i8), int(bool(lpt)))
+    check(lib().tg_build_tables(pool.handle, ctypes.byref(res.struct), _share_ptr(share),
+                                ctypes.byref(opts), ctypes.byref(t.struct)), "tg_build_tables")
+    t.sizes = sizes
+    return t
+
+
+def tg_release(pool: Pool, tables: Tables, r: int) -> None:
+    if not 0 <= r < tables.B:
+        raise IndexError(r)
+    check(lib().tg_release(pool.handle, ctypes.byref(tables.struct), int(r)), "tg_release")
+
+
+def tg_decode_workspace_bytes(n_items: int, G: int, d: int) -> int:
+    return int(lib().tg_decode_workspace_bytes(int(n_items), int(G), int(d)))
+
+
+# --------------------------------------------------------------------------- device
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+class DeviceCache:
+    """Device memory of one populated cache: the (cluster, tier) pools sized
+    from ``pool`` and the uploaded tables, plus the ``tg_cache`` view."""
+
+    def __init__(self, pool: Pool, res: Reservation, tables: Tables, device="cuda"):
+        torch = _torch()
+        self.device = torch.device(device)
+        self.G_hint = None
+        C = res.C
+        self.pools = [[None, None] for _ in range(C)]
+        self.bt = [[None, None] for _ in range(C)]
+        c_s = L.Cache()
+        c_s.B, c_s.n_kv_heads, c_s.head_dim = res.B, res.H, pool.head_dim
+        c_s.page_size, c_s.quant_block, c_s.n_clusters = pool.page_size, pool.quant_block, C
+        for c in range(C):
+            for t in range(2):
+                cap = pool.capacity(c, t)
+                pb = pool.page_bytes(c, t)
+                if cap > 0:
+                    self.pools[c][t] = torch.empty(cap * pb, dtype=torch.uint8, device=self.device)
+                if tables.stride[c][t] > 0:
+                    self.bt[c][t] = torch.from_numpy(tables.bt[c][t]).to(self.device)
+                c_s.pool[c][t] = _ptr(self.pools[c][t])
+                c_s.page_bytes[c][t] = pb
+                c_s.n_pages[c][t] = cap
+                c_s.bt[c][t] = _ptr(self.bt[c][t])
+                c_s.stride[c][t] = tables.stride[c][t]
+        self.cluster_of_head = torch.from_numpy(res.cluster_of_head).to(self.device)
+        self.slot_in_cluster = torch.from_numpy(res.slot_in_cluster).to(self.device)
+        self.len = torch.from_numpy(tables.len.reshape(-1).copy()).to(self.device)
+        self.work = torch.from_numpy(tables.plan.copy()).to(self.device)
+        self.part_off = torch.from_numpy(tables.part_off).to(self.device)
+        self.n_items = tables.n_items
+        c_s.cluster_of_head = _ptr(self.cluster_of_head)
+        c_s.slot_in_cluster = _ptr(self.slot_in_cluster)
+        c_s.len = _ptr(self.len)
+        self.struct = c_s
+        self.B, self.H, self.d = res.B, res.H, pool.head_dim
+
+    def pool_bytes(self) -> int:
+        return sum(int(p.numel()) for row in self.pools for p in row if p is not None)
+
+
+def tg_write_kv(cache: DeviceCache, rows, index, offsets, stream=None) -> None:
+    check(lib().tg_write_kv(ctypes.byref(cache.struct), _ptr(rows), _ptr(index), _ptr(offsets),
+                            _stream_ptr(stream)), "tg_write_kv")
+
+
+def _decode_args(cache, q, out, workspace, n_q_heads, sm_scale, work, part_off, n_items):
+    torch = _torch()
+    if q.dtype == torch.float32:
+        qd = TG_Q_F32
+    elif q.dtype == torch.bfloat16:
+        qd = TG_Q_BF16
+    else:
+        raise TypeError("q must be float32 or bfloat16")
+    a = L.DecodeArgs()
+    a.n_q_heads = int(n_q_heads)
+    a.q_dtype = qd
+    a.q = _ptr(q)
+    a.work = _ptr(cache.work if work is None else work)
+    a.n_items = int(cache.n_items if n_items is None else n_items)
+    a.part_off = _ptr(cache.part_off if part_off is None else part_off)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = int(workspace.numel() * workspace.element_size())
+    a.out = _ptr(out)
+    a.sm_scale = float(sm_scale)
+    return a
+
+
+def tg_decode_attn(cache: DeviceCache, q, out, workspace, n_q_heads: int, sm_scale: float = 0.0,
+                   work=None, part_off=None, n_items: Optional[int] = None, stream=None) -> None:
+    """Enqueue one decode step.  ``q`` is fp32 or bf16 [B][Hq][d] on the
+    device; ``out`` fp32 [B][Hq][d]; ``workspace`` fp32 of at least
+    ``tg_decode_workspace_bytes`` bytes.  The plan defaults to the one
+    uploaded with the cache."""
+    a = _decode_args(cache, q, out, workspace, n_q_heads, sm_scale, work, part_off, n_items)
+    check(lib().tg_decode_attn(ctypes.byref(cache.struct), ctypes.byref(a), _stream_ptr(stream)),
+          "tg_decode_attn")
+
+
+def tg_decode_split(cache: DeviceCache, q, workspace, n_q_heads: int, sm_scale: float = 0.0,
+                    work=None, n_items: Optional[int] = None, stream=None) -> None:
+    """Enqueue the split stage alone (partials into ``workspace``)."""
+    a = _decode_args(cache, q, None, workspace, n_q_heads, sm_scale, work, None, n_items)
+    check(lib().tg_decode_split(ctypes.byref(cache.struct), ctypes.byref(a), _stream_ptr(stream)),
+          "tg_decode_split")
+
+
+def tg_merge_partials(workspace, n_slots: int, n_pairs: int, G: int, d: int, part_off, out,
+                      stream=None) -> None:
+    check(lib().tg_merge_partials(_ptr(workspace), int(n_slots), int(n_pairs), int(G), int(d),
+                                  _ptr(part_off), _ptr(out), _stream_ptr(stream)), "tg_merge_partials")

@@ -1,0 +1,63 @@
+"""Build ``libtg.so`` in-tree with hipcc for gfx950.
+
+    python -m non_uniform_paged_amd.build
+
+The HIP sources are compiled with packed-fp32 instructions disabled and IEEE
+fp32 division/sqrt; the host planner is plain C++17.  Objects go to
+``_build/`` at the repository root; the shared library is written next to
+this file.
+"""
+from __future__ import annotations
+
+import os
+import shlex
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libtg.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fhip-fp32-correctly-rounded-divide-sqrt", "-Wno-unused-command-line-argument",
+]
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-I", INCLUDE, "-Wall", "-Wextra"]
+
+HIP_SOURCES = ["tg_decode.hip", "tg_kvwrite.hip"]
+CXX_SOURCES = ["tg_host.cpp"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(shlex.quote(c) for c in cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link ``libtg.so``; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        _run([HIPCC, *HIP_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    for src in CXX_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        _run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-q" not in sys.argv))

@@ -1,0 +1,590 @@
+// Host side of the C ABI: budget reservation, clustering, tier split, the
+// ref-counted ragged page pools, block tables and the ahead-of-time split
+// plan.  Pure C++17, no device calls.
+//
+// Sources: Tangram page (arXiv 2606.06302 explainer), "Key finding: two-level
+// structural law" and "Three mechanisms" items 1-3 (Budget Reservation,
+// Ragged Paging, AOT load balancing); TTKV page (arXiv 2604.19769 explainer),
+// "Tier Content" (newest share stays high precision, the rest is quantised in
+// blocks); RadixAttention lesson, "The concept" (radix nodes own token ranges
+// and their KV blocks, reused by every request on the branch).  The exact
+// integer rules are the ones documented in include/tg.h.
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <limits>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "tg.h"
+
+namespace {
+
+constexpr int64_t kPpm = 1000000;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct ShareKey {
+  int32_t c, t, node;
+  int64_t start;
+  bool operator==(const ShareKey& o) const {
+    return c == o.c && t == o.t && node == o.node && start == o.start;
+  }
+};
+struct ShareKeyHash {
+  size_t operator()(const ShareKey& k) const {
+    uint64_t h = static_cast<uint64_t>(k.start) * 0x9E3779B97F4A7C15ull;
+    h ^= (static_cast<uint64_t>(k.node) + 0x7F4A7C15ull) * 0xBF58476D1CE4E5B9ull;
+    h ^= static_cast<uint64_t>(k.c * 2 + k.t) * 0x94D049BB133111EBull;
+    return static_cast<size_t>(h ^ (h >> 31));
+  }
+};
+
+// One (cluster, tier) pool: refcounts, plus a bitmap of free pages searched
+// lowest-first.  `hint` is the lowest word that may hold a free bit.
+struct SubPool {
+  int64_t cap = 0;
+  int64_t page_bytes = 0;
+  std::vector<int32_t> ref;
+  std::vector<uint64_t> free_bits;  // bit set = page free
+  int64_t hint = 0;
+  int64_t n_free = 0;
+  std::vector<ShareKey> key_of;     // valid where has_key
+  std::vector<uint8_t> has_key;
+
+  void init(int64_t capacity, int64_t bytes) {
+    cap = capacity;
+    page_bytes = bytes;
+    ref.assign(static_cast<size_t>(cap), 0);
+    free_bits.assign(static_cast<size_t>((cap + 63) / 64), ~0ull);
+    if (cap % 64) free_bits.back() = (1ull << (cap % 64)) - 1;
+    hint = 0;
+    n_free = cap;
+    key_of.assign(static_cast<size_t>(cap), ShareKey{0, 0, 0, 0});
+    has_key.assign(static_cast<size_t>(cap), 0);
+  }
+  int64_t take_lowest() {
+    const int64_t nw = static_cast<int64_t>(free_bits.size());
+    for (int64_t w = hint; w < nw; ++w) {
+      if (free_bits[w]) {
+        hint = w;
+        const int b = __builtin_ctzll(free_bits[w]);
+        free_bits[w] &= ~(1ull << b);
+        --n_free;
+        const int64_t pid = w * 64 + b;
+        ref[pid] = 1;
+        return pid;
+      }
+    }
+    hint = nw;
+    return -1;
+  }
+  void give_back(int64_t pid) {
+    free_bits[pid / 64] |= 1ull << (pid % 64);
+    ++n_free;
+    if (pid / 64 < hint) hint = pid / 64;
+  }
+};
+
+}  // namespace
+
+struct tg_pool {
+  int32_t C = 0, d = 0, page_size = 0, quant_block = 0;
+  std::vector<int32_t> cluster_size;
+  SubPool sub[TG_MAX_CLUSTERS][2];
+  std::unordered_map<ShareKey, int64_t, ShareKeyHash> registry;
+};
+
+extern "C" const char* tg_strerror(int status) {
+  switch (status) {
+    case TG_OK: return "ok";
+    case TG_EINVAL: return "invalid argument";
+    case TG_ENOMEM: return "page pool exhausted";
+    case TG_EOVERFLOW: return "integer overflow";
+    case TG_EDEVICE: return "device error";
+    case TG_EUNSUPPORTED: return "unsupported shape";
+    default: return "unknown status";
+  }
+}
+
+// --------------------------------------------------------------------------
+// reservation
+// --------------------------------------------------------------------------
+extern "C" int tg_reserve(const tg_budget_table* tb, int32_t B, const int32_t* n_comp,
+                          const int32_t* n_fixed, const int32_t* override_b,
+                          tg_reservation* out) {
+  if (!tb || !out || !n_comp || !tb->head_rank || B < 1) return TG_EINVAL;
+  const int32_t H = tb->n_kv_heads, C = tb->n_clusters;
+  if (H < 1) return TG_EINVAL;
+  if (!(0 < tb->ratio_lo_ppm && tb->ratio_lo_ppm <= tb->ratio_hi_ppm && tb->ratio_hi_ppm <= kPpm))
+    return TG_EINVAL;
+  if (C < 1 || C > H || C > TG_MAX_CLUSTERS) return TG_EINVAL;
+  if (tb->recent_ppm < 0 || tb->recent_ppm > kPpm || tb->quant_block < 1) return TG_EINVAL;
+  if (!out->budget || !out->length || !out->n_i8 || !out->n_bf || !out->cluster_of_head ||
+      !out->slot_in_cluster || !out->cluster_size)
+    return TG_EINVAL;
+  std::vector<int32_t> head_at_rank(H, -1);
+  for (int32_t h = 0; h < H; ++h) {
+    const int32_t k = tb->head_rank[h];
+    if (k < 0 || k >= H || head_at_rank[k] != -1) return TG_EINVAL;
+    head_at_rank[k] = h;
+  }
+  for (int32_t r = 0; r < B; ++r) {
+    if (n_comp[r] < 1) return TG_EINVAL;
+    if (n_fixed && n_fixed[r] < 0) return TG_EINVAL;
+    if (override_b)
+      for (int32_t h = 0; h < H; ++h) {
+        const int32_t b = override_b[int64_t(r) * H + h];
+        if (b < 1 || b > n_comp[r]) return TG_EINVAL;
+      }
+  }
+  // validate everything (including overflow) before writing any output
+  for (int32_t r = 0; r < B; ++r) {
+    const int64_t nf = n_fixed ? n_fixed[r] : 0;
+    if (nf + n_comp[r] > std::numeric_limits<int32_t>::max()) return TG_EOVERFLOW;
+  }
+  const int64_t hi = tb->ratio_hi_ppm, lo = tb->ratio_lo_ppm;
+  for (int32_t r = 0; r < B; ++r) {
+    const int64_t n = n_comp[r];
+    const int64_t nf = n_fixed ? n_fixed[r] : 0;
+    for (int32_t h = 0; h < H; ++h) {
+      const int64_t i = int64_t(r) * H + h;
+      int64_t b;
+      if (override_b) {
+        b = override_b[i];
+      } else {
+        const int64_t k = tb->head_rank[h];
+        const int64_t ratio = (H == 1) ? hi : hi - ((hi - lo) * k) / (H - 1);
+        b = ceil_div(ratio * n, kPpm);
+        b = std::min<int64_t>(std::max<int64_t>(b, 1), n);
+      }
+      const int64_t L = nf + b;
+      const int64_t old = L - ceil_div(L * tb->recent_ppm, kPpm);
+      const int64_t i8 = (old / tb->quant_block) * tb->quant_block;
+      out->budget[i] = static_cast<int32_t>(b);
+      out->length[i] = static_cast<int32_t>(L);
+      out->n_i8[i] = static_cast<int32_t>(i8);
+      out->n_bf[i] = static_cast<int32_t>(L - i8);
+    }
+  }
+  int32_t k = 0;
+  for (int32_t c = 0; c < C; ++c) {
+    const int32_t sz = (c < H % C) ? (H + C - 1) / C : H / C;
+    out->cluster_size[c] = sz;
+    for (int32_t s = 0; s < sz; ++s, ++k) {
+      out->cluster_of_head[head_at_rank[k]] = c;
+      out->slot_in_cluster[head_at_rank[k]] = s;
+    }
+  }
+  out->B = B;
+  out->n_kv_heads = H;
+  out->n_clusters = C;
+  return TG_OK;
+}
+
+// --------------------------------------------------------------------------
+// pools
+// --------------------------------------------------------------------------
+static int64_t head_bytes(int32_t tier, int32_t d, int32_t ps, int32_t qb) {
+  return tier == TG_TIER_BF16 ? int64_t(4) * ps * d : int64_t(2) * qb * d + int64_t(4) * d;
+}
+
+extern "C" int tg_pool_create(int32_t C, const int32_t* cluster_size, int32_t d, int32_t ps,
+                              int32_t qb, const int64_t* pages_bf, const int64_t* pages_i8,
+                              tg_pool** out) {
+  if (!out || !cluster_size || !pages_bf || !pages_i8) return TG_EINVAL;
+  if (C < 1 || C > TG_MAX_CLUSTERS || d < 1 || ps < 1 || qb < 1) return TG_EINVAL;
+  for (int32_t c = 0; c < C; ++c)
+    if (cluster_size[c] < 1 || pages_bf[c] < 0 || pages_i8[c] < 0) return TG_EINVAL;
+  for (int32_t c = 0; c < C; ++c)
+    for (int32_t t = 0; t < 2; ++t) {
+      const int64_t pb = head_bytes(t, d, ps, qb) * cluster_size[c];
+      const int64_t cap = t == TG_TIER_BF16 ? pages_bf[c] : pages_i8[c];
+      if (cap > 0 && pb > std::numeric_limits<int64_t>::max() / cap) return TG_EOVERFLOW;
+    }
+  tg_pool* p = new (std::nothrow) tg_pool;
+  if (!p) return TG_ENOMEM;
+  try {
+    p->C = C;
+    p->d = d;
+    p->page_size = ps;
+    p->quant_block = qb;
+    p->cluster_size.assign(cluster_size, cluster_size + C);
+    for (int32_t c = 0; c < C; ++c) {
+      p->sub[c][TG_TIER_BF16].init(pages_bf[c], head_bytes(TG_TIER_BF16, d, ps, qb) * cluster_size[c]);
+      p->sub[c][TG_TIER_I8].init(pages_i8[c], head_bytes(TG_TIER_I8, d, ps, qb) * cluster_size[c]);
+    }
+  } catch (...) {
+    delete p;
+    return TG_ENOMEM;
+  }
+  *out = p;
+  return TG_OK;
+}
+
+extern "C" void tg_pool_destroy(tg_pool* p) { delete p; }
+
+static bool bad_index(const tg_pool* p, int32_t c, int32_t t) {
+  return !p || c < 0 || c >= p->C || (t != TG_TIER_I8 && t != TG_TIER_BF16);
+}
+extern "C" int64_t tg_pool_page_bytes(const tg_pool* p, int32_t c, int32_t t) {
+  return bad_index(p, c, t) ? -1 : p->sub[c][t].page_bytes;
+}
+extern "C" int64_t tg_pool_capacity(const tg_pool* p, int32_t c, int32_t t) {
+  return bad_index(p, c, t) ? -1 : p->sub[c][t].cap;
+}
+extern "C" int64_t tg_pool_free_pages(const tg_pool* p, int32_t c, int32_t t) {
+  return bad_index(p, c, t) ? -1 : p->sub[c][t].n_free;
+}
+extern "C" int32_t tg_pool_refcount(const tg_pool* p, int32_t c, int32_t t, int64_t page) {
+  if (bad_index(p, c, t) || page < 0 || page >= p->sub[c][t].cap) return -1;
+  return p->sub[c][t].ref[page];
+}
+
+// --------------------------------------------------------------------------
+// tables and plan
+// --------------------------------------------------------------------------
+namespace {
+
+struct Geometry {
+  int32_t B, H, C, ps, qb;
+  std::vector<std::vector<int32_t>> heads;  // heads[c] in slot order
+};
+
+int check_reservation(const tg_reservation* res, int32_t ps, int32_t qb, Geometry* g) {
+  if (!res || ps < 1 || qb < 1) return TG_EINVAL;
+  if (res->B < 1 || res->n_kv_heads < 1 || res->n_clusters < 1 || res->n_clusters > TG_MAX_CLUSTERS)
+    return TG_EINVAL;
+  if (!res->length || !res->n_i8 || !res->n_bf || !res->cluster_of_head || !res->slot_in_cluster ||
+      !res->cluster_size || !res->budget)
+    return TG_EINVAL;
+  g->B = res->B;
+  g->H = res->n_kv_heads;
+  g->C = res->n_clusters;
+  g->ps = ps;
+  g->qb = qb;
+  g->heads.assign(g->C, {});
+  for (int32_t c = 0; c < g->C; ++c) {
+    if (res->cluster_size[c] < 1) return TG_EINVAL;
+    g->heads[c].assign(res->cluster_size[c], -1);
+  }
+  for (int32_t h = 0; h < g->H; ++h) {
+    const int32_t c = res->cluster_of_head[h], s = res->slot_in_cluster[h];
+    if (c < 0 || c >= g->C || s < 0 || s >= res->cluster_size[c] || g->heads[c][s] != -1)
+      return TG_EINVAL;
+    g->heads[c][s] = h;
+  }
+  for (int32_t c = 0; c < g->C; ++c)
+    for (int32_t h : g->heads[c])
+      if (h < 0) return TG_EINVAL;
+  for (int64_t i = 0; i < int64_t(g->B) * g->H; ++i) {
+    if (res->n_i8[i] < 0 || res->n_bf[i] < 0 || res->n_i8[i] % qb) return TG_EINVAL;
+    if (int64_t(res->n_i8[i]) + res->n_bf[i] != res->length[i] || res->length[i] < 1)
+      return TG_EINVAL;
+    if (res->budget[i] < 1 || res->budget[i] > res->length[i]) return TG_EINVAL;
+  }
+  return TG_OK;
+}
+
+// Flattened radix paths per request; validated against n_fixed = L - budget.
+struct Paths {
+  bool on = false;
+  std::vector<std::vector<int32_t>> ids;
+  std::vector<int64_t> node_len;
+};
+
+int check_share(const tg_share_desc* sh, const tg_reservation* res, const Geometry& g, Paths* p) {
+  p->on = false;
+  if (!sh) return TG_OK;
+  if (!sh->n_nodes || !sh->node_len || sh->n_node_table < 0) return TG_EINVAL;
+  p->on = true;
+  p->node_len.resize(sh->n_node_table);
+  for (int32_t n = 0; n < sh->n_node_table; ++n) {
+    if (sh->node_len[n] < 0) return TG_EINVAL;
+    p->node_len[n] = sh->node_len[n];
+  }
+  p->ids.assign(g.B, {});
+  int64_t off = 0;
+  for (int32_t r = 0; r < g.B; ++r) {
+    if (sh->n_nodes[r] < 0) return TG_EINVAL;
+    if (sh->n_nodes[r] > 0 && !sh->node_ids) return TG_EINVAL;
+    int64_t tot = 0;
+    for (int32_t k = 0; k < sh->n_nodes[r]; ++k) {
+      const int32_t nid = sh->node_ids[off + k];
+      if (nid < 0 || nid >= sh->n_node_table) return TG_EINVAL;
+      p->ids[r].push_back(nid);
+      tot += p->node_len[nid];
+    }
+    off += sh->n_nodes[r];
+    for (int32_t h = 0; h < g.H; ++h) {
+      const int64_t i = int64_t(r) * g.H + h;
+      if (res->length[i] - res->budget[i] != tot) return TG_EINVAL;
+    }
+  }
+  return TG_OK;
+}
+
+int check_opts(const tg_plan_opts* o, int32_t ps, int32_t qb) {
+  if (!o) return TG_EINVAL;
+  if (o->chunk_bf < ps || o->chunk_bf % ps || o->chunk_i8 < qb || o->chunk_i8 % qb) return TG_EINVAL;
+  return TG_OK;
+}
+
+inline int64_t pages_of(const tg_reservation* res, const Geometry& g, int32_t r, int32_t c, int32_t t) {
+  int64_t m = 0;
+  for (int32_t h : g.heads[c]) {
+    const int64_t i = int64_t(r) * g.H + h;
+    m = std::max<int64_t>(m, t == TG_TIER_BF16 ? res->n_bf[i] : res->n_i8[i]);
+  }
+  return t == TG_TIER_BF16 ? ceil_div(m, g.ps) : m / g.qb;
+}
+
+// Share key of page j of row (r, c, t); false when the page is private.
+bool share_key(const tg_reservation* res, const Geometry& g, const Paths& paths, int32_t r,
+               int32_t c, int32_t t, int64_t j, ShareKey* key) {
+  if (!paths.on) return false;
+  const int64_t S = t == TG_TIER_BF16 ? g.ps : g.qb;
+  int64_t start = -1;
+  for (int32_t h : g.heads[c]) {
+    const int64_t i = int64_t(r) * g.H + h;
+    const int64_t s = (t == TG_TIER_I8 ? 0 : res->n_i8[i]) + j * S;
+    if (start >= 0 && s != start) return false;
+    start = s;
+  }
+  const int64_t n_fixed = res->length[int64_t(r) * g.H] - res->budget[int64_t(r) * g.H];
+  if (start + S > n_fixed) return false;
+  const int64_t last = start + S - 1;
+  int64_t acc = 0;
+  for (int32_t nid : paths.ids[r]) {
+    acc += paths.node_len[nid];
+    if (last < acc) {
+      *key = ShareKey{c, t, nid, start};
+      return true;
+    }
+  }
+  return false;  // unreachable: last < n_fixed = total path length
+}
+
+struct PlanCounts {
+  int64_t n_items = 0;
+};
+
+int count_plan(const tg_reservation* res, const Geometry& g, const tg_plan_opts* o, int64_t* n) {
+  int64_t items = 0;
+  for (int64_t i = 0; i < int64_t(g.B) * g.H; ++i)
+    items += ceil_div(res->n_i8[i], o->chunk_i8) + ceil_div(res->n_bf[i], o->chunk_bf);
+  if (items > std::numeric_limits<int32_t>::max()) return TG_EOVERFLOW;
+  *n = items;
+  return TG_OK;
+}
+
+}  // namespace
+
+extern "C" int tg_size_tables(const tg_reservation* res, int32_t ps, int32_t qb,
+                              const tg_share_desc* share, const tg_plan_opts* opts,
+                              tg_table_sizes* out) {
+  if (!out) return TG_EINVAL;
+  Geometry g;
+  int st = check_reservation(res, ps, qb, &g);
+  if (st) return st;
+  Paths paths;
+  if ((st = check_share(share, res, g, &paths))) return st;
+  if ((st = check_opts(opts, ps, qb))) return st;
+  int64_t items = 0;
+  if ((st = count_plan(res, g, opts, &items))) return st;
+  std::memset(out, 0, sizeof(*out));
+  out->n_items = static_cast<int32_t>(items);
+  for (int32_t c = 0; c < g.C; ++c)
+    for (int32_t t = 0; t < 2; ++t) {
+      int64_t stride = 0, need = 0;
+      std::unordered_map<ShareKey, int64_t, ShareKeyHash> seen;
+      for (int32_t r = 0; r < g.B; ++r) {
+        const int64_t np = pages_of(res, g, r, c, t);
+        stride = std::max(stride, np);
+        for (int64_t j = 0; j < np; ++j) {
+          ShareKey k;
+          if (share_key(res, g, paths, r, c, t, j, &k)) {
+            if (seen.emplace(k, 0).second) ++need;
+          } else {
+            ++need;
+          }
+        }
+      }
+      if (stride > std::numeric_limits<int32_t>::max()) return TG_EOVERFLOW;
+      out->stride[c][t] = static_cast<int32_t>(stride);
+      out->pages_needed[c][t] = need;
+    }
+  return TG_OK;
+}
+
+extern "C" int tg_build_tables(tg_pool* pool, const tg_reservation* res, const tg_share_desc* share,
+                               const tg_plan_opts* opts, tg_tables* out) {
+  if (!pool || !out) return TG_EINVAL;
+  tg_table_sizes sz;
+  int st = tg_size_tables(res, pool->page_size, pool->quant_block, share, opts, &sz);
+  if (st) return st;
+  Geometry g;
+  check_reservation(res, pool->page_size, pool->quant_block, &g);
+  Paths paths;
+  check_share(share, res, g, &paths);
+  if (g.C != pool->C || out->n_items != sz.n_items || !out->len || !out->part_off || !out->released ||
+      (sz.n_items > 0 && !out->work))
+    return TG_EINVAL;
+  for (int32_t c = 0; c < g.C; ++c) {
+    if (pool->cluster_size[c] != res->cluster_size[c]) return TG_EINVAL;
+    for (int32_t t = 0; t < 2; ++t) {
+      if (out->stride[c][t] != sz.stride[c][t]) return TG_EINVAL;
+      if (sz.stride[c][t] > 0 && !out->bt[c][t]) return TG_EINVAL;
+    }
+  }
+
+  // Allocate with an undo journal so that a failure leaves the pool intact.
+  enum Kind : uint8_t { kAlloc, kRef, kReg };
+  struct Entry {
+    Kind kind;
+    int8_t c, t;
+    int64_t pid;
+  };
+  std::vector<Entry> journal;
+  std::vector<ShareKey> reg_keys;
+  auto undo = [&]() {
+    for (size_t k = journal.size(); k-- > 0;) {
+      const Entry& e = journal[k];
+      SubPool& sp = pool->sub[e.c][e.t];
+      if (e.kind == kAlloc) {
+        sp.ref[e.pid] = 0;
+        sp.give_back(e.pid);
+      } else if (e.kind == kRef) {
+        --sp.ref[e.pid];
+      } else {
+        pool->registry.erase(sp.key_of[e.pid]);
+        sp.has_key[e.pid] = 0;
+      }
+    }
+  };
+  try {
+    for (int32_t r = 0; r < g.B; ++r)
+      for (int32_t c = 0; c < g.C; ++c)
+        for (int32_t t : {TG_TIER_I8, TG_TIER_BF16}) {
+          SubPool& sp = pool->sub[c][t];
+          const int64_t np = pages_of(res, g, r, c, t);
+          int32_t* row = sz.stride[c][t] ? out->bt[c][t] + int64_t(r) * sz.stride[c][t] : nullptr;
+          for (int64_t j = 0; j < np; ++j) {
+            ShareKey key;
+            const bool shared = share_key(res, g, paths, r, c, t, j, &key);
+            int64_t pid = -1;
+            if (shared) {
+              auto it = pool->registry.find(key);
+              if (it != pool->registry.end()) {
+                pid = it->second;
+                ++sp.ref[pid];
+                journal.push_back({kRef, int8_t(c), int8_t(t), pid});
+              }
+            }
+            if (pid < 0) {
+              pid = sp.take_lowest();
+              if (pid < 0) {
+                undo();
+                return TG_ENOMEM;
+              }
+              journal.push_back({kAlloc, int8_t(c), int8_t(t), pid});
+              if (shared) {
+                pool->registry.emplace(key, pid);
+                sp.key_of[pid] = key;
+                sp.has_key[pid] = 1;
+                journal.push_back({kReg, int8_t(c), int8_t(t), pid});
+              }
+            }
+            if (pid > std::numeric_limits<int32_t>::max()) {
+              undo();
+              return TG_EOVERFLOW;
+            }
+            row[j] = static_cast<int32_t>(pid);
+          }
+          for (int64_t j = np; j < sz.stride[c][t]; ++j) row[j] = -1;
+        }
+  } catch (...) {
+    undo();
+    return TG_ENOMEM;
+  }
+
+  // lengths
+  for (int64_t i = 0; i < int64_t(g.B) * g.H; ++i) {
+    out->len[2 * i] = res->n_i8[i];
+    out->len[2 * i + 1] = res->n_bf[i];
+  }
+  // plan, in natural order
+  int32_t n = 0;
+  for (int32_t r = 0; r < g.B; ++r)
+    for (int32_t h = 0; h < g.H; ++h) {
+      const int64_t i = int64_t(r) * g.H + h;
+      out->part_off[i] = n;
+      for (int32_t t : {TG_TIER_I8, TG_TIER_BF16}) {
+        const int32_t len = t == TG_TIER_BF16 ? res->n_bf[i] : res->n_i8[i];
+        const int32_t ch = t == TG_TIER_BF16 ? opts->chunk_bf : opts->chunk_i8;
+        for (int64_t t0 = 0; t0 < len; t0 += ch) {
+          int32_t* w = out->work + int64_t(n) * 6;
+          w[0] = r;
+          w[1] = h;
+          w[2] = t;
+          w[3] = static_cast<int32_t>(t0);
+          w[4] = static_cast<int32_t>(std::min<int64_t>(t0 + ch, len));
+          w[5] = n;
+          ++n;
+        }
+      }
+    }
+  out->part_off[int64_t(g.B) * g.H] = n;
+  if (opts->lpt && n > 1) {
+    std::vector<int32_t> order(n);
+    for (int32_t k = 0; k < n; ++k) order[k] = k;
+    auto cost = [&](int32_t k) {
+      const int32_t* w = out->work + int64_t(k) * 6;
+      return int64_t(w[4] - w[3]) * (w[2] == TG_TIER_BF16 ? 2 : 1);
+    };
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return cost(a) > cost(b); });
+    std::vector<int32_t> tmp(out->work, out->work + int64_t(n) * 6);
+    for (int32_t k = 0; k < n; ++k)
+      std::memcpy(out->work + int64_t(k) * 6, tmp.data() + int64_t(order[k]) * 6, 6 * sizeof(int32_t));
+  }
+  for (int32_t r = 0; r < g.B; ++r) out->released[r] = 0;
+  return TG_OK;
+}
+
+extern "C" int tg_release(tg_pool* pool, tg_tables* t, int32_t r) {
+  if (!pool || !t || !t->released || r < 0) return TG_EINVAL;
+  // B is implicit in the tables; the caller guarantees r < B.
+  if (t->released[r]) return TG_EINVAL;
+  for (int32_t c = 0; c < pool->C; ++c)
+    for (int32_t tier = 0; tier < 2; ++tier) {
+      const int32_t stride = t->stride[c][tier];
+      if (!stride) continue;
+      const int32_t* row = t->bt[c][tier] + int64_t(r) * stride;
+      SubPool& sp = pool->sub[c][tier];
+      for (int32_t j = 0; j < stride && row[j] >= 0; ++j) {
+        const int64_t pid = row[j];
+        if (pid >= sp.cap || sp.ref[pid] <= 0) return TG_EINVAL;
+      }
+    }
+  for (int32_t c = 0; c < pool->C; ++c)
+    for (int32_t tier = 0; tier < 2; ++tier) {
+      const int32_t stride = t->stride[c][tier];
+      if (!stride) continue;
+      const int32_t* row = t->bt[c][tier] + int64_t(r) * stride;
+      SubPool& sp = pool->sub[c][tier];
+      for (int32_t j = 0; j < stride && row[j] >= 0; ++j) {
+        const int64_t pid = row[j];
+        if (--sp.ref[pid] == 0) {
+          sp.give_back(pid);
+          if (sp.has_key[pid]) {
+            pool->registry.erase(sp.key_of[pid]);
+            sp.has_key[pid] = 0;
+          }
+        }
+      }
+    }
+  t->released[r] = 1;
+  return TG_OK;
+}

@@ -1,0 +1,140 @@
+// Cache fill: scatter logical K/V rows into their ragged pages, quantising the
+// oldest rows into the INT8 tier (gfx950).
+//
+// TTKV page (arXiv 2604.19769 explainer): "Tier Layout" (slow tier holds older
+// KV states at INT8), "Tier Content" (the newest share stays high precision)
+// and "Tier Interaction" (the slow tier is quantised block by block).  The
+// quantiser is symmetric absmax per (64-token block, channel), computed in
+// fp32:  s = fp16_rne(absmax / 127) (+inf saturates to 65504),
+//        q8 = s > 0 ? clamp(rint_even(x / s), -127, 127) : 0.
+// Page layouts are the ones documented in include/tg.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "tg.h"
+
+namespace {
+
+constexpr int kPage = 16;
+constexpr int kQBlock = 64;
+
+struct WriteArgs {
+  char* pool[TG_MAX_CLUSTERS][2];
+  int64_t page_bytes[TG_MAX_CLUSTERS][2];
+  const int32_t* bt[TG_MAX_CLUSTERS][2];
+  int32_t stride[TG_MAX_CLUSTERS][2];
+  const int32_t* cluster_of_head;
+  const int32_t* slot_in_cluster;
+  const int32_t* len;
+  const uint16_t* rows;
+  const int32_t* index;
+  const int64_t* offsets;
+  int32_t H;
+};
+
+// One thread per 8 channels of one bf16-tier row; 256 threads = 256/(D/8) rows.
+template <int D>
+__global__ __launch_bounds__(256) void write_bf16_kernel(WriteArgs a) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
+  const int rh = blockIdx.y;
+  const int r = rh / a.H, h = rh % a.H;
+  const int n_i8 = a.len[2 * rh], n_bf = a.len[2 * rh + 1];
+  const int u = blockIdx.x * RPB + threadIdx.x / LPR;
+  const int c8 = threadIdx.x % LPR;
+  if (u >= n_bf) return;
+  const int cl = a.cluster_of_head[h], hs = a.slot_in_cluster[h];
+  const int64_t src_row = a.index[a.offsets[rh] + n_i8 + u];
+  const uint16_t* src = a.rows + src_row * 2 * D + 8 * c8;
+  const int pid = a.bt[cl][TG_TIER_BF16][static_cast<int64_t>(r) * a.stride[cl][TG_TIER_BF16] + u / kPage];
+  char* dst = a.pool[cl][TG_TIER_BF16] + static_cast<int64_t>(pid) * a.page_bytes[cl][TG_TIER_BF16] +
+              static_cast<int64_t>(hs) * (4 * kPage * D) + (u % kPage) * D * 2 + 16 * c8;
+  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+  *reinterpret_cast<uint4*>(dst + kPage * D * 2) = *reinterpret_cast<const uint4*>(src + D);
+}
+
+// One block of 2*D threads per (r, h, 64-row INT8 block): thread = (K|V, channel).
+template <int D>
+__global__ __launch_bounds__(2 * D) void write_i8_kernel(WriteArgs a) {
+  const int rh = blockIdx.y;
+  const int r = rh / a.H, h = rh % a.H;
+  const int n_i8 = a.len[2 * rh];
+  const int b = blockIdx.x;
+  if (b * kQBlock >= n_i8) return;
+  const int kv = threadIdx.x / D, ch = threadIdx.x % D;
+  const int cl = a.cluster_of_head[h], hs = a.slot_in_cluster[h];
+  const int64_t base = a.offsets[rh] + static_cast<int64_t>(b) * kQBlock;
+  float amax = 0.f;
+  for (int t = 0; t < kQBlock; ++t) {
+    const int64_t row = a.index[base + t];
+    const float x = __uint_as_float(static_cast<uint32_t>(a.rows[row * 2 * D + kv * D + ch]) << 16);
+    amax = fmaxf(amax, fabsf(x));
+  }
+  _Float16 s16 = static_cast<_Float16>(amax / 127.0f);
+  if (__builtin_isinf(static_cast<float>(s16))) s16 = static_cast<_Float16>(65504.0f);
+  const float sf = static_cast<float>(s16);
+  const int pid = a.bt[cl][TG_TIER_I8][static_cast<int64_t>(r) * a.stride[cl][TG_TIER_I8] + b];
+  char* head = a.pool[cl][TG_TIER_I8] + static_cast<int64_t>(pid) * a.page_bytes[cl][TG_TIER_I8] +
+               static_cast<int64_t>(hs) * (2 * kQBlock * D + 4 * D);
+  int8_t* codes = reinterpret_cast<int8_t*>(head + kv * kQBlock * D);
+  for (int t = 0; t < kQBlock; ++t) {
+    const int64_t row = a.index[base + t];
+    const float x = __uint_as_float(static_cast<uint32_t>(a.rows[row * 2 * D + kv * D + ch]) << 16);
+    int q = 0;
+    if (sf > 0.f) q = static_cast<int>(fminf(fmaxf(__builtin_rintf(x / sf), -127.f), 127.f));
+    codes[t * D + ch] = static_cast<int8_t>(q);
+  }
+  reinterpret_cast<_Float16*>(head + 2 * kQBlock * D + kv * D * 2)[ch] = s16;
+}
+
+}  // namespace
+
+extern "C" int tg_write_kv(const tg_cache* c, const uint16_t* rows, const int32_t* index,
+                           const int64_t* offsets, void* stream) {
+  if (!c || !rows || !index || !offsets || !c->len || !c->cluster_of_head || !c->slot_in_cluster)
+    return TG_EINVAL;
+  if (c->B < 1 || c->n_kv_heads < 1 || c->n_clusters < 1 || c->n_clusters > TG_MAX_CLUSTERS)
+    return TG_EINVAL;
+  if (c->head_dim != 64 && c->head_dim != 128) return TG_EUNSUPPORTED;
+  if (c->page_size != kPage || c->quant_block != kQBlock) return TG_EUNSUPPORTED;
+  WriteArgs a{};
+  int32_t max_bf = 0, max_i8 = 0;
+  for (int32_t cl = 0; cl < c->n_clusters; ++cl)
+    for (int t = 0; t < 2; ++t) {
+      if (c->stride[cl][t] > 0 && (!c->bt[cl][t] || !c->pool[cl][t])) return TG_EINVAL;
+      a.pool[cl][t] = static_cast<char*>(c->pool[cl][t]);
+      a.page_bytes[cl][t] = c->page_bytes[cl][t];
+      a.bt[cl][t] = c->bt[cl][t];
+      a.stride[cl][t] = c->stride[cl][t];
+      if (t == TG_TIER_BF16) max_bf = c->stride[cl][t] > max_bf ? c->stride[cl][t] : max_bf;
+      else max_i8 = c->stride[cl][t] > max_i8 ? c->stride[cl][t] : max_i8;
+    }
+  a.cluster_of_head = c->cluster_of_head;
+  a.slot_in_cluster = c->slot_in_cluster;
+  a.len = c->len;
+  a.rows = rows;
+  a.index = index;
+  a.offsets = offsets;
+  a.H = c->n_kv_heads;
+  const int64_t pairs = static_cast<int64_t>(c->B) * c->n_kv_heads;
+  if (pairs > 65535) return TG_EUNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int d = c->head_dim;
+  const int rpb = 256 / (d / 8);
+  if (max_bf > 0) {
+    const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(max_bf) * kPage + rpb - 1) / rpb),
+                    static_cast<unsigned>(pairs));
+    if (d == 128) hipLaunchKernelGGL(write_bf16_kernel<128>, grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(write_bf16_kernel<64>, grid, dim3(256), 0, st, a);
+    if (hipGetLastError() != hipSuccess) return TG_EDEVICE;
+  }
+  if (max_i8 > 0) {
+    const dim3 grid(static_cast<unsigned>(max_i8), static_cast<unsigned>(pairs));
+    if (d == 128) hipLaunchKernelGGL(write_i8_kernel<128>, grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(write_i8_kernel<64>, grid, dim3(128), 0, st, a);
+    if (hipGetLastError() != hipSuccess) return TG_EDEVICE;
+  }
+  return TG_OK;
+}

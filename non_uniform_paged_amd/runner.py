@@ -1,0 +1,127 @@
+"""Drive one seeded workload through the library: admission, cache fill and
+decode steps on one GPU.
+
+This is the harness used by the GPU tests, ``smoke()`` and ``bench.py``; it
+only marshals arguments into the C ABI (``api``) and owns device memory
+through PyTorch.  ``w`` is any object with the fields of
+``workloads.Workload``.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+from . import api
+
+
+def reserve_workload(w) -> api.Reservation:
+    return api.tg_reserve(w.head_rank, w.ratio_hi_ppm, w.ratio_lo_ppm, w.n_clusters, w.recent_ppm,
+                          w.quant_block, w.n_comp, w.n_fixed, w.budget_override)
+
+
+def share_of(w) -> Optional[api.Share]:
+    if getattr(w, "paths", None) is None:
+        return None
+    n_nodes = [len(p) for p in w.paths]
+    ids = [n for p in w.paths for n in p]
+    return api.Share(n_nodes, ids, w.node_len)
+
+
+class Prepared:
+    """A populated cache plus the buffers of one decode step."""
+
+    def __init__(self, w, chunk_bf: int = 512, chunk_i8: int = 1024, lpt: bool = True,
+                 slack_pages: int = 0, shift_pages: int = 0, device: str = "cuda"):
+        import torch
+
+        self.w = w
+        dev = torch.device(device)
+        self.res = reserve_workload(w)
+        self.share = share_of(w)
+        sizes = api.tg_size_tables(self.res, w.page_size, w.quant_block, self.share, chunk_bf, chunk_i8, lpt)
+        need = sizes["pages_needed"]
+        C = self.res.C
+        extra = slack_pages + shift_pages
+        self.pool = api.Pool(self.res.cluster_size, w.d, w.page_size, w.quant_block,
+                             [need[c][1] + extra for c in range(C)], [need[c][0] + extra for c in range(C)])
+        if shift_pages:
+            # occupy the lowest pages first so that this batch lands elsewhere
+            filler = api.tg_reserve(w.head_rank, 10**6, 10**6, C, 10**6, w.quant_block,
+                                    [shift_pages * w.page_size], None, None)
+            ftab = api.tg_build_tables(self.pool, filler, None, w.page_size * 4, w.quant_block, False)
+        self.tables = api.tg_build_tables(self.pool, self.res, self.share, chunk_bf, chunk_i8, lpt)
+        if shift_pages:
+            api.tg_release(self.pool, ftab, 0)
+        self.cache = api.DeviceCache(self.pool, self.res, self.tables, dev)
+
+        rows, index, offsets = w.source_buffer(self.res.length)
+        rows_t = torch.from_numpy(rows.view(np.uint16).reshape(-1).view(np.int16)).to(dev)
+        index_t = torch.from_numpy(index).to(dev)
+        off_t = torch.from_numpy(offsets).to(dev)
+        del rows
+        api.tg_write_kv(self.cache, rows_t, index_t, off_t)
+        torch.cuda.synchronize(dev)
+        del rows_t, index_t, off_t
+
+        qn = w.q()
+        if w.q_dtype == "f32":
+            self.q = torch.from_numpy(np.ascontiguousarray(qn, dtype=np.float32)).to(dev)
+        else:
+            self.q = torch.from_numpy(qn.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
+        ws = api.tg_decode_workspace_bytes(self.tables.n_items, w.Hq // w.Hkv, w.d)
+        self.workspace = torch.empty(max(ws // 4, 1), dtype=torch.float32, device=dev)
+
+    # ------------------------------------------------------------------ run
+    def step(self, stream=None):
+        api.tg_decode_attn(self.cache, self.q, self.out, self.workspace, self.w.Hq, 0.0, stream=stream)
+
+    def output(self) -> np.ndarray:
+        import torch
+        torch.cuda.synchronize()
+        return self.out.cpu().numpy()
+
+    # ------------------------------------------------------------------ accounting
+    def traffic(self) -> dict:
+        """Algorithmic bytes of one step.
+
+        ``effective``: every (r, h) pays for the rows it attends over (a row
+        is 4d bytes bf16, 2d bytes INT8, plus 4d bytes of scales per INT8
+        block), plus q, o and the tables it reads.  ``roofline``: the same, but
+        a shared page's head block counts once however many sequences read
+        it.  Flops: 4 * d * G per retained row per KV-head.
+        """
+        w, res, t = self.w, self.res, self.tables
+        d, G = w.d, w.Hq // w.Hkv
+        qbytes = 4 if w.q_dtype == "f32" else 2
+        n_i8 = res.n_i8.astype(np.int64)
+        n_bf = res.n_bf.astype(np.int64)
+        kv_eff = int((n_bf * 4 * d).sum() + (n_i8 * 2 * d).sum() + (n_i8 // w.quant_block * 4 * d).sum())
+        # unique page blocks: (cluster, tier, page id, head slot) -> rows read
+        seen = {}
+        for r in range(w.B):
+            for h in range(w.Hkv):
+                c = int(res.cluster_of_head[h])
+                s = int(res.slot_in_cluster[h])
+                for tier, n, S in ((0, int(n_i8[r, h]), w.quant_block), (1, int(n_bf[r, h]), w.page_size)):
+                    npg = -(-n // S)
+                    ids = t.bt[c][tier][r, :npg]
+                    for j, pid in enumerate(ids):
+                        rows = min(S, n - j * S)
+                        key = (c, tier, int(pid), s)
+                        if seen.get(key, 0) < rows:
+                            seen[key] = rows
+        kv_roof = 0
+        for (c, tier, pid, s), rows in seen.items():
+            kv_roof += rows * 4 * d if tier == 1 else rows * 2 * d + 4 * d
+        q_o = w.B * w.Hq * d * (qbytes + 4)
+        tables = t.n_items * 24 + (w.B * w.Hkv + 1) * 4 + sum(
+            int(-(-n_bf[r, h] // w.page_size) + n_i8[r, h] // w.quant_block) * 4
+            for r in range(w.B) for h in range(w.Hkv))
+        rows_total = int(n_bf.sum() + n_i8.sum())
+        return {"kv_effective": kv_eff, "kv_roofline": kv_roof, "q_o": q_o, "tables": tables,
+                "effective": kv_eff + q_o + tables, "roofline": kv_roof + q_o + tables,
+                "head_rows": rows_total, "flops": 4 * d * G * rows_total,
+                "n_items": t.n_items}

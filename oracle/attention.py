@@ -87,21 +87,30 @@ def q_f64(w) -> np.ndarray:
     return np.asarray(q, np.float64) if w.q_dtype == "f32" else bf16_to_f64(q)
 
 
-def head_rows(w, res: planner.Reservation, r: int, h: int) -> Tuple[np.ndarray, np.ndarray]:
-    """fp64 K, V rows (r, h) attends over: bf16 rows, with the oldest n_i8
-    rows replaced by their INT8 dequantised values."""
-    L = res.L[r][h]
-    K16, V16 = w.logical_kv(r, h, L)
+def rows_f64(K16: np.ndarray, V16: np.ndarray, n_i8: int, qb: int) -> Tuple[np.ndarray, np.ndarray]:
+    """fp64 K, V a sequence attends over: its bf16 rows, with the oldest
+    ``n_i8`` rows replaced by their INT8 dequantised values."""
     K = bf16_to_f64(K16)
     V = bf16_to_f64(V16)
-    n8 = res.n_i8[r][h]
-    if n8:
-        qb = w.quant_block
-        qk, sk = quant.quantize_rows(K[:n8].astype(np.float32), qb)
-        qv, sv = quant.quantize_rows(V[:n8].astype(np.float32), qb)
-        K[:n8] = quant.dequantize_rows(qk, sk, qb)
-        V[:n8] = quant.dequantize_rows(qv, sv, qb)
+    if n_i8:
+        qk, sk = quant.quantize_rows(K[:n_i8].astype(np.float32), qb)
+        qv, sv = quant.quantize_rows(V[:n_i8].astype(np.float32), qb)
+        K[:n_i8] = quant.dequantize_rows(qk, sk, qb)
+        V[:n_i8] = quant.dequantize_rows(qv, sv, qb)
     return K, V
+
+
+def head_rows(w, res: planner.Reservation, r: int, h: int) -> Tuple[np.ndarray, np.ndarray]:
+    """fp64 K, V rows of (r, h) (see ``rows_f64``)."""
+    K16, V16 = w.logical_kv(r, h, res.L[r][h])
+    return rows_f64(K16, V16, res.n_i8[r][h], w.quant_block)
+
+
+def decode_rows(q_group: np.ndarray, K16: np.ndarray, V16: np.ndarray, n_i8: int, qb: int,
+                scale: float) -> np.ndarray:
+    """Outputs [G][d] of one GQA group from its raw rows (bf16 bits)."""
+    K, V = rows_f64(K16, V16, n_i8, qb)
+    return attend(q_group, K, V, scale)
 
 
 def decode_pair(w, res: planner.Reservation, r: int, h: int, q: Optional[np.ndarray] = None,
@@ -112,8 +121,8 @@ def decode_pair(w, res: planner.Reservation, r: int, h: int, q: Optional[np.ndar
         q = q_f64(w)
     if scale is None:
         scale = 1.0 / math.sqrt(w.d)
-    K, V = head_rows(w, res, r, h)
-    return attend(q[r, h * G:(h + 1) * G], K, V, scale)
+    K16, V16 = w.logical_kv(r, h, res.L[r][h])
+    return decode_rows(q[r, h * G:(h + 1) * G], K16, V16, res.n_i8[r][h], w.quant_block, scale)
 
 
 def decode(w, res: Optional[planner.Reservation] = None,

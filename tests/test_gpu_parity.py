@@ -1,0 +1,268 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Tolerance (stated by the workload specification): every fp32 output element
+satisfies |gpu - oracle| <= 2e-3 + 1e-2 * |oracle|.  Integer work (budgets,
+tables, INT8 codes and scales) must match bit for bit."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from oracle import planner as P
+from oracle import quant as Q
+from workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL = 2e-3, 1e-2
+
+
+def _need_gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _prep(w, **kw):
+    from non_uniform_paged_amd.runner import Prepared
+    return Prepared(w, **kw)
+
+
+def _check(got, ref, pairs, G, what):
+    worst_abs = worst_rel = 0.0
+    for r, h in pairs:
+        g = got[r, h * G:(h + 1) * G]
+        o = ref[r, h * G:(h + 1) * G]
+        err = np.abs(g - o)
+        assert np.all(np.isfinite(g)), (what, r, h)
+        bad = err > ATOL + RTOL * np.abs(o)
+        assert not bad.any(), f"{what}: (r={r}, h={h}) max err {err.max():.3g}"
+        worst_abs = max(worst_abs, float(err.max()))
+        big = np.abs(o) >= 1e-3
+        if big.any():
+            worst_rel = max(worst_rel, float((err[big] / np.abs(o[big])).max()))
+    _say(f"{what}: max-abs {worst_abs:.3g} max-rel {worst_rel:.3g} over {len(pairs)} (r,h)")
+    return worst_abs, worst_rel
+
+
+def _run_and_compare(w, pairs=None, what="", **kw):
+    _say(f"case {what or w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} d={w.d} C={w.n_clusters} {kw}")
+    p = _prep(w, **kw)
+    p.step()
+    got = p.output()
+    res_o = A.reserve_for(w)
+    assert np.array_equal(p.res.length, np.array(res_o.L))
+    if pairs is None:
+        pairs = [(r, h) for r in range(w.B) for h in range(w.Hkv)]
+    ref = A.decode(w, res_o, pairs)
+    _check(got, ref, pairs, w.Hq // w.Hkv, what or w.name)
+    return p, got
+
+
+SMALL = {
+    "tiny": {},
+    "llama8b": dict(B=4, ctx=("uniform", 300, 1500)),
+    "ragged": dict(B=8, ctx=("loguniform", 64, 4000)),
+    "tiered": dict(B=2, ctx=("fixed", 5000)),
+    "radix": dict(B=10, share=dict(prefix=200, branch=50, n_branches=4, suffix=(8, 300))),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_configs_all_outputs(name):
+    _need_gpu()
+    _run_and_compare(make_workload(name, **SMALL[name]), chunk_bf=64, chunk_i8=128)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_configs_default_plan(name):
+    _need_gpu()
+    _run_and_compare(make_workload(name, **SMALL[name]))
+
+
+def _sample_pairs(w, k, seed):
+    rnd = np.random.default_rng(seed)
+    idx = rnd.choice(w.B * w.Hkv, size=min(k, w.B * w.Hkv), replace=False)
+    return sorted((int(i) // w.Hkv, int(i) % w.Hkv) for i in idx)
+
+
+@pytest.mark.parametrize("name,k", [("llama8b", 24), ("ragged", 24), ("tiered", 8), ("radix", 24)])
+def test_full_size_configs_sampled(name, k):
+    _need_gpu()
+    w = make_workload(name)
+    _run_and_compare(w, pairs=_sample_pairs(w, k, 11), what=f"{name}-full")
+
+
+def test_single_row_returns_value_row_exactly():
+    torch = _need_gpu()
+    w = make_workload("llama8b", B=3, ctx=("uniform", 20, 40), budget=None)
+    w.budget_override = np.ones(w.B * w.Hkv, np.int32)
+    p = _prep(w)
+    p.step()
+    got = p.output()
+    for r in range(w.B):
+        for h in range(w.Hkv):
+            K16, V16 = w.logical_kv(r, h, 1)
+            v = A.bf16_to_f64(V16)[0].astype(np.float32)
+            for g in range(4):
+                assert np.array_equal(got[r, 4 * h + g], v)
+
+
+def test_page_placement_invariance_bitwise():
+    _need_gpu()
+    w = make_workload("ragged", B=6, ctx=("loguniform", 100, 3000))
+    a = _prep(w, chunk_bf=128)
+    a.step()
+    ga = a.output()
+    b = _prep(w, chunk_bf=128, shift_pages=37)
+    assert any((b.tables.bt[c][1] != a.tables.bt[c][1]).any() for c in range(w.n_clusters))
+    b.step()
+    gb = b.output()
+    assert np.array_equal(ga, gb)
+
+
+@pytest.mark.parametrize("C", [1, 2, 8])
+def test_cluster_count_invariance(C):
+    _need_gpu()
+    w = make_workload("llama8b", B=3, ctx=("uniform", 400, 900), n_clusters=C)
+    _run_and_compare(w, what=f"llama8b-C{C}")
+
+
+@pytest.mark.parametrize("chunk", [16, 48, 4096])
+def test_split_invariance(chunk):
+    _need_gpu()
+    w = make_workload("llama8b", B=2, ctx=("uniform", 600, 1200))
+    _run_and_compare(w, what=f"chunk{chunk}", chunk_bf=chunk, lpt=chunk != 48)
+
+
+def test_uniform_budgets_dense():
+    _need_gpu()
+    w = make_workload("llama8b", B=2, ctx=("uniform", 300, 700), ratio_ppm=(10**6, 10**6), n_clusters=1)
+    _run_and_compare(w, what="dense")
+
+
+def _read_i8_pages(p, r, h):
+    """Codes and scales of (r, h)'s INT8 rows, read back from the device pool
+    through the layout include/tg.h documents."""
+    w = p.w
+    d, qb = w.d, w.quant_block
+    c = int(p.res.cluster_of_head[h])
+    s = int(p.res.slot_in_cluster[h])
+    n8 = int(p.res.n_i8[r, h])
+    pb = p.pool.page_bytes(c, 0)
+    hb = 2 * qb * d + 4 * d
+    pool = p.cache.pools[c][0].cpu().numpy()
+    kq, vq, ks, vs = [], [], [], []
+    for j in range(n8 // qb):
+        pid = int(p.tables.bt[c][0][r, j])
+        base = pid * pb + s * hb
+        blk = pool[base:base + hb]
+        kq.append(blk[:qb * d].view(np.int8).reshape(qb, d))
+        vq.append(blk[qb * d:2 * qb * d].view(np.int8).reshape(qb, d))
+        ks.append(blk[2 * qb * d:2 * qb * d + 2 * d].view(np.float16))
+        vs.append(blk[2 * qb * d + 2 * d:].view(np.float16))
+    return np.concatenate(kq), np.concatenate(vq), np.stack(ks), np.stack(vs)
+
+
+def test_int8_codes_and_scales_bit_exact():
+    _need_gpu()
+    w = make_workload("tiered", B=2, Hq=8, Hkv=2, ctx=("fixed", 3000))
+    p = _prep(w)
+    for r in range(w.B):
+        for h in range(w.Hkv):
+            n8 = int(p.res.n_i8[r, h])
+            K16, V16 = w.logical_kv(r, h, int(p.res.length[r, h]))
+            kq, vq, ks, vs = _read_i8_pages(p, r, h)
+            from workloads import bf16_bits_to_f32
+            okq, oks = Q.quantize_rows(bf16_bits_to_f32(K16[:n8]), 64)
+            ovq, ovs = Q.quantize_rows(bf16_bits_to_f32(V16[:n8]), 64)
+            assert np.array_equal(kq, okq) and np.array_equal(vq, ovq)
+            assert np.array_equal(ks.view(np.uint16), oks.view(np.uint16))
+            assert np.array_equal(vs.view(np.uint16), ovs.view(np.uint16))
+
+
+class _ExactRows:
+    """Rows that are integer multiples of 2^-5 with a +-127 code in the first
+    row of every 64-row block, so symmetric absmax INT8 reproduces them
+    exactly (step 2^-5)."""
+
+    @staticmethod
+    def make(base, recent_ppm):
+        import dataclasses
+        from workloads.gen import Workload, bf16_round
+
+        class W(Workload):
+            def stream_rows(self, key, n):
+                tag, a, h = key
+                rr = np.random.default_rng([0 if tag == "seq" else 1, a, h])
+                k = rr.integers(-127, 128, size=(n, self.d))
+                v = rr.integers(-127, 128, size=(n, self.d))
+                k[::64] = 127
+                v[::64] = -127
+                return (bf16_round((k * 2.0 ** -5).astype(np.float32)),
+                        bf16_round((v * 2.0 ** -5).astype(np.float32)))
+
+        fields = {f.name: getattr(base, f.name) for f in dataclasses.fields(base)}
+        fields["recent_ppm"] = recent_ppm
+        return W(**fields)
+
+
+def test_int8_tier_equals_bf16_tier_on_exact_values():
+    _need_gpu()
+    base = make_workload("tiered", B=2, Hq=8, Hkv=2, ctx=("fixed", 1024))
+    a = _prep(_ExactRows.make(base, 10**6))
+    b = _prep(_ExactRows.make(base, 125_000))
+    assert int(b.res.n_i8.min()) > 0 and int(a.res.n_i8.max()) == 0
+    a.step()
+    b.step()
+    ga, gb = a.output(), b.output()
+    _say(f"int8-vs-bf16 exact rows: max diff {np.max(np.abs(ga - gb)):.3g}")
+    assert np.max(np.abs(ga - gb)) < 1e-5
+
+
+def test_merge_partials_against_lse_oracle():
+    torch = _need_gpu()
+    from non_uniform_paged_amd import api
+    rnd = np.random.default_rng(5)
+    G, d = 4, 128
+    counts = [1, 3, 7, 0, 2, 16]
+    n_slots = sum(counts)
+    m = rnd.normal(0, 5, size=(n_slots, G)).astype(np.float32)
+    l = rnd.uniform(0.5, 50, size=(n_slots, G)).astype(np.float32)
+    acc = rnd.normal(0, 3, size=(n_slots, G, d)).astype(np.float32)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    ws = np.concatenate([acc.reshape(-1), np.stack([m, l], -1).reshape(-1)]).astype(np.float32)
+    out = torch.empty((len(counts) * G, d), dtype=torch.float32, device="cuda")
+    api.tg_merge_partials(torch.from_numpy(ws).cuda(), n_slots, len(counts), G, d,
+                          torch.from_numpy(off).cuda(), out)
+    got = out.cpu().numpy().reshape(len(counts), G, d)
+    for p_, cnt in enumerate(counts):
+        if cnt == 0:
+            assert np.all(got[p_] == 0)
+            continue
+        sl = slice(off[p_], off[p_ + 1])
+        ref = A.lse_merge(m[sl], l[sl], acc[sl])
+        assert np.all(np.abs(got[p_] - ref) <= 1e-5 + 1e-5 * np.abs(ref))
+
+
+@pytest.mark.parametrize("G,d,qd", [(1, 128, "bf16"), (8, 128, "bf16"), (2, 64, "bf16"), (8, 64, "f32"), (4, 128, "f32")])
+def test_head_shapes(G, d, qd):
+    _need_gpu()
+    w = make_workload("llama8b", B=2, Hq=2 * G, Hkv=2, d=d, q_dtype=qd, ctx=("uniform", 200, 600),
+                      n_clusters=2, recent_ppm=300_000)
+    _run_and_compare(w, what=f"G{G}-d{d}-{qd}", chunk_bf=96, chunk_i8=64)
+
+
+def test_all_int8_and_empty_bf16_tier():
+    _need_gpu()
+    w = make_workload("tiered", B=2, Hq=8, Hkv=2, ctx=("fixed", 640), recent_ppm=0)
+    p, _ = _run_and_compare(w, what="int8-only")
+    assert int(p.res.n_bf.max()) == 0

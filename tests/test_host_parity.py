@@ -1,0 +1,192 @@
+"""Host planner of libtg.so (C++) against the integer oracle, bit for bit.
+
+Runs on the CPU: only host entry points are called.  Also checks that the
+library loads and exports every function include/tg.h declares."""
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+from oracle import planner as P
+from workloads import make_workload
+from workloads.gen import share_arrays
+
+tg = pytest.importorskip("non_uniform_paged_amd")
+from non_uniform_paged_amd import _lib  # noqa: E402
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "tg.h")
+
+
+def test_library_exports_every_declared_symbol():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = set(re.findall(r"\b(tg_[a-z_0-9]+)\s*\(", text))
+    assert len(names) >= 14
+    L = _lib.lib()
+    for n in sorted(names):
+        assert hasattr(L, n), n
+    assert names == set(_lib.SIGNATURES), names ^ set(_lib.SIGNATURES)
+
+
+def _both(w, chunk_bf=512, chunk_i8=1024, lpt=True, slack=0):
+    res_o = P.reserve(w.head_rank, w.ratio_hi_ppm, w.ratio_lo_ppm, w.n_clusters, w.recent_ppm,
+                      w.quant_block, w.n_comp, w.n_fixed, w.budget_override)
+    res_g = tg.tg_reserve(w.head_rank, w.ratio_hi_ppm, w.ratio_lo_ppm, w.n_clusters, w.recent_ppm,
+                          w.quant_block, w.n_comp, w.n_fixed, w.budget_override)
+    return res_o, res_g
+
+
+def _compare_reservation(res_o, res_g):
+    assert np.array_equal(res_g.budget, np.array(res_o.budget))
+    assert np.array_equal(res_g.length, np.array(res_o.L))
+    assert np.array_equal(res_g.n_i8, np.array(res_o.n_i8))
+    assert np.array_equal(res_g.n_bf, np.array(res_o.n_bf))
+    assert list(res_g.cluster_of_head) == res_o.cluster_of_head
+    assert list(res_g.slot_in_cluster) == res_o.slot_in_cluster
+    assert list(res_g.cluster_size) == res_o.cluster_size
+
+
+def _share(w):
+    if w.paths is None:
+        return None, ()
+    n_nodes, ids, node_len = share_arrays(w)
+    return tg.Share(n_nodes, ids, node_len), (w.n_fixed, w.paths, w.node_len)
+
+
+def _tables_parity(w, chunk_bf=512, chunk_i8=1024, lpt=True, slack=3):
+    res_o, res_g = _both(w)
+    _compare_reservation(res_o, res_g)
+    share, sh_o = _share(w)
+    need_bf, need_i8 = P.pages_needed(res_o, w.page_size, w.quant_block, *sh_o)
+    sizes = tg.tg_size_tables(res_g, w.page_size, w.quant_block, share, chunk_bf, chunk_i8, lpt)
+    assert [row[1] for row in sizes["pages_needed"]] == need_bf
+    assert [row[0] for row in sizes["pages_needed"]] == need_i8
+    pool_g = tg.Pool(res_g.cluster_size, w.d, w.page_size, w.quant_block,
+                     [x + slack for x in need_bf], [x + slack for x in need_i8])
+    pool_o = P.Pool([x + slack for x in need_bf], [x + slack for x in need_i8])
+    t_g = tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt)
+    t_o = P.build_tables(pool_o, res_o, w.page_size, w.quant_block, chunk_bf, chunk_i8, lpt, *sh_o)
+    for c in range(w.n_clusters):
+        for t in range(2):
+            assert t_g.stride[c][t] == t_o.stride[c][t]
+            if t_o.stride[c][t]:
+                assert np.array_equal(t_g.bt[c][t], np.array(t_o.bt[c][t], dtype=np.int32)), (c, t)
+            assert pool_g.free_pages(c, t) == pool_o.free_pages(c, t)
+    assert np.array_equal(t_g.len, np.array(t_o.lens, dtype=np.int32))
+    assert np.array_equal(t_g.plan, np.array(t_o.work, dtype=np.int32).reshape(-1, 6))
+    assert list(t_g.part_off) == t_o.part_off
+    return res_o, res_g, pool_o, pool_g, t_o, t_g
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama8b", "ragged", "tiered", "radix"])
+def test_full_size_configs_bit_exact(name):
+    w = make_workload(name)
+    res_o, res_g, pool_o, pool_g, t_o, t_g = _tables_parity(w)
+    # refcounts agree page by page on a sample of pages
+    for c in range(w.n_clusters):
+        for t in range(2):
+            cap = pool_g.capacity(c, t)
+            for pid in range(0, cap, max(1, cap // 97)):
+                assert pool_g.refcount(c, t, pid) == pool_o.refcount(c, t, pid)
+
+
+def test_release_and_reallocation_bit_exact():
+    w = make_workload("radix", B=24, share=dict(prefix=100, branch=37, n_branches=3, suffix=(5, 90)))
+    res_o, res_g, pool_o, pool_g, t_o, t_g = _tables_parity(w, chunk_bf=64, slack=40)
+    rnd = random.Random(7)
+    order = list(range(w.B))
+    rnd.shuffle(order)
+    for r in order[:15]:
+        tg.tg_release(pool_g, t_g, r)
+        P.release(pool_o, t_o.pages[r])
+        for c in range(w.n_clusters):
+            for t in range(2):
+                assert pool_g.free_pages(c, t) == pool_o.free_pages(c, t)
+    with pytest.raises(tg.TGError) as e:
+        tg.tg_release(pool_g, t_g, order[0])
+    assert e.value.name == "TG_EINVAL"
+    # a second batch lands in the holes, lowest id first, identically
+    w2 = make_workload("radix", B=9, share=dict(prefix=100, branch=37, n_branches=3, suffix=(5, 90)))
+    res2_o, res2_g = _both(w2)
+    share2, sh2_o = _share(w2)
+    t2_g = tg.tg_build_tables(pool_g, res2_g, share2, 64, 1024, True)
+    t2_o = P.build_tables(pool_o, res2_o, w2.page_size, w2.quant_block, 64, 1024, True, *sh2_o)
+    for c in range(w2.n_clusters):
+        assert np.array_equal(t2_g.bt[c][1], np.array(t2_o.bt[c][1], dtype=np.int32))
+
+
+def test_randomised_small_cases_bit_exact():
+    rnd = random.Random(2026)
+    for case in range(120):
+        H = rnd.choice([1, 2, 3, 4, 5, 8])
+        C = rnd.randint(1, H)
+        B = rnd.randint(1, 5)
+        hi = rnd.randint(1, 10**6)
+        lo = rnd.randint(1, hi)
+        qb = rnd.choice([4, 8, 64])
+        ps = rnd.choice([2, 4, 16])
+        recent = rnd.choice([0, 1, 125_000, 500_000, 10**6])
+        rank = list(range(H))
+        rnd.shuffle(rank)
+        n_comp = [rnd.randint(1, 300) for _ in range(B)]
+        use_share = rnd.random() < 0.5
+        node_len = [rnd.randint(0, 40) for _ in range(4)]
+        paths = [[0, rnd.randint(1, 3)] for _ in range(B)] if use_share else None
+        n_fixed = [sum(node_len[n] for n in p) for p in paths] if use_share else [0] * B
+        override = [rnd.randint(1, n) for n in n_comp for _ in range(H)] if rnd.random() < 0.3 else None
+        res_o = P.reserve(rank, hi, lo, C, recent, qb, n_comp, n_fixed, override)
+        res_g = tg.tg_reserve(rank, hi, lo, C, recent, qb, n_comp, n_fixed, override)
+        _compare_reservation(res_o, res_g)
+        sh_o = (n_fixed, paths, node_len) if use_share else ()
+        share = tg.Share([2] * B, [x for p in paths for x in p], node_len) if use_share else None
+        chunk_bf = ps * rnd.randint(1, 6)
+        chunk_i8 = qb * rnd.randint(1, 3)
+        lpt = rnd.random() < 0.5
+        need_bf, need_i8 = P.pages_needed(res_o, ps, qb, *sh_o)
+        cap_bf = [n + rnd.randint(-1, 2) for n in need_bf]
+        cap_i8 = [n + rnd.randint(-1, 2) for n in need_i8]
+        cap_bf = [max(0, x) for x in cap_bf]
+        cap_i8 = [max(0, x) for x in cap_i8]
+        pool_g = tg.Pool(res_g.cluster_size, 16, ps, qb, cap_bf, cap_i8)
+        pool_o = P.Pool(cap_bf, cap_i8)
+        try:
+            t_o = P.build_tables(pool_o, res_o, ps, qb, chunk_bf, chunk_i8, lpt, *sh_o)
+        except P.OracleError as e:
+            assert e.code == "ENOMEM"
+            with pytest.raises(tg.TGError) as ge:
+                tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt)
+            assert ge.value.name == "TG_ENOMEM"
+            for c in range(C):
+                for t in range(2):
+                    assert pool_g.free_pages(c, t) == pool_g.capacity(c, t)
+            continue
+        t_g = tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt)
+        for c in range(C):
+            for t in range(2):
+                if t_o.stride[c][t]:
+                    assert np.array_equal(t_g.bt[c][t], np.array(t_o.bt[c][t], dtype=np.int32)), case
+        assert np.array_equal(t_g.plan, np.array(t_o.work, dtype=np.int32).reshape(-1, 6)), case
+        assert list(t_g.part_off) == t_o.part_off
+
+
+def test_error_codes():
+    w = make_workload("tiny")
+    with pytest.raises(tg.TGError) as e:
+        tg.tg_reserve([0, 0], 10, 10, 1, 10**6, 64, [5])
+    assert e.value.name == "TG_EINVAL"
+    with pytest.raises(tg.TGError) as e:
+        tg.tg_reserve([0, 1], 10, 10, 1, 10**6, 64, [2**31 - 5], [10])
+    assert e.value.name == "TG_EOVERFLOW"
+    res = tg.tg_reserve(w.head_rank, 10**6, 10**6, 2, 10**6, 64, w.n_comp)
+    with pytest.raises(tg.TGError) as e:
+        tg.tg_size_tables(res, 16, 64, None, chunk_bf=24)
+    assert e.value.name == "TG_EINVAL"
+    with pytest.raises(tg.TGError) as e:
+        tg.Pool([1, 1], 64, 0, 64, [1, 1], [0, 0])
+    assert e.value.name == "TG_EINVAL"
+    # share paths inconsistent with n_fixed
+    with pytest.raises(tg.TGError) as e:
+        tg.tg_size_tables(res, 16, 64, tg.Share([1, 1], [0, 0], [5]))
+    assert e.value.name == "TG_EINVAL"
