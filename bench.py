@@ -6,9 +6,11 @@
 One step = the whole decode hot path over one batch: the split-K kernel over
 every plan item (bf16 pages and INT8 blocks) and the log-sum-exp merge, on a
 cache that is already resident in HBM.  Before every timed step a 1 GiB
-device write evicts L2 and the 256 MB last-level cache (outside the timed
-events).  Each step is bracketed by HIP events on the stream the kernels run
-on; the K steps together are bracketed by device synchronisation.
+device read evicts L2 and the 256 MB last-level cache with clean lines
+(outside the timed events; ``--flush write`` uses a 1 GiB write instead, whose
+dirty lines then drain to HBM during the timed kernels).  Each step is
+bracketed by HIP events on the stream the kernels run on; the K steps together
+are bracketed by device synchronisation.
 
 Prints one JSON line (see the ``result`` dict at the end).  ``--gpus`` above 1
 is refused: this build measures one GPU.
@@ -111,10 +113,12 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="llama8b", choices=sorted(DESCRIPTIONS))
-    ap.add_argument("--chunk-bf", type=int, default=512)
+    ap.add_argument("--chunk-bf", type=int, default=1024)
     ap.add_argument("--chunk-i8", type=int, default=1024)
-    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--flush", choices=["read", "write", "none"], default="read")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -125,6 +129,20 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / 5
+        print(json.dumps({"copy_bytes_each_way": n, "copies": 5, "ms_per_copy": round(dt * 1e3, 4),
+                          "GBps_read_plus_write": round(2 * n / dt / 1e9, 1)}), flush=True)
+        return
 
     from non_uniform_paged_amd import api
     from non_uniform_paged_amd.runner import Prepared
@@ -138,7 +156,13 @@ def main():
     tr = prep.traffic()
     G = w.Hq // w.Hkv
     stream = torch.cuda.current_stream()
-    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = None if args.flush == "none" else torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def evict(i):
+        if args.flush == "read":
+            torch.amax(flush)
+        elif args.flush == "write":
+            flush.fill_(i & 0xFF)
 
     def one_step(evs=None):
         if evs is not None:
@@ -152,16 +176,14 @@ def main():
             evs[2].record(stream)
 
     for i in range(args.warmup):
-        if flush is not None:
-            flush.fill_(i & 0xFF)
+        evict(i)
         one_step()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(args.steps):
-        if flush is not None:
-            flush.fill_((i + 1) & 0xFF)
+        evict(i + 1)
         one_step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -203,7 +225,7 @@ def main():
         "p90_ms": round(float(np.percentile(step_ms, 90)), 5),
         "split_ms": round(float(split_ms.mean()), 5),
         "merge_ms": round(float(merge_ms.mean()), 5),
-        "cache_flush_between_steps": flush is not None,
+        "cache_eviction_between_steps": args.flush,
         "wall_s_timed_region": round(wall, 4),
         "prepare_s": round(t_prep, 2),
         "roofline": {

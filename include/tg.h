@@ -122,7 +122,11 @@ int tg_reserve(const tg_budget_table* table, int32_t B, const int32_t* n_comp,
  * (cluster, tier).  A page of cluster c holds S token slots for each of its
  * n_c heads, S = page_size (bf16) or quant_block (INT8).  Device layout of
  * one page, head slot s = slot_in_cluster at byte offset s * head_bytes:
- *   bf16 : K [S][d] bf16, then V [S][d] bf16          head_bytes = 4*S*d
+ *   bf16 : K block then V block, 2*S*d bytes each      head_bytes = 4*S*d
+ *          (S = 16; element (row t, channel c) at byte
+ *           K: ((c>>5)*64 + ((c>>3)&3)*16 + t)*16 + (c&7)*2
+ *           V: ((c>>5)*64 + (t>>2)*16 + (c&15))*16 + ((c>>4)&1)*8 + (t&3)*2,
+ *           so that each contiguous 1 KiB is one matrix-core operand)
  *   INT8 : K codes [S][d] int8, V codes [S][d] int8,
  *          K scales [d] fp16, V scales [d] fp16       head_bytes = 2*S*d + 4*d
  * Pages are handed out lowest free id first; shared pages are
@@ -224,6 +228,10 @@ typedef struct tg_cache {
   const int32_t* cluster_of_head;            /* device [H] */
   const int32_t* slot_in_cluster;            /* device [H] */
   const int32_t* len;                        /* device [B*H*2] (n_i8, n_bf) */
+  const int32_t* n_fixed;                    /* device [B] shared-path rows of each request, or
+                                                NULL when nothing is shared; rows on the
+                                                shared path are read through the caches, all
+                                                other rows with streaming (non-temporal) loads */
 } tg_cache;
 
 /* ------------------------------------------------------------------------

@@ -69,7 +69,8 @@ class Cache(ctypes.Structure):
                 ("n_pages", (c_int64 * 2) * TG_MAX_CLUSTERS),
                 ("bt", (c_void_p * 2) * TG_MAX_CLUSTERS),
                 ("stride", (c_int32 * 2) * TG_MAX_CLUSTERS),
-                ("cluster_of_head", c_void_p), ("slot_in_cluster", c_void_p), ("len", c_void_p)]
+                ("cluster_of_head", c_void_p), ("slot_in_cluster", c_void_p), ("len", c_void_p),
+                ("n_fixed", c_void_p)]
 
 
 class DecodeArgs(ctypes.Structure):

@@ -126,7 +126,7 @@ class Pool:
 
 
 def tg_size_tables(res: Reservation, page_size: int, quant_block: int, share: Optional[Share] = None,
-                   chunk_bf: int = 512, chunk_i8: int = 1024, lpt: bool = True) -> dict:
+                   chunk_bf: int = 1024, chunk_i8: int = 1024, lpt: bool = True) -> dict:
     opts = L.PlanOpts(int(chunk_bf), int(chunk_i8), int(bool(lpt)))
     sz = L.TableSizes()
     check(lib().tg_size_tables(ctypes.byref(res.struct), int(page_size), int(quant_block),
@@ -167,7 +167,7 @@ class Tables:
         return self.work[:self.n_items]
 
 
-def tg_build_tables(pool: Pool, res: Reservation, share: Optional[Share] = None, chunk_bf: int = 512,
+def tg_build_tables(pool: Pool, res: Reservation, share: Optional[Share] = None, chunk_bf: int = 1024,
                     chunk_i8: int = 1024, lpt: bool = True) -> Tables:
     sizes = tg_size_tables(res, pool.page_size, pool.quant_block, share, chunk_bf, chunk_i8, lpt)
     t = Tables(res, sizes)
@@ -208,7 +208,8 @@ class DeviceCache:
     """Device memory of one populated cache: the (cluster, tier) pools sized
     from ``pool`` and the uploaded tables, plus the ``tg_cache`` view."""
 
-    def __init__(self, pool: Pool, res: Reservation, tables: Tables, device="cuda"):
+    def __init__(self, pool: Pool, res: Reservation, tables: Tables, device="cuda",
+                 share: Optional[Share] = None):
         torch = _torch()
         self.device = torch.device(device)
         self.G_hint = None
@@ -240,6 +241,11 @@ class DeviceCache:
         c_s.cluster_of_head = _ptr(self.cluster_of_head)
         c_s.slot_in_cluster = _ptr(self.slot_in_cluster)
         c_s.len = _ptr(self.len)
+        self.n_fixed = None
+        nf = res.length[:, 0] - res.budget[:, 0]
+        if share is not None and int(nf.max()) > 0:
+            self.n_fixed = torch.from_numpy(np.ascontiguousarray(nf, dtype=np.int32)).to(self.device)
+        c_s.n_fixed = _ptr(self.n_fixed)
         self.struct = c_s
         self.B, self.H, self.d = res.B, res.H, pool.head_dim
 

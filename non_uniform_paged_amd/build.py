@@ -28,6 +28,7 @@ HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-Wno-unused-command-line-argument",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-I", INCLUDE, "-Wall", "-Wextra"]
 

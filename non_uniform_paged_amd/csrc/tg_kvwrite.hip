@@ -7,7 +7,9 @@
 // quantiser is symmetric absmax per (64-token block, channel), computed in
 // fp32:  s = fp16_rne(absmax / 127) (+inf saturates to 65504),
 //        q8 = s > 0 ? clamp(rint_even(x / s), -127, 127) : 0.
-// Page layouts are the ones documented in include/tg.h.
+// Page layouts are the ones documented in include/tg.h (the bf16 one is
+// arranged so that each 1 KiB wave load in the decode kernel is one MFMA
+// operand).
 
 #include <hip/hip_runtime.h>
 
@@ -49,10 +51,21 @@ __global__ __launch_bounds__(256) void write_bf16_kernel(WriteArgs a) {
   const int64_t src_row = a.index[a.offsets[rh] + n_i8 + u];
   const uint16_t* src = a.rows + src_row * 2 * D + 8 * c8;
   const int pid = a.bt[cl][TG_TIER_BF16][static_cast<int64_t>(r) * a.stride[cl][TG_TIER_BF16] + u / kPage];
-  char* dst = a.pool[cl][TG_TIER_BF16] + static_cast<int64_t>(pid) * a.page_bytes[cl][TG_TIER_BF16] +
-              static_cast<int64_t>(hs) * (4 * kPage * D) + (u % kPage) * D * 2 + 16 * c8;
-  *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-  *reinterpret_cast<uint4*>(dst + kPage * D * 2) = *reinterpret_cast<const uint4*>(src + D);
+  char* head = a.pool[cl][TG_TIER_BF16] + static_cast<int64_t>(pid) * a.page_bytes[cl][TG_TIER_BF16] +
+               static_cast<int64_t>(hs) * (4 * kPage * D);
+  const int t = u % kPage;
+  // K: channels 8c8..8c8+7 of row t are one contiguous 16-byte group
+  *reinterpret_cast<uint4*>(head + (((c8 >> 2) * 64 + (c8 & 3) * 16 + t) * 16)) =
+      *reinterpret_cast<const uint4*>(src);
+  // V: channel d of row t sits with the same channel of rows t^1..t^3
+  uint16_t* vblk = reinterpret_cast<uint16_t*>(head + kPage * D * 2);
+  const uint16_t* vsrc = src + D;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int d = 8 * c8 + e;
+    const int off = (((d >> 5) * 64 + (t >> 2) * 16 + (d & 15)) * 16 + ((d >> 4) & 1) * 8 + (t & 3) * 2) / 2;
+    vblk[off] = vsrc[e];
+  }
 }
 
 // One block of 2*D threads per (r, h, 64-row INT8 block): thread = (K|V, channel).

@@ -32,7 +32,7 @@ def share_of(w) -> Optional[api.Share]:
 class Prepared:
     """A populated cache plus the buffers of one decode step."""
 
-    def __init__(self, w, chunk_bf: int = 512, chunk_i8: int = 1024, lpt: bool = True,
+    def __init__(self, w, chunk_bf: int = 1024, chunk_i8: int = 1024, lpt: bool = True,
                  slack_pages: int = 0, shift_pages: int = 0, device: str = "cuda"):
         import torch
 
@@ -54,7 +54,7 @@ class Prepared:
         self.tables = api.tg_build_tables(self.pool, self.res, self.share, chunk_bf, chunk_i8, lpt)
         if shift_pages:
             api.tg_release(self.pool, ftab, 0)
-        self.cache = api.DeviceCache(self.pool, self.res, self.tables, dev)
+        self.cache = api.DeviceCache(self.pool, self.res, self.tables, dev, self.share)
 
         rows, index, offsets = w.source_buffer(self.res.length)
         rows_t = torch.from_numpy(rows.view(np.uint16).reshape(-1).view(np.int16)).to(dev)
