@@ -39,12 +39,17 @@ DESCRIPTIONS = {
     "radix": "prefix-shared radix: batch 256, 2000-token prefix + 1 of 4 500-token branches + 80..1000 suffix, ratio 0.60->0.20 on suffix",
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_traffic.txt")
-KERNEL_SRC = os.path.join(ROOT, "non_uniform_paged_amd", "csrc", "tg_decode.hip")
+# sources of the bf16 split kernel (the dominant kernel of the default workload)
+KERNEL_SRCS = [os.path.join(ROOT, "non_uniform_paged_amd", "csrc", f)
+               for f in ("tg_split_bf16.hip", "tg_device.h")]
 
 
 def _kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for p in KERNEL_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _traffic_record(config: str):

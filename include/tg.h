@@ -127,8 +127,13 @@ int tg_reserve(const tg_budget_table* table, int32_t B, const int32_t* n_comp,
  *           K: ((c>>5)*64 + ((c>>3)&3)*16 + t)*16 + (c&7)*2
  *           V: ((c>>5)*64 + (t>>2)*16 + (c&15))*16 + ((c>>4)&1)*8 + (t&3)*2,
  *           so that each contiguous 1 KiB is one matrix-core operand)
- *   INT8 : K codes [S][d] int8, V codes [S][d] int8,
- *          K scales [d] fp16, V scales [d] fp16       head_bytes = 2*S*d + 4*d
+ *   INT8 : K codes, V codes (S*d int8 each), then     head_bytes = 2*S*d + 4*d
+ *          K scales [d] fp16, V scales [d] fp16
+ *          (S = 64; code of (row t, channel c) at byte
+ *           K: ((t>>4)*(d/64) + (c>>6))*1024 + (((c>>3)&3)*16 + (t&15))*16
+ *              + ((c>>5)&1)*8 + (c&7)
+ *           V: S*d + ((t>>4)*(d/64) + (c>>6))*1024 + (((t>>2)&3)*16 + (c&15))*16
+ *              + ((c>>4)&3)*4 + (t&3))
  * Pages are handed out lowest free id first; shared pages are
  * reference-counted; a failing allocation changes nothing.
  * ---------------------------------------------------------------------- */

@@ -92,12 +92,18 @@ __global__ __launch_bounds__(2 * D) void write_i8_kernel(WriteArgs a) {
   char* head = a.pool[cl][TG_TIER_I8] + static_cast<int64_t>(pid) * a.page_bytes[cl][TG_TIER_I8] +
                static_cast<int64_t>(hs) * (2 * kQBlock * D + 4 * D);
   int8_t* codes = reinterpret_cast<int8_t*>(head + kv * kQBlock * D);
+  constexpr int NL = D / 64;
   for (int t = 0; t < kQBlock; ++t) {
     const int64_t row = a.index[base + t];
     const float x = __uint_as_float(static_cast<uint32_t>(a.rows[row * 2 * D + kv * D + ch]) << 16);
     int q = 0;
     if (sf > 0.f) q = static_cast<int>(fminf(fmaxf(__builtin_rintf(x / sf), -127.f), 127.f));
-    codes[t * D + ch] = static_cast<int8_t>(q);
+    // matrix-core operand order of the decode kernel (include/tg.h)
+    const int c = ch;
+    const int off = kv == 0
+        ? ((t >> 4) * NL + (c >> 6)) * 1024 + (((c >> 3) & 3) * 16 + (t & 15)) * 16 + ((c >> 5) & 1) * 8 + (c & 7)
+        : ((t >> 4) * NL + (c >> 6)) * 1024 + (((t >> 2) & 3) * 16 + (c & 15)) * 16 + ((c >> 4) & 3) * 4 + (t & 3);
+    codes[off] = static_cast<int8_t>(q);
   }
   reinterpret_cast<_Float16*>(head + 2 * kQBlock * D + kv * D * 2)[ch] = s16;
 }

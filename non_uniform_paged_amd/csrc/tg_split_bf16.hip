@@ -1,0 +1,265 @@
+// Split kernel, bf16 tier (gfx950): one wavefront per plan item
+// (r, h, bf16, [t0, t1)) computes the online-normaliser partial of the G
+// q-heads of KV-head h over rows [t0, t1) of the bf16 tier.
+//
+// The maths is the online normaliser (CAP survey page, section 2.4.3
+// "Distributed acceleration", online normaliser [88]): per chunk keep
+// m = max s, l = sum e^{s-m}, acc = sum e^{s-m} v; chunks merge exactly with
+// weights e^{m_i - M}.  Scores are kept in base 2 (s * log2 e) inside the
+// kernel; partial m is stored in natural-log units.
+//
+// Per 16-row page the scores of the G heads are one matrix-core tile
+// S^T = K Q^T (16 rows x G columns, padded to 16) and the value update is P V
+// over 16-row k-slices (bf16 P split into a high and a low part so that the
+// weights keep ~16 significant bits).  The page layout (include/tg.h) is
+// chosen so that each contiguous 1 KiB wave load is exactly one MFMA operand:
+//   K: byte ((c>>5)*64 + ((c>>3)&3)*16 + t)*16 + (c&7)*2
+//   V: byte ((c>>5)*64 + (t>>2)*16 + (c&15))*16 + ((c>>4)&1)*8 + (t&3)*2
+// Lane l = 16*lj + lg: in S^T it holds rows (tokens) 4lj..4lj+3 of column
+// (head) lg; in the P V accumulators rows (heads) 4lj..4lj+3 of channel lg of
+// each 16-channel tile.  The online-normaliser state m, l of head lg is kept
+// in the lanes of column lg.
+
+#include <cmath>
+#include <cstdlib>
+
+#include "tg_device.h"
+
+namespace tg_dev {
+namespace {
+
+// One 16-row page.  TAIL masks rows at or past `valid`, both in the scores
+// and in the V operand.
+template <int NK, int NT, int NQ, bool TAIL>
+__device__ __forceinline__ void bf16_page(const u32x4_t (&kb)[NK], const u32x4_t (&vb)[NK],
+                                          const u32x4_t (&qop)[NQ][NK], f32x4_t (&acc)[NT],
+                                          float& m_ref, float& l_run, float scale_log2, int valid,
+                                          int lj) {
+  f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < NK; ++s)
+#pragma unroll
+    for (int qp = 0; qp < NQ; ++qp) sacc = mfma_bf16_k32(kb[s], qop[qp][s], sacc);
+  float sc[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    sc[rr] = sacc[rr] * scale_log2;
+    if (TAIL && 4 * lj + rr >= valid) sc[rr] = -INFINITY;
+  }
+  float pm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+  pm = xor32_max(xor16_max(pm));
+  if (__builtin_amdgcn_ballot_w64(pm > m_ref + kSlack) != 0) {
+    const float mn = fmaxf(m_ref, pm);
+    const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);
+    l_run *= alpha;
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const float ar = __shfl(alpha, 4 * lj + rr, 64);  // alpha of head 4lj+rr
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[n][rr] *= ar;
+    }
+    m_ref = mn;
+  }
+  float pw[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    pw[rr] = __builtin_amdgcn_exp2f(sc[rr] - m_ref);
+    l_run += pw[rr];
+  }
+  uint32_t ph[4], pl[4];
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) split_bf16(pw[rr], ph[rr], pl[rr]);
+  const u32x2_t Ph = {ph[0] | (ph[1] << 16), ph[2] | (ph[3] << 16)};
+  const u32x2_t Pl = {pl[0] | (pl[1] << 16), pl[2] | (pl[3] << 16)};
+  // V rows 4lj..4lj+3; in a tail page the rows past the item end are zeroed
+  // so that whatever the page holds there cannot reach the sums
+  uint32_t keep01 = 0xFFFFFFFFu, keep23 = 0xFFFFFFFFu;
+  if (TAIL) {
+    const int v0 = valid - 4 * lj;
+    keep01 = (v0 > 0 ? 0x0000FFFFu : 0u) | (v0 > 1 ? 0xFFFF0000u : 0u);
+    keep23 = (v0 > 2 ? 0x0000FFFFu : 0u) | (v0 > 3 ? 0xFFFF0000u : 0u);
+  }
+#pragma unroll
+  for (int s = 0; s < NK; ++s) {
+    const u32x4_t x = vb[s];
+    const u32x2_t v0 = TAIL ? u32x2_t{x[0] & keep01, x[1] & keep23} : u32x2_t{x[0], x[1]};
+    const u32x2_t v1 = TAIL ? u32x2_t{x[2] & keep01, x[3] & keep23} : u32x2_t{x[2], x[3]};
+    acc[2 * s] = mfma_bf16_k16(Ph, v0, acc[2 * s]);
+    acc[2 * s] = mfma_bf16_k16(Pl, v0, acc[2 * s]);
+    acc[2 * s + 1] = mfma_bf16_k16(Ph, v1, acc[2 * s + 1]);
+    acc[2 * s + 1] = mfma_bf16_k16(Pl, v1, acc[2 * s + 1]);
+  }
+}
+
+// One item.  A register pipeline of DEPTH page buffers: page i + DEPTH - 1 is
+// requested before page i is consumed.  Requests past the last page repeat the
+// last page (an L2 hit), so every request is unconditional and the waits
+// before a page's use cover exactly that page's loads.  Page ids of up to 64
+// pages sit one per lane and are read with readlane.
+template <int D, int G, bool QF32, int DEPTH, bool STREAM>
+__device__ __forceinline__ void bf16_item(const SplitArgs& a, int r, int h, int t0, int t1, int slot,
+                                          int hs, const TG_GLOBAL int32_t* bt_row, gptr pool,
+                                          int64_t pbytes) {
+  constexpr int NK = D / 32;           // 1 KiB loads per K (and per V) block
+  constexpr int NT = D / 16;           // 16-channel tiles of V
+  constexpr int NQ = QF32 ? 2 : 1;     // bf16 pieces of q
+  static_assert(G <= 16, "G must fit one MFMA tile");
+  const int lane = threadIdx.x & 63;
+  const int lg = lane & 15;
+  const int lj = lane >> 4;
+
+  // Q^T operand of step s: lane (lg, lj) holds q[lg][32 s + 8 lj + e], e < 8
+  u32x4_t qop[NQ][NK];
+  {
+    const bool has = lg < G;
+    const int64_t row = static_cast<int64_t>(r) * a.n_q_heads + h * G + (has ? lg : 0);
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      if constexpr (QF32) {
+        const u32x4_t x0 = ldv16(a.q + (row * D + 32 * s + 8 * lj) * 4);
+        const u32x4_t x1 = ldv16(a.q + (row * D + 32 * s + 8 * lj + 4) * 4);
+        const float f[8] = {__uint_as_float(x0[0]), __uint_as_float(x0[1]), __uint_as_float(x0[2]),
+                            __uint_as_float(x0[3]), __uint_as_float(x1[0]), __uint_as_float(x1[1]),
+                            __uint_as_float(x1[2]), __uint_as_float(x1[3])};
+        uint32_t hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) split_bf16(f[e], hi[e], lo[e]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qop[0][s][e] = has ? (hi[2 * e] | (hi[2 * e + 1] << 16)) : 0u;
+          qop[1][s][e] = has ? (lo[2 * e] | (lo[2 * e + 1] << 16)) : 0u;
+        }
+      } else {
+        const u32x4_t x = ldv16(a.q + (row * D + 32 * s + 8 * lj) * 2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qop[0][s][e] = has ? x[e] : 0u;
+      }
+    }
+  }
+
+  const int64_t head_off = static_cast<int64_t>(hs) * (4 * kPage * D);
+  const int lane_off = lane * 16;
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY;  // reference max of head lg (base-2 scaled score)
+  float l_run = 0.f;        // sum of weights of head lg over this lane's rows
+  const int p0 = t0 / kPage;
+  const int np = (t1 - t0 + kPage - 1) / kPage;
+  u32x4_t kb[DEPTH][NK], vb[DEPTH][NK];
+
+  for (int w0 = 0; w0 < np; w0 += 64) {
+    const int nw = min(64, np - w0);
+    const int pid_lane = bt_row[p0 + w0 + min(lane, nw - 1)];
+    auto issue = [&](u32x4_t (&kk)[NK], u32x4_t (&vv)[NK], int i) {
+      const int pid = __builtin_amdgcn_readlane(pid_lane, min(i, nw - 1));
+      gptr pp = pool + static_cast<int64_t>(pid) * pbytes + head_off + lane_off;
+#pragma unroll
+      for (int s = 0; s < NK; ++s) kk[s] = ldpage<STREAM>(pp + s * 1024);
+#pragma unroll
+      for (int s = 0; s < NK; ++s) vv[s] = ldpage<STREAM>(pp + kPage * D * 2 + s * 1024);
+    };
+#pragma unroll
+    for (int u = 0; u < DEPTH - 1; ++u) issue(kb[u], vb[u], u);
+    for (int base = 0; base < nw; base += DEPTH) {
+#pragma unroll
+      for (int u = 0; u < DEPTH; ++u) {
+        const int i = base + u;
+        const int nxt = (u + DEPTH - 1) % DEPTH;
+        issue(kb[nxt], vb[nxt], i + DEPTH - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < nw) {
+          const int valid = t1 - (t0 + (w0 + i) * kPage);  // rows of this page in the item
+          if (valid >= kPage)
+            bf16_page<NK, NT, NQ, false>(kb[u], vb[u], qop, acc, m_ref, l_run, a.scale_log2, kPage, lj);
+          else
+            bf16_page<NK, NT, NQ, true>(kb[u], vb[u], qop, acc, m_ref, l_run, a.scale_log2, valid, lj);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  // partial of the item: m and l of head lg, accumulator rows 4lj+rr
+  const float l_tot = xor32_sum(xor16_sum(l_run));
+  TG_GLOBAL float* acc_out = a.ws_acc + static_cast<int64_t>(slot) * G * D;
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int g = 4 * lj + rr;
+    if (g < G) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc_out[g * D + 16 * n + lg] = acc[n][rr];
+    }
+  }
+  if (lj == 0 && lg < G) {
+    a.ws_ml[(static_cast<int64_t>(slot) * G + lg) * 2 + 0] = m_ref * kLn2;
+    a.ws_ml[(static_cast<int64_t>(slot) * G + lg) * 2 + 1] = l_tot;
+  }
+}
+
+template <int D, int G, bool QF32, int DEPTH>
+__global__ __launch_bounds__(64 * kWavesPerBlock) void split_bf16_kernel(SplitArgs a) {
+  const int item = uniform(static_cast<int>(blockIdx.x) * kWavesPerBlock + (static_cast<int>(threadIdx.x) >> 6));
+  if (item >= a.n_items) return;
+  const TG_GLOBAL int32_t* w = a.work + static_cast<int64_t>(item) * 6;
+  const int tier = uniform(w[2]);
+  if (tier != TG_TIER_BF16) return;  // the INT8 kernel takes this item
+  const int r = uniform(w[0]), h = uniform(w[1]);
+  const int t0 = uniform(w[3]), t1 = uniform(w[4]), slot = uniform(w[5]);
+  const int cl = uniform(a.cluster_of_head[h]);
+  const int hs = uniform(a.slot_in_cluster[h]);
+  const TG_GLOBAL int32_t* bt_row = a.bt[cl][TG_TIER_BF16] + static_cast<int64_t>(r) * a.stride[cl][TG_TIER_BF16];
+  gptr pool = a.pool[cl][TG_TIER_BF16];
+  const int64_t pbytes = a.page_bytes[cl][TG_TIER_BF16];
+  // an item that starts on the shared radix path reads through the caches
+  bool shared = false;
+  if (a.n_fixed) {
+    const int n_i8 = uniform(a.len[2 * (r * a.n_kv_heads + h)]);
+    shared = n_i8 + t0 + kPage <= uniform(a.n_fixed[r]);
+  }
+  if (shared)
+    bf16_item<D, G, QF32, DEPTH, false>(a, r, h, t0, t1, slot, hs, bt_row, pool, pbytes);
+  else
+    bf16_item<D, G, QF32, DEPTH, true>(a, r, h, t0, t1, slot, hs, bt_row, pool, pbytes);
+}
+
+template <int D, int G, bool QF32>
+hipError_t launch(const SplitArgs& a, hipStream_t s) {
+  const int blocks = (a.n_items + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks == 0) return hipSuccess;
+  static const int depth = [] {
+    const char* e = getenv("TG_SPLIT_DEPTH");  // tuning knob: 2 or 3 page buffers
+    return (e && atoi(e) == 3) ? 3 : 2;
+  }();
+  const dim3 grid(blocks), block(64 * kWavesPerBlock);
+  if (depth == 3)
+    hipLaunchKernelGGL((split_bf16_kernel<D, G, QF32, 3>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((split_bf16_kernel<D, G, QF32, 2>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const SplitArgs& a, int G, bool qf32, hipStream_t s) {
+  switch (G * 2 + (qf32 ? 1 : 0)) {
+    case 2: return launch<D, 1, false>(a, s);
+    case 3: return launch<D, 1, true>(a, s);
+    case 4: return launch<D, 2, false>(a, s);
+    case 5: return launch<D, 2, true>(a, s);
+    case 8: return launch<D, 4, false>(a, s);
+    case 9: return launch<D, 4, true>(a, s);
+    case 16: return launch<D, 8, false>(a, s);
+    case 17: return launch<D, 8, true>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_split_bf16(const SplitArgs& a, int d, int G, bool qf32, hipStream_t s) {
+  if (d == 128) return launch_d<128>(a, G, qf32, s);
+  if (d == 64) return launch_d<64>(a, G, qf32, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tg_dev

@@ -1,0 +1,307 @@
+// Split kernel, INT8 tier (gfx950): one wavefront per plan item
+// (r, h, INT8, [t0, t1)) computes the online-normaliser partial of the G
+// q-heads of KV-head h over rows [t0, t1) of the INT8 tier, dequantising in
+// registers (TTKV page, "Tier Layout" / "Tier Interaction": the slow tier is
+// block-quantised; here every 64-row block has one fp16 scale per channel for
+// K and one for V).
+//
+// Matrix-core form of a 16-row group:
+//   * codes q8 become the exact fp16 values 1152 + q8 with one byte permute
+//     (0x64 high byte, q8 ^ 0x80 low byte);
+//   * S^T = K' Q'^T where Q' = q * s_K (per block, split into fp16 high + low
+//     parts) and K' = 1152 + q8; the constant part 1152 * sum_c Q'[g][c] is
+//     one extra tile per block against a constant-1152 operand and is
+//     subtracted from the scores;
+//   * the value sum uses V' = 1152 + q8 with the weights P split into fp16 high
+//     + low parts; the constant part 1152 * sum_t P[g][t] is accumulated by the
+//     same tiles against a constant-1152 operand; at the end of a block
+//     acc += s_V[c] * (sum P V' - bias) folds in the per-channel V scale.
+// The running accumulator lives in LDS (32 KiB per workgroup at d = 128); the
+// per-block tiles live in registers.
+//
+// INT8 page layout per head slot (64 rows, d channels; include/tg.h):
+//   K codes: row t, channel c at
+//     ((t>>4)*(d/64) + (c>>6))*1024 + (((c>>3)&3)*16 + (t&15))*16 + ((c>>5)&1)*8 + (c&7)
+//   V codes (at +64*d):
+//     ((t>>4)*(d/64) + (c>>6))*1024 + (((t>>2)&3)*16 + (c&15))*16 + ((c>>4)&3)*4 + (t&3)
+//   K scales [d] fp16 at +128*d, V scales [d] fp16 at +130*d
+// so that each contiguous 1 KiB wave load holds matrix-core operands.
+
+#include <cmath>
+
+#include "tg_device.h"
+
+namespace tg_dev {
+namespace {
+
+constexpr uint32_t kF16x2_1152 = 0x64806480u;  // two fp16 1152.0
+
+// 4 int8 codes (one dword) -> 4 fp16 values 1152 + q8 (two dwords)
+__device__ __forceinline__ u32x2_t codes_to_f16(uint32_t w) {
+  const uint32_t x = w ^ 0x80808080u;
+  return u32x2_t{__builtin_amdgcn_perm(0x64646464u, x, 0x04010400u),
+                 __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u)};
+}
+
+__device__ __forceinline__ float half_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)));
+}
+__device__ __forceinline__ float half_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
+template <int D, int G, bool QF32, int DEPTH, bool STREAM>
+__device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0, int t1, int slot,
+                                        int hs, const TG_GLOBAL int32_t* bt_row, gptr pool,
+                                        int64_t pbytes, float* lds) {
+  constexpr int NL = D / 64;           // 1 KiB loads per 16-row group (K codes, V codes)
+  constexpr int NK = D / 32;           // score steps (32 channels each)
+  constexpr int NT = D / 16;           // 16-channel tiles of V
+  constexpr int GR = kQBlock / kPage;  // 16-row groups per block
+  static_assert(G <= 16, "G must fit one MFMA tile");
+  static_assert(GR % DEPTH == 0, "pipeline depth must divide the groups of a block");
+  const int lane = threadIdx.x & 63;
+  const int lg = lane & 15;
+  const int lj = lane >> 4;
+  const bool has = lg < G;
+
+  // q of head lg, channels 32 s + 8 lj + e
+  float qf[NK][8];
+  {
+    const int64_t row = static_cast<int64_t>(r) * a.n_q_heads + h * G + (has ? lg : 0);
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      if constexpr (QF32) {
+        const u32x4_t x0 = ldv16(a.q + (row * D + 32 * s + 8 * lj) * 4);
+        const u32x4_t x1 = ldv16(a.q + (row * D + 32 * s + 8 * lj + 4) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qf[s][e] = has ? __uint_as_float(x0[e]) : 0.f;
+          qf[s][e + 4] = has ? __uint_as_float(x1[e]) : 0.f;
+        }
+      } else {
+        const u32x4_t x = ldv16(a.q + (row * D + 32 * s + 8 * lj) * 2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qf[s][2 * e] = has ? __uint_as_float(x[e] << 16) : 0.f;
+          qf[s][2 * e + 1] = has ? __uint_as_float(x[e] & 0xffff0000u) : 0.f;
+        }
+      }
+    }
+  }
+
+  // running accumulator in LDS: this lane's rows 4lj+rr, channel 16n+lg
+#pragma unroll
+  for (int k = 0; k < NT * 4; ++k) lds[k * 64 + lane] = 0.f;
+  float m_ref = -INFINITY;
+  float l_run = 0.f;
+  const int64_t head_off = static_cast<int64_t>(hs) * (2 * kQBlock * D + 4 * D);
+  const int lane_off = lane * 16;
+  const u32x4_t c1152x8 = {kF16x2_1152, kF16x2_1152, kF16x2_1152, kF16x2_1152};
+  const u32x2_t c1152x4 = {kF16x2_1152, kF16x2_1152};
+  const int b0 = t0 / kQBlock;
+  const int nb = (t1 - t0) / kQBlock;
+
+  for (int w0 = 0; w0 < nb; w0 += 64) {
+    const int nw = min(64, nb - w0);
+    const int pid_lane = bt_row[b0 + w0 + min(lane, nw - 1)];
+    auto blk_ptr = [&](int b) {
+      const int pid = __builtin_amdgcn_readlane(pid_lane, min(b, nw - 1));
+      return pool + static_cast<int64_t>(pid) * pbytes + head_off;
+    };
+    u32x4_t kc[DEPTH][NL], vc[DEPTH][NL];
+    auto issue = [&](u32x4_t (&kk)[NL], u32x4_t (&vv)[NL], int b, int k) {
+      gptr bp = blk_ptr(b) + lane_off;
+#pragma unroll
+      for (int L = 0; L < NL; ++L) kk[L] = ldpage<STREAM>(bp + (k * NL + L) * 1024);
+#pragma unroll
+      for (int L = 0; L < NL; ++L) vv[L] = ldpage<STREAM>(bp + kQBlock * D + (k * NL + L) * 1024);
+    };
+    u32x4_t skraw[NK];  // K scales 32 s + 8 lj .. +8 of the next block to start
+    uint32_t svraw[NT];  // V scale of channel 16 n + lg of the current block
+    auto load_sk = [&](int b) {
+      gptr bp = blk_ptr(b) + 2 * kQBlock * D;
+#pragma unroll
+      for (int s = 0; s < NK; ++s) skraw[s] = ldv16(bp + (32 * s + 8 * lj) * 2);
+    };
+    load_sk(0);
+#pragma unroll
+    for (int u = 0; u < DEPTH - 1; ++u) issue(kc[u], vc[u], 0, u);
+
+    for (int blk = 0; blk < nw; ++blk) {
+      // Q' = q * s_K as fp16 high + low parts, and the score bias of the block
+      u32x4_t qop[2][NK];
+#pragma unroll
+      for (int s = 0; s < NK; ++s) {
+        uint32_t hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          split_f16(qf[s][2 * e] * half_lo(skraw[s][e]), hi[2 * e], lo[2 * e]);
+          split_f16(qf[s][2 * e + 1] * half_hi(skraw[s][e]), hi[2 * e + 1], lo[2 * e + 1]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qop[0][s][e] = hi[2 * e] | (hi[2 * e + 1] << 16);
+          qop[1][s][e] = lo[2 * e] | (lo[2 * e + 1] << 16);
+        }
+      }
+      f32x4_t qb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NK; ++s) {
+        qb = mfma_f16_k32(c1152x8, qop[0][s], qb);
+        qb = mfma_f16_k32(c1152x8, qop[1][s], qb);
+      }
+      const float qk_bias = qb[0];  // 1152 * sum_c Q'[lg][c], the same in every row
+
+      f32x4_t accb[NT];
+#pragma unroll
+      for (int n = 0; n < NT; ++n) accb[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      f32x4_t pbias = {0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+      for (int k = 0; k < GR; ++k) {
+        const int kn = k + DEPTH - 1;  // group requested now: block blk + kn/GR, group kn%GR
+        issue(kc[kn % DEPTH], vc[kn % DEPTH], blk + kn / GR, kn % GR);
+        if (k == 1) {
+          gptr sp = blk_ptr(blk) + 2 * kQBlock * D + 2 * D;
+#pragma unroll
+          for (int n = 0; n < NT; ++n) svraw[n] = *(const TG_GLOBAL uint16_t*)(sp + (16 * n + lg) * 2);
+        }
+        if (k == 2) load_sk(blk + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int u = k % DEPTH;
+        // scores of rows 4lj..4lj+3 for head lg
+        f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NK; ++s) {
+          const u32x4_t x = kc[u][s / 2];
+          const u32x2_t c0 = codes_to_f16(x[(s % 2) * 2]);
+          const u32x2_t c1 = codes_to_f16(x[(s % 2) * 2 + 1]);
+          const u32x4_t A = {c0[0], c0[1], c1[0], c1[1]};
+          sacc = mfma_f16_k32(A, qop[0][s], sacc);
+          sacc = mfma_f16_k32(A, qop[1][s], sacc);
+        }
+        float sc[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) sc[rr] = (sacc[rr] - qk_bias) * a.scale_log2;
+        float pm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        pm = xor32_max(xor16_max(pm));
+        if (__builtin_amdgcn_ballot_w64(pm > m_ref + kSlack) != 0) {
+          const float mn = fmaxf(m_ref, pm);
+          const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);
+          l_run *= alpha;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const float ar = __shfl(alpha, 4 * lj + rr, 64);  // alpha of head 4lj+rr
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+              accb[n][rr] *= ar;
+              lds[(4 * n + rr) * 64 + lane] *= ar;
+            }
+            pbias[rr] *= ar;
+          }
+          m_ref = mn;
+        }
+        float pw[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          pw[rr] = __builtin_amdgcn_exp2f(sc[rr] - m_ref);
+          l_run += pw[rr];
+        }
+        uint32_t ph[4], pl[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) split_f16(pw[rr], ph[rr], pl[rr]);
+        const u32x2_t Ph = {ph[0] | (ph[1] << 16), ph[2] | (ph[3] << 16)};
+        const u32x2_t Pl = {pl[0] | (pl[1] << 16), pl[2] | (pl[3] << 16)};
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          const u32x2_t B = codes_to_f16(vc[u][n / 4][n % 4]);
+          accb[n] = mfma_f16_k16(Ph, B, accb[n]);
+          accb[n] = mfma_f16_k16(Pl, B, accb[n]);
+        }
+        pbias = mfma_f16_k16(Ph, c1152x4, pbias);
+        pbias = mfma_f16_k16(Pl, c1152x4, pbias);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // end of block: fold in the V scales
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const float sv = half_lo(svraw[n]);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) lds[(4 * n + rr) * 64 + lane] += sv * (accb[n][rr] - pbias[rr]);
+      }
+    }
+  }
+
+  const float l_tot = xor32_sum(xor16_sum(l_run));
+  TG_GLOBAL float* acc_out = a.ws_acc + static_cast<int64_t>(slot) * G * D;
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int g = 4 * lj + rr;
+    if (g < G) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc_out[g * D + 16 * n + lg] = lds[(4 * n + rr) * 64 + lane];
+    }
+  }
+  if (lj == 0 && has) {
+    a.ws_ml[(static_cast<int64_t>(slot) * G + lg) * 2 + 0] = m_ref * kLn2;
+    a.ws_ml[(static_cast<int64_t>(slot) * G + lg) * 2 + 1] = l_tot;
+  }
+}
+
+template <int D, int G, bool QF32, int DEPTH>
+__global__ __launch_bounds__(64 * kWavesPerBlock) void split_i8_kernel(SplitArgs a) {
+  __shared__ float lds[kWavesPerBlock][(D / 16) * 4 * 64];
+  const int wave = uniform(static_cast<int>(threadIdx.x) >> 6);
+  const int item = uniform(static_cast<int>(blockIdx.x) * kWavesPerBlock + wave);
+  if (item >= a.n_items) return;
+  const TG_GLOBAL int32_t* w = a.work + static_cast<int64_t>(item) * 6;
+  const int tier = uniform(w[2]);
+  if (tier != TG_TIER_I8) return;  // the bf16 kernel takes this item
+  const int r = uniform(w[0]), h = uniform(w[1]);
+  const int t0 = uniform(w[3]), t1 = uniform(w[4]), slot = uniform(w[5]);
+  const int cl = uniform(a.cluster_of_head[h]);
+  const int hs = uniform(a.slot_in_cluster[h]);
+  const TG_GLOBAL int32_t* bt_row = a.bt[cl][TG_TIER_I8] + static_cast<int64_t>(r) * a.stride[cl][TG_TIER_I8];
+  gptr pool = a.pool[cl][TG_TIER_I8];
+  const int64_t pbytes = a.page_bytes[cl][TG_TIER_I8];
+  bool shared = false;  // an item that starts on the shared radix path reads through the caches
+  if (a.n_fixed) shared = t0 + kQBlock <= uniform(a.n_fixed[r]);
+  if (shared)
+    i8_item<D, G, QF32, DEPTH, false>(a, r, h, t0, t1, slot, hs, bt_row, pool, pbytes, lds[wave]);
+  else
+    i8_item<D, G, QF32, DEPTH, true>(a, r, h, t0, t1, slot, hs, bt_row, pool, pbytes, lds[wave]);
+}
+
+template <int D, int G, bool QF32>
+hipError_t launch(const SplitArgs& a, hipStream_t s) {
+  const int blocks = (a.n_items + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((split_i8_kernel<D, G, QF32, 2>), dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const SplitArgs& a, int G, bool qf32, hipStream_t s) {
+  switch (G * 2 + (qf32 ? 1 : 0)) {
+    case 2: return launch<D, 1, false>(a, s);
+    case 3: return launch<D, 1, true>(a, s);
+    case 4: return launch<D, 2, false>(a, s);
+    case 5: return launch<D, 2, true>(a, s);
+    case 8: return launch<D, 4, false>(a, s);
+    case 9: return launch<D, 4, true>(a, s);
+    case 16: return launch<D, 8, false>(a, s);
+    case 17: return launch<D, 8, true>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_split_i8(const SplitArgs& a, int d, int G, bool qf32, hipStream_t s) {
+  if (d == 128) return launch_d<128>(a, G, qf32, s);
+  if (d == 64) return launch_d<64>(a, G, qf32, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tg_dev

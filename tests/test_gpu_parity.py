@@ -154,19 +154,25 @@ def _read_i8_pages(p, r, h):
     through the layout include/tg.h documents."""
     w = p.w
     d, qb = w.d, w.quant_block
-    c = int(p.res.cluster_of_head[h])
+    cl = int(p.res.cluster_of_head[h])
     s = int(p.res.slot_in_cluster[h])
     n8 = int(p.res.n_i8[r, h])
-    pb = p.pool.page_bytes(c, 0)
+    pb = p.pool.page_bytes(cl, 0)
     hb = 2 * qb * d + 4 * d
-    pool = p.cache.pools[c][0].cpu().numpy()
+    pool = p.cache.pools[cl][0].cpu().numpy()
     kq, vq, ks, vs = [], [], [], []
+    t = np.arange(qb)[:, None]
+    c = np.arange(d)[None, :]
+    nl = d // 64
+    koff = ((t >> 4) * nl + (c >> 6)) * 1024 + (((c >> 3) & 3) * 16 + (t & 15)) * 16 + ((c >> 5) & 1) * 8 + (c & 7)
+    voff = ((t >> 4) * nl + (c >> 6)) * 1024 + (((t >> 2) & 3) * 16 + (c & 15)) * 16 + ((c >> 4) & 3) * 4 + (t & 3)
+    assert sorted(koff.ravel()) == list(range(qb * d)) and sorted(voff.ravel()) == list(range(qb * d))
     for j in range(n8 // qb):
-        pid = int(p.tables.bt[c][0][r, j])
+        pid = int(p.tables.bt[cl][0][r, j])
         base = pid * pb + s * hb
         blk = pool[base:base + hb]
-        kq.append(blk[:qb * d].view(np.int8).reshape(qb, d))
-        vq.append(blk[qb * d:2 * qb * d].view(np.int8).reshape(qb, d))
+        kq.append(blk[:qb * d].view(np.int8)[koff])
+        vq.append(blk[qb * d:2 * qb * d].view(np.int8)[voff])
         ks.append(blk[2 * qb * d:2 * qb * d + 2 * d].view(np.float16))
         vs.append(blk[2 * qb * d + 2 * d:].view(np.float16))
     return np.concatenate(kq), np.concatenate(vq), np.stack(ks), np.stack(vs)
