@@ -166,6 +166,10 @@ class Tables:
     def plan(self) -> np.ndarray:
         return self.work[:self.n_items]
 
+    @property
+    def stride_has_i8(self) -> bool:
+        return any(self.stride[c][0] > 0 for c in range(self.C))
+
 
 def tg_build_tables(pool: Pool, res: Reservation, share: Optional[Share] = None, chunk_bf: int = 1024,
                     chunk_i8: int = 1024, lpt: bool = True) -> Tables:

@@ -267,6 +267,27 @@ def test_head_shapes(G, d, qd):
     _run_and_compare(w, what=f"G{G}-d{d}-{qd}", chunk_bf=96, chunk_i8=64)
 
 
+@pytest.mark.parametrize("name", ["llama8b", "tiered", "radix"])
+def test_split_then_merge_equals_decode(name):
+    """tg_decode_split + tg_merge_partials (the sharded form) gives the
+    tg_decode_attn result, and repeated calls agree bit for bit."""
+    torch = _need_gpu()
+    from non_uniform_paged_amd import api
+    p = _prep(make_workload(name, **SMALL[name]), chunk_bf=64, chunk_i8=128)
+    p.step()
+    fused = p.output().copy()
+    p.step()
+    assert np.array_equal(fused, p.output())
+    ws = torch.empty_like(p.workspace)
+    out = torch.empty_like(p.out)
+    api.tg_decode_split(p.cache, p.q, ws, p.w.Hq)
+    api.tg_merge_partials(ws, p.tables.n_items, p.w.B * p.w.Hkv, p.w.Hq // p.w.Hkv, p.w.d,
+                          p.cache.part_off, out)
+    torch.cuda.synchronize()
+    sep = out.cpu().numpy()
+    assert np.array_equal(sep, fused)
+
+
 def test_all_int8_and_empty_bf16_tier():
     _need_gpu()
     w = make_workload("tiered", B=2, Hq=8, Hkv=2, ctx=("fixed", 640), recent_ppm=0)
