@@ -121,6 +121,8 @@ def main():
     ap.add_argument("--chunk-bf", type=int, default=1024)
     ap.add_argument("--chunk-i8", type=int, default=1024)
     ap.add_argument("--flush", choices=["read", "write", "none"], default="read")
+    ap.add_argument("--group-size", type=int, default=None,
+                    help="requests per shared-prefix group item (default 16 / G when pages are shared)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (counter calibration)")
@@ -156,7 +158,7 @@ def main():
     torch.cuda.set_device(0)
     w = make_workload(args.config)
     t_prep = time.perf_counter()
-    prep = Prepared(w, chunk_bf=args.chunk_bf, chunk_i8=args.chunk_i8)
+    prep = Prepared(w, chunk_bf=args.chunk_bf, chunk_i8=args.chunk_i8, group_size=args.group_size)
     t_prep = time.perf_counter() - t_prep
     tr = prep.traffic()
     G = w.Hq // w.Hkv
@@ -178,7 +180,7 @@ def main():
         api.tg_decode_split(prep.cache, prep.q, prep.workspace, w.Hq, stream=stream)
         if evs is not None:
             evs[1].record(stream)
-        api.tg_merge_partials(prep.workspace, prep.tables.n_items, w.B * w.Hkv, G, w.d,
+        api.tg_merge_partials(prep.workspace, prep.tables.n_slots, w.B * w.Hkv, G, w.d,
                               prep.cache.part_off, prep.out, stream=stream)
         if evs is not None:
             evs[2].record(stream)
@@ -204,7 +206,7 @@ def main():
     # algorithmic bytes of the split kernel(s) (the dominant kernels): retained
     # rows (shared pages once), q, tables, partials written; timed alone above
     split_bytes = tr["kv_roofline"] + w.B * w.Hq * w.d * (4 if w.q_dtype == "f32" else 2) + tr["tables"] \
-        + prep.tables.n_items * G * (w.d + 2) * 4
+        + prep.tables.n_slots * G * (w.d + 2) * 4
     split_ms = float(split_ms_all.mean())
     achieved = split_bytes / (split_ms * 1e-3) / 1e9
     traffic = _traffic_record(args.config)
@@ -225,7 +227,8 @@ def main():
         "config": {"workload": DESCRIPTIONS[args.config], "name": args.config, "batch": w.B,
                    "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "clusters": w.n_clusters,
                    "page": w.page_size, "chunk_bf": args.chunk_bf, "chunk_i8": args.chunk_i8,
-                   "plan_items": prep.tables.n_items, "retained_head_rows": tr["head_rows"],
+                   "plan_items": prep.tables.n_items, "group_items": prep.tables.n_gitems,
+                   "group_size": prep.group_size, "retained_head_rows": tr["head_rows"],
                    "parallelism": "single GPU"},
         "hbm_frac_roofline_bytes": round(tr["roofline"] / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "effective_bytes": tr["effective"],

@@ -62,6 +62,7 @@ extern "C" {
 #define TG_TIER_I8 0
 #define TG_TIER_BF16 1
 #define TG_MAX_CLUSTERS 16
+#define TG_GROUP_WIDTH 16  /* member entries per group item of the plan */
 
 #define TG_Q_F32 0
 #define TG_Q_BF16 1
@@ -172,9 +173,21 @@ int32_t tg_pool_refcount(const tg_pool* pool, int32_t c, int32_t tier, int64_t p
  *           padded with -1; stride = max_r pages; len [B*H*2] = (n_i8, n_bf).
  *   plan    items {r, h, tier, t0, t1, slot} for r, h, tier (INT8 first),
  *           t0 = 0, chunk, 2*chunk, ... (t0, t1 are row indices inside the
- *           tier); slot = the item's index in that natural order; part_off
- *           [B*H + 1] = first slot of each (r, h).  With lpt != 0 the items
- *           are stably sorted by descending (t1 - t0) * (2 bf16 | 1 INT8).
+ *           tier); slot = index of the item's partial; part_off [B*H + 1] =
+ *           first slot of each (r, h).  With lpt != 0 the items are stably
+ *           sorted by descending (t1 - t0) * (2 bf16 | 1 INT8).
+ *   groups  with group_size > 1 and `share`, the leading shared bf16 pages of
+ *           each (r, h) are cut into runs of one radix node; requests whose
+ *           run has the same (node, first row, pages, n_i8) are taken in
+ *           ascending r, group_size at a time, and each group's rows are
+ *           chunked by chunk_bf from the run's first row into a group item
+ *           {-1 - k, h, bf16, t0, t1, -1}: one pass over those pages for up
+ *           to group_size requests.  gitems[k] lists its members as
+ *           TG_GROUP_WIDTH (r, slot) pairs, padded with (-1, -1).  Group items
+ *           come first (per h, runs in order of first appearance, groups,
+ *           chunks); a request's own bf16 items start after its shared rows.
+ *           Slots of each (r, h): its group memberships in group-item order,
+ *           then its own items in the order above.
  * ---------------------------------------------------------------------- */
 typedef struct tg_share_desc {
   const int32_t* n_nodes;   /* host [B] radix-path length of each request */
@@ -187,11 +200,15 @@ typedef struct tg_plan_opts {
   int32_t chunk_bf;  /* bf16 item length, a positive multiple of page_size */
   int32_t chunk_i8;  /* INT8 item length, a positive multiple of quant_block */
   int32_t lpt;       /* nonzero: longest items first */
+  int32_t group_size; /* 0 or 1: no group items; at most TG_GROUP_WIDTH.  The
+                         decode kernels take group_size * G <= 16 */
 } tg_plan_opts;
 
 typedef struct tg_table_sizes {
   int32_t stride[TG_MAX_CLUSTERS][2];        /* entries per table row */
   int32_t n_items;                           /* plan length */
+  int32_t n_gitems;                          /* group items */
+  int32_t n_slots;                           /* partials = part_off[B*H] */
   int64_t pages_needed[TG_MAX_CLUSTERS][2];  /* from an empty pool */
 } tg_table_sizes;
 
@@ -209,6 +226,8 @@ typedef struct tg_tables {
   int32_t n_items;                     /* in: must equal tg_size_tables' value */
   int32_t* part_off;                   /* host [B*H + 1] */
   int32_t* released;                   /* host [B] zeroed here; set by tg_release */
+  int32_t* gitems;                     /* host [n_gitems][TG_GROUP_WIDTH][2] (may be NULL if 0) */
+  int32_t n_gitems;                    /* in: must equal tg_size_tables' value */
 } tg_tables;
 
 /* Allocate every page of the batch from `pool` (all or nothing) and fill the
@@ -266,17 +285,21 @@ int tg_write_kv(const tg_cache* cache, const uint16_t* rows, const int32_t* inde
  *   o = sum_s e^{m_s - M} acc_s / sum_s e^{m_s - M} l_s,  M = max_s m_s.
  *
  *   q         device [B][Hq][d], fp32 (TG_Q_F32) or bf16 bits (TG_Q_BF16)
- *   work, part_off, n_items  device copies of tg_build_tables' plan
- *   workspace device fp32, >= tg_decode_workspace_bytes(n_items, G, d) bytes:
- *             acc [n_items][G][d] then (m, l) [n_items][G][2] (m in natural
+ *   work, part_off, gitems, n_items, n_gitems  device copies of
+ *             tg_build_tables' plan; n_slots = part_off[B*H]
+ *   workspace device fp32, >= tg_decode_workspace_bytes(n_slots, G, d) bytes:
+ *             acc [n_slots][G][d] then (m, l) [n_slots][G][2] (m in natural
  *             log units of the scaled score)
  *   out       device fp32 [B][Hq][d]
  *   sm_scale  score scale; 0 means 1/sqrt(d)
  * TG_EUNSUPPORTED unless d in {64, 128}, G in {1, 2, 4, 8}, page_size 16 and
  * quant_block 64; TG_EINVAL on inconsistent arguments; TG_EDEVICE on a
- * failed launch.
+ * failed launch.  A group item computes the partials of all its members in
+ * one pass (G columns of the score tile per member); its members must fit
+ * the tile: members * G <= 16, else the result is undefined (plan with
+ * group_size <= 16 / G).
  * ---------------------------------------------------------------------- */
-size_t tg_decode_workspace_bytes(int32_t n_items, int32_t G, int32_t d);
+size_t tg_decode_workspace_bytes(int32_t n_slots, int32_t G, int32_t d);
 
 typedef struct tg_decode_args {
   int32_t n_q_heads;
@@ -289,6 +312,9 @@ typedef struct tg_decode_args {
   size_t workspace_bytes;
   float* out;
   float sm_scale;
+  const int32_t* gitems;  /* device [n_gitems][TG_GROUP_WIDTH][2], or NULL if n_gitems 0 */
+  int32_t n_gitems;
+  int32_t n_slots;
 } tg_decode_args;
 
 int tg_decode_attn(const tg_cache* cache, const tg_decode_args* args, void* stream);

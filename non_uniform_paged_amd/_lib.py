@@ -22,6 +22,7 @@ STATUS_NAMES = {0: "TG_OK", -1: "TG_EINVAL", -2: "TG_ENOMEM", -3: "TG_EOVERFLOW"
 
 TG_TIER_I8 = 0
 TG_TIER_BF16 = 1
+TG_GROUP_WIDTH = 16
 TG_MAX_CLUSTERS = 16
 TG_Q_F32 = 0
 TG_Q_BF16 = 1
@@ -47,18 +48,19 @@ class ShareDesc(ctypes.Structure):
 
 
 class PlanOpts(ctypes.Structure):
-    _fields_ = [("chunk_bf", c_int32), ("chunk_i8", c_int32), ("lpt", c_int32)]
+    _fields_ = [("chunk_bf", c_int32), ("chunk_i8", c_int32), ("lpt", c_int32), ("group_size", c_int32)]
 
 
 class TableSizes(ctypes.Structure):
     _fields_ = [("stride", (c_int32 * 2) * TG_MAX_CLUSTERS), ("n_items", c_int32),
+                ("n_gitems", c_int32), ("n_slots", c_int32),
                 ("pages_needed", (c_int64 * 2) * TG_MAX_CLUSTERS)]
 
 
 class Tables(ctypes.Structure):
     _fields_ = [("bt", (P32 * 2) * TG_MAX_CLUSTERS), ("stride", (c_int32 * 2) * TG_MAX_CLUSTERS),
                 ("len", P32), ("work", P32), ("n_items", c_int32), ("part_off", P32),
-                ("released", P32)]
+                ("released", P32), ("gitems", P32), ("n_gitems", c_int32)]
 
 
 class Cache(ctypes.Structure):
@@ -76,7 +78,8 @@ class Cache(ctypes.Structure):
 class DecodeArgs(ctypes.Structure):
     _fields_ = [("n_q_heads", c_int32), ("q_dtype", c_int32), ("q", c_void_p), ("work", c_void_p),
                 ("n_items", c_int32), ("part_off", c_void_p), ("workspace", c_void_p),
-                ("workspace_bytes", c_size_t), ("out", c_void_p), ("sm_scale", c_float)]
+                ("workspace_bytes", c_size_t), ("out", c_void_p), ("sm_scale", c_float),
+                ("gitems", c_void_p), ("n_gitems", c_int32), ("n_slots", c_int32)]
 
 
 # name -> (restype, argtypes); the full exported surface of include/tg.h

@@ -126,14 +126,15 @@ class Pool:
 
 
 def tg_size_tables(res: Reservation, page_size: int, quant_block: int, share: Optional[Share] = None,
-                   chunk_bf: int = 1024, chunk_i8: int = 1024, lpt: bool = True) -> dict:
-    opts = L.PlanOpts(int(chunk_bf), int(chunk_i8), int(bool(lpt)))
+                   chunk_bf: int = 1024, chunk_i8: int = 1024, lpt: bool = True,
+                   group_size: int = 0) -> dict:
+    opts = L.PlanOpts(int(chunk_bf), int(chunk_i8), int(bool(lpt)), int(group_size))
     sz = L.TableSizes()
     check(lib().tg_size_tables(ctypes.byref(res.struct), int(page_size), int(quant_block),
                                _share_ptr(share), ctypes.byref(opts), ctypes.byref(sz)), "tg_size_tables")
     C = res.C
     return {"stride": [[sz.stride[c][t] for t in range(2)] for c in range(C)],
-            "n_items": int(sz.n_items),
+            "n_items": int(sz.n_items), "n_gitems": int(sz.n_gitems), "n_slots": int(sz.n_slots),
             "pages_needed": [[int(sz.pages_needed[c][t]) for t in range(2)] for c in range(C)]}
 
 
@@ -145,11 +146,14 @@ class Tables:
         self.B, self.H, self.C = B, H, C
         self.stride = sizes["stride"]
         self.n_items = sizes["n_items"]
+        self.n_gitems = sizes["n_gitems"]
+        self.n_slots = sizes["n_slots"]
         self.bt = [[np.full((B, self.stride[c][t]), -1, np.int32) for t in range(2)] for c in range(C)]
         self.len = np.zeros((B, H, 2), np.int32)
         self.work = np.zeros((max(self.n_items, 1), 6), np.int32)
         self.part_off = np.zeros(B * H + 1, np.int32)
         self.released = np.zeros(B, np.int32)
+        self.gitems_buf = np.full((max(self.n_gitems, 1), L.TG_GROUP_WIDTH, 2), -1, np.int32)
         s = L.Tables()
         for c in range(C):
             for t in range(2):
@@ -160,6 +164,8 @@ class Tables:
         s.n_items = self.n_items
         s.part_off = _p32(self.part_off)
         s.released = _p32(self.released)
+        s.gitems = _p32(self.gitems_buf)
+        s.n_gitems = self.n_gitems
         self.struct = s
 
     @property
@@ -167,15 +173,20 @@ class Tables:
         return self.work[:self.n_items]
 
     @property
+    def gitems(self) -> np.ndarray:
+        """[n_gitems][TG_GROUP_WIDTH][2] member table (request, slot)."""
+        return self.gitems_buf[:self.n_gitems]
+
+    @property
     def stride_has_i8(self) -> bool:
         return any(self.stride[c][0] > 0 for c in range(self.C))
 
 
 def tg_build_tables(pool: Pool, res: Reservation, share: Optional[Share] = None, chunk_bf: int = 1024,
-                    chunk_i8: int = 1024, lpt: bool = True) -> Tables:
-    sizes = tg_size_tables(res, pool.page_size, pool.quant_block, share, chunk_bf, chunk_i8, lpt)
+                    chunk_i8: int = 1024, lpt: bool = True, group_size: int = 0) -> Tables:
+    sizes = tg_size_tables(res, pool.page_size, pool.quant_block, share, chunk_bf, chunk_i8, lpt, group_size)
     t = Tables(res, sizes)
-    opts = L.PlanOpts(int(chunk_bf), int(chunk_i8), int(bool(lpt)))
+    opts = L.PlanOpts(int(chunk_bf), int(chunk_i8), int(bool(lpt)), int(group_size))
     check(lib().tg_build_tables(pool.handle, ctypes.byref(res.struct), _share_ptr(share),
                                 ctypes.byref(opts), ctypes.byref(t.struct)), "tg_build_tables")
     t.sizes = sizes
@@ -188,8 +199,8 @@ def tg_release(pool: Pool, tables: Tables, r: int) -> None:
     check(lib().tg_release(pool.handle, ctypes.byref(tables.struct), int(r)), "tg_release")
 
 
-def tg_decode_workspace_bytes(n_items: int, G: int, d: int) -> int:
-    return int(lib().tg_decode_workspace_bytes(int(n_items), int(G), int(d)))
+def tg_decode_workspace_bytes(n_slots: int, G: int, d: int) -> int:
+    return int(lib().tg_decode_workspace_bytes(int(n_slots), int(G), int(d)))
 
 
 # --------------------------------------------------------------------------- device
@@ -242,6 +253,10 @@ class DeviceCache:
         self.work = torch.from_numpy(tables.plan.copy()).to(self.device)
         self.part_off = torch.from_numpy(tables.part_off).to(self.device)
         self.n_items = tables.n_items
+        self.n_gitems = tables.n_gitems
+        self.n_slots = tables.n_slots
+        self.gitems = (torch.from_numpy(tables.gitems.reshape(-1).copy()).to(self.device)
+                       if tables.n_gitems else None)
         c_s.cluster_of_head = _ptr(self.cluster_of_head)
         c_s.slot_in_cluster = _ptr(self.slot_in_cluster)
         c_s.len = _ptr(self.len)
@@ -262,7 +277,7 @@ def tg_write_kv(cache: DeviceCache, rows, index, offsets, stream=None) -> None:
                             _stream_ptr(stream)), "tg_write_kv")
 
 
-def _decode_args(cache, q, out, workspace, n_q_heads, sm_scale, work, part_off, n_items):
+def _decode_args(cache, q, out, workspace, n_q_heads, sm_scale):
     torch = _torch()
     if q.dtype == torch.float32:
         qd = TG_Q_F32
@@ -274,9 +289,12 @@ def _decode_args(cache, q, out, workspace, n_q_heads, sm_scale, work, part_off, 
     a.n_q_heads = int(n_q_heads)
     a.q_dtype = qd
     a.q = _ptr(q)
-    a.work = _ptr(cache.work if work is None else work)
-    a.n_items = int(cache.n_items if n_items is None else n_items)
-    a.part_off = _ptr(cache.part_off if part_off is None else part_off)
+    a.work = _ptr(cache.work)
+    a.n_items = int(cache.n_items)
+    a.part_off = _ptr(cache.part_off)
+    a.gitems = _ptr(cache.gitems)
+    a.n_gitems = int(cache.n_gitems)
+    a.n_slots = int(cache.n_slots)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = int(workspace.numel() * workspace.element_size())
     a.out = _ptr(out)
@@ -285,20 +303,20 @@ def _decode_args(cache, q, out, workspace, n_q_heads, sm_scale, work, part_off, 
 
 
 def tg_decode_attn(cache: DeviceCache, q, out, workspace, n_q_heads: int, sm_scale: float = 0.0,
-                   work=None, part_off=None, n_items: Optional[int] = None, stream=None) -> None:
-    """Enqueue one decode step.  ``q`` is fp32 or bf16 [B][Hq][d] on the
-    device; ``out`` fp32 [B][Hq][d]; ``workspace`` fp32 of at least
-    ``tg_decode_workspace_bytes`` bytes.  The plan defaults to the one
-    uploaded with the cache."""
-    a = _decode_args(cache, q, out, workspace, n_q_heads, sm_scale, work, part_off, n_items)
+                   stream=None) -> None:
+    """Enqueue one decode step with the plan uploaded with the cache.  ``q``
+    is fp32 or bf16 [B][Hq][d] on the device; ``out`` fp32 [B][Hq][d];
+    ``workspace`` fp32 of at least ``tg_decode_workspace_bytes(n_slots)``
+    bytes."""
+    a = _decode_args(cache, q, out, workspace, n_q_heads, sm_scale)
     check(lib().tg_decode_attn(ctypes.byref(cache.struct), ctypes.byref(a), _stream_ptr(stream)),
           "tg_decode_attn")
 
 
 def tg_decode_split(cache: DeviceCache, q, workspace, n_q_heads: int, sm_scale: float = 0.0,
-                    work=None, n_items: Optional[int] = None, stream=None) -> None:
+                    stream=None) -> None:
     """Enqueue the split stage alone (partials into ``workspace``)."""
-    a = _decode_args(cache, q, None, workspace, n_q_heads, sm_scale, work, None, n_items)
+    a = _decode_args(cache, q, None, workspace, n_q_heads, sm_scale)
     check(lib().tg_decode_split(ctypes.byref(cache.struct), ctypes.byref(a), _stream_ptr(stream)),
           "tg_decode_split")
 

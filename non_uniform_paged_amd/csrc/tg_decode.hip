@@ -110,9 +110,9 @@ bool supported(int32_t d, int32_t G) {
 
 using namespace tg_dev;
 
-extern "C" size_t tg_decode_workspace_bytes(int32_t n_items, int32_t G, int32_t d) {
-  if (n_items < 0 || G < 1 || d < 1) return 0;
-  return static_cast<size_t>(n_items) * G * (d + 2) * sizeof(float);
+extern "C" size_t tg_decode_workspace_bytes(int32_t n_slots, int32_t G, int32_t d) {
+  if (n_slots < 0 || G < 1 || d < 1) return 0;
+  return static_cast<size_t>(n_slots) * G * (d + 2) * sizeof(float);
 }
 
 extern "C" int tg_merge_partials(const float* workspace, int32_t n_slots, int32_t n_pairs, int32_t G,
@@ -136,10 +136,13 @@ int decode_split(const tg_cache* c, const tg_decode_args* a, void* stream, bool 
   const int32_t d = c->head_dim;
   if (!supported(d, G) || c->page_size != kPage || c->quant_block != kQBlock) return TG_EUNSUPPORTED;
   if (a->q_dtype != TG_Q_F32 && a->q_dtype != TG_Q_BF16) return TG_EINVAL;
-  if (a->n_items < 0 || !a->q || !c->cluster_of_head || !c->slot_in_cluster || !c->len) return TG_EINVAL;
+  if (a->n_items < 0 || a->n_gitems < 0 || a->n_slots < 0 || !a->q || !c->cluster_of_head ||
+      !c->slot_in_cluster || !c->len)
+    return TG_EINVAL;
   if (merge && (!a->out || !a->part_off)) return TG_EINVAL;
-  if (a->n_items > 0 && (!a->work || !a->workspace)) return TG_EINVAL;
-  if (a->workspace_bytes < tg_decode_workspace_bytes(a->n_items, G, d)) return TG_EINVAL;
+  if (a->n_items > 0 && (!a->work || !a->workspace || a->n_slots == 0)) return TG_EINVAL;
+  if (a->n_gitems > 0 && !a->gitems) return TG_EINVAL;
+  if (a->workspace_bytes < tg_decode_workspace_bytes(a->n_slots, G, d)) return TG_EINVAL;
   for (int32_t cl = 0; cl < c->n_clusters; ++cl)
     for (int t = 0; t < 2; ++t) {
       if (c->stride[cl][t] < 0 || c->n_pages[cl][t] < 0) return TG_EINVAL;
@@ -163,8 +166,10 @@ int decode_split(const tg_cache* c, const tg_decode_args* a, void* stream, bool 
   s.q = (gptr)(a->q);
   s.work = (const TG_GLOBAL int32_t*)(a->work);
   s.ws_acc = (TG_GLOBAL float*)(a->workspace);
-  s.ws_ml = (TG_GLOBAL float*)(a->workspace + static_cast<int64_t>(a->n_items) * G * d);
+  s.ws_ml = (TG_GLOBAL float*)(a->workspace + static_cast<int64_t>(a->n_slots) * G * d);
   s.n_items = a->n_items;
+  s.gitems = (const TG_GLOBAL int32_t*)(a->gitems);
+  s.n_gitems = a->n_gitems;
   s.n_q_heads = a->n_q_heads;
   const float scale = a->sm_scale != 0.f ? a->sm_scale : 1.f / std::sqrt(static_cast<float>(d));
   s.scale_log2 = scale * kLog2e;
@@ -182,7 +187,7 @@ int decode_split(const tg_cache* c, const tg_decode_args* a, void* stream, bool 
   if (e == hipSuccess && has_bf) e = launch_split_bf16(s, d, G, qf32, st);
   if (e != hipSuccess) return TG_EDEVICE;
   if (!merge) return TG_OK;
-  e = launch_merge(a->workspace, a->workspace + static_cast<int64_t>(a->n_items) * G * d, a->part_off,
+  e = launch_merge(a->workspace, a->workspace + static_cast<int64_t>(a->n_slots) * G * d, a->part_off,
                    c->B * c->n_kv_heads, G, d, a->out, st);
   return e == hipSuccess ? TG_OK : TG_EDEVICE;
 }

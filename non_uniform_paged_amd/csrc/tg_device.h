@@ -39,9 +39,11 @@ struct SplitArgs {
   const TG_GLOBAL int32_t* n_fixed;  // [B] or null
   gptr q;
   const TG_GLOBAL int32_t* work;
-  TG_GLOBAL float* ws_acc;  // [n_items][G][D]
-  TG_GLOBAL float* ws_ml;   // [n_items][G][2]
+  const TG_GLOBAL int32_t* gitems;  // [n_gitems][TG_GROUP_WIDTH][2] (request, slot)
+  TG_GLOBAL float* ws_acc;  // [n_slots][G][D]
+  TG_GLOBAL float* ws_ml;   // [n_slots][G][2]
   int32_t n_items;
+  int32_t n_gitems;
   int32_t n_q_heads;
   int32_t n_kv_heads;
   float scale_log2;

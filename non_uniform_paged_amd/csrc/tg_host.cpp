@@ -329,6 +329,7 @@ int check_share(const tg_share_desc* sh, const tg_reservation* res, const Geomet
 int check_opts(const tg_plan_opts* o, int32_t ps, int32_t qb) {
   if (!o) return TG_EINVAL;
   if (o->chunk_bf < ps || o->chunk_bf % ps || o->chunk_i8 < qb || o->chunk_i8 % qb) return TG_EINVAL;
+  if (o->group_size < 0 || o->group_size > TG_GROUP_WIDTH) return TG_EINVAL;
   return TG_OK;
 }
 
@@ -367,16 +368,159 @@ bool share_key(const tg_reservation* res, const Geometry& g, const Paths& paths,
   return false;  // unreachable: last < n_fixed = total path length
 }
 
-struct PlanCounts {
-  int64_t n_items = 0;
-};
-
 int count_plan(const tg_reservation* res, const Geometry& g, const tg_plan_opts* o, int64_t* n) {
   int64_t items = 0;
   for (int64_t i = 0; i < int64_t(g.B) * g.H; ++i)
     items += ceil_div(res->n_i8[i], o->chunk_i8) + ceil_div(res->n_bf[i], o->chunk_bf);
   if (items > std::numeric_limits<int32_t>::max()) return TG_EOVERFLOW;
   *n = items;
+  return TG_OK;
+}
+
+// The split plan: work items {r, h, tier, t0, t1, slot}, the slot CSR per
+// (r, h) and the member table of group items.
+struct Plan {
+  std::vector<int32_t> work;      // [n_items * 6]
+  std::vector<int32_t> part_off;  // [B*H + 1]
+  std::vector<int32_t> gitems;    // [n_gitems * TG_GROUP_WIDTH * 2]
+  int64_t n_items() const { return int64_t(work.size()) / 6; }
+  int64_t n_gitems() const { return int64_t(gitems.size()) / (2 * TG_GROUP_WIDTH); }
+};
+
+// A run of leading shared bf16 pages of (r, c) that belong to one radix node.
+struct Run {
+  int32_t node;
+  int64_t ja, jb, start;
+};
+
+std::vector<Run> shared_runs(const tg_reservation* res, const Geometry& g, const Paths& paths, int32_t r,
+                             int32_t c) {
+  std::vector<Run> runs;
+  const int64_t np = pages_of(res, g, r, c, TG_TIER_BF16);
+  ShareKey k;
+  for (int64_t j = 0; j < np && share_key(res, g, paths, r, c, TG_TIER_BF16, j, &k); ++j) {
+    if (!runs.empty() && runs.back().node == k.node && runs.back().jb == j)
+      runs.back().jb = j + 1;
+    else
+      runs.push_back(Run{k.node, j, j + 1, k.start});
+  }
+  return runs;
+}
+
+struct RunIdent {
+  int64_t node, start, npages, n_i8;
+  bool operator==(const RunIdent& o) const {
+    return node == o.node && start == o.start && npages == o.npages && n_i8 == o.n_i8;
+  }
+};
+struct RunIdentHash {
+  size_t operator()(const RunIdent& x) const {
+    uint64_t h = 1469598103934665603ull;
+    for (int64_t v : {x.node, x.start, x.npages, x.n_i8}) h = (h ^ uint64_t(v)) * 1099511628211ull;
+    return size_t(h);
+  }
+};
+
+int make_plan(const tg_reservation* res, const Geometry& g, const Paths& paths, const tg_plan_opts* o,
+              Plan* p) {
+  int64_t bound = 0;
+  int st = count_plan(res, g, o, &bound);
+  if (st) return st;
+  const int64_t BH = int64_t(g.B) * g.H;
+  std::vector<int64_t> shared_rows(BH, 0);
+  // group items: head, row range, members (ascending r)
+  struct GItem {
+    int32_t h;
+    int64_t t0, t1;
+    std::vector<int32_t> members;
+  };
+  std::vector<GItem> gi;
+  if (o->group_size > 1 && paths.on) {
+    std::vector<std::vector<Run>> runs(int64_t(g.B) * g.C);
+    for (int32_t r = 0; r < g.B; ++r)
+      for (int32_t c = 0; c < g.C; ++c) runs[int64_t(r) * g.C + c] = shared_runs(res, g, paths, r, c);
+    for (int32_t h = 0; h < g.H; ++h) {
+      const int32_t c = res->cluster_of_head[h];
+      std::unordered_map<RunIdent, size_t, RunIdentHash> index;
+      struct Group {
+        RunIdent id;
+        int64_t ja;
+        std::vector<int32_t> members;
+      };
+      std::vector<Group> order;
+      for (int32_t r = 0; r < g.B; ++r) {
+        const std::vector<Run>& rr = runs[int64_t(r) * g.C + c];
+        if (!rr.empty()) shared_rows[int64_t(r) * g.H + h] = rr.back().jb * g.ps;
+        for (const Run& u : rr) {
+          const RunIdent id{u.node, u.start, u.jb - u.ja, res->n_i8[int64_t(r) * g.H + h]};
+          auto it = index.find(id);
+          if (it == index.end()) {
+            it = index.emplace(id, order.size()).first;
+            order.push_back(Group{id, u.ja, {}});
+          }
+          order[it->second].members.push_back(r);
+        }
+      }
+      for (const Group& grp : order) {
+        const int64_t lo = grp.ja * g.ps, hi = (grp.ja + grp.id.npages) * g.ps;
+        for (size_t k = 0; k < grp.members.size(); k += o->group_size) {
+          const size_t e = std::min(grp.members.size(), k + size_t(o->group_size));
+          for (int64_t t0 = lo; t0 < hi; t0 += o->chunk_bf)
+            gi.push_back(GItem{h, t0, std::min<int64_t>(t0 + o->chunk_bf, hi),
+                               std::vector<int32_t>(grp.members.begin() + k, grp.members.begin() + e)});
+        }
+      }
+    }
+  }
+  // memberships of each (r, h), in group-item order
+  std::vector<std::vector<std::pair<int32_t, int32_t>>> member_of(BH);  // (group item, member index)
+  for (size_t k = 0; k < gi.size(); ++k)
+    for (size_t m = 0; m < gi[k].members.size(); ++m)
+      member_of[int64_t(gi[k].members[m]) * g.H + gi[k].h].push_back({int32_t(k), int32_t(m)});
+  if (int64_t(gi.size()) + bound > std::numeric_limits<int32_t>::max()) return TG_EOVERFLOW;
+  p->gitems.assign(gi.size() * 2 * TG_GROUP_WIDTH, -1);
+  p->part_off.assign(BH + 1, 0);
+  p->work.clear();
+  p->work.reserve((gi.size() + size_t(bound)) * 6);
+  for (size_t k = 0; k < gi.size(); ++k) {
+    const int32_t w[6] = {-1 - int32_t(k), gi[k].h, TG_TIER_BF16, int32_t(gi[k].t0), int32_t(gi[k].t1), -1};
+    p->work.insert(p->work.end(), w, w + 6);
+  }
+  int64_t slot = 0;
+  for (int32_t r = 0; r < g.B; ++r)
+    for (int32_t h = 0; h < g.H; ++h) {
+      const int64_t i = int64_t(r) * g.H + h;
+      p->part_off[i] = int32_t(slot);
+      for (const auto& km : member_of[i]) {
+        int32_t* e = p->gitems.data() + (int64_t(km.first) * TG_GROUP_WIDTH + km.second) * 2;
+        e[0] = r;
+        e[1] = int32_t(slot++);
+      }
+      for (int32_t t : {TG_TIER_I8, TG_TIER_BF16}) {
+        const int64_t len = t == TG_TIER_BF16 ? res->n_bf[i] : res->n_i8[i];
+        const int64_t lo = t == TG_TIER_BF16 ? shared_rows[i] : 0;
+        const int32_t ch = t == TG_TIER_BF16 ? o->chunk_bf : o->chunk_i8;
+        for (int64_t t0 = lo; t0 < len; t0 += ch) {
+          const int32_t w[6] = {r, h, t, int32_t(t0), int32_t(std::min<int64_t>(t0 + ch, len)), int32_t(slot++)};
+          p->work.insert(p->work.end(), w, w + 6);
+        }
+      }
+    }
+  if (slot > std::numeric_limits<int32_t>::max()) return TG_EOVERFLOW;
+  p->part_off[BH] = int32_t(slot);
+  const int64_t n = p->n_items();
+  if (o->lpt && n > 1) {
+    std::vector<int32_t> order(n);
+    for (int32_t k = 0; k < n; ++k) order[k] = k;
+    auto cost = [&](int32_t k) {
+      const int32_t* w = p->work.data() + int64_t(k) * 6;
+      return int64_t(w[4] - w[3]) * (w[2] == TG_TIER_BF16 ? 2 : 1);
+    };
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return cost(a) > cost(b); });
+    std::vector<int32_t> tmp(p->work);
+    for (int64_t k = 0; k < n; ++k)
+      std::memcpy(p->work.data() + k * 6, tmp.data() + int64_t(order[k]) * 6, 6 * sizeof(int32_t));
+  }
   return TG_OK;
 }
 
@@ -392,10 +536,16 @@ extern "C" int tg_size_tables(const tg_reservation* res, int32_t ps, int32_t qb,
   Paths paths;
   if ((st = check_share(share, res, g, &paths))) return st;
   if ((st = check_opts(opts, ps, qb))) return st;
-  int64_t items = 0;
-  if ((st = count_plan(res, g, opts, &items))) return st;
+  Plan plan;
+  try {
+    if ((st = make_plan(res, g, paths, opts, &plan))) return st;
+  } catch (...) {
+    return TG_ENOMEM;
+  }
   std::memset(out, 0, sizeof(*out));
-  out->n_items = static_cast<int32_t>(items);
+  out->n_items = static_cast<int32_t>(plan.n_items());
+  out->n_gitems = static_cast<int32_t>(plan.n_gitems());
+  out->n_slots = plan.part_off.back();
   for (int32_t c = 0; c < g.C; ++c)
     for (int32_t t = 0; t < 2; ++t) {
       int64_t stride = 0, need = 0;
@@ -429,9 +579,16 @@ extern "C" int tg_build_tables(tg_pool* pool, const tg_reservation* res, const t
   check_reservation(res, pool->page_size, pool->quant_block, &g);
   Paths paths;
   check_share(share, res, g, &paths);
-  if (g.C != pool->C || out->n_items != sz.n_items || !out->len || !out->part_off || !out->released ||
-      (sz.n_items > 0 && !out->work))
+  if (g.C != pool->C || out->n_items != sz.n_items || out->n_gitems != sz.n_gitems || !out->len ||
+      !out->part_off || !out->released || (sz.n_items > 0 && !out->work) ||
+      (sz.n_gitems > 0 && !out->gitems))
     return TG_EINVAL;
+  Plan plan;
+  try {
+    if ((st = make_plan(res, g, paths, opts, &plan))) return st;
+  } catch (...) {
+    return TG_ENOMEM;
+  }
   for (int32_t c = 0; c < g.C; ++c) {
     if (pool->cluster_size[c] != res->cluster_size[c]) return TG_EINVAL;
     for (int32_t t = 0; t < 2; ++t) {
@@ -515,40 +672,9 @@ extern "C" int tg_build_tables(tg_pool* pool, const tg_reservation* res, const t
     out->len[2 * i] = res->n_i8[i];
     out->len[2 * i + 1] = res->n_bf[i];
   }
-  // plan, in natural order
-  int32_t n = 0;
-  for (int32_t r = 0; r < g.B; ++r)
-    for (int32_t h = 0; h < g.H; ++h) {
-      const int64_t i = int64_t(r) * g.H + h;
-      out->part_off[i] = n;
-      for (int32_t t : {TG_TIER_I8, TG_TIER_BF16}) {
-        const int32_t len = t == TG_TIER_BF16 ? res->n_bf[i] : res->n_i8[i];
-        const int32_t ch = t == TG_TIER_BF16 ? opts->chunk_bf : opts->chunk_i8;
-        for (int64_t t0 = 0; t0 < len; t0 += ch) {
-          int32_t* w = out->work + int64_t(n) * 6;
-          w[0] = r;
-          w[1] = h;
-          w[2] = t;
-          w[3] = static_cast<int32_t>(t0);
-          w[4] = static_cast<int32_t>(std::min<int64_t>(t0 + ch, len));
-          w[5] = n;
-          ++n;
-        }
-      }
-    }
-  out->part_off[int64_t(g.B) * g.H] = n;
-  if (opts->lpt && n > 1) {
-    std::vector<int32_t> order(n);
-    for (int32_t k = 0; k < n; ++k) order[k] = k;
-    auto cost = [&](int32_t k) {
-      const int32_t* w = out->work + int64_t(k) * 6;
-      return int64_t(w[4] - w[3]) * (w[2] == TG_TIER_BF16 ? 2 : 1);
-    };
-    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return cost(a) > cost(b); });
-    std::vector<int32_t> tmp(out->work, out->work + int64_t(n) * 6);
-    for (int32_t k = 0; k < n; ++k)
-      std::memcpy(out->work + int64_t(k) * 6, tmp.data() + int64_t(order[k]) * 6, 6 * sizeof(int32_t));
-  }
+  std::copy(plan.work.begin(), plan.work.end(), out->work);
+  std::copy(plan.part_off.begin(), plan.part_off.end(), out->part_off);
+  std::copy(plan.gitems.begin(), plan.gitems.end(), out->gitems);
   for (int32_t r = 0; r < g.B; ++r) out->released[r] = 0;
   return TG_OK;
 }

@@ -1,6 +1,8 @@
 // Split kernel, bf16 tier (gfx950): one wavefront per plan item
 // (r, h, bf16, [t0, t1)) computes the online-normaliser partial of the G
-// q-heads of KV-head h over rows [t0, t1) of the bf16 tier.
+// q-heads of KV-head h over rows [t0, t1) of the bf16 tier.  A group item
+// does the same for up to 16 / G requests that share those pages (radix
+// prefix), one set of G score columns per member, in one pass over the pages.
 //
 // The maths is the online normaliser (CAP survey page, section 2.4.3
 // "Distributed acceleration", online normaliser [88]): per chunk keep
@@ -96,10 +98,14 @@ __device__ __forceinline__ void bf16_page(const u32x4_t (&kb)[NK], const u32x4_t
 // last page (an L2 hit), so every request is unconditional and the waits
 // before a page's use cover exactly that page's loads.  Page ids of up to 64
 // pages sit one per lane and are read with readlane.
+//
+// Score column lg belongs to member lg / G (its q-head lg % G).  A plain item
+// has one member (r, slot); a group item's members come from `gm`, the
+// (request, slot) pairs of its member table row.
 template <int D, int G, bool QF32, int DEPTH, bool STREAM>
 __device__ __forceinline__ void bf16_item(const SplitArgs& a, int r, int h, int t0, int t1, int slot,
-                                          int hs, const TG_GLOBAL int32_t* bt_row, gptr pool,
-                                          int64_t pbytes) {
+                                          const TG_GLOBAL int32_t* gm, int hs,
+                                          const TG_GLOBAL int32_t* bt_row, gptr pool, int64_t pbytes) {
   constexpr int NK = D / 32;           // 1 KiB loads per K (and per V) block
   constexpr int NT = D / 16;           // 16-channel tiles of V
   constexpr int NQ = QF32 ? 2 : 1;     // bf16 pieces of q
@@ -108,11 +114,22 @@ __device__ __forceinline__ void bf16_item(const SplitArgs& a, int r, int h, int 
   const int lg = lane & 15;
   const int lj = lane >> 4;
 
-  // Q^T operand of step s: lane (lg, lj) holds q[lg][32 s + 8 lj + e], e < 8
+  // column lg: member request and partial slot (-1: unused column)
+  int col_r = r, col_slot = lg < G ? slot : -1;
+  if (gm != nullptr) {
+    const int mu = lg / G;  // < 16 = TG_GROUP_WIDTH
+    col_r = gm[2 * mu];
+    col_slot = gm[2 * mu + 1];
+    if (col_r < 0) {
+      col_r = r;
+      col_slot = -1;
+    }
+  }
+  // Q^T operand of step s: lane (lg, lj) holds q[column lg][32 s + 8 lj + e]
   u32x4_t qop[NQ][NK];
   {
-    const bool has = lg < G;
-    const int64_t row = static_cast<int64_t>(r) * a.n_q_heads + h * G + (has ? lg : 0);
+    const bool has = col_slot >= 0;
+    const int64_t row = static_cast<int64_t>(col_r) * a.n_q_heads + h * G + lg % G;
 #pragma unroll
     for (int s = 0; s < NK; ++s) {
       if constexpr (QF32) {
@@ -180,20 +197,20 @@ __device__ __forceinline__ void bf16_item(const SplitArgs& a, int r, int h, int 
     }
   }
 
-  // partial of the item: m and l of head lg, accumulator rows 4lj+rr
+  // partials: m and l of column lg, accumulator rows (columns) 4lj+rr
   const float l_tot = xor32_sum(xor16_sum(l_run));
-  TG_GLOBAL float* acc_out = a.ws_acc + static_cast<int64_t>(slot) * G * D;
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
-    const int g = 4 * lj + rr;
-    if (g < G) {
+    const int cslot = __shfl(col_slot, 4 * lj + rr, 64);  // lane 4lj+rr owns that column
+    if (cslot >= 0) {
+      TG_GLOBAL float* acc_out = a.ws_acc + (static_cast<int64_t>(cslot) * G + (4 * lj + rr) % G) * D;
 #pragma unroll
-      for (int n = 0; n < NT; ++n) acc_out[g * D + 16 * n + lg] = acc[n][rr];
+      for (int n = 0; n < NT; ++n) acc_out[16 * n + lg] = acc[n][rr];
     }
   }
-  if (lj == 0 && lg < G) {
-    a.ws_ml[(static_cast<int64_t>(slot) * G + lg) * 2 + 0] = m_ref * kLn2;
-    a.ws_ml[(static_cast<int64_t>(slot) * G + lg) * 2 + 1] = l_tot;
+  if (lj == 0 && col_slot >= 0) {
+    a.ws_ml[(static_cast<int64_t>(col_slot) * G + lg % G) * 2 + 0] = m_ref * kLn2;
+    a.ws_ml[(static_cast<int64_t>(col_slot) * G + lg % G) * 2 + 1] = l_tot;
   }
 }
 
@@ -204,23 +221,31 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void split_bf16_kernel(SplitAr
   const TG_GLOBAL int32_t* w = a.work + static_cast<int64_t>(item) * 6;
   const int tier = uniform(w[2]);
   if (tier != TG_TIER_BF16) return;  // the INT8 kernel takes this item
-  const int r = uniform(w[0]), h = uniform(w[1]);
+  int r = uniform(w[0]);
+  const int h = uniform(w[1]);
   const int t0 = uniform(w[3]), t1 = uniform(w[4]), slot = uniform(w[5]);
+  const TG_GLOBAL int32_t* gm = nullptr;
+  if (r < 0) {  // group item: rows [t0, t1) are the same pages for every member
+    const int k = -1 - r;
+    if (k >= a.n_gitems) return;
+    gm = a.gitems + static_cast<int64_t>(k) * (2 * TG_GROUP_WIDTH);
+    r = uniform(gm[0]);
+  }
   const int cl = uniform(a.cluster_of_head[h]);
   const int hs = uniform(a.slot_in_cluster[h]);
   const TG_GLOBAL int32_t* bt_row = a.bt[cl][TG_TIER_BF16] + static_cast<int64_t>(r) * a.stride[cl][TG_TIER_BF16];
   gptr pool = a.pool[cl][TG_TIER_BF16];
   const int64_t pbytes = a.page_bytes[cl][TG_TIER_BF16];
   // an item that starts on the shared radix path reads through the caches
-  bool shared = false;
-  if (a.n_fixed) {
+  bool shared = gm != nullptr;
+  if (!shared && a.n_fixed) {
     const int n_i8 = uniform(a.len[2 * (r * a.n_kv_heads + h)]);
     shared = n_i8 + t0 + kPage <= uniform(a.n_fixed[r]);
   }
   if (shared)
-    bf16_item<D, G, QF32, DEPTH, false>(a, r, h, t0, t1, slot, hs, bt_row, pool, pbytes);
+    bf16_item<D, G, QF32, DEPTH, false>(a, r, h, t0, t1, slot, gm, hs, bt_row, pool, pbytes);
   else
-    bf16_item<D, G, QF32, DEPTH, true>(a, r, h, t0, t1, slot, hs, bt_row, pool, pbytes);
+    bf16_item<D, G, QF32, DEPTH, true>(a, r, h, t0, t1, slot, gm, hs, bt_row, pool, pbytes);
 }
 
 template <int D, int G, bool QF32>

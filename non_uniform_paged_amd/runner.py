@@ -33,14 +33,23 @@ class Prepared:
     """A populated cache plus the buffers of one decode step."""
 
     def __init__(self, w, chunk_bf: int = 1024, chunk_i8: int = 1024, lpt: bool = True,
-                 slack_pages: int = 0, shift_pages: int = 0, device: str = "cuda"):
+                 slack_pages: int = 0, shift_pages: int = 0, device: str = "cuda",
+                 group_size: Optional[int] = None):
+        """``group_size`` None: group shared-prefix pages for as many requests
+        as fill the 16 score columns (16 / G) when the batch shares a radix
+        prefix, else no groups."""
         import torch
 
         self.w = w
         dev = torch.device(device)
         self.res = reserve_workload(w)
         self.share = share_of(w)
-        sizes = api.tg_size_tables(self.res, w.page_size, w.quant_block, self.share, chunk_bf, chunk_i8, lpt)
+        G = w.Hq // w.Hkv
+        if group_size is None:
+            group_size = 16 // G if self.share is not None else 0
+        self.group_size = group_size
+        sizes = api.tg_size_tables(self.res, w.page_size, w.quant_block, self.share, chunk_bf, chunk_i8, lpt,
+                                   group_size)
         need = sizes["pages_needed"]
         C = self.res.C
         extra = slack_pages + shift_pages
@@ -51,7 +60,7 @@ class Prepared:
             filler = api.tg_reserve(w.head_rank, 10**6, 10**6, C, 10**6, w.quant_block,
                                     [shift_pages * w.page_size], None, None)
             ftab = api.tg_build_tables(self.pool, filler, None, w.page_size * 4, w.quant_block, False)
-        self.tables = api.tg_build_tables(self.pool, self.res, self.share, chunk_bf, chunk_i8, lpt)
+        self.tables = api.tg_build_tables(self.pool, self.res, self.share, chunk_bf, chunk_i8, lpt, group_size)
         if shift_pages:
             api.tg_release(self.pool, ftab, 0)
         self.cache = api.DeviceCache(self.pool, self.res, self.tables, dev, self.share)
@@ -71,7 +80,7 @@ class Prepared:
         else:
             self.q = torch.from_numpy(qn.view(np.int16)).to(dev).view(torch.bfloat16)
         self.out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
-        ws = api.tg_decode_workspace_bytes(self.tables.n_items, w.Hq // w.Hkv, w.d)
+        ws = api.tg_decode_workspace_bytes(self.tables.n_slots, G, w.d)
         self.workspace = torch.empty(max(ws // 4, 1), dtype=torch.float32, device=dev)
 
     # ------------------------------------------------------------------ run
@@ -117,11 +126,11 @@ class Prepared:
         for (c, tier, pid, s), rows in seen.items():
             kv_roof += rows * 4 * d if tier == 1 else rows * 2 * d + 4 * d
         q_o = w.B * w.Hq * d * (qbytes + 4)
-        tables = t.n_items * 24 + (w.B * w.Hkv + 1) * 4 + sum(
+        tables = t.n_items * 24 + t.n_gitems * 128 + (w.B * w.Hkv + 1) * 4 + sum(
             int(-(-n_bf[r, h] // w.page_size) + n_i8[r, h] // w.quant_block) * 4
             for r in range(w.B) for h in range(w.Hkv))
         rows_total = int(n_bf.sum() + n_i8.sum())
         return {"kv_effective": kv_eff, "kv_roofline": kv_roof, "q_o": q_o, "tables": tables,
                 "effective": kv_eff + q_o + tables, "roofline": kv_roof + q_o + tables,
                 "head_rows": rows_total, "flops": 4 * d * G * rows_total,
-                "n_items": t.n_items}
+                "n_items": t.n_items, "n_gitems": t.n_gitems, "n_slots": t.n_slots}

@@ -45,6 +45,15 @@ R-plan   items (r, h, tier, t0, t1, slot) in order r, h, tier (INT8 first),
          t0 = 0, chunk, 2*chunk, ...; slot is the natural index; part_off is the
          CSR of slots per (r, h).  With lpt, items are stably sorted by
          descending cost (t1 - t0) * (2 for bf16, 1 for INT8).
+R-group  (only with a group size > 1 and radix paths) the leading shared bf16
+         pages of each (r, h) are cut into runs with the same radix node;
+         requests whose run has the same (node, first row, page count, INT8
+         rows) are taken in ascending r, group_size at a time, and each group's
+         rows are chunked from the run's first row into group items (listed
+         first: per h, runs in order of first appearance, groups, chunks).  A
+         request's own bf16 items then start after its shared rows.  Slots: per
+         (r, h) in natural order, its group memberships (in group-item order)
+         then its own items.
 
 Pinned by: tests/test_oracle_planner.py (hand-worked golden tables, the
 worked radix example's consistent block counts, a second allocator written
@@ -327,31 +336,110 @@ def release(pool: Pool, pages_of_request: List[List[List[int]]]):
 
 
 # ---------------------------------------------------------------- tables & plan
-def plan(res: Reservation, chunk_bf: int, chunk_i8: int, lpt: bool):
-    """Split plan and partial CSR (R-plan)."""
+GROUP_WIDTH = 16  # member slots per group item in the member table
+
+
+def shared_segments(res: Reservation, r: int, c: int, page_size: int, quant_block: int,
+                    n_fixed, paths, node_len):
+    """Leading shared bf16 pages of row (r, c), cut into runs with the same
+    radix node: [(node, first page, end page, first row)] (R-group)."""
+    np_bf = page_counts_row(res, r, c, page_size)
+    segs = []
+    j = 0
+    while j < np_bf:
+        key = share_key(res, r, c, TIER_BF, j, page_size, quant_block, n_fixed, paths, node_len)
+        if key is None:
+            break
+        node, start = key[2], key[3]
+        if segs and segs[-1][0] == node and segs[-1][2] == j:
+            segs[-1][2] = j + 1
+        else:
+            segs.append([node, j, j + 1, start])
+        j += 1
+    return segs
+
+
+def page_counts_row(res: Reservation, r: int, c: int, page_size: int) -> int:
+    hs = heads_of_cluster(res, c)
+    return _ceil_div(max(res.n_bf[r][h] for h in hs), page_size)
+
+
+def plan(res: Reservation, chunk_bf: int, chunk_i8: int, lpt: bool, group_size: int = 0,
+         page_size: int = 16, quant_block: int = 64, n_fixed=None, paths=None, node_len=None):
+    """Split plan, partial CSR and group-item member table (R-plan, R-group).
+
+    Returns (work, part_off, gitems).  A work item is (r, h, tier, t0, t1,
+    slot); a group item has r = -1 - g (g its index in gitems), slot -1, and
+    gitems[g] lists its (request, slot) members, padded with (-1, -1) to
+    GROUP_WIDTH."""
     B = len(res.L)
     H = len(res.cluster_of_head)
-    work = []
+    grouping = group_size > 1 and paths is not None
+    gitems_members = []   # per group item: member requests
+    gitem_rows = []       # per group item: (h, t0, t1)
+    shared_rows = [[0] * H for _ in range(B)]
+    if grouping:
+        for h in range(H):
+            c = res.cluster_of_head[h]
+            members = {}
+            order = []
+            for r in range(B):
+                segs = shared_segments(res, r, c, page_size, quant_block, n_fixed, paths, node_len)
+                if segs:
+                    shared_rows[r][h] = segs[-1][2] * page_size
+                for node, ja, jb, start in segs:
+                    ident = (node, start, jb - ja, res.n_i8[r][h])
+                    if ident not in members:
+                        members[ident] = []
+                        order.append((ident, ja))
+                    members[ident].append(r)
+            for ident, ja in order:
+                mem = members[ident]
+                lo, hi = ja * page_size, (ja + ident[2]) * page_size
+                for k in range(0, len(mem), group_size):
+                    grp = mem[k:k + group_size]
+                    for t0 in range(lo, hi, chunk_bf):
+                        gitems_members.append(grp)
+                        gitem_rows.append((h, t0, min(t0 + chunk_bf, hi)))
+    # slots in natural (r, h) order: group memberships first, then own items
+    member_of = {}
+    for gi, grp in enumerate(gitems_members):
+        h = gitem_rows[gi][0]
+        for m in grp:
+            member_of.setdefault((m, h), []).append(gi)
+    gslot = [[-1] * len(grp) for grp in gitems_members]
+    own = []
     part_off = []
+    slot = 0
     for r in range(B):
         for h in range(H):
-            part_off.append(len(work))
-            for t, n, ch in ((TIER_I8, res.n_i8[r][h], chunk_i8), (TIER_BF, res.n_bf[r][h], chunk_bf)):
-                for t0 in range(0, n, ch):
-                    work.append((r, h, t, t0, min(t0 + ch, n), len(work)))
-    part_off.append(len(work))
+            part_off.append(slot)
+            for gi in member_of.get((r, h), []):
+                gslot[gi][gitems_members[gi].index(r)] = slot
+                slot += 1
+            for t, lo, n, ch in ((TIER_I8, 0, res.n_i8[r][h], chunk_i8),
+                                 (TIER_BF, shared_rows[r][h], res.n_bf[r][h], chunk_bf)):
+                for t0 in range(lo, n, ch):
+                    own.append((r, h, t, t0, min(t0 + ch, n), slot))
+                    slot += 1
+    part_off.append(slot)
+    work = [(-1 - gi, h, TIER_BF, t0, t1, -1) for gi, (h, t0, t1) in enumerate(gitem_rows)] + own
+    gitems = [[(m, gslot[gi][k]) for k, m in enumerate(grp)] + [(-1, -1)] * (GROUP_WIDTH - len(grp))
+              for gi, grp in enumerate(gitems_members)]
     if lpt:
         work = sorted(work, key=lambda it: -(it[4] - it[3]) * (2 if it[2] == TIER_BF else 1))
-    return work, part_off
+    return work, part_off, gitems
 
 
 def build_tables(pool: Pool, res: Reservation, page_size: int, quant_block: int,
                  chunk_bf: int, chunk_i8: int, lpt: bool,
-                 n_fixed=None, paths=None, node_len=None) -> Tables:
+                 n_fixed=None, paths=None, node_len=None, group_size: int = 0) -> Tables:
     """Allocate pages and emit block tables, lengths and the plan (R-alloc,
-    R-page, R-plan)."""
+    R-page, R-plan, R-group)."""
     if chunk_bf < page_size or chunk_bf % page_size or chunk_i8 < quant_block or chunk_i8 % quant_block:
         raise OracleError("EINVAL", "chunk sizes")
+    if not 0 <= group_size <= GROUP_WIDTH:
+        raise OracleError("EINVAL", "group size")
     B = len(res.L)
     C = len(res.cluster_size)
     H = len(res.cluster_of_head)
@@ -360,5 +448,9 @@ def build_tables(pool: Pool, res: Reservation, page_size: int, quant_block: int,
     bt = [[[pages[r][c][t] + [-1] * (stride[c][t] - len(pages[r][c][t])) for r in range(B)]
            for t in range(2)] for c in range(C)]
     lens = [[(res.n_i8[r][h], res.n_bf[r][h]) for h in range(H)] for r in range(B)]
-    work, part_off = plan(res, chunk_bf, chunk_i8, lpt)
-    return Tables(bt, stride, lens, work, part_off, pages)
+    nf = [0] * B if n_fixed is None else list(n_fixed)
+    work, part_off, gitems = plan(res, chunk_bf, chunk_i8, lpt, group_size, page_size, quant_block,
+                                  nf, paths, node_len)
+    t = Tables(bt, stride, lens, work, part_off, pages)
+    t.gitems = gitems
+    return t

@@ -281,7 +281,7 @@ def test_split_then_merge_equals_decode(name):
     ws = torch.empty_like(p.workspace)
     out = torch.empty_like(p.out)
     api.tg_decode_split(p.cache, p.q, ws, p.w.Hq)
-    api.tg_merge_partials(ws, p.tables.n_items, p.w.B * p.w.Hkv, p.w.Hq // p.w.Hkv, p.w.d,
+    api.tg_merge_partials(ws, p.tables.n_slots, p.w.B * p.w.Hkv, p.w.Hq // p.w.Hkv, p.w.d,
                           p.cache.part_off, out)
     torch.cuda.synchronize()
     sep = out.cpu().numpy()
@@ -293,3 +293,17 @@ def test_all_int8_and_empty_bf16_tier():
     w = make_workload("tiered", B=2, Hq=8, Hkv=2, ctx=("fixed", 640), recent_ppm=0)
     p, _ = _run_and_compare(w, what="int8-only")
     assert int(p.res.n_bf.max()) == 0
+
+
+@pytest.mark.parametrize("gs,G,recent,qd", [(0, 4, 10**6, "bf16"), (1, 4, 10**6, "bf16"), (2, 4, 10**6, "bf16"),
+                                            (4, 4, 10**6, "f32"), (3, 4, 250_000, "bf16"),
+                                            (16, 1, 10**6, "bf16"), (8, 2, 250_000, "f32"),
+                                            (2, 8, 10**6, "bf16")])
+def test_group_items(gs, G, recent, qd):
+    """Shared-prefix group items (one pass over a shared page for up to 16 / G
+    requests) against the oracle, for several group sizes and head shapes."""
+    _need_gpu()
+    w = make_workload("radix", B=11, Hq=2 * G, Hkv=2, recent_ppm=recent, q_dtype=qd,
+                      share=dict(prefix=200, branch=50, n_branches=3, suffix=(8, 300)))
+    p, _ = _run_and_compare(w, what=f"group{gs}-G{G}-{recent}-{qd}", chunk_bf=48, group_size=gs)
+    assert (p.tables.n_gitems > 0) == (gs > 1)

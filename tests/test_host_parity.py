@@ -55,19 +55,24 @@ def _share(w):
     return tg.Share(n_nodes, ids, node_len), (w.n_fixed, w.paths, w.node_len)
 
 
-def _tables_parity(w, chunk_bf=512, chunk_i8=1024, lpt=True, slack=3):
+def _gitems_of(t_o):
+    return np.array(t_o.gitems, dtype=np.int32).reshape(-1, 16, 2)
+
+
+def _tables_parity(w, chunk_bf=512, chunk_i8=1024, lpt=True, slack=3, group_size=0):
     res_o, res_g = _both(w)
     _compare_reservation(res_o, res_g)
     share, sh_o = _share(w)
     need_bf, need_i8 = P.pages_needed(res_o, w.page_size, w.quant_block, *sh_o)
-    sizes = tg.tg_size_tables(res_g, w.page_size, w.quant_block, share, chunk_bf, chunk_i8, lpt)
+    sizes = tg.tg_size_tables(res_g, w.page_size, w.quant_block, share, chunk_bf, chunk_i8, lpt, group_size)
     assert [row[1] for row in sizes["pages_needed"]] == need_bf
     assert [row[0] for row in sizes["pages_needed"]] == need_i8
     pool_g = tg.Pool(res_g.cluster_size, w.d, w.page_size, w.quant_block,
                      [x + slack for x in need_bf], [x + slack for x in need_i8])
     pool_o = P.Pool([x + slack for x in need_bf], [x + slack for x in need_i8])
-    t_g = tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt)
-    t_o = P.build_tables(pool_o, res_o, w.page_size, w.quant_block, chunk_bf, chunk_i8, lpt, *sh_o)
+    t_g = tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt, group_size)
+    t_o = P.build_tables(pool_o, res_o, w.page_size, w.quant_block, chunk_bf, chunk_i8, lpt, *sh_o,
+                         **({"group_size": group_size} if sh_o else {}))
     for c in range(w.n_clusters):
         for t in range(2):
             assert t_g.stride[c][t] == t_o.stride[c][t]
@@ -77,13 +82,18 @@ def _tables_parity(w, chunk_bf=512, chunk_i8=1024, lpt=True, slack=3):
     assert np.array_equal(t_g.len, np.array(t_o.lens, dtype=np.int32))
     assert np.array_equal(t_g.plan, np.array(t_o.work, dtype=np.int32).reshape(-1, 6))
     assert list(t_g.part_off) == t_o.part_off
+    assert t_g.n_slots == t_o.part_off[-1] and t_g.n_gitems == len(t_o.gitems)
+    assert np.array_equal(t_g.gitems, _gitems_of(t_o))
     return res_o, res_g, pool_o, pool_g, t_o, t_g
 
 
-@pytest.mark.parametrize("name", ["tiny", "llama8b", "ragged", "tiered", "radix"])
-def test_full_size_configs_bit_exact(name):
+@pytest.mark.parametrize("name,gs", [("tiny", 0), ("llama8b", 0), ("ragged", 0), ("tiered", 0), ("radix", 0),
+                                     ("radix", 2), ("radix", 16)])
+def test_full_size_configs_bit_exact(name, gs):
     w = make_workload(name)
-    res_o, res_g, pool_o, pool_g, t_o, t_g = _tables_parity(w)
+    res_o, res_g, pool_o, pool_g, t_o, t_g = _tables_parity(w, group_size=gs)
+    if gs > 1:
+        assert t_g.n_gitems > 0
     # refcounts agree page by page on a sample of pages
     for c in range(w.n_clusters):
         for t in range(2):
@@ -144,6 +154,8 @@ def test_randomised_small_cases_bit_exact():
         chunk_bf = ps * rnd.randint(1, 6)
         chunk_i8 = qb * rnd.randint(1, 3)
         lpt = rnd.random() < 0.5
+        gs = rnd.choice([0, 1, 2, 3, 16])
+        grp = {"group_size": gs} if use_share else {}
         need_bf, need_i8 = P.pages_needed(res_o, ps, qb, *sh_o)
         cap_bf = [n + rnd.randint(-1, 2) for n in need_bf]
         cap_i8 = [n + rnd.randint(-1, 2) for n in need_i8]
@@ -152,23 +164,24 @@ def test_randomised_small_cases_bit_exact():
         pool_g = tg.Pool(res_g.cluster_size, 16, ps, qb, cap_bf, cap_i8)
         pool_o = P.Pool(cap_bf, cap_i8)
         try:
-            t_o = P.build_tables(pool_o, res_o, ps, qb, chunk_bf, chunk_i8, lpt, *sh_o)
+            t_o = P.build_tables(pool_o, res_o, ps, qb, chunk_bf, chunk_i8, lpt, *sh_o, **grp)
         except P.OracleError as e:
             assert e.code == "ENOMEM"
             with pytest.raises(tg.TGError) as ge:
-                tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt)
+                tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt, gs)
             assert ge.value.name == "TG_ENOMEM"
             for c in range(C):
                 for t in range(2):
                     assert pool_g.free_pages(c, t) == pool_g.capacity(c, t)
             continue
-        t_g = tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt)
+        t_g = tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt, gs)
         for c in range(C):
             for t in range(2):
                 if t_o.stride[c][t]:
                     assert np.array_equal(t_g.bt[c][t], np.array(t_o.bt[c][t], dtype=np.int32)), case
         assert np.array_equal(t_g.plan, np.array(t_o.work, dtype=np.int32).reshape(-1, 6)), case
         assert list(t_g.part_off) == t_o.part_off
+        assert np.array_equal(t_g.gitems, _gitems_of(t_o)), case
 
 
 def test_error_codes():
@@ -189,4 +202,7 @@ def test_error_codes():
     # share paths inconsistent with n_fixed
     with pytest.raises(tg.TGError) as e:
         tg.tg_size_tables(res, 16, 64, tg.Share([1, 1], [0, 0], [5]))
+    assert e.value.name == "TG_EINVAL"
+    with pytest.raises(tg.TGError) as e:
+        tg.tg_size_tables(res, 16, 64, None, group_size=17)
     assert e.value.name == "TG_EINVAL"

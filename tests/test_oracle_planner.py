@@ -33,7 +33,8 @@ def test_hand_worked_budgets_clusters_tables_plan():
     assert t.bt[1][P.TIER_BF] == g["expect_bt_c1_bf"]
     assert [list(w) for w in t.work] == g["expect_work"]
     assert t.part_off == g["expect_part_off"]
-    work_lpt, off2 = P.plan(res, g["chunk_bf"], g["chunk_i8"], True)
+    work_lpt, off2, gi2 = P.plan(res, g["chunk_bf"], g["chunk_i8"], True)
+    assert gi2 == []
     assert [w[5] for w in work_lpt] == g["expect_lpt_slots"]
     assert off2 == g["expect_part_off"]
 
@@ -272,3 +273,83 @@ def test_rejects_bad_admission_inputs():
         P.reserve([0, 1], 10, 10, 1, 10**6, 64, [0])
     with pytest.raises(P.OracleError):
         P.reserve([0, 1], 10, 10, 1, 10**6, 64, [5], None, [1, 6])
+
+
+# ---------------------------------------------------------------- group items (R-group)
+def test_hand_worked_group_items():
+    g, res, n_fixed = _share_case()
+    c = _gold("planner_hand.json")["case_group"]
+    for lpt in (False, True):
+        pool = P.Pool([g["expect_pages_needed"]], [0])
+        t = P.build_tables(pool, res, g["page_size"], g["quant_block"], c["chunk_bf"], c["chunk_i8"], lpt,
+                           n_fixed, g["paths"], g["node_len"], c["group_size"])
+        assert t.part_off == c["expect_part_off"]
+        assert [[list(x) for x in gi] for gi in t.gitems] == c["expect_gitems"]
+        if not lpt:
+            assert [list(w) for w in t.work] == c["expect_work"]
+        else:
+            order = ["g%d" % (-1 - w[0]) if w[0] < 0 else w[5] for w in t.work]
+            assert order == c["expect_lpt_order"]
+        # same pages as the ungrouped plan: grouping only changes the work list
+        pool2 = P.Pool([g["expect_pages_needed"]], [0])
+        t2 = P.build_tables(pool2, res, g["page_size"], g["quant_block"], c["chunk_bf"], c["chunk_i8"], lpt,
+                            n_fixed, g["paths"], g["node_len"])
+        assert t2.bt == t.bt and t2.gitems == []
+
+
+def _group_check(w, res, t, gs):
+    """Coverage, slot and page-identity invariants of a grouped plan."""
+    H, B, ps = w.Hkv, w.B, w.page_size
+    covered = {}
+    slots = []
+    for (r, h, tier, t0, t1, slot) in t.work:
+        assert 0 <= t0 < t1
+        if r >= 0:
+            covered.setdefault((r, h, tier), []).append((t0, t1))
+            slots.append(slot)
+            assert t.part_off[r * H + h] <= slot < t.part_off[r * H + h + 1]
+            continue
+        assert slot == -1 and tier == P.TIER_BF
+        mem = [m for m in t.gitems[-1 - r] if m[0] >= 0]
+        assert 1 <= len(mem) <= gs and all(m == (-1, -1) for m in t.gitems[-1 - r][len(mem):])
+        rs = [m[0] for m in mem]
+        assert rs == sorted(set(rs))
+        c = res.cluster_of_head[h]
+        assert t0 % ps == 0 and t1 % ps == 0
+        for (m, s) in mem:
+            covered.setdefault((m, h, tier), []).append((t0, t1))
+            slots.append(s)
+            assert t.part_off[m * H + h] <= s < t.part_off[m * H + h + 1]
+            # group rows lie in the fixed (shared) prefix of every member
+            assert res.n_i8[m][h] + t1 <= w.n_fixed[m]
+            assert res.n_i8[m][h] == res.n_i8[rs[0]][h]
+        # every member reads the very same physical pages for these rows
+        ref = t.bt[c][P.TIER_BF][rs[0]][t0 // ps:t1 // ps]
+        for m in rs[1:]:
+            assert t.bt[c][P.TIER_BF][m][t0 // ps:t1 // ps] == ref
+    assert sorted(slots) == list(range(t.part_off[-1]))
+    for r in range(B):
+        for h in range(H):
+            for tier, n in ((0, res.n_i8[r][h]), (1, res.n_bf[r][h])):
+                pos = 0
+                for a, b in sorted(covered.get((r, h, tier), [])):
+                    assert a == pos
+                    pos = b
+                assert pos == n
+
+
+@pytest.mark.parametrize("gs", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("recent_ppm", [1_000_000, 250_000])
+def test_group_invariants(gs, recent_ppm):
+    w = make_workload("radix", B=14, recent_ppm=recent_ppm,
+                      share=dict(prefix=300, branch=70, n_branches=3, suffix=(8, 120)))
+    res = P.reserve(w.head_rank, w.ratio_hi_ppm, w.ratio_lo_ppm, w.n_clusters, w.recent_ppm,
+                    w.quant_block, w.n_comp, w.n_fixed, w.budget_override)
+    share = (w.n_fixed, w.paths, w.node_len)
+    need_bf, need_i8 = P.pages_needed(res, w.page_size, w.quant_block, *share)
+    for chunk in (w.page_size, 3 * w.page_size, 64 * w.page_size):
+        pool = P.Pool(need_bf, need_i8)
+        t = P.build_tables(pool, res, w.page_size, w.quant_block, chunk, w.quant_block, True, *share, gs)
+        _group_check(w, res, t, gs)
+        n_group = sum(1 for it in t.work if it[0] < 0)
+        assert n_group == len(t.gitems) and (n_group > 0) == (gs > 1)
