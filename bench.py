@@ -38,10 +38,11 @@ DESCRIPTIONS = {
     "tiered": "TTKV tiered: batch 4, ctx 131072, 32/8 heads, d 128, newest 12.5% bf16, rest INT8 64-token blocks",
     "radix": "prefix-shared radix: batch 256, 2000-token prefix + 1 of 4 500-token branches + 80..1000 suffix, ratio 0.60->0.20 on suffix",
 }
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_traffic.txt")
-# sources of the bf16 split kernel (the dominant kernel of the default workload)
+# HBM bytes per split stage from rocprofv3 counter runs, one file per workload
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "split_kernel_{config}_traffic.txt")
+# sources of the split kernels (the dominant kernels of every workload)
 KERNEL_SRCS = [os.path.join(ROOT, "non_uniform_paged_amd", "csrc", f)
-               for f in ("tg_split_bf16.hip", "tg_device.h")]
+               for f in ("tg_split.hip", "tg_item_bf16.h", "tg_item_i8.h", "tg_device.h")]
 
 
 def _kernel_hash() -> str:
@@ -55,10 +56,11 @@ def _kernel_hash() -> str:
 def _traffic_record(config: str):
     """HBM bytes per split launch from the committed rocprofv3 counter runs,
     or None when absent or taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILE.format(config=config)
+    if not os.path.exists(path):
         return None
     rec = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.lstrip().startswith("#"):
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip()
@@ -115,7 +117,7 @@ def cpu_baseline(w, prep, budget_s: float = 12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="llama8b", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--chunk-bf", type=int, default=1024)
@@ -172,24 +174,29 @@ def main():
             flush.fill_(i & 0xFF)
 
     def one_step(evs=None):
-        # the decode step, i.e. tg_decode_attn: the split kernel(s), then the
-        # merge kernel (issued as its two halves so that the split kernel can
-        # be timed on its own; the tests check the two forms are bit-identical)
+        # the decode step: tg_decode_attn (split kernel(s), then the merge)
         if evs is not None:
             evs[0].record(stream)
-        api.tg_decode_split(prep.cache, prep.q, prep.workspace, w.Hq, stream=stream)
+        api.tg_decode_attn(prep.cache, prep.q, prep.out, prep.workspace, w.Hq, stream=stream)
         if evs is not None:
             evs[1].record(stream)
+
+    def split_step(evs):
+        # the same step issued as its two halves, with an event between them,
+        # to time the split kernel(s) alone (the tests check that the two
+        # forms give bit-identical outputs)
+        evs[0].record(stream)
+        api.tg_decode_split(prep.cache, prep.q, prep.workspace, w.Hq, stream=stream)
+        evs[1].record(stream)
         api.tg_merge_partials(prep.workspace, prep.tables.n_slots, w.B * w.Hkv, G, w.d,
                               prep.cache.part_off, prep.out, stream=stream)
-        if evs is not None:
-            evs[2].record(stream)
+        evs[2].record(stream)
 
     for i in range(args.warmup):
         evict(i)
         one_step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(args.steps):
@@ -197,14 +204,21 @@ def main():
         one_step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    split_ms_all = np.array([e[0].elapsed_time(e[1]) for e in events])
-    merge_ms_all = np.array([e[1].elapsed_time(e[2]) for e in events])
-    step_ms = np.array([e[0].elapsed_time(e[2]) for e in events])
+    step_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
     ms = float(step_ms.mean())
     med = float(np.median(step_ms))
+    # kernel timing: as many steps again, split and merge timed separately
+    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        evict(i + 1)
+        split_step(kev[i])
+    torch.cuda.synchronize()
+    split_ms_all = np.array([e[0].elapsed_time(e[1]) for e in kev])
+    merge_ms_all = np.array([e[1].elapsed_time(e[2]) for e in kev])
 
     # algorithmic bytes of the split kernel(s) (the dominant kernels): retained
-    # rows (shared pages once), q, tables, partials written; timed alone above
+    # rows (shared pages once), q, tables, partials written; timed alone in
+    # the kernel-timing steps
     split_bytes = tr["kv_roofline"] + w.B * w.Hq * w.d * (4 if w.q_dtype == "f32" else 2) + tr["tables"] \
         + prep.tables.n_slots * G * (w.d + 2) * 4
     split_ms = float(split_ms_all.mean())

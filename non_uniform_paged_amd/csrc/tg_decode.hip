@@ -1,8 +1,8 @@
 // Decode attention over the ragged, tiered, paged cache (gfx950): the C-ABI
 // entry points of the decode step and the log-sum-exp merge kernel.
 //
-// tg_decode_split launches one split kernel per tier present in the cache
-// (tg_split_bf16.hip, tg_split_i8.hip); each writes, per plan item, the
+// tg_decode_split launches the split kernel (tg_split.hip, with the work
+// items of tg_item_bf16.h and tg_item_i8.h), which writes, per plan item, the
 // online-normaliser partial (m, l, acc) of the item's rows.  tg_merge_partials
 // combines the partials of each (r, h) with the weights e^{m_s - M} (CAP survey
 // page, section 2.4.3 "Distributed acceleration", online normaliser [88]) and
@@ -17,87 +17,124 @@ namespace tg_dev {
 namespace {
 
 // ---------------------------------------------------------------- merge kernel
-// One wavefront per (pair, g).  The wave finds M = max_s m_s and the
-// denominator sum_s e^{m_s - M} l_s with one slot per lane, then sums the
-// weighted accumulators with NG = 64/(D/8) slots in flight at once (lane
-// group q takes slots q, q + NG, ...; each lane owns 8 channels) and folds
-// the groups together.
-template <int D>
+// WPR wavefronts per (pair, g) row.  Lanes form NG = 64/(D/8) groups of D/8
+// lanes; each lane owns 8 channels.  Group q of wave w takes slots
+// s0 + (w*NG + q), stepping by WPR*NG, and keeps its own running maximum:
+//   m <- max(m, m_s);  den = sum e^{m_s - m} l_s;  num = sum e^{m_s - m} acc_s
+// rescaling den and num when m grows, so every slot is read once.  The groups
+// (then the waves, through LDS) are folded with the same rescaling, and
+// o = num / den.
+template <int D, int WPR>
 __global__ __launch_bounds__(256) void merge_kernel(const TG_GLOBAL float* __restrict__ ws_acc,
                                                     const TG_GLOBAL float* __restrict__ ws_ml,
                                                     const TG_GLOBAL int32_t* __restrict__ part_off,
                                                     int32_t n_pairs, int32_t G,
                                                     TG_GLOBAL float* __restrict__ out) {
-  constexpr int LPR = D / 8;   // lanes per channel row
-  constexpr int NG = 64 / LPR; // slots merged concurrently
+  constexpr int LPR = D / 8;    // lanes per channel row
+  constexpr int NG = 64 / LPR;  // slot groups per wave
+  constexpr int RPB = 4 / WPR;  // rows per 256-thread block
+  __shared__ float red[WPR > 1 ? 4 : 1][WPR > 1 ? LPR : 1][10];
   const int lane = threadIdx.x & 63;
-  const int64_t rowid = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (rowid >= static_cast<int64_t>(n_pairs) * G) return;
+  const int wave = threadIdx.x >> 6;
+  const int w = wave % WPR;
+  const int64_t rowid = static_cast<int64_t>(blockIdx.x) * RPB + wave / WPR;
+  if (rowid >= static_cast<int64_t>(n_pairs) * G) return;  // uniform per block when WPR > 1
   const int64_t pair = rowid / G;
   const int g = static_cast<int>(rowid % G);
   const int s0 = part_off[pair], s1 = part_off[pair + 1];
   const int q = lane / LPR, c8 = lane % LPR;
   TG_GLOBAL float* dst = out + rowid * D + 8 * c8;
-  auto ml = [&](int s, int k) { return ws_ml[(static_cast<int64_t>(s) * G + g) * 2 + k]; };
-  auto accp = [&](int s) { return ws_acc + (static_cast<int64_t>(s) * G + g) * D + 8 * c8; };
-  if (s1 - s0 <= 1) {
-    if (q == 0) {
-      if (s1 == s0) {
-        st16(dst, 0.f, 0.f, 0.f, 0.f);
-        st16(dst + 4, 0.f, 0.f, 0.f, 0.f);
-      } else {
-        const float inv = 1.f / ml(s0, 1);
-        const f32x4_t x0 = *(const TG_GLOBAL f32x4_t*)(accp(s0));
-        const f32x4_t x1 = *(const TG_GLOBAL f32x4_t*)(accp(s0) + 4);
-        st16(dst, x0[0] * inv, x0[1] * inv, x0[2] * inv, x0[3] * inv);
-        st16(dst + 4, x1[0] * inv, x1[1] * inv, x1[2] * inv, x1[3] * inv);
-      }
-    }
-    return;
-  }
-  float mx = -INFINITY;
-  for (int s = s0 + lane; s < s1; s += 64) mx = fmaxf(mx, ml(s, 0));
-#pragma unroll
-  for (int k = 1; k < 64; k <<= 1) mx = fmaxf(mx, __shfl_xor(mx, k, 64));
-  float den = 0.f;
-  for (int s = s0 + lane; s < s1; s += 64) den += __expf(ml(s, 0) - mx) * ml(s, 1);
-#pragma unroll
-  for (int k = 1; k < 64; k <<= 1) den += __shfl_xor(den, k, 64);
+  float m = -INFINITY, den = 0.f;
   float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s = s0 + q; s < s1; s += NG) {
-    const float wgt = __expf(ml(s, 0) - mx);
-    const f32x4_t x0 = *(const TG_GLOBAL f32x4_t*)(accp(s));
-    const f32x4_t x1 = *(const TG_GLOBAL f32x4_t*)(accp(s) + 4);
+  for (int s = s0 + w * NG + q; s < s1; s += WPR * NG) {
+    const int64_t base = static_cast<int64_t>(s) * G + g;
+    const float ms = ws_ml[base * 2 + 0], ls = ws_ml[base * 2 + 1];
+    const f32x4_t x0 = *(const TG_GLOBAL f32x4_t*)(ws_acc + base * D + 8 * c8);
+    const f32x4_t x1 = *(const TG_GLOBAL f32x4_t*)(ws_acc + base * D + 8 * c8 + 4);
+    if (ms > m) {
+      const float sc = __expf(m - ms);
+      den *= sc;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) num[e] *= sc;
+      m = ms;
+    }
+    const float wgt = __expf(ms - m);
+    den = fmaf(wgt, ls, den);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       num[e] = fmaf(wgt, x0[e], num[e]);
       num[e + 4] = fmaf(wgt, x1[e], num[e + 4]);
     }
   }
+  auto fold = [&](float mo, float dno, const float* nmo) {
+    const float mn = fmaxf(m, mo);
+    const float a = m == -INFINITY ? 0.f : __expf(m - mn);
+    const float b = mo == -INFINITY ? 0.f : __expf(mo - mn);
+    den = a * den + b * dno;
 #pragma unroll
-  for (int k = LPR; k < 64; k <<= 1)
+    for (int e = 0; e < 8; ++e) num[e] = a * num[e] + b * nmo[e];
+    m = mn;
+  };
 #pragma unroll
-    for (int e = 0; e < 8; ++e) num[e] += __shfl_xor(num[e], k, 64);
+  for (int k = LPR; k < 64; k <<= 1) {
+    float nmo[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) nmo[e] = __shfl_xor(num[e], k, 64);
+    fold(__shfl_xor(m, k, 64), __shfl_xor(den, k, 64), nmo);
+  }
+  if constexpr (WPR > 1) {
+    if (q == 0) {
+      float* r = red[w][c8];
+      r[0] = m;
+      r[1] = den;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[2 + e] = num[e];
+    }
+    __syncthreads();
+    if (w != 0) return;
+    for (int o = 1; o < WPR; ++o) {
+      const float* r = red[o][c8];
+      fold(r[0], r[1], r + 2);
+    }
+  }
   if (q == 0) {
-    const float inv = 1.f / den;
-    st16(dst, num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv);
-    st16(dst + 4, num[4] * inv, num[5] * inv, num[6] * inv, num[7] * inv);
+    if (s1 == s0) {
+      st16(dst, 0.f, 0.f, 0.f, 0.f);
+      st16(dst + 4, 0.f, 0.f, 0.f, 0.f);
+    } else {
+      const float inv = 1.f / den;
+      st16(dst, num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv);
+      st16(dst + 4, num[4] * inv, num[5] * inv, num[6] * inv, num[7] * inv);
+    }
   }
 }
 
+template <int D>
+void launch_merge_d(const TG_GLOBAL float* acc, const TG_GLOBAL float* ml, const TG_GLOBAL int32_t* po,
+                    int32_t n_pairs, int32_t G, TG_GLOBAL float* o, int64_t n_slots, hipStream_t s) {
+  const int64_t rows = static_cast<int64_t>(n_pairs) * G;
+  // many slots per pair (long sequences split into many items): a block of
+  // four waves per row; otherwise one wave per row
+  if (n_slots >= 16 * static_cast<int64_t>(n_pairs))
+    hipLaunchKernelGGL((merge_kernel<D, 4>), dim3(static_cast<unsigned>(rows)), dim3(256), 0, s, acc, ml,
+                       po, n_pairs, G, o);
+  else
+    hipLaunchKernelGGL((merge_kernel<D, 1>), dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s,
+                       acc, ml, po, n_pairs, G, o);
+}
+
 hipError_t launch_merge(const float* ws_acc, const float* ws_ml, const int32_t* part_off,
-                        int32_t n_pairs, int32_t G, int32_t d, float* out, hipStream_t s) {
+                        int32_t n_pairs, int32_t G, int32_t d, float* out, int64_t n_slots, hipStream_t s) {
   const int64_t rows = static_cast<int64_t>(n_pairs) * G;
   if (rows == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((rows + 3) / 4));
   auto acc = (const TG_GLOBAL float*)(ws_acc);
   auto ml = (const TG_GLOBAL float*)(ws_ml);
   auto po = (const TG_GLOBAL int32_t*)(part_off);
   auto o = (TG_GLOBAL float*)(out);
   if (d == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(256), 0, s, acc, ml, po, n_pairs, G, o);
+    launch_merge_d<128>(acc, ml, po, n_pairs, G, o, n_slots, s);
   else
-    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(256), 0, s, acc, ml, po, n_pairs, G, o);
+    launch_merge_d<64>(acc, ml, po, n_pairs, G, o, n_slots, s);
   return hipGetLastError();
 }
 
@@ -121,7 +158,8 @@ extern "C" int tg_merge_partials(const float* workspace, int32_t n_slots, int32_
   if (n_slots < 0 || n_pairs < 0 || (n_pairs > 0 && (!part_off || !out)) || (n_slots > 0 && !workspace))
     return TG_EINVAL;
   const float* ws_ml = workspace + static_cast<int64_t>(n_slots) * G * d;
-  hipError_t e = launch_merge(workspace, ws_ml, part_off, n_pairs, G, d, out, static_cast<hipStream_t>(stream));
+  hipError_t e =
+      launch_merge(workspace, ws_ml, part_off, n_pairs, G, d, out, n_slots, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? TG_OK : TG_EDEVICE;
 }
 
@@ -174,21 +212,14 @@ int decode_split(const tg_cache* c, const tg_decode_args* a, void* stream, bool 
   const float scale = a->sm_scale != 0.f ? a->sm_scale : 1.f / std::sqrt(static_cast<float>(d));
   s.scale_log2 = scale * kLog2e;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // one launch per tier present in the cache (a tier whose tables are all
-  // empty has no items)
-  bool has_i8 = false, has_bf = false;
-  for (int32_t cl = 0; cl < c->n_clusters; ++cl) {
-    has_i8 |= c->stride[cl][TG_TIER_I8] > 0;
-    has_bf |= c->stride[cl][TG_TIER_BF16] > 0;
-  }
-  const bool qf32 = a->q_dtype == TG_Q_F32;
-  hipError_t e = hipSuccess;
-  if (has_i8) e = launch_split_i8(s, d, G, qf32, st);
-  if (e == hipSuccess && has_bf) e = launch_split_bf16(s, d, G, qf32, st);
+  // one launch over both tiers when the cache has INT8 pages
+  bool has_i8 = false;
+  for (int32_t cl = 0; cl < c->n_clusters; ++cl) has_i8 |= c->stride[cl][TG_TIER_I8] > 0;
+  hipError_t e = launch_split(s, d, G, a->q_dtype == TG_Q_F32, has_i8, st);
   if (e != hipSuccess) return TG_EDEVICE;
   if (!merge) return TG_OK;
   e = launch_merge(a->workspace, a->workspace + static_cast<int64_t>(a->n_slots) * G * d, a->part_off,
-                   c->B * c->n_kv_heads, G, d, a->out, st);
+                   c->B * c->n_kv_heads, G, d, a->out, a->n_slots, st);
   return e == hipSuccess ? TG_OK : TG_EDEVICE;
 }
 

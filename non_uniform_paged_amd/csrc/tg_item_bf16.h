@@ -1,4 +1,6 @@
-// Split kernel, bf16 tier (gfx950): one wavefront per plan item
+#ifndef TG_ITEM_BF16_H_
+#define TG_ITEM_BF16_H_
+// Split work item, bf16 tier (gfx950): one wavefront per plan item
 // (r, h, bf16, [t0, t1)) computes the online-normaliser partial of the G
 // q-heads of KV-head h over rows [t0, t1) of the bf16 tier.  A group item
 // does the same for up to 16 / G requests that share those pages (radix
@@ -23,12 +25,10 @@
 // in the lanes of column lg.
 
 #include <cmath>
-#include <cstdlib>
 
 #include "tg_device.h"
 
 namespace tg_dev {
-namespace {
 
 // One 16-row page.  TAIL masks rows at or past `valid`, both in the scores
 // and in the V operand.
@@ -214,13 +214,10 @@ __device__ __forceinline__ void bf16_item(const SplitArgs& a, int r, int h, int 
   }
 }
 
+// Runs plan item `w` (a bf16-tier item): reads its fields and tables and
+// calls bf16_item with the load flavour of its pages.
 template <int D, int G, bool QF32, int DEPTH>
-__global__ __launch_bounds__(64 * kWavesPerBlock) void split_bf16_kernel(SplitArgs a) {
-  const int item = uniform(static_cast<int>(blockIdx.x) * kWavesPerBlock + (static_cast<int>(threadIdx.x) >> 6));
-  if (item >= a.n_items) return;
-  const TG_GLOBAL int32_t* w = a.work + static_cast<int64_t>(item) * 6;
-  const int tier = uniform(w[2]);
-  if (tier != TG_TIER_BF16) return;  // the INT8 kernel takes this item
+__device__ __forceinline__ void bf16_dispatch(const SplitArgs& a, const TG_GLOBAL int32_t* w) {
   int r = uniform(w[0]);
   const int h = uniform(w[1]);
   const int t0 = uniform(w[3]), t1 = uniform(w[4]), slot = uniform(w[5]);
@@ -248,43 +245,6 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void split_bf16_kernel(SplitAr
     bf16_item<D, G, QF32, DEPTH, true>(a, r, h, t0, t1, slot, gm, hs, bt_row, pool, pbytes);
 }
 
-template <int D, int G, bool QF32>
-hipError_t launch(const SplitArgs& a, hipStream_t s) {
-  const int blocks = (a.n_items + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (blocks == 0) return hipSuccess;
-  static const int depth = [] {
-    const char* e = getenv("TG_SPLIT_DEPTH");  // tuning knob: 2 or 3 page buffers
-    return (e && atoi(e) == 3) ? 3 : 2;
-  }();
-  const dim3 grid(blocks), block(64 * kWavesPerBlock);
-  if (depth == 3)
-    hipLaunchKernelGGL((split_bf16_kernel<D, G, QF32, 3>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((split_bf16_kernel<D, G, QF32, 2>), grid, block, 0, s, a);
-  return hipGetLastError();
-}
-
-template <int D>
-hipError_t launch_d(const SplitArgs& a, int G, bool qf32, hipStream_t s) {
-  switch (G * 2 + (qf32 ? 1 : 0)) {
-    case 2: return launch<D, 1, false>(a, s);
-    case 3: return launch<D, 1, true>(a, s);
-    case 4: return launch<D, 2, false>(a, s);
-    case 5: return launch<D, 2, true>(a, s);
-    case 8: return launch<D, 4, false>(a, s);
-    case 9: return launch<D, 4, true>(a, s);
-    case 16: return launch<D, 8, false>(a, s);
-    case 17: return launch<D, 8, true>(a, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-}  // namespace
-
-hipError_t launch_split_bf16(const SplitArgs& a, int d, int G, bool qf32, hipStream_t s) {
-  if (d == 128) return launch_d<128>(a, G, qf32, s);
-  if (d == 64) return launch_d<64>(a, G, qf32, s);
-  return hipErrorInvalidValue;
-}
-
 }  // namespace tg_dev
+
+#endif  // TG_ITEM_BF16_H_

@@ -1,4 +1,6 @@
-// Split kernel, INT8 tier (gfx950): one wavefront per plan item
+#ifndef TG_ITEM_I8_H_
+#define TG_ITEM_I8_H_
+// Split work item, INT8 tier (gfx950): one wavefront per plan item
 // (r, h, INT8, [t0, t1)) computes the online-normaliser partial of the G
 // q-heads of KV-head h over rows [t0, t1) of the INT8 tier, dequantising in
 // registers (TTKV page, "Tier Layout" / "Tier Interaction": the slow tier is
@@ -32,7 +34,6 @@
 #include "tg_device.h"
 
 namespace tg_dev {
-namespace {
 
 constexpr uint32_t kF16x2_1152 = 0x64806480u;  // two fp16 1152.0
 
@@ -249,15 +250,14 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
   }
 }
 
+// Floats of LDS accumulator one wavefront needs for an INT8 item.
+template <int D>
+constexpr int kI8LdsFloats = (D / 16) * 4 * 64;
+
+// Runs plan item `w` (an INT8-tier item) with `lds` as the wave's
+// accumulator (kI8LdsFloats<D> floats).
 template <int D, int G, bool QF32, int DEPTH>
-__global__ __launch_bounds__(64 * kWavesPerBlock) void split_i8_kernel(SplitArgs a) {
-  __shared__ float lds[kWavesPerBlock][(D / 16) * 4 * 64];
-  const int wave = uniform(static_cast<int>(threadIdx.x) >> 6);
-  const int item = uniform(static_cast<int>(blockIdx.x) * kWavesPerBlock + wave);
-  if (item >= a.n_items) return;
-  const TG_GLOBAL int32_t* w = a.work + static_cast<int64_t>(item) * 6;
-  const int tier = uniform(w[2]);
-  if (tier != TG_TIER_I8) return;  // the bf16 kernel takes this item
+__device__ __forceinline__ void i8_dispatch(const SplitArgs& a, const TG_GLOBAL int32_t* w, float* lds) {
   const int r = uniform(w[0]), h = uniform(w[1]);
   const int t0 = uniform(w[3]), t1 = uniform(w[4]), slot = uniform(w[5]);
   const int cl = uniform(a.cluster_of_head[h]);
@@ -268,40 +268,11 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void split_i8_kernel(SplitArgs
   bool shared = false;  // an item that starts on the shared radix path reads through the caches
   if (a.n_fixed) shared = t0 + kQBlock <= uniform(a.n_fixed[r]);
   if (shared)
-    i8_item<D, G, QF32, DEPTH, false>(a, r, h, t0, t1, slot, hs, bt_row, pool, pbytes, lds[wave]);
+    i8_item<D, G, QF32, DEPTH, false>(a, r, h, t0, t1, slot, hs, bt_row, pool, pbytes, lds);
   else
-    i8_item<D, G, QF32, DEPTH, true>(a, r, h, t0, t1, slot, hs, bt_row, pool, pbytes, lds[wave]);
-}
-
-template <int D, int G, bool QF32>
-hipError_t launch(const SplitArgs& a, hipStream_t s) {
-  const int blocks = (a.n_items + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((split_i8_kernel<D, G, QF32, 2>), dim3(blocks), dim3(64 * kWavesPerBlock), 0, s, a);
-  return hipGetLastError();
-}
-
-template <int D>
-hipError_t launch_d(const SplitArgs& a, int G, bool qf32, hipStream_t s) {
-  switch (G * 2 + (qf32 ? 1 : 0)) {
-    case 2: return launch<D, 1, false>(a, s);
-    case 3: return launch<D, 1, true>(a, s);
-    case 4: return launch<D, 2, false>(a, s);
-    case 5: return launch<D, 2, true>(a, s);
-    case 8: return launch<D, 4, false>(a, s);
-    case 9: return launch<D, 4, true>(a, s);
-    case 16: return launch<D, 8, false>(a, s);
-    case 17: return launch<D, 8, true>(a, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-}  // namespace
-
-hipError_t launch_split_i8(const SplitArgs& a, int d, int G, bool qf32, hipStream_t s) {
-  if (d == 128) return launch_d<128>(a, G, qf32, s);
-  if (d == 64) return launch_d<64>(a, G, qf32, s);
-  return hipErrorInvalidValue;
+    i8_item<D, G, QF32, DEPTH, true>(a, r, h, t0, t1, slot, hs, bt_row, pool, pbytes, lds);
 }
 
 }  // namespace tg_dev
+
+#endif  // TG_ITEM_I8_H_
