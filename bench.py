@@ -31,6 +31,12 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "effective KV GB/s (and % of HBM peak) in ragged-paged decode attention"
+# Plan item lengths (bf16 rows, INT8 rows) per workload, chosen by sweeping
+# the split-kernel time on MI355X: the best length depends on how the item
+# count falls against the ~2048 resident wavefronts and on the length mix.
+PLAN_CHUNKS = {"tiny": (1024, 1024), "llama8b": (1024, 1024), "ragged": (4096, 1024),
+               "tiered": (1024, 1536), "radix": (768, 1024)}
+
 DESCRIPTIONS = {
     "tiny": "tiny: 2 requests, 4/2 heads, d 64, ctx 256, budgets in {32..256}, 2 clusters",
     "llama8b": "Llama-3-8B-shaped layer: batch 64, 32/8 heads, d 128, ctx U[4096,16384], ratio 0.50->0.10 by head rank, 2 clusters, page 16, bf16",
@@ -120,8 +126,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="llama8b", choices=sorted(DESCRIPTIONS))
-    ap.add_argument("--chunk-bf", type=int, default=1024)
-    ap.add_argument("--chunk-i8", type=int, default=1024)
+    ap.add_argument("--chunk-bf", type=int, default=None, help="bf16 rows per plan item (default per workload)")
+    ap.add_argument("--chunk-i8", type=int, default=None, help="INT8 rows per plan item (default per workload)")
     ap.add_argument("--flush", choices=["read", "write", "none"], default="read")
     ap.add_argument("--group-size", type=int, default=None,
                     help="requests per shared-prefix group item (default 16 / G when pages are shared)")
@@ -160,6 +166,10 @@ def main():
     torch.cuda.set_device(0)
     w = make_workload(args.config)
     t_prep = time.perf_counter()
+    if args.chunk_bf is None:
+        args.chunk_bf = PLAN_CHUNKS[args.config][0]
+    if args.chunk_i8 is None:
+        args.chunk_i8 = PLAN_CHUNKS[args.config][1]
     prep = Prepared(w, chunk_bf=args.chunk_bf, chunk_i8=args.chunk_i8, group_size=args.group_size)
     t_prep = time.perf_counter() - t_prep
     tr = prep.traffic()

@@ -62,7 +62,7 @@ extern "C" {
 #define TG_TIER_I8 0
 #define TG_TIER_BF16 1
 #define TG_MAX_CLUSTERS 16
-#define TG_GROUP_WIDTH 16  /* member entries per group item of the plan */
+#define TG_GROUP_WIDTH 32  /* member entries per group item of the plan */
 
 #define TG_Q_F32 0
 #define TG_Q_BF16 1
@@ -171,16 +171,18 @@ int32_t tg_pool_refcount(const tg_pool* pool, int32_t c, int32_t tier, int64_t p
  *           one takes a fresh page.  Other pages are always fresh.
  *   tables  bt[c][t] is [B][stride[c][t]] int32 page ids in logical order,
  *           padded with -1; stride = max_r pages; len [B*H*2] = (n_i8, n_bf).
- *   plan    items {r, h, tier, t0, t1, slot} for r, h, tier (INT8 first),
- *           t0 = 0, chunk, 2*chunk, ... (t0, t1 are row indices inside the
- *           tier); slot = index of the item's partial; part_off [B*H + 1] =
- *           first slot of each (r, h).  With lpt != 0 the items are stably
- *           sorted by descending (t1 - t0) * (2 bf16 | 1 INT8).
+ *   plan    items {r, h, tier, t0, t1, slot} for r, h, tier (INT8 first);
+ *           t0, t1 are row indices inside the tier.  A range of u units
+ *           (pages, or INT8 blocks; the last may be partial) becomes
+ *           k = ceil(u / (chunk / unit)) near-equal items, item i starting at
+ *           unit floor(i * u / k).  slot = index of the item's partial;
+ *           part_off [B*H + 1] = first slot of each (r, h).  With lpt != 0 the
+ *           items are stably sorted by descending (t1 - t0) * (2 bf16 | 1 INT8).
  *   groups  with group_size > 1 and `share`, the leading shared bf16 pages of
  *           each (r, h) are cut into runs of one radix node; requests whose
  *           run has the same (node, first row, pages, n_i8) are taken in
  *           ascending r, group_size at a time, and each group's rows are
- *           chunked by chunk_bf from the run's first row into a group item
+ *           split as above (chunk_bf) from the run's first row into group items
  *           {-1 - k, h, bf16, t0, t1, -1}: one pass over those pages for up
  *           to group_size requests.  gitems[k] lists its members as
  *           TG_GROUP_WIDTH (r, slot) pairs, padded with (-1, -1).  Group items
@@ -201,7 +203,7 @@ typedef struct tg_plan_opts {
   int32_t chunk_i8;  /* INT8 item length, a positive multiple of quant_block */
   int32_t lpt;       /* nonzero: longest items first */
   int32_t group_size; /* 0 or 1: no group items; at most TG_GROUP_WIDTH.  The
-                         decode kernels take group_size * G <= 16 */
+                         decode kernels take group_size * G <= 32 */
 } tg_plan_opts;
 
 typedef struct tg_table_sizes {
@@ -296,8 +298,8 @@ int tg_write_kv(const tg_cache* cache, const uint16_t* rows, const int32_t* inde
  * quant_block 64; TG_EINVAL on inconsistent arguments; TG_EDEVICE on a
  * failed launch.  A group item computes the partials of all its members in
  * one pass (G columns of the score tile per member); its members must fit
- * the tile: members * G <= 16, else the result is undefined (plan with
- * group_size <= 16 / G).
+ * two score tiles: members * G <= 32, else the result is undefined (plan
+ * with group_size <= 32 / G).
  * ---------------------------------------------------------------------- */
 size_t tg_decode_workspace_bytes(int32_t n_slots, int32_t G, int32_t d);
 

@@ -12,10 +12,10 @@ from typing import Optional, Sequence
 import numpy as np
 
 from . import _lib as L
-from ._lib import TG_Q_BF16, TG_Q_F32, TG_TIER_BF16, TG_TIER_I8, TGError, check, lib
+from ._lib import TG_GROUP_WIDTH, TG_Q_BF16, TG_Q_F32, TG_TIER_BF16, TG_TIER_I8, TGError, check, lib
 
 __all__ = [
-    "TGError", "TG_TIER_I8", "TG_TIER_BF16", "TG_Q_F32", "TG_Q_BF16",
+    "TGError", "TG_TIER_I8", "TG_TIER_BF16", "TG_Q_F32", "TG_Q_BF16", "TG_GROUP_WIDTH",
     "Reservation", "Share", "Pool", "Tables", "DeviceCache",
     "tg_reserve", "tg_size_tables", "tg_build_tables", "tg_release",
     "tg_write_kv", "tg_decode_workspace_bytes", "tg_decode_attn", "tg_decode_split",

@@ -46,11 +46,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const TG_GLOBAL float* __res
   TG_GLOBAL float* dst = out + rowid * D + 8 * c8;
   float m = -INFINITY, den = 0.f;
   float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s = s0 + w * NG + q; s < s1; s += WPR * NG) {
-    const int64_t base = static_cast<int64_t>(s) * G + g;
-    const float ms = ws_ml[base * 2 + 0], ls = ws_ml[base * 2 + 1];
-    const f32x4_t x0 = *(const TG_GLOBAL f32x4_t*)(ws_acc + base * D + 8 * c8);
-    const f32x4_t x1 = *(const TG_GLOBAL f32x4_t*)(ws_acc + base * D + 8 * c8 + 4);
+  auto add = [&](float ms, float ls, const f32x4_t& x0, const f32x4_t& x1) {
     if (ms > m) {
       const float sc = __expf(m - ms);
       den *= sc;
@@ -65,6 +61,21 @@ __global__ __launch_bounds__(256) void merge_kernel(const TG_GLOBAL float* __res
       num[e] = fmaf(wgt, x0[e], num[e]);
       num[e + 4] = fmaf(wgt, x1[e], num[e + 4]);
     }
+  };
+  constexpr int STEP = WPR * NG;
+  // two slots per iteration, both loaded before either is folded in
+  for (int s = s0 + w * NG + q; s < s1; s += 2 * STEP) {
+    const int64_t b0 = static_cast<int64_t>(s) * G + g;
+    const bool two = s + STEP < s1;
+    const int64_t b1 = two ? b0 + static_cast<int64_t>(STEP) * G : b0;
+    const float m0 = ws_ml[b0 * 2 + 0], l0 = ws_ml[b0 * 2 + 1];
+    const f32x4_t x00 = *(const TG_GLOBAL f32x4_t*)(ws_acc + b0 * D + 8 * c8);
+    const f32x4_t x01 = *(const TG_GLOBAL f32x4_t*)(ws_acc + b0 * D + 8 * c8 + 4);
+    const float m1 = ws_ml[b1 * 2 + 0], l1 = ws_ml[b1 * 2 + 1];
+    const f32x4_t x10 = *(const TG_GLOBAL f32x4_t*)(ws_acc + b1 * D + 8 * c8);
+    const f32x4_t x11 = *(const TG_GLOBAL f32x4_t*)(ws_acc + b1 * D + 8 * c8 + 4);
+    add(m0, l0, x00, x01);
+    if (two) add(m1, l1, x10, x11);
   }
   auto fold = [&](float mo, float dno, const float* nmo) {
     const float mn = fmaxf(m, mo);

@@ -377,6 +377,18 @@ int count_plan(const tg_reservation* res, const Geometry& g, const tg_plan_opts*
   return TG_OK;
 }
 
+// Rows [lo, hi) as near-equal items of whole units (pages or INT8 blocks),
+// at most `chunk` rows each: k = ceil(u / (chunk / unit)) items over u units,
+// item i starting at unit floor(i * u / k).
+template <typename F>
+void split_range(int64_t lo, int64_t hi, int64_t unit, int64_t chunk, F&& emit) {
+  const int64_t u = ceil_div(hi - lo, unit);
+  if (u <= 0) return;
+  const int64_t k = ceil_div(u, chunk / unit);
+  for (int64_t i = 0; i < k; ++i)
+    emit(lo + (i * u / k) * unit, std::min(lo + ((i + 1) * u / k) * unit, hi));
+}
+
 // The split plan: work items {r, h, tier, t0, t1, slot}, the slot CSR per
 // (r, h) and the member table of group items.
 struct Plan {
@@ -465,9 +477,9 @@ int make_plan(const tg_reservation* res, const Geometry& g, const Paths& paths, 
         const int64_t lo = grp.ja * g.ps, hi = (grp.ja + grp.id.npages) * g.ps;
         for (size_t k = 0; k < grp.members.size(); k += o->group_size) {
           const size_t e = std::min(grp.members.size(), k + size_t(o->group_size));
-          for (int64_t t0 = lo; t0 < hi; t0 += o->chunk_bf)
-            gi.push_back(GItem{h, t0, std::min<int64_t>(t0 + o->chunk_bf, hi),
-                               std::vector<int32_t>(grp.members.begin() + k, grp.members.begin() + e)});
+          split_range(lo, hi, g.ps, o->chunk_bf, [&](int64_t t0, int64_t t1) {
+            gi.push_back(GItem{h, t0, t1, std::vector<int32_t>(grp.members.begin() + k, grp.members.begin() + e)});
+          });
         }
       }
     }
@@ -500,10 +512,11 @@ int make_plan(const tg_reservation* res, const Geometry& g, const Paths& paths, 
         const int64_t len = t == TG_TIER_BF16 ? res->n_bf[i] : res->n_i8[i];
         const int64_t lo = t == TG_TIER_BF16 ? shared_rows[i] : 0;
         const int32_t ch = t == TG_TIER_BF16 ? o->chunk_bf : o->chunk_i8;
-        for (int64_t t0 = lo; t0 < len; t0 += ch) {
-          const int32_t w[6] = {r, h, t, int32_t(t0), int32_t(std::min<int64_t>(t0 + ch, len)), int32_t(slot++)};
+        const int32_t unit = t == TG_TIER_BF16 ? g.ps : g.qb;
+        split_range(lo, len, unit, ch, [&](int64_t t0, int64_t t1) {
+          const int32_t w[6] = {r, h, t, int32_t(t0), int32_t(t1), int32_t(slot++)};
           p->work.insert(p->work.end(), w, w + 6);
-        }
+        });
       }
     }
   if (slot > std::numeric_limits<int32_t>::max()) return TG_EOVERFLOW;

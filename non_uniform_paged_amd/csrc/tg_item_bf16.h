@@ -3,8 +3,9 @@
 // Split work item, bf16 tier (gfx950): one wavefront per plan item
 // (r, h, bf16, [t0, t1)) computes the online-normaliser partial of the G
 // q-heads of KV-head h over rows [t0, t1) of the bf16 tier.  A group item
-// does the same for up to 16 / G requests that share those pages (radix
-// prefix), one set of G score columns per member, in one pass over the pages.
+// does the same for up to 32 / G requests that share those pages (radix
+// prefix), one set of G score columns per member (two 16-column score tiles
+// past 16 / G members), in one pass over the pages.
 //
 // The maths is the online normaliser (CAP survey page, section 2.4.3
 // "Distributed acceleration", online normaliser [88]): per chunk keep
@@ -99,10 +100,11 @@ __device__ __forceinline__ void bf16_page(const u32x4_t (&kb)[NK], const u32x4_t
 // before a page's use cover exactly that page's loads.  Page ids of up to 64
 // pages sit one per lane and are read with readlane.
 //
-// Score column lg belongs to member lg / G (its q-head lg % G).  A plain item
-// has one member (r, slot); a group item's members come from `gm`, the
+// NTILE score tiles of 16 columns share every page load.  Column
+// c = lg + 16 * tile belongs to member c / G (its q-head c % G).  A plain
+// item has one member (r, slot); a group item's members come from `gm`, the
 // (request, slot) pairs of its member table row.
-template <int D, int G, bool QF32, int DEPTH, bool STREAM>
+template <int D, int G, bool QF32, int DEPTH, bool STREAM, int NTILE>
 __device__ __forceinline__ void bf16_item(const SplitArgs& a, int r, int h, int t0, int t1, int slot,
                                           const TG_GLOBAL int32_t* gm, int hs,
                                           const TG_GLOBAL int32_t* bt_row, gptr pool, int64_t pbytes) {
@@ -110,26 +112,30 @@ __device__ __forceinline__ void bf16_item(const SplitArgs& a, int r, int h, int 
   constexpr int NT = D / 16;           // 16-channel tiles of V
   constexpr int NQ = QF32 ? 2 : 1;     // bf16 pieces of q
   static_assert(G <= 16, "G must fit one MFMA tile");
+  static_assert(16 * NTILE <= 2 * TG_GROUP_WIDTH, "member table too narrow");
   const int lane = threadIdx.x & 63;
   const int lg = lane & 15;
   const int lj = lane >> 4;
 
-  // column lg: member request and partial slot (-1: unused column)
-  int col_r = r, col_slot = lg < G ? slot : -1;
-  if (gm != nullptr) {
-    const int mu = lg / G;  // < 16 = TG_GROUP_WIDTH
-    col_r = gm[2 * mu];
-    col_slot = gm[2 * mu + 1];
-    if (col_r < 0) {
-      col_r = r;
-      col_slot = -1;
+  // column lg + 16 tile: member request and partial slot (-1: unused column)
+  int col_r[NTILE], col_slot[NTILE];
+#pragma unroll
+  for (int tile = 0; tile < NTILE; ++tile) {
+    col_r[tile] = r;
+    col_slot[tile] = (tile == 0 && lg < G) ? slot : -1;
+    if (gm != nullptr) {
+      const int mu = (lg + 16 * tile) / G;  // < TG_GROUP_WIDTH
+      const int mr = gm[2 * mu], ms = gm[2 * mu + 1];
+      col_r[tile] = mr < 0 ? r : mr;
+      col_slot[tile] = mr < 0 ? -1 : ms;
     }
   }
   // Q^T operand of step s: lane (lg, lj) holds q[column lg][32 s + 8 lj + e]
-  u32x4_t qop[NQ][NK];
-  {
-    const bool has = col_slot >= 0;
-    const int64_t row = static_cast<int64_t>(col_r) * a.n_q_heads + h * G + lg % G;
+  u32x4_t qop[NTILE][NQ][NK];
+#pragma unroll
+  for (int tile = 0; tile < NTILE; ++tile) {
+    const bool has = col_slot[tile] >= 0;
+    const int64_t row = static_cast<int64_t>(col_r[tile]) * a.n_q_heads + h * G + lg % G;
 #pragma unroll
     for (int s = 0; s < NK; ++s) {
       if constexpr (QF32) {
@@ -143,24 +149,30 @@ __device__ __forceinline__ void bf16_item(const SplitArgs& a, int r, int h, int 
         for (int e = 0; e < 8; ++e) split_bf16(f[e], hi[e], lo[e]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          qop[0][s][e] = has ? (hi[2 * e] | (hi[2 * e + 1] << 16)) : 0u;
-          qop[1][s][e] = has ? (lo[2 * e] | (lo[2 * e + 1] << 16)) : 0u;
+          qop[tile][0][s][e] = has ? (hi[2 * e] | (hi[2 * e + 1] << 16)) : 0u;
+          qop[tile][1][s][e] = has ? (lo[2 * e] | (lo[2 * e + 1] << 16)) : 0u;
         }
       } else {
         const u32x4_t x = ldv16(a.q + (row * D + 32 * s + 8 * lj) * 2);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) qop[0][s][e] = has ? x[e] : 0u;
+        for (int e = 0; e < 4; ++e) qop[tile][0][s][e] = has ? x[e] : 0u;
       }
     }
   }
 
   const int64_t head_off = static_cast<int64_t>(hs) * (4 * kPage * D);
   const int lane_off = lane * 16;
-  f32x4_t acc[NT];
+  f32x4_t acc[NTILE][NT];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY;  // reference max of head lg (base-2 scaled score)
-  float l_run = 0.f;        // sum of weights of head lg over this lane's rows
+  for (int tile = 0; tile < NTILE; ++tile)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[tile][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_ref[NTILE], l_run[NTILE];  // per column: reference max (base-2 scaled score), weight sum
+#pragma unroll
+  for (int tile = 0; tile < NTILE; ++tile) {
+    m_ref[tile] = -INFINITY;
+    l_run[tile] = 0.f;
+  }
   const int p0 = t0 / kPage;
   const int np = (t1 - t0 + kPage - 1) / kPage;
   u32x4_t kb[DEPTH][NK], vb[DEPTH][NK];
@@ -187,10 +199,15 @@ __device__ __forceinline__ void bf16_item(const SplitArgs& a, int r, int h, int 
         __builtin_amdgcn_sched_barrier(0);
         if (i < nw) {
           const int valid = t1 - (t0 + (w0 + i) * kPage);  // rows of this page in the item
-          if (valid >= kPage)
-            bf16_page<NK, NT, NQ, false>(kb[u], vb[u], qop, acc, m_ref, l_run, a.scale_log2, kPage, lj);
-          else
-            bf16_page<NK, NT, NQ, true>(kb[u], vb[u], qop, acc, m_ref, l_run, a.scale_log2, valid, lj);
+#pragma unroll
+          for (int tile = 0; tile < NTILE; ++tile) {
+            if (valid >= kPage)
+              bf16_page<NK, NT, NQ, false>(kb[u], vb[u], qop[tile], acc[tile], m_ref[tile], l_run[tile],
+                                           a.scale_log2, kPage, lj);
+            else
+              bf16_page<NK, NT, NQ, true>(kb[u], vb[u], qop[tile], acc[tile], m_ref[tile], l_run[tile],
+                                          a.scale_log2, valid, lj);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -198,19 +215,22 @@ __device__ __forceinline__ void bf16_item(const SplitArgs& a, int r, int h, int 
   }
 
   // partials: m and l of column lg, accumulator rows (columns) 4lj+rr
-  const float l_tot = xor32_sum(xor16_sum(l_run));
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const int cslot = __shfl(col_slot, 4 * lj + rr, 64);  // lane 4lj+rr owns that column
-    if (cslot >= 0) {
-      TG_GLOBAL float* acc_out = a.ws_acc + (static_cast<int64_t>(cslot) * G + (4 * lj + rr) % G) * D;
+  for (int tile = 0; tile < NTILE; ++tile) {
+    const float l_tot = xor32_sum(xor16_sum(l_run[tile]));
 #pragma unroll
-      for (int n = 0; n < NT; ++n) acc_out[16 * n + lg] = acc[n][rr];
+    for (int rr = 0; rr < 4; ++rr) {
+      const int cslot = __shfl(col_slot[tile], 4 * lj + rr, 64);  // lane 4lj+rr owns that column
+      if (cslot >= 0) {
+        TG_GLOBAL float* acc_out = a.ws_acc + (static_cast<int64_t>(cslot) * G + (4 * lj + rr) % G) * D;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc_out[16 * n + lg] = acc[tile][n][rr];
+      }
     }
-  }
-  if (lj == 0 && col_slot >= 0) {
-    a.ws_ml[(static_cast<int64_t>(col_slot) * G + lg % G) * 2 + 0] = m_ref * kLn2;
-    a.ws_ml[(static_cast<int64_t>(col_slot) * G + lg % G) * 2 + 1] = l_tot;
+    if (lj == 0 && col_slot[tile] >= 0) {
+      a.ws_ml[(static_cast<int64_t>(col_slot[tile]) * G + lg % G) * 2 + 0] = m_ref[tile] * kLn2;
+      a.ws_ml[(static_cast<int64_t>(col_slot[tile]) * G + lg % G) * 2 + 1] = l_tot;
+    }
   }
 }
 
@@ -239,10 +259,14 @@ __device__ __forceinline__ void bf16_dispatch(const SplitArgs& a, const TG_GLOBA
     const int n_i8 = uniform(a.len[2 * (r * a.n_kv_heads + h)]);
     shared = n_i8 + t0 + kPage <= uniform(a.n_fixed[r]);
   }
-  if (shared)
-    bf16_item<D, G, QF32, DEPTH, false>(a, r, h, t0, t1, slot, gm, hs, bt_row, pool, pbytes);
+  // a group with members past the first 16 columns takes a second score tile
+  const bool two = gm != nullptr && uniform(gm[2 * (16 / G)]) >= 0;
+  if (two)
+    bf16_item<D, G, QF32, DEPTH, false, 2>(a, r, h, t0, t1, slot, gm, hs, bt_row, pool, pbytes);
+  else if (shared)
+    bf16_item<D, G, QF32, DEPTH, false, 1>(a, r, h, t0, t1, slot, gm, hs, bt_row, pool, pbytes);
   else
-    bf16_item<D, G, QF32, DEPTH, true>(a, r, h, t0, t1, slot, gm, hs, bt_row, pool, pbytes);
+    bf16_item<D, G, QF32, DEPTH, true, 1>(a, r, h, t0, t1, slot, gm, hs, bt_row, pool, pbytes);
 }
 
 }  // namespace tg_dev

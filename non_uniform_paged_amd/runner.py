@@ -36,7 +36,7 @@ class Prepared:
                  slack_pages: int = 0, shift_pages: int = 0, device: str = "cuda",
                  group_size: Optional[int] = None):
         """``group_size`` None: group shared-prefix pages for as many requests
-        as fill the 16 score columns (16 / G) when the batch shares a radix
+        as fill two 16-column score tiles (32 / G) when the batch shares a radix
         prefix, else no groups."""
         import torch
 
@@ -46,7 +46,7 @@ class Prepared:
         self.share = share_of(w)
         G = w.Hq // w.Hkv
         if group_size is None:
-            group_size = 16 // G if self.share is not None else 0
+            group_size = min(32 // G, api.TG_GROUP_WIDTH) if self.share is not None else 0
         self.group_size = group_size
         sizes = api.tg_size_tables(self.res, w.page_size, w.quant_block, self.share, chunk_bf, chunk_i8, lpt,
                                    group_size)

@@ -41,10 +41,13 @@ R-alloc  each (cluster, tier) pool hands out the lowest free page id.  Order:
          s + S_t - 1, s).  A key seen before adds a reference, otherwise a
          fresh page is taken and the key registered.  A failed call leaves the
          pool exactly as it was.
-R-plan   items (r, h, tier, t0, t1, slot) in order r, h, tier (INT8 first),
-         t0 = 0, chunk, 2*chunk, ...; slot is the natural index; part_off is the
-         CSR of slots per (r, h).  With lpt, items are stably sorted by
-         descending cost (t1 - t0) * (2 for bf16, 1 for INT8).
+R-plan   items (r, h, tier, t0, t1, slot) in order r, h, tier (INT8 first).
+         A row range of u units (pages, or INT8 blocks; the last may be
+         partial) is cut into k = ceil(u / (chunk / unit)) items as equal as
+         whole units allow: item i starts at unit floor(i * u / k).  slot is
+         the natural index; part_off is the CSR of slots per (r, h).  With lpt,
+         items are stably sorted by descending cost (t1 - t0) * (2 for bf16,
+         1 for INT8).
 R-group  (only with a group size > 1 and radix paths) the leading shared bf16
          pages of each (r, h) are cut into runs with the same radix node;
          requests whose run has the same (node, first row, page count, INT8
@@ -336,7 +339,7 @@ def release(pool: Pool, pages_of_request: List[List[List[int]]]):
 
 
 # ---------------------------------------------------------------- tables & plan
-GROUP_WIDTH = 16  # member slots per group item in the member table
+GROUP_WIDTH = 32  # member slots per group item in the member table
 
 
 def shared_segments(res: Reservation, r: int, c: int, page_size: int, quant_block: int,
@@ -362,6 +365,16 @@ def shared_segments(res: Reservation, r: int, c: int, page_size: int, quant_bloc
 def page_counts_row(res: Reservation, r: int, c: int, page_size: int) -> int:
     hs = heads_of_cluster(res, c)
     return _ceil_div(max(res.n_bf[r][h] for h in hs), page_size)
+
+
+def split_range(lo: int, hi: int, unit: int, chunk: int):
+    """Rows [lo, hi) as near-equal items of whole units, at most chunk rows
+    each (R-plan)."""
+    u = _ceil_div(hi - lo, unit)
+    if u <= 0:
+        return []
+    k = _ceil_div(u, chunk // unit)
+    return [(lo + (i * u // k) * unit, min(lo + ((i + 1) * u // k) * unit, hi)) for i in range(k)]
 
 
 def plan(res: Reservation, chunk_bf: int, chunk_i8: int, lpt: bool, group_size: int = 0,
@@ -398,9 +411,9 @@ def plan(res: Reservation, chunk_bf: int, chunk_i8: int, lpt: bool, group_size: 
                 lo, hi = ja * page_size, (ja + ident[2]) * page_size
                 for k in range(0, len(mem), group_size):
                     grp = mem[k:k + group_size]
-                    for t0 in range(lo, hi, chunk_bf):
+                    for t0, t1 in split_range(lo, hi, page_size, chunk_bf):
                         gitems_members.append(grp)
-                        gitem_rows.append((h, t0, min(t0 + chunk_bf, hi)))
+                        gitem_rows.append((h, t0, t1))
     # slots in natural (r, h) order: group memberships first, then own items
     member_of = {}
     for gi, grp in enumerate(gitems_members):
@@ -417,10 +430,10 @@ def plan(res: Reservation, chunk_bf: int, chunk_i8: int, lpt: bool, group_size: 
             for gi in member_of.get((r, h), []):
                 gslot[gi][gitems_members[gi].index(r)] = slot
                 slot += 1
-            for t, lo, n, ch in ((TIER_I8, 0, res.n_i8[r][h], chunk_i8),
-                                 (TIER_BF, shared_rows[r][h], res.n_bf[r][h], chunk_bf)):
-                for t0 in range(lo, n, ch):
-                    own.append((r, h, t, t0, min(t0 + ch, n), slot))
+            for t, lo, n, unit, ch in ((TIER_I8, 0, res.n_i8[r][h], quant_block, chunk_i8),
+                                       (TIER_BF, shared_rows[r][h], res.n_bf[r][h], page_size, chunk_bf)):
+                for t0, t1 in split_range(lo, n, unit, ch):
+                    own.append((r, h, t, t0, t1, slot))
                     slot += 1
     part_off.append(slot)
     work = [(-1 - gi, h, TIER_BF, t0, t1, -1) for gi, (h, t0, t1) in enumerate(gitem_rows)] + own

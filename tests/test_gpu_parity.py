@@ -298,12 +298,16 @@ def test_all_int8_and_empty_bf16_tier():
 @pytest.mark.parametrize("gs,G,recent,qd", [(0, 4, 10**6, "bf16"), (1, 4, 10**6, "bf16"), (2, 4, 10**6, "bf16"),
                                             (4, 4, 10**6, "f32"), (3, 4, 250_000, "bf16"),
                                             (16, 1, 10**6, "bf16"), (8, 2, 250_000, "f32"),
-                                            (2, 8, 10**6, "bf16")])
+                                            (2, 8, 10**6, "bf16"), (8, 4, 10**6, "bf16"),
+                                            (5, 4, 250_000, "f32"), (32, 1, 10**6, "f32"),
+                                            (16, 2, 10**6, "bf16"), (3, 8, 250_000, "bf16"),
+                                            (4, 8, 10**6, "f32")])
 def test_group_items(gs, G, recent, qd):
-    """Shared-prefix group items (one pass over a shared page for up to 16 / G
-    requests) against the oracle, for several group sizes and head shapes."""
+    """Shared-prefix group items (one pass over a shared page for up to 32 / G
+    requests, in one or two 16-column score tiles) against the oracle, for
+    several group sizes and head shapes."""
     _need_gpu()
-    w = make_workload("radix", B=11, Hq=2 * G, Hkv=2, recent_ppm=recent, q_dtype=qd,
+    w = make_workload("radix", B=40, Hq=2 * G, Hkv=2, recent_ppm=recent, q_dtype=qd,
                       share=dict(prefix=200, branch=50, n_branches=3, suffix=(8, 300)))
     p, _ = _run_and_compare(w, what=f"group{gs}-G{G}-{recent}-{qd}", chunk_bf=48, group_size=gs)
     assert (p.tables.n_gitems > 0) == (gs > 1)

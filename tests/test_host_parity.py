@@ -56,7 +56,7 @@ def _share(w):
 
 
 def _gitems_of(t_o):
-    return np.array(t_o.gitems, dtype=np.int32).reshape(-1, 16, 2)
+    return np.array(t_o.gitems, dtype=np.int32).reshape(-1, 32, 2)
 
 
 def _tables_parity(w, chunk_bf=512, chunk_i8=1024, lpt=True, slack=3, group_size=0):
@@ -88,7 +88,7 @@ def _tables_parity(w, chunk_bf=512, chunk_i8=1024, lpt=True, slack=3, group_size
 
 
 @pytest.mark.parametrize("name,gs", [("tiny", 0), ("llama8b", 0), ("ragged", 0), ("tiered", 0), ("radix", 0),
-                                     ("radix", 2), ("radix", 16)])
+                                     ("radix", 2), ("radix", 8), ("radix", 32)])
 def test_full_size_configs_bit_exact(name, gs):
     w = make_workload(name)
     res_o, res_g, pool_o, pool_g, t_o, t_g = _tables_parity(w, group_size=gs)
@@ -154,7 +154,7 @@ def test_randomised_small_cases_bit_exact():
         chunk_bf = ps * rnd.randint(1, 6)
         chunk_i8 = qb * rnd.randint(1, 3)
         lpt = rnd.random() < 0.5
-        gs = rnd.choice([0, 1, 2, 3, 16])
+        gs = rnd.choice([0, 1, 2, 3, 16, 32])
         grp = {"group_size": gs} if use_share else {}
         need_bf, need_i8 = P.pages_needed(res_o, ps, qb, *sh_o)
         cap_bf = [n + rnd.randint(-1, 2) for n in need_bf]
@@ -204,5 +204,5 @@ def test_error_codes():
         tg.tg_size_tables(res, 16, 64, tg.Share([1, 1], [0, 0], [5]))
     assert e.value.name == "TG_EINVAL"
     with pytest.raises(tg.TGError) as e:
-        tg.tg_size_tables(res, 16, 64, None, group_size=17)
+        tg.tg_size_tables(res, 16, 64, None, group_size=33)
     assert e.value.name == "TG_EINVAL"

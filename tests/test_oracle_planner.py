@@ -338,7 +338,7 @@ def _group_check(w, res, t, gs):
                 assert pos == n
 
 
-@pytest.mark.parametrize("gs", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("gs", [1, 2, 3, 8, 16, 32])
 @pytest.mark.parametrize("recent_ppm", [1_000_000, 250_000])
 def test_group_invariants(gs, recent_ppm):
     w = make_workload("radix", B=14, recent_ppm=recent_ppm,
