@@ -160,7 +160,7 @@ def main():
         return
 
     from non_uniform_paged_amd import api
-    from non_uniform_paged_amd.runner import Prepared
+    from non_uniform_paged_amd.runner import Prepared, allocated_bytes
     from workloads import make_workload
 
     torch.cuda.set_device(0)
@@ -233,6 +233,26 @@ def main():
         + prep.tables.n_slots * G * (w.d + 2) * 4
     split_ms = float(split_ms_all.mean())
     achieved = split_bytes / (split_ms * 1e-3) / 1e9
+
+    # achievable streaming-read rate of this device (2 GiB, non-temporal
+    # loads), the practical ceiling besides the 8 TB/s peak
+    rbuf = torch.ones(1 << 31, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(api.TG_BENCH_READ_BLOCKS, dtype=torch.int32, device="cuda")
+    api.tg_bench_read(rbuf, sink, stream=stream)
+    rev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    rev[0].record(stream)
+    for k in range(5):
+        api.tg_bench_read(rbuf, sink, stream=stream)
+        rev[k + 1].record(stream)
+    torch.cuda.synchronize()
+    read_ms = float(np.median([rev[k].elapsed_time(rev[k + 1]) for k in range(5)]))
+    read_gbps = rbuf.numel() / (read_ms * 1e-3) / 1e9
+    del rbuf
+
+    # pool bytes the batch needs at the configured cluster count, one cluster
+    # and one cluster per KV-head, against the bytes it retains
+    alloc = {str(C): allocated_bytes(w, C, args.chunk_bf, args.chunk_i8)
+             for C in sorted({w.n_clusters, 1, w.Hkv})}
     traffic = _traffic_record(args.config)
     value = tr["effective"] / (ms * 1e-3) / 1e9
     result = {
@@ -266,6 +286,10 @@ def main():
         "cache_eviction_between_steps": args.flush,
         "wall_s_timed_region": round(wall, 4),
         "prepare_s": round(t_prep, 2),
+        "read_ceiling_GBps": round(read_gbps, 1),
+        "split_frac_of_read_ceiling": round(achieved / read_gbps, 4),
+        "fragmentation": {"retained_bytes": tr["kv_roofline"], "allocated_bytes_by_clusters": alloc,
+                          "ratio_by_clusters": {k: round(v / tr["kv_roofline"], 4) for k, v in alloc.items()}},
         "roofline": {
             "kernel": "split_bf16_kernel" if not prep.tables.stride_has_i8 else
                       "split_i8_kernel + split_bf16_kernel",

@@ -334,6 +334,18 @@ int tg_decode_split(const tg_cache* cache, const tg_decode_args* args, void* str
 int tg_merge_partials(const float* workspace, int32_t n_slots, int32_t n_pairs, int32_t G,
                       int32_t d, const int32_t* part_off, float* out, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Measurement aid  (device)
+ *
+ * Streaming read of `bytes` (a multiple of 16) at `src` (16-byte aligned
+ * device memory) with non-temporal loads over TG_BENCH_READ_BLOCKS
+ * workgroups; each writes one fold of what it read to sink[block] (device
+ * uint32 [TG_BENCH_READ_BLOCKS]) so that no load is elided.  Timing it gives
+ * the device's achievable read rate.  TG_EINVAL on a bad size or pointer.
+ * ---------------------------------------------------------------------- */
+#define TG_BENCH_READ_BLOCKS 2048
+int tg_bench_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

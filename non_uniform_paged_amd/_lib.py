@@ -23,6 +23,7 @@ STATUS_NAMES = {0: "TG_OK", -1: "TG_EINVAL", -2: "TG_ENOMEM", -3: "TG_EOVERFLOW"
 TG_TIER_I8 = 0
 TG_TIER_BF16 = 1
 TG_GROUP_WIDTH = 32
+TG_BENCH_READ_BLOCKS = 2048
 TG_MAX_CLUSTERS = 16
 TG_Q_F32 = 0
 TG_Q_BF16 = 1
@@ -103,6 +104,7 @@ SIGNATURES = {
     "tg_decode_split": (ctypes.c_int, [POINTER(Cache), POINTER(DecodeArgs), c_void_p]),
     "tg_merge_partials": (ctypes.c_int, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                          c_void_p, c_void_p]),
+    "tg_bench_read": (ctypes.c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
 }
 
 _LIB = None

@@ -12,14 +12,14 @@ from typing import Optional, Sequence
 import numpy as np
 
 from . import _lib as L
-from ._lib import TG_GROUP_WIDTH, TG_Q_BF16, TG_Q_F32, TG_TIER_BF16, TG_TIER_I8, TGError, check, lib
+from ._lib import TG_BENCH_READ_BLOCKS, TG_GROUP_WIDTH, TG_Q_BF16, TG_Q_F32, TG_TIER_BF16, TG_TIER_I8, TGError, check, lib
 
 __all__ = [
     "TGError", "TG_TIER_I8", "TG_TIER_BF16", "TG_Q_F32", "TG_Q_BF16", "TG_GROUP_WIDTH",
     "Reservation", "Share", "Pool", "Tables", "DeviceCache",
     "tg_reserve", "tg_size_tables", "tg_build_tables", "tg_release",
     "tg_write_kv", "tg_decode_workspace_bytes", "tg_decode_attn", "tg_decode_split",
-    "tg_merge_partials",
+    "tg_merge_partials", "tg_bench_read", "TG_BENCH_READ_BLOCKS",
 ]
 
 
@@ -325,3 +325,13 @@ def tg_merge_partials(workspace, n_slots: int, n_pairs: int, G: int, d: int, par
                       stream=None) -> None:
     check(lib().tg_merge_partials(_ptr(workspace), int(n_slots), int(n_pairs), int(G), int(d),
                                   _ptr(part_off), _ptr(out), _stream_ptr(stream)), "tg_merge_partials")
+
+
+def tg_bench_read(src, sink, stream=None) -> None:
+    """Streaming read of the whole of ``src`` (a device tensor, size a
+    multiple of 16 bytes); ``sink`` is a device int32 tensor of at least
+    TG_BENCH_READ_BLOCKS elements."""
+    if sink.numel() * sink.element_size() < 4 * TG_BENCH_READ_BLOCKS:
+        raise ValueError("sink too small")
+    check(lib().tg_bench_read(_ptr(src), int(src.numel() * src.element_size()), _ptr(sink),
+                              _stream_ptr(stream)), "tg_bench_read")

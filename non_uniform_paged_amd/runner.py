@@ -134,3 +134,13 @@ class Prepared:
                 "effective": kv_eff + q_o + tables, "roofline": kv_roof + q_o + tables,
                 "head_rows": rows_total, "flops": 4 * d * G * rows_total,
                 "n_items": t.n_items, "n_gitems": t.n_gitems, "n_slots": t.n_slots}
+
+
+def allocated_bytes(w, n_clusters: int, chunk_bf: int = 1024, chunk_i8: int = 1024) -> int:
+    """Device bytes of the page pools a batch needs from empty pools when its
+    KV-heads are cut into ``n_clusters`` clusters (host computation only)."""
+    res = api.tg_reserve(w.head_rank, w.ratio_hi_ppm, w.ratio_lo_ppm, n_clusters, w.recent_ppm,
+                         w.quant_block, w.n_comp, w.n_fixed, w.budget_override)
+    need = api.tg_size_tables(res, w.page_size, w.quant_block, share_of(w), chunk_bf, chunk_i8)["pages_needed"]
+    pool = api.Pool(res.cluster_size, w.d, w.page_size, w.quant_block, [0] * res.C, [0] * res.C)
+    return sum(need[c][t] * pool.page_bytes(c, t) for c in range(res.C) for t in range(2))
