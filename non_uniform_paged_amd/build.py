@@ -42,13 +42,36 @@ def _run(cmd, verbose):
     subprocess.run(cmd, check=True)
 
 
+def _run_checking_scratch(cmd, verbose):
+    """Compile with resource-usage remarks and refuse kernels that spill to
+    scratch memory: every kernel here is meant to live in registers and LDS
+    (a spill, or a by-value kernel-argument struct copied to scratch, costs
+    a large share of the streaming rate)."""
+    if verbose:
+        print(" ".join(shlex.quote(c) for c in cmd), flush=True)
+    r = subprocess.run([*cmd, "-Rpass-analysis=kernel-resource-usage"], capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stderr)
+        raise subprocess.CalledProcessError(r.returncode, cmd)
+    name, bad = None, []
+    for line in r.stderr.splitlines():
+        if "Function Name:" in line:
+            name = line.split("Function Name:")[1].strip()
+        elif "ScratchSize [bytes/lane]:" in line:
+            size = int(line.split("ScratchSize [bytes/lane]:")[1].split()[0])
+            if size > 0:
+                bad.append(f"{name}: {size} bytes/lane")
+    if bad:
+        raise RuntimeError("kernels use scratch memory:\n  " + "\n  ".join(bad))
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link ``libtg.so``; returns its path."""
     os.makedirs(BUILD, exist_ok=True)
     objs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        _run([HIPCC, *HIP_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        _run_checking_scratch([HIPCC, *HIP_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
