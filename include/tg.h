@@ -105,6 +105,7 @@ typedef struct tg_reservation {
   int32_t* cluster_of_head;  /* host [H] */
   int32_t* slot_in_cluster;  /* host [H] */
   int32_t* cluster_size;     /* host [C] */
+  int32_t recent_ppm, quant_block; /* written by tg_reserve: the tier rule */
 } tg_reservation;
 
 /* Fill `out` (all arrays caller-allocated, sizes as listed).  n_comp [B]
@@ -190,6 +191,18 @@ int32_t tg_pool_refcount(const tg_pool* pool, int32_t c, int32_t tier, int64_t p
  *           chunks); a request's own bf16 items start after its shared rows.
  *           Slots of each (r, h): its group memberships in group-item order,
  *           then its own items in the order above.
+ *   growth  with gen_tokens = T > 0 (TTKV page, "Tier Content" / "Tier
+ *           Interaction": recent rows stay bf16, older ones are quantised in
+ *           blocks), each (r, h) may gain T rows by tg_append_kv.  An
+ *           appended row becomes the newest bf16 row and the tier split above
+ *           is applied to the new length; when the INT8 boundary moves (one
+ *           block) the oldest Qb bf16 rows become the next INT8 block.  Pages
+ *           are reserved now for the largest sizes on the way (INT8 rows of
+ *           L + T, the most bf16 rows at any length from L to L + T), and the
+ *           plan covers those capacities; the decode kernels clip every item
+ *           to the live lengths.  The bf16 tier turns over its ring[r][c]
+ *           pages (logical bf16 row j of (r, h) lives at ring row
+ *           (bf_base[r][h] + j) mod (16 ring[r][c])).
  * ---------------------------------------------------------------------- */
 typedef struct tg_share_desc {
   const int32_t* n_nodes;   /* host [B] radix-path length of each request */
@@ -204,6 +217,8 @@ typedef struct tg_plan_opts {
   int32_t lpt;       /* nonzero: longest items first */
   int32_t group_size; /* 0 or 1: no group items; at most TG_GROUP_WIDTH.  The
                          decode kernels take group_size * G <= 32 */
+  int32_t gen_tokens; /* >= 0: rows each (r, h) may still gain by tg_append_kv
+                         (see growth below); 0 with `share` only */
 } tg_plan_opts;
 
 typedef struct tg_table_sizes {
@@ -230,6 +245,7 @@ typedef struct tg_tables {
   int32_t* released;                   /* host [B] zeroed here; set by tg_release */
   int32_t* gitems;                     /* host [n_gitems][TG_GROUP_WIDTH][2] (may be NULL if 0) */
   int32_t n_gitems;                    /* in: must equal tg_size_tables' value */
+  int32_t* ring;                       /* host [B][C]: bf16 pages of (r, c) (nullable) */
 } tg_tables;
 
 /* Allocate every page of the batch from `pool` (all or nothing) and fill the
@@ -253,11 +269,17 @@ typedef struct tg_cache {
   int32_t stride[TG_MAX_CLUSTERS][2];
   const int32_t* cluster_of_head;            /* device [H] */
   const int32_t* slot_in_cluster;            /* device [H] */
-  const int32_t* len;                        /* device [B*H*2] (n_i8, n_bf) */
+  int32_t* len;                              /* device [B*H*2] live (n_i8, n_bf); updated by
+                                                tg_append_kv */
   const int32_t* n_fixed;                    /* device [B] shared-path rows of each request, or
                                                 NULL when nothing is shared; rows on the
                                                 shared path are read through the caches, all
                                                 other rows with streaming (non-temporal) loads */
+  const int32_t* ring;                       /* device [B*C] bf16 ring pages (tg_tables.ring),
+                                                or NULL: no ring (bf_base unused) */
+  int32_t* bf_base;                          /* device [B*H] ring row of logical bf16 row 0
+                                                (zero at admission; updated by tg_append_kv) */
+  int32_t recent_ppm;                        /* tier rule of the reservation (tg_append_kv) */
 } tg_cache;
 
 /* ------------------------------------------------------------------------
@@ -275,6 +297,24 @@ typedef struct tg_cache {
  * ---------------------------------------------------------------------- */
 int tg_write_kv(const tg_cache* cache, const uint16_t* rows, const int32_t* index,
                 const int64_t* offsets, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode-step append and tier ageing  (device)
+ *
+ * For every (r, h): the new row rows[r*H + h] ([2][d] bf16 bits: K then V;
+ * device uint16 [B*H][2][d]) is written in place as the newest bf16 row, in
+ * the page reserved for it (ring row (bf_base + n_bf) mod 16 ring[r][c]).
+ * Then the tier split is applied to the new length (TTKV page, "Tier
+ * Content": the newest share stays bf16; "Tier Interaction": older rows are
+ * quantised block by block): when it moves the INT8 boundary, the oldest Qb
+ * bf16 rows are quantised as in tg_write_kv into INT8 block n_i8 / Qb, and
+ * the ring advances by Qb rows.  cache->len and cache->bf_base are updated
+ * on the device.  The cache must come from tables built with gen_tokens > 0
+ * (cache->ring, cache->bf_base set).  A (r, h) whose step would pass the
+ * capacity reserved at admission is left unchanged and sets bit 0 of
+ * *status (device int32, nullable).  TG_EINVAL on a malformed cache.
+ * ---------------------------------------------------------------------- */
+int tg_append_kv(const tg_cache* cache, const uint16_t* rows, int32_t* status, void* stream);
 
 /* ------------------------------------------------------------------------
  * Decode attention  (device)

@@ -41,7 +41,8 @@ class BudgetTable(ctypes.Structure):
 class Reservation(ctypes.Structure):
     _fields_ = [("B", c_int32), ("n_kv_heads", c_int32), ("n_clusters", c_int32),
                 ("budget", P32), ("length", P32), ("n_i8", P32), ("n_bf", P32),
-                ("cluster_of_head", P32), ("slot_in_cluster", P32), ("cluster_size", P32)]
+                ("cluster_of_head", P32), ("slot_in_cluster", P32), ("cluster_size", P32),
+                ("recent_ppm", c_int32), ("quant_block", c_int32)]
 
 
 class ShareDesc(ctypes.Structure):
@@ -49,7 +50,8 @@ class ShareDesc(ctypes.Structure):
 
 
 class PlanOpts(ctypes.Structure):
-    _fields_ = [("chunk_bf", c_int32), ("chunk_i8", c_int32), ("lpt", c_int32), ("group_size", c_int32)]
+    _fields_ = [("chunk_bf", c_int32), ("chunk_i8", c_int32), ("lpt", c_int32), ("group_size", c_int32),
+                ("gen_tokens", c_int32)]
 
 
 class TableSizes(ctypes.Structure):
@@ -61,7 +63,7 @@ class TableSizes(ctypes.Structure):
 class Tables(ctypes.Structure):
     _fields_ = [("bt", (P32 * 2) * TG_MAX_CLUSTERS), ("stride", (c_int32 * 2) * TG_MAX_CLUSTERS),
                 ("len", P32), ("work", P32), ("n_items", c_int32), ("part_off", P32),
-                ("released", P32), ("gitems", P32), ("n_gitems", c_int32)]
+                ("released", P32), ("gitems", P32), ("n_gitems", c_int32), ("ring", P32)]
 
 
 class Cache(ctypes.Structure):
@@ -73,7 +75,7 @@ class Cache(ctypes.Structure):
                 ("bt", (c_void_p * 2) * TG_MAX_CLUSTERS),
                 ("stride", (c_int32 * 2) * TG_MAX_CLUSTERS),
                 ("cluster_of_head", c_void_p), ("slot_in_cluster", c_void_p), ("len", c_void_p),
-                ("n_fixed", c_void_p)]
+                ("n_fixed", c_void_p), ("ring", c_void_p), ("bf_base", c_void_p), ("recent_ppm", c_int32)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -105,6 +107,7 @@ SIGNATURES = {
     "tg_merge_partials": (ctypes.c_int, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                          c_void_p, c_void_p]),
     "tg_bench_read": (ctypes.c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
+    "tg_append_kv": (ctypes.c_int, [POINTER(Cache), c_void_p, c_void_p, c_void_p]),
 }
 
 _LIB = None

@@ -19,7 +19,7 @@ __all__ = [
     "Reservation", "Share", "Pool", "Tables", "DeviceCache",
     "tg_reserve", "tg_size_tables", "tg_build_tables", "tg_release",
     "tg_write_kv", "tg_decode_workspace_bytes", "tg_decode_attn", "tg_decode_split",
-    "tg_merge_partials", "tg_bench_read", "TG_BENCH_READ_BLOCKS",
+    "tg_merge_partials", "tg_bench_read", "TG_BENCH_READ_BLOCKS", "tg_append_kv",
 ]
 
 
@@ -127,8 +127,8 @@ class Pool:
 
 def tg_size_tables(res: Reservation, page_size: int, quant_block: int, share: Optional[Share] = None,
                    chunk_bf: int = 1024, chunk_i8: int = 1024, lpt: bool = True,
-                   group_size: int = 0) -> dict:
-    opts = L.PlanOpts(int(chunk_bf), int(chunk_i8), int(bool(lpt)), int(group_size))
+                   group_size: int = 0, gen_tokens: int = 0) -> dict:
+    opts = L.PlanOpts(int(chunk_bf), int(chunk_i8), int(bool(lpt)), int(group_size), int(gen_tokens))
     sz = L.TableSizes()
     check(lib().tg_size_tables(ctypes.byref(res.struct), int(page_size), int(quant_block),
                                _share_ptr(share), ctypes.byref(opts), ctypes.byref(sz)), "tg_size_tables")
@@ -154,6 +154,8 @@ class Tables:
         self.part_off = np.zeros(B * H + 1, np.int32)
         self.released = np.zeros(B, np.int32)
         self.gitems_buf = np.full((max(self.n_gitems, 1), L.TG_GROUP_WIDTH, 2), -1, np.int32)
+        self.ring = np.zeros((B, C), np.int32)
+        self.gen_tokens = 0
         s = L.Tables()
         for c in range(C):
             for t in range(2):
@@ -166,6 +168,7 @@ class Tables:
         s.released = _p32(self.released)
         s.gitems = _p32(self.gitems_buf)
         s.n_gitems = self.n_gitems
+        s.ring = _p32(self.ring)
         self.struct = s
 
     @property
@@ -183,10 +186,13 @@ class Tables:
 
 
 def tg_build_tables(pool: Pool, res: Reservation, share: Optional[Share] = None, chunk_bf: int = 1024,
-                    chunk_i8: int = 1024, lpt: bool = True, group_size: int = 0) -> Tables:
-    sizes = tg_size_tables(res, pool.page_size, pool.quant_block, share, chunk_bf, chunk_i8, lpt, group_size)
+                    chunk_i8: int = 1024, lpt: bool = True, group_size: int = 0,
+                    gen_tokens: int = 0) -> Tables:
+    sizes = tg_size_tables(res, pool.page_size, pool.quant_block, share, chunk_bf, chunk_i8, lpt, group_size,
+                           gen_tokens)
     t = Tables(res, sizes)
-    opts = L.PlanOpts(int(chunk_bf), int(chunk_i8), int(bool(lpt)), int(group_size))
+    t.gen_tokens = int(gen_tokens)
+    opts = L.PlanOpts(int(chunk_bf), int(chunk_i8), int(bool(lpt)), int(group_size), int(gen_tokens))
     check(lib().tg_build_tables(pool.handle, ctypes.byref(res.struct), _share_ptr(share),
                                 ctypes.byref(opts), ctypes.byref(t.struct)), "tg_build_tables")
     t.sizes = sizes
@@ -265,6 +271,14 @@ class DeviceCache:
         if share is not None and int(nf.max()) > 0:
             self.n_fixed = torch.from_numpy(np.ascontiguousarray(nf, dtype=np.int32)).to(self.device)
         c_s.n_fixed = _ptr(self.n_fixed)
+        # decode-step growth: the bf16 ring and its offsets
+        self.ring = self.bf_base = None
+        if tables.gen_tokens > 0:
+            self.ring = torch.from_numpy(tables.ring.reshape(-1).copy()).to(self.device)
+            self.bf_base = torch.zeros(res.B * res.H, dtype=torch.int32, device=self.device)
+        c_s.ring = _ptr(self.ring)
+        c_s.bf_base = _ptr(self.bf_base)
+        c_s.recent_ppm = int(res.struct.recent_ppm)
         self.struct = c_s
         self.B, self.H, self.d = res.B, res.H, pool.head_dim
 
@@ -335,3 +349,12 @@ def tg_bench_read(src, sink, stream=None) -> None:
         raise ValueError("sink too small")
     check(lib().tg_bench_read(_ptr(src), int(src.numel() * src.element_size()), _ptr(sink),
                               _stream_ptr(stream)), "tg_bench_read")
+
+
+def tg_append_kv(cache: DeviceCache, rows, status=None, stream=None) -> None:
+    """Append one row per (r, h) (device uint16/int16 [B*H][2][d] bf16 bits)
+    and age the oldest bf16 block into INT8 where the tier split says so;
+    ``status`` (device int32, optional) gets bit 0 if a (r, h) ran out of the
+    reserved capacity."""
+    check(lib().tg_append_kv(ctypes.byref(cache.struct), _ptr(rows), _ptr(status), _stream_ptr(stream)),
+          "tg_append_kv")

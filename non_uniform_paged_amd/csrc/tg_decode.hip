@@ -47,6 +47,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const TG_GLOBAL float* __res
   float m = -INFINITY, den = 0.f;
   float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   auto add = [&](float ms, float ls, const f32x4_t& x0, const f32x4_t& x1) {
+    if (ms == -INFINITY) return;  // a partial with no rows
     if (ms > m) {
       const float sc = __expf(m - ms);
       den *= sc;
@@ -197,17 +198,22 @@ int decode_split(const tg_cache* c, const tg_decode_args* a, void* stream, bool 
       if (c->stride[cl][t] < 0 || c->n_pages[cl][t] < 0) return TG_EINVAL;
       if (c->stride[cl][t] > 0 && (!c->bt[cl][t] || !c->pool[cl][t] || c->page_bytes[cl][t] <= 0))
         return TG_EINVAL;
+      if (c->page_bytes[cl][t] > INT32_MAX) return TG_EUNSUPPORTED;
       if (reinterpret_cast<uintptr_t>(c->pool[cl][t]) % 16) return TG_EINVAL;
     }
   SplitArgs s{};
   for (int32_t cl = 0; cl < c->n_clusters; ++cl)
     for (int t = 0; t < 2; ++t) {
       s.pool[cl][t] = (gptr)(c->pool[cl][t]);
-      s.page_bytes[cl][t] = c->page_bytes[cl][t];
+      s.page_bytes[cl][t] = static_cast<int32_t>(c->page_bytes[cl][t]);
       s.bt[cl][t] = (const TG_GLOBAL int32_t*)(c->bt[cl][t]);
       s.stride[cl][t] = c->stride[cl][t];
     }
   s.len = (const TG_GLOBAL int32_t*)(c->len);
+  s.ring = (const TG_GLOBAL int32_t*)(c->ring);
+  s.bf_base = (const TG_GLOBAL int32_t*)(c->bf_base);
+  s.n_clusters = c->n_clusters;
+  if (c->ring != nullptr && c->bf_base == nullptr) return TG_EINVAL;
   s.n_fixed = (const TG_GLOBAL int32_t*)(c->n_fixed);
   s.n_kv_heads = c->n_kv_heads;
   s.cluster_of_head = (const TG_GLOBAL int32_t*)(c->cluster_of_head);

@@ -30,13 +30,15 @@ constexpr float kSlack = 8.f;
 
 struct SplitArgs {
   gptr pool[TG_MAX_CLUSTERS][2];
-  int64_t page_bytes[TG_MAX_CLUSTERS][2];
+  int32_t page_bytes[TG_MAX_CLUSTERS][2];  // < 2^31 (checked on the host)
   const TG_GLOBAL int32_t* bt[TG_MAX_CLUSTERS][2];
   int32_t stride[TG_MAX_CLUSTERS][2];
   const TG_GLOBAL int32_t* cluster_of_head;
   const TG_GLOBAL int32_t* slot_in_cluster;
-  const TG_GLOBAL int32_t* len;      // [B*H*2] (n_i8, n_bf)
+  const TG_GLOBAL int32_t* len;      // [B*H*2] live (n_i8, n_bf): items are clipped to them
   const TG_GLOBAL int32_t* n_fixed;  // [B] or null
+  const TG_GLOBAL int32_t* ring;     // [B*C] bf16 ring pages, or null (no ring)
+  const TG_GLOBAL int32_t* bf_base;  // [B*H] ring row of logical bf16 row 0 (with ring)
   gptr q;
   const TG_GLOBAL int32_t* work;
   const TG_GLOBAL int32_t* gitems;  // [n_gitems][TG_GROUP_WIDTH][2] (request, slot)
@@ -46,8 +48,22 @@ struct SplitArgs {
   int32_t n_gitems;
   int32_t n_q_heads;
   int32_t n_kv_heads;
+  int32_t n_clusters;
   float scale_log2;
 };
+
+// Partial of an item with no live rows (m = -inf, l = 0, acc = 0): the merge
+// gives it no weight.
+template <int D, int G>
+__device__ __forceinline__ void write_empty_partial(const SplitArgs& a, int slot) {
+  const int lane = threadIdx.x & 63;
+  TG_GLOBAL float* acc = a.ws_acc + static_cast<int64_t>(slot) * G * D;
+  for (int i = lane; i < G * D; i += 64) acc[i] = 0.f;
+  if (lane < G) {
+    a.ws_ml[(static_cast<int64_t>(slot) * G + lane) * 2 + 0] = -INFINITY;
+    a.ws_ml[(static_cast<int64_t>(slot) * G + lane) * 2 + 1] = 0.f;
+  }
+}
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));

@@ -181,6 +181,8 @@ extern "C" int tg_reserve(const tg_budget_table* tb, int32_t B, const int32_t* n
   out->B = B;
   out->n_kv_heads = H;
   out->n_clusters = C;
+  out->recent_ppm = tb->recent_ppm;
+  out->quant_block = tb->quant_block;
   return TG_OK;
 }
 
@@ -326,10 +328,53 @@ int check_share(const tg_share_desc* sh, const tg_reservation* res, const Geomet
   return TG_OK;
 }
 
+// Tier split of a sequence of L rows: INT8 rows (whole blocks of the rows
+// older than the recent share).
+int64_t i8_rows(int64_t L, int64_t recent_ppm, int64_t qb) {
+  return ((L - ceil_div(L * recent_ppm, kPpm)) / qb) * qb;
+}
+
+// Sizes when every (r, h) may grow by T rows: INT8 rows of L + T and the most
+// bf16 rows held at any length from L to L + T (the tables are built for
+// these; lengths stay the live ones).
+struct Capacity {
+  std::vector<int32_t> length, n_i8, n_bf;
+  tg_reservation view;
+};
+
+int make_capacity(const tg_reservation* res, int32_t T, Capacity* cap) {
+  const int64_t n = int64_t(res->B) * res->n_kv_heads;
+  if (res->quant_block < 1 || res->recent_ppm < 0 || res->recent_ppm > kPpm) return TG_EINVAL;
+  cap->length.resize(n);
+  cap->n_i8.resize(n);
+  cap->n_bf.resize(n);
+  for (int64_t i = 0; i < n; ++i) {
+    int64_t i8 = res->n_i8[i], bf = res->n_bf[i], top = bf;
+    for (int32_t k = 0; k < T; ++k) {
+      ++bf;
+      if (i8_rows(i8 + bf, res->recent_ppm, res->quant_block) > i8) {
+        i8 += res->quant_block;
+        bf -= res->quant_block;
+      }
+      top = std::max(top, bf);
+    }
+    if (i8 + top > std::numeric_limits<int32_t>::max()) return TG_EOVERFLOW;
+    cap->n_i8[i] = static_cast<int32_t>(i8);
+    cap->n_bf[i] = static_cast<int32_t>(top);
+    cap->length[i] = static_cast<int32_t>(i8 + top);
+  }
+  cap->view = *res;
+  cap->view.length = cap->length.data();
+  cap->view.n_i8 = cap->n_i8.data();
+  cap->view.n_bf = cap->n_bf.data();
+  return TG_OK;
+}
+
 int check_opts(const tg_plan_opts* o, int32_t ps, int32_t qb) {
   if (!o) return TG_EINVAL;
   if (o->chunk_bf < ps || o->chunk_bf % ps || o->chunk_i8 < qb || o->chunk_i8 % qb) return TG_EINVAL;
   if (o->group_size < 0 || o->group_size > TG_GROUP_WIDTH) return TG_EINVAL;
+  if (o->gen_tokens < 0) return TG_EINVAL;
   return TG_OK;
 }
 
@@ -539,16 +584,27 @@ int make_plan(const tg_reservation* res, const Geometry& g, const Paths& paths, 
 
 }  // namespace
 
-extern "C" int tg_size_tables(const tg_reservation* res, int32_t ps, int32_t qb,
+extern "C" int tg_size_tables(const tg_reservation* live, int32_t ps, int32_t qb,
                               const tg_share_desc* share, const tg_plan_opts* opts,
                               tg_table_sizes* out) {
   if (!out) return TG_EINVAL;
   Geometry g;
-  int st = check_reservation(res, ps, qb, &g);
+  int st = check_reservation(live, ps, qb, &g);
   if (st) return st;
   Paths paths;
-  if ((st = check_share(share, res, g, &paths))) return st;
+  if ((st = check_share(share, live, g, &paths))) return st;
   if ((st = check_opts(opts, ps, qb))) return st;
+  if (opts->gen_tokens > 0 && paths.on) return TG_EINVAL;
+  Capacity cap;
+  const tg_reservation* res = live;
+  if (opts->gen_tokens > 0) {
+    try {
+      if ((st = make_capacity(live, opts->gen_tokens, &cap))) return st;
+    } catch (...) {
+      return TG_ENOMEM;
+    }
+    res = &cap.view;
+  }
   Plan plan;
   try {
     if ((st = make_plan(res, g, paths, opts, &plan))) return st;
@@ -582,16 +638,26 @@ extern "C" int tg_size_tables(const tg_reservation* res, int32_t ps, int32_t qb,
   return TG_OK;
 }
 
-extern "C" int tg_build_tables(tg_pool* pool, const tg_reservation* res, const tg_share_desc* share,
+extern "C" int tg_build_tables(tg_pool* pool, const tg_reservation* live, const tg_share_desc* share,
                                const tg_plan_opts* opts, tg_tables* out) {
   if (!pool || !out) return TG_EINVAL;
   tg_table_sizes sz;
-  int st = tg_size_tables(res, pool->page_size, pool->quant_block, share, opts, &sz);
+  int st = tg_size_tables(live, pool->page_size, pool->quant_block, share, opts, &sz);
   if (st) return st;
   Geometry g;
-  check_reservation(res, pool->page_size, pool->quant_block, &g);
+  check_reservation(live, pool->page_size, pool->quant_block, &g);
   Paths paths;
-  check_share(share, res, g, &paths);
+  check_share(share, live, g, &paths);
+  Capacity cap;
+  const tg_reservation* res = live;
+  if (opts->gen_tokens > 0) {
+    try {
+      if ((st = make_capacity(live, opts->gen_tokens, &cap))) return st;
+    } catch (...) {
+      return TG_ENOMEM;
+    }
+    res = &cap.view;
+  }
   if (g.C != pool->C || out->n_items != sz.n_items || out->n_gitems != sz.n_gitems || !out->len ||
       !out->part_off || !out->released || (sz.n_items > 0 && !out->work) ||
       (sz.n_gitems > 0 && !out->gitems))
@@ -682,12 +748,16 @@ extern "C" int tg_build_tables(tg_pool* pool, const tg_reservation* res, const t
 
   // lengths
   for (int64_t i = 0; i < int64_t(g.B) * g.H; ++i) {
-    out->len[2 * i] = res->n_i8[i];
-    out->len[2 * i + 1] = res->n_bf[i];
+    out->len[2 * i] = live->n_i8[i];
+    out->len[2 * i + 1] = live->n_bf[i];
   }
   std::copy(plan.work.begin(), plan.work.end(), out->work);
   std::copy(plan.part_off.begin(), plan.part_off.end(), out->part_off);
   std::copy(plan.gitems.begin(), plan.gitems.end(), out->gitems);
+  if (out->ring)
+    for (int32_t r = 0; r < g.B; ++r)
+      for (int32_t c = 0; c < g.C; ++c)
+        out->ring[int64_t(r) * g.C + c] = static_cast<int32_t>(pages_of(res, g, r, c, TG_TIER_BF16));
   for (int32_t r = 0; r < g.B; ++r) out->released[r] = 0;
   return TG_OK;
 }

@@ -103,11 +103,14 @@ __device__ __forceinline__ void bf16_page(const u32x4_t (&kb)[NK], const u32x4_t
 // NTILE score tiles of 16 columns share every page load.  Column
 // c = lg + 16 * tile belongs to member c / G (its q-head c % G).  A plain
 // item has one member (r, slot); a group item's members come from `gm`, the
-// (request, slot) pairs of its member table row.
+// (request, slot) pairs of its member table row.  With ring_pg > 0 the
+// tier's pages form a ring: logical page p is table entry
+// (ring_base + p) mod ring_pg.
 template <int D, int G, bool QF32, int DEPTH, bool STREAM, int NTILE>
 __device__ __forceinline__ void bf16_item(const SplitArgs& a, int r, int h, int t0, int t1, int slot,
                                           const TG_GLOBAL int32_t* gm, int hs,
-                                          const TG_GLOBAL int32_t* bt_row, gptr pool, int64_t pbytes) {
+                                          const TG_GLOBAL int32_t* bt_row, int ring_base, int ring_pg,
+                                          gptr pool, int64_t pbytes) {
   constexpr int NK = D / 32;           // 1 KiB loads per K (and per V) block
   constexpr int NT = D / 16;           // 16-channel tiles of V
   constexpr int NQ = QF32 ? 2 : 1;     // bf16 pieces of q
@@ -179,7 +182,9 @@ __device__ __forceinline__ void bf16_item(const SplitArgs& a, int r, int h, int 
 
   for (int w0 = 0; w0 < np; w0 += 64) {
     const int nw = min(64, np - w0);
-    const int pid_lane = bt_row[p0 + w0 + min(lane, nw - 1)];
+    int lp = p0 + w0 + min(lane, nw - 1);
+    if (ring_pg > 0) lp = (ring_base + lp) % ring_pg;
+    const int pid_lane = bt_row[lp];
     auto issue = [&](u32x4_t (&kk)[NK], u32x4_t (&vv)[NK], int i) {
       const int pid = __builtin_amdgcn_readlane(pid_lane, min(i, nw - 1));
       gptr pp = pool + static_cast<int64_t>(pid) * pbytes + head_off + lane_off;
@@ -250,23 +255,41 @@ __device__ __forceinline__ void bf16_dispatch(const SplitArgs& a, const TG_GLOBA
   }
   const int cl = uniform(a.cluster_of_head[h]);
   const int hs = uniform(a.slot_in_cluster[h]);
+  const int rh = r * a.n_kv_heads + h;
+  int t1c = t1;
+  if (gm == nullptr) {
+    // plans built for growth cover the reserved capacity: clip to the live rows
+    t1c = min(t1, uniform(a.len[2 * rh + 1]));
+    if (t0 >= t1c) {
+      write_empty_partial<D, G>(a, slot);
+      return;
+    }
+  }
+  int ring_pg = 0, ring_base = 0;
+  if (a.ring != nullptr) {
+    ring_pg = uniform(a.ring[r * a.n_clusters + cl]);
+    ring_base = uniform(a.bf_base[rh]) / kPage;
+  }
   const TG_GLOBAL int32_t* bt_row = a.bt[cl][TG_TIER_BF16] + static_cast<int64_t>(r) * a.stride[cl][TG_TIER_BF16];
   gptr pool = a.pool[cl][TG_TIER_BF16];
   const int64_t pbytes = a.page_bytes[cl][TG_TIER_BF16];
   // an item that starts on the shared radix path reads through the caches
   bool shared = gm != nullptr;
   if (!shared && a.n_fixed) {
-    const int n_i8 = uniform(a.len[2 * (r * a.n_kv_heads + h)]);
+    const int n_i8 = uniform(a.len[2 * rh]);
     shared = n_i8 + t0 + kPage <= uniform(a.n_fixed[r]);
   }
   // a group with members past the first 16 columns takes a second score tile
   const bool two = gm != nullptr && uniform(gm[2 * (16 / G)]) >= 0;
   if (two)
-    bf16_item<D, G, QF32, DEPTH, false, 2>(a, r, h, t0, t1, slot, gm, hs, bt_row, pool, pbytes);
+    bf16_item<D, G, QF32, DEPTH, false, 2>(a, r, h, t0, t1c, slot, gm, hs, bt_row, ring_base, ring_pg, pool,
+                                           pbytes);
   else if (shared)
-    bf16_item<D, G, QF32, DEPTH, false, 1>(a, r, h, t0, t1, slot, gm, hs, bt_row, pool, pbytes);
+    bf16_item<D, G, QF32, DEPTH, false, 1>(a, r, h, t0, t1c, slot, gm, hs, bt_row, ring_base, ring_pg, pool,
+                                           pbytes);
   else
-    bf16_item<D, G, QF32, DEPTH, true, 1>(a, r, h, t0, t1, slot, gm, hs, bt_row, pool, pbytes);
+    bf16_item<D, G, QF32, DEPTH, true, 1>(a, r, h, t0, t1c, slot, gm, hs, bt_row, ring_base, ring_pg, pool,
+                                          pbytes);
 }
 
 }  // namespace tg_dev

@@ -259,7 +259,13 @@ constexpr int kI8LdsFloats = (D / 16) * 4 * 64;
 template <int D, int G, bool QF32, int DEPTH>
 __device__ __forceinline__ void i8_dispatch(const SplitArgs& a, const TG_GLOBAL int32_t* w, float* lds) {
   const int r = uniform(w[0]), h = uniform(w[1]);
-  const int t0 = uniform(w[3]), t1 = uniform(w[4]), slot = uniform(w[5]);
+  const int t0 = uniform(w[3]), slot = uniform(w[5]);
+  // plans built for growth cover the reserved capacity: clip to the live rows
+  const int t1 = min(uniform(w[4]), uniform(a.len[2 * (r * a.n_kv_heads + h)]));
+  if (t0 >= t1) {
+    write_empty_partial<D, G>(a, slot);
+    return;
+  }
   const int cl = uniform(a.cluster_of_head[h]);
   const int hs = uniform(a.slot_in_cluster[h]);
   const TG_GLOBAL int32_t* bt_row = a.bt[cl][TG_TIER_I8] + static_cast<int64_t>(r) * a.stride[cl][TG_TIER_I8];

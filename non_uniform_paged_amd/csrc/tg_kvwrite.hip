@@ -108,7 +108,143 @@ __global__ __launch_bounds__(2 * D) void write_i8_kernel(WriteArgs a) {
   reinterpret_cast<_Float16*>(head + 2 * kQBlock * D + kv * D * 2)[ch] = s16;
 }
 
+// ---------------------------------------------------------------- decode-step append
+struct AppendArgs {
+  char* pool[TG_MAX_CLUSTERS][2];
+  int64_t page_bytes[TG_MAX_CLUSTERS][2];
+  const int32_t* bt[TG_MAX_CLUSTERS][2];
+  int32_t stride[TG_MAX_CLUSTERS][2];
+  const int32_t* cluster_of_head;
+  const int32_t* slot_in_cluster;
+  const int32_t* ring;
+  int32_t* len;
+  int32_t* bf_base;
+  const uint16_t* rows;
+  int32_t* status;
+  int32_t H, C, recent_ppm;
+};
+
+__device__ __forceinline__ int64_t i8_rows(int64_t L, int64_t recent_ppm) {
+  const int64_t recent = (L * recent_ppm + 999999) / 1000000;
+  return ((L - recent) / kQBlock) * kQBlock;
+}
+
+// Byte offset of (row t, channel c) inside a head's bf16 page (K, or V at
+// +2*kPage*D), the layout of include/tg.h.
+template <int D>
+__device__ __forceinline__ int bf16_offset(int kv, int t, int c) {
+  return kv == 0 ? (((c >> 5) * 64 + ((c >> 3) & 3) * 16 + t) * 16 + (c & 7) * 2)
+                 : 2 * kPage * D + (((c >> 5) * 64 + (t >> 2) * 16 + (c & 15)) * 16 + ((c >> 4) & 1) * 8 + (t & 3) * 2);
+}
+
+// One workgroup of 2*D threads per (r, h), thread = (K|V, channel): writes
+// the new row as the newest bf16 row (ring row base + n_bf) and, when the
+// tier split of the new length moves the INT8 boundary, quantises the oldest
+// kQBlock bf16 rows into INT8 block n_i8 / kQBlock and advances the ring.
+template <int D>
+__global__ __launch_bounds__(2 * D) void append_kernel(AppendArgs a) {
+  const int rh = blockIdx.x;
+  const int r = rh / a.H, h = rh % a.H;
+  const int kv = threadIdx.x / D, ch = threadIdx.x % D;
+  const int cl = a.cluster_of_head[h], hs = a.slot_in_cluster[h];
+  const int n_i8 = a.len[2 * rh], n_bf = a.len[2 * rh + 1];
+  const int base = a.bf_base[rh];
+  const int ring_rows = a.ring[r * a.C + cl] * kPage;
+  const bool age = i8_rows(static_cast<int64_t>(n_i8) + n_bf + 1, a.recent_ppm) > n_i8;
+  const int blk = n_i8 / kQBlock;
+  const int32_t* bt_i8 = a.bt[cl][TG_TIER_I8] + static_cast<int64_t>(r) * a.stride[cl][TG_TIER_I8];
+  bool ok = n_bf + 1 <= ring_rows;
+  if (age) ok = ok && blk < a.stride[cl][TG_TIER_I8] && bt_i8[blk] >= 0;
+  if (!ok) {  // past the capacity reserved at admission: nothing is written
+    if (threadIdx.x == 0 && a.status != nullptr) atomicOr(a.status, 1);
+    return;
+  }
+  const int32_t* bt_bf = a.bt[cl][TG_TIER_BF16] + static_cast<int64_t>(r) * a.stride[cl][TG_TIER_BF16];
+  auto bf_head = [&](int ring_row) {
+    const int pid = bt_bf[ring_row / kPage];
+    return a.pool[cl][TG_TIER_BF16] + static_cast<int64_t>(pid) * a.page_bytes[cl][TG_TIER_BF16] +
+           static_cast<int64_t>(hs) * (4 * kPage * D);
+  };
+  {
+    const int pos = (base + n_bf) % ring_rows;
+    *reinterpret_cast<uint16_t*>(bf_head(pos) + bf16_offset<D>(kv, pos % kPage, ch)) =
+        a.rows[static_cast<int64_t>(rh) * 2 * D + kv * D + ch];
+  }
+  if (!age) {
+    if (threadIdx.x == 0) a.len[2 * rh + 1] = n_bf + 1;
+    return;
+  }
+  __syncthreads();  // the new row may be one of the rows that age
+  auto value = [&](int t) {
+    const int pos = (base + t) % ring_rows;
+    const uint16_t x = *reinterpret_cast<const uint16_t*>(bf_head(pos) + bf16_offset<D>(kv, pos % kPage, ch));
+    return __uint_as_float(static_cast<uint32_t>(x) << 16);
+  };
+  float amax = 0.f;
+  for (int t = 0; t < kQBlock; ++t) amax = fmaxf(amax, fabsf(value(t)));
+  _Float16 s16 = static_cast<_Float16>(amax / 127.0f);
+  if (__builtin_isinf(static_cast<float>(s16))) s16 = static_cast<_Float16>(65504.0f);
+  const float sf = static_cast<float>(s16);
+  char* head = a.pool[cl][TG_TIER_I8] + static_cast<int64_t>(bt_i8[blk]) * a.page_bytes[cl][TG_TIER_I8] +
+               static_cast<int64_t>(hs) * (2 * kQBlock * D + 4 * D);
+  int8_t* codes = reinterpret_cast<int8_t*>(head + kv * kQBlock * D);
+  constexpr int NL = D / 64;
+  for (int t = 0; t < kQBlock; ++t) {
+    const float x = value(t);
+    int q = 0;
+    if (sf > 0.f) q = static_cast<int>(fminf(fmaxf(__builtin_rintf(x / sf), -127.f), 127.f));
+    const int c = ch;
+    const int off = kv == 0
+        ? ((t >> 4) * NL + (c >> 6)) * 1024 + (((c >> 3) & 3) * 16 + (t & 15)) * 16 + ((c >> 5) & 1) * 8 + (c & 7)
+        : ((t >> 4) * NL + (c >> 6)) * 1024 + (((t >> 2) & 3) * 16 + (c & 15)) * 16 + ((c >> 4) & 3) * 4 + (t & 3);
+    codes[off] = static_cast<int8_t>(q);
+  }
+  reinterpret_cast<_Float16*>(head + 2 * kQBlock * D + kv * D * 2)[ch] = s16;
+  if (threadIdx.x == 0) {
+    a.len[2 * rh] = n_i8 + kQBlock;
+    a.len[2 * rh + 1] = n_bf + 1 - kQBlock;
+    a.bf_base[rh] = (base + kQBlock) % ring_rows;
+  }
+}
+
 }  // namespace
+
+extern "C" int tg_append_kv(const tg_cache* c, const uint16_t* rows, int32_t* status, void* stream) {
+  if (!c || !rows || !c->len || !c->ring || !c->bf_base || !c->cluster_of_head || !c->slot_in_cluster)
+    return TG_EINVAL;
+  if (c->B < 1 || c->n_kv_heads < 1 || c->n_clusters < 1 || c->n_clusters > TG_MAX_CLUSTERS)
+    return TG_EINVAL;
+  if (c->head_dim != 64 && c->head_dim != 128) return TG_EUNSUPPORTED;
+  if (c->page_size != kPage || c->quant_block != kQBlock) return TG_EUNSUPPORTED;
+  if (c->recent_ppm < 0 || c->recent_ppm > 1000000) return TG_EINVAL;
+  AppendArgs a{};
+  for (int32_t cl = 0; cl < c->n_clusters; ++cl)
+    for (int t = 0; t < 2; ++t) {
+      if (c->stride[cl][t] > 0 && (!c->bt[cl][t] || !c->pool[cl][t])) return TG_EINVAL;
+      a.pool[cl][t] = static_cast<char*>(c->pool[cl][t]);
+      a.page_bytes[cl][t] = c->page_bytes[cl][t];
+      a.bt[cl][t] = c->bt[cl][t];
+      a.stride[cl][t] = c->stride[cl][t];
+    }
+  a.cluster_of_head = c->cluster_of_head;
+  a.slot_in_cluster = c->slot_in_cluster;
+  a.ring = c->ring;
+  a.len = c->len;
+  a.bf_base = c->bf_base;
+  a.rows = rows;
+  a.status = status;
+  a.H = c->n_kv_heads;
+  a.C = c->n_clusters;
+  a.recent_ppm = c->recent_ppm;
+  const int64_t pairs = static_cast<int64_t>(c->B) * c->n_kv_heads;
+  if (pairs > INT32_MAX) return TG_EUNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (c->head_dim == 128)
+    hipLaunchKernelGGL(append_kernel<128>, dim3(static_cast<unsigned>(pairs)), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(append_kernel<64>, dim3(static_cast<unsigned>(pairs)), dim3(128), 0, st, a);
+  return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
+}
 
 extern "C" int tg_write_kv(const tg_cache* c, const uint16_t* rows, const int32_t* index,
                            const int64_t* offsets, void* stream) {

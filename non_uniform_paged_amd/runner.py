@@ -34,10 +34,12 @@ class Prepared:
 
     def __init__(self, w, chunk_bf: int = 1024, chunk_i8: int = 1024, lpt: bool = True,
                  slack_pages: int = 0, shift_pages: int = 0, device: str = "cuda",
-                 group_size: Optional[int] = None):
+                 group_size: Optional[int] = None, gen_tokens: int = 0):
         """``group_size`` None: group shared-prefix pages for as many requests
         as fill two 16-column score tiles (32 / G) when the batch shares a radix
-        prefix, else no groups."""
+        prefix, else no groups.  ``gen_tokens`` > 0 reserves room for that
+        many appended rows per (r, h) and stages them (the continuation of
+        each sequence) on the device for ``append``."""
         import torch
 
         self.w = w
@@ -48,8 +50,9 @@ class Prepared:
         if group_size is None:
             group_size = min(32 // G, api.TG_GROUP_WIDTH) if self.share is not None else 0
         self.group_size = group_size
+        self.gen_tokens = gen_tokens
         sizes = api.tg_size_tables(self.res, w.page_size, w.quant_block, self.share, chunk_bf, chunk_i8, lpt,
-                                   group_size)
+                                   group_size, gen_tokens)
         need = sizes["pages_needed"]
         C = self.res.C
         extra = slack_pages + shift_pages
@@ -60,15 +63,24 @@ class Prepared:
             filler = api.tg_reserve(w.head_rank, 10**6, 10**6, C, 10**6, w.quant_block,
                                     [shift_pages * w.page_size], None, None)
             ftab = api.tg_build_tables(self.pool, filler, None, w.page_size * 4, w.quant_block, False)
-        self.tables = api.tg_build_tables(self.pool, self.res, self.share, chunk_bf, chunk_i8, lpt, group_size)
+        self.tables = api.tg_build_tables(self.pool, self.res, self.share, chunk_bf, chunk_i8, lpt, group_size,
+                                          gen_tokens)
         if shift_pages:
             api.tg_release(self.pool, ftab, 0)
         self.cache = api.DeviceCache(self.pool, self.res, self.tables, dev, self.share)
 
-        rows, index, offsets = w.source_buffer(self.res.length)
+        rows, index, offsets = w.source_buffer(self.res.length + gen_tokens)
         rows_t = torch.from_numpy(rows.view(np.uint16).reshape(-1).view(np.int16)).to(dev)
         index_t = torch.from_numpy(index).to(dev)
         off_t = torch.from_numpy(offsets).to(dev)
+        self.appended = None
+        if gen_tokens > 0:
+            # row L0 + k of every (r, h), step-major: [T][B*H][2][d]
+            L0 = self.res.length.reshape(-1).astype(np.int64)
+            src = index[offsets[:-1][None, :] + L0[None, :] + np.arange(gen_tokens)[:, None]]
+            self.appended = torch.from_numpy(rows[src].view(np.int16)).to(dev)
+            self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.steps_appended = 0
         del rows
         api.tg_write_kv(self.cache, rows_t, index_t, off_t)
         torch.cuda.synchronize(dev)
@@ -86,6 +98,19 @@ class Prepared:
     # ------------------------------------------------------------------ run
     def step(self, stream=None):
         api.tg_decode_attn(self.cache, self.q, self.out, self.workspace, self.w.Hq, 0.0, stream=stream)
+
+    def append(self, stream=None):
+        """Append the next staged row to every (r, h) (tg_append_kv)."""
+        if self.appended is None or self.steps_appended >= self.gen_tokens:
+            raise ValueError("no staged rows left")
+        api.tg_append_kv(self.cache, self.appended[self.steps_appended], self.status, stream=stream)
+        self.steps_appended += 1
+
+    def live_lengths(self) -> np.ndarray:
+        """[B][H][2] (n_i8, n_bf) as the device holds them."""
+        import torch
+        torch.cuda.synchronize()
+        return self.cache.len.cpu().numpy().reshape(self.w.B, self.w.Hkv, 2)
 
     def output(self) -> np.ndarray:
         import torch

@@ -48,6 +48,13 @@ R-plan   items (r, h, tier, t0, t1, slot) in order r, h, tier (INT8 first).
          the natural index; part_off is the CSR of slots per (r, h).  With lpt,
          items are stably sorted by descending cost (t1 - t0) * (2 for bf16,
          1 for INT8).
+R-step   (decode-step growth) an appended row becomes the newest bf16 row
+         and R-tier is applied to the new length; when the INT8 boundary moves
+         (by one block) the oldest Qb bf16 rows are quantised (R-q) into the
+         next INT8 block.  Pages for gen_tokens appended rows are reserved at
+         admission: INT8 rows of the final length, and the most bf16 rows held
+         at any length on the way; the bf16 tier turns over its pages as a
+         ring.  Not combined with shared radix pages.
 R-group  (only with a group size > 1 and radix paths) the leading shared bf16
          pages of each (r, h) are cut into runs with the same radix node;
          requests whose run has the same (node, first row, page count, INT8
@@ -100,6 +107,15 @@ class Reservation:
     cluster_of_head: List[int]       # [H]
     slot_in_cluster: List[int]       # [H]
     cluster_size: List[int]          # [C]
+    recent_ppm: int = PPM
+    quant_block: int = 64
+
+
+def tier_split(L: int, recent_ppm: int, quant_block: int) -> Tuple[int, int]:
+    """(n_i8, n_bf) of a sequence of L rows (R-tier)."""
+    old = L - _ceil_div(L * recent_ppm, PPM)
+    i8 = (old // quant_block) * quant_block
+    return i8, L - i8
 
 
 def reserve(head_rank: Sequence[int], ratio_hi_ppm: int, ratio_lo_ppm: int,
@@ -153,14 +169,44 @@ def reserve(head_rank: Sequence[int], ratio_hi_ppm: int, ratio_lo_ppm: int,
     for r in range(B):
         ri, rb = [], []
         for h in range(H):
-            l = L[r][h]
-            old = l - _ceil_div(l * recent_ppm, PPM)
-            i8 = (old // quant_block) * quant_block
+            i8, bf = tier_split(L[r][h], recent_ppm, quant_block)
             ri.append(i8)
-            rb.append(l - i8)
+            rb.append(bf)
         n_i8.append(ri)
         n_bf.append(rb)
-    return Reservation(budget, L, n_i8, n_bf, coh, sic, sizes)
+    return Reservation(budget, L, n_i8, n_bf, coh, sic, sizes, recent_ppm, quant_block)
+
+
+# ---------------------------------------------------------------- decode-step growth
+def append_step(n_i8: int, n_bf: int, recent_ppm: int, quant_block: int) -> Tuple[int, int, bool]:
+    """One appended row (R-step): the row becomes the newest bf16 row, then
+    the tier split of the new length decides whether the oldest quant_block
+    bf16 rows become the next INT8 block.  Returns (n_i8, n_bf, aged)."""
+    n_bf += 1
+    i8, _ = tier_split(n_i8 + n_bf, recent_ppm, quant_block)
+    if i8 > n_i8:
+        return n_i8 + quant_block, n_bf - quant_block, True
+    return n_i8, n_bf, False
+
+
+def capacity(res: Reservation, gen_tokens: int) -> Reservation:
+    """The reservation's sizes when every (r, h) may grow by gen_tokens rows
+    (R-step): INT8 rows of the final length, and the most bf16 rows held at
+    any length on the way.  Only the sizes are meaningful."""
+    B, H = len(res.L), len(res.cluster_of_head)
+    n_i8 = [[0] * H for _ in range(B)]
+    n_bf = [[0] * H for _ in range(B)]
+    for r in range(B):
+        for h in range(H):
+            i8, bf = res.n_i8[r][h], res.n_bf[r][h]
+            top = bf
+            for _ in range(gen_tokens):
+                i8, bf, _aged = append_step(i8, bf, res.recent_ppm, res.quant_block)
+                top = max(top, bf)
+            n_i8[r][h], n_bf[r][h] = i8, top
+    L = [[n_i8[r][h] + n_bf[r][h] for h in range(H)] for r in range(B)]
+    return Reservation(res.budget, L, n_i8, n_bf, res.cluster_of_head, res.slot_in_cluster,
+                       res.cluster_size, res.recent_ppm, res.quant_block)
 
 
 # ---------------------------------------------------------------- pages
@@ -446,24 +492,34 @@ def plan(res: Reservation, chunk_bf: int, chunk_i8: int, lpt: bool, group_size: 
 
 def build_tables(pool: Pool, res: Reservation, page_size: int, quant_block: int,
                  chunk_bf: int, chunk_i8: int, lpt: bool,
-                 n_fixed=None, paths=None, node_len=None, group_size: int = 0) -> Tables:
+                 n_fixed=None, paths=None, node_len=None, group_size: int = 0,
+                 gen_tokens: int = 0) -> Tables:
     """Allocate pages and emit block tables, lengths and the plan (R-alloc,
-    R-page, R-plan, R-group)."""
+    R-page, R-plan, R-group).  With gen_tokens > 0 pages and plan cover the
+    capacity for that many appended rows (R-step); lengths stay the live ones
+    and ring[r][c] is the bf16 page count of (r, c), the ring the bf16 tier
+    turns over."""
     if chunk_bf < page_size or chunk_bf % page_size or chunk_i8 < quant_block or chunk_i8 % quant_block:
         raise OracleError("EINVAL", "chunk sizes")
     if not 0 <= group_size <= GROUP_WIDTH:
         raise OracleError("EINVAL", "group size")
+    if gen_tokens < 0 or (gen_tokens > 0 and paths is not None):
+        raise OracleError("EINVAL", "growth")
     B = len(res.L)
     C = len(res.cluster_size)
     H = len(res.cluster_of_head)
+    live = res
+    if gen_tokens > 0:
+        res = capacity(res, gen_tokens)
     pages = allocate(pool, res, page_size, quant_block, n_fixed, paths, node_len)
     stride = [[max(len(pages[r][c][t]) for r in range(B)) for t in range(2)] for c in range(C)]
     bt = [[[pages[r][c][t] + [-1] * (stride[c][t] - len(pages[r][c][t])) for r in range(B)]
            for t in range(2)] for c in range(C)]
-    lens = [[(res.n_i8[r][h], res.n_bf[r][h]) for h in range(H)] for r in range(B)]
+    lens = [[(live.n_i8[r][h], live.n_bf[r][h]) for h in range(H)] for r in range(B)]
     nf = [0] * B if n_fixed is None else list(n_fixed)
     work, part_off, gitems = plan(res, chunk_bf, chunk_i8, lpt, group_size, page_size, quant_block,
                                   nf, paths, node_len)
     t = Tables(bt, stride, lens, work, part_off, pages)
     t.gitems = gitems
+    t.ring = [[len(pages[r][c][TIER_BF]) for c in range(C)] for r in range(B)]
     return t

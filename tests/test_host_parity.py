@@ -59,20 +59,20 @@ def _gitems_of(t_o):
     return np.array(t_o.gitems, dtype=np.int32).reshape(-1, 32, 2)
 
 
-def _tables_parity(w, chunk_bf=512, chunk_i8=1024, lpt=True, slack=3, group_size=0):
+def _tables_parity(w, chunk_bf=512, chunk_i8=1024, lpt=True, slack=3, group_size=0, gen=0):
     res_o, res_g = _both(w)
     _compare_reservation(res_o, res_g)
     share, sh_o = _share(w)
-    need_bf, need_i8 = P.pages_needed(res_o, w.page_size, w.quant_block, *sh_o)
-    sizes = tg.tg_size_tables(res_g, w.page_size, w.quant_block, share, chunk_bf, chunk_i8, lpt, group_size)
+    need_bf, need_i8 = P.pages_needed(P.capacity(res_o, gen), w.page_size, w.quant_block, *sh_o)
+    sizes = tg.tg_size_tables(res_g, w.page_size, w.quant_block, share, chunk_bf, chunk_i8, lpt, group_size, gen)
     assert [row[1] for row in sizes["pages_needed"]] == need_bf
     assert [row[0] for row in sizes["pages_needed"]] == need_i8
     pool_g = tg.Pool(res_g.cluster_size, w.d, w.page_size, w.quant_block,
                      [x + slack for x in need_bf], [x + slack for x in need_i8])
     pool_o = P.Pool([x + slack for x in need_bf], [x + slack for x in need_i8])
-    t_g = tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt, group_size)
+    t_g = tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt, group_size, gen)
     t_o = P.build_tables(pool_o, res_o, w.page_size, w.quant_block, chunk_bf, chunk_i8, lpt, *sh_o,
-                         **({"group_size": group_size} if sh_o else {}))
+                         **({"group_size": group_size} if sh_o else {"gen_tokens": gen}))
     for c in range(w.n_clusters):
         for t in range(2):
             assert t_g.stride[c][t] == t_o.stride[c][t]
@@ -84,7 +84,15 @@ def _tables_parity(w, chunk_bf=512, chunk_i8=1024, lpt=True, slack=3, group_size
     assert list(t_g.part_off) == t_o.part_off
     assert t_g.n_slots == t_o.part_off[-1] and t_g.n_gitems == len(t_o.gitems)
     assert np.array_equal(t_g.gitems, _gitems_of(t_o))
+    assert np.array_equal(t_g.ring, np.array(t_o.ring, dtype=np.int32))
     return res_o, res_g, pool_o, pool_g, t_o, t_g
+
+
+@pytest.mark.parametrize("name,gen", [("tiny", 37), ("llama8b", 256), ("tiered", 1000), ("ragged", 64)])
+def test_growth_tables_bit_exact(name, gen):
+    w = make_workload(name)
+    res_o, res_g, pool_o, pool_g, t_o, t_g = _tables_parity(w, gen=gen)
+    assert np.array_equal(t_g.len[..., 0], np.array(res_o.n_i8)) and np.array_equal(t_g.len[..., 1], np.array(res_o.n_bf))
 
 
 @pytest.mark.parametrize("name,gs", [("tiny", 0), ("llama8b", 0), ("ragged", 0), ("tiered", 0), ("radix", 0),
@@ -155,8 +163,9 @@ def test_randomised_small_cases_bit_exact():
         chunk_i8 = qb * rnd.randint(1, 3)
         lpt = rnd.random() < 0.5
         gs = rnd.choice([0, 1, 2, 3, 16, 32])
-        grp = {"group_size": gs} if use_share else {}
-        need_bf, need_i8 = P.pages_needed(res_o, ps, qb, *sh_o)
+        gen = 0 if use_share else rnd.choice([0, 0, 1, 70, 300])
+        grp = {"group_size": gs} if use_share else {"gen_tokens": gen}
+        need_bf, need_i8 = P.pages_needed(P.capacity(res_o, gen), ps, qb, *sh_o)
         cap_bf = [n + rnd.randint(-1, 2) for n in need_bf]
         cap_i8 = [n + rnd.randint(-1, 2) for n in need_i8]
         cap_bf = [max(0, x) for x in cap_bf]
@@ -168,13 +177,14 @@ def test_randomised_small_cases_bit_exact():
         except P.OracleError as e:
             assert e.code == "ENOMEM"
             with pytest.raises(tg.TGError) as ge:
-                tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt, gs)
+                tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt, gs, gen)
             assert ge.value.name == "TG_ENOMEM"
             for c in range(C):
                 for t in range(2):
                     assert pool_g.free_pages(c, t) == pool_g.capacity(c, t)
             continue
-        t_g = tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt, gs)
+        t_g = tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt, gs, gen)
+        assert np.array_equal(t_g.ring, np.array(t_o.ring, dtype=np.int32)), case
         for c in range(C):
             for t in range(2):
                 if t_o.stride[c][t]:
@@ -205,4 +215,15 @@ def test_error_codes():
     assert e.value.name == "TG_EINVAL"
     with pytest.raises(tg.TGError) as e:
         tg.tg_size_tables(res, 16, 64, None, group_size=33)
+    assert e.value.name == "TG_EINVAL"
+    with pytest.raises(tg.TGError) as e:
+        tg.tg_size_tables(res, 16, 64, None, gen_tokens=-1)
+    assert e.value.name == "TG_EINVAL"
+    # growth is not combined with shared pages
+    wr = make_workload("radix", B=3, share=dict(prefix=40, branch=10, n_branches=2, suffix=(5, 30)))
+    rr = tg.tg_reserve(wr.head_rank, wr.ratio_hi_ppm, wr.ratio_lo_ppm, wr.n_clusters, wr.recent_ppm,
+                       wr.quant_block, wr.n_comp, wr.n_fixed, wr.budget_override)
+    n_nodes, ids, node_len = share_arrays(wr)
+    with pytest.raises(tg.TGError) as e:
+        tg.tg_size_tables(rr, 16, 64, tg.Share(n_nodes, ids, node_len), gen_tokens=8)
     assert e.value.name == "TG_EINVAL"

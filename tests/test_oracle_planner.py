@@ -6,6 +6,8 @@ import json
 import os
 import random
 
+import numpy as np
+
 import pytest
 
 from oracle import planner as P
@@ -353,3 +355,83 @@ def test_group_invariants(gs, recent_ppm):
         _group_check(w, res, t, gs)
         n_group = sum(1 for it in t.work if it[0] < 0)
         assert n_group == len(t.gitems) and (n_group > 0) == (gs > 1)
+
+
+# ---------------------------------------------------------------- decode-step growth (R-step)
+def _n_bf_closed(L, rho, qb):
+    """bf16 rows at length L written out: the recent share plus what is left
+    of the older rows after whole blocks."""
+    recent = -(-L * rho // 10**6)
+    return recent + (L - recent) % qb
+
+
+@pytest.mark.parametrize("rho,qb", [(125_000, 64), (300_000, 64), (10**6, 64), (0, 64), (500_000, 4), (1, 16)])
+def test_append_steps_follow_the_tier_split(rho, qb):
+    rnd = random.Random(rho + qb)
+    for _ in range(40):
+        L0, T = rnd.randint(1, 3000), rnd.randint(0, 400)
+        i8, bf = P.tier_split(L0, rho, qb)
+        aged = 0
+        for k in range(1, T + 1):
+            i8, bf, a = P.append_step(i8, bf, rho, qb)
+            aged += a
+            assert (i8, bf) == P.tier_split(L0 + k, rho, qb)
+            assert bf == _n_bf_closed(L0 + k, rho, qb) and i8 % qb == 0
+        assert aged * qb == i8 - P.tier_split(L0, rho, qb)[0]
+
+
+def test_capacity_is_the_largest_split_on_the_way():
+    res = P.reserve([0, 1, 2], 900_000, 300_000, 2, 125_000, 64, [700, 5000, 131], [17, 0, 3000])
+    for T in (0, 1, 63, 64, 65, 1000):
+        cap = P.capacity(res, T)
+        for r in range(3):
+            for h in range(3):
+                L0 = res.L[r][h]
+                assert cap.n_i8[r][h] == P.tier_split(L0 + T, 125_000, 64)[0]
+                assert cap.n_bf[r][h] == max(_n_bf_closed(L, 125_000, 64) for L in range(L0, L0 + T + 1))
+
+
+def test_incremental_blocks_equal_blocks_of_the_whole_sequence():
+    """Quantising the oldest bf16 rows block by block as they age gives the
+    same INT8 codes and scales as quantising the grown sequence at once."""
+    from oracle import quant as Q
+    rng = np.random.default_rng(5)
+    qb, rho = 64, 125_000
+    L0, T = 900, 700
+    x = (rng.standard_normal((L0 + T, 16)) * 3).astype(np.float32)
+    i8, bf = P.tier_split(L0, rho, qb)
+    blocks = [Q.quantize_block(x[b * qb:(b + 1) * qb]) for b in range(i8 // qb)]
+    for k in range(T):
+        i8n, bf, aged = P.append_step(i8, bf, rho, qb)
+        if aged:
+            blocks.append(Q.quantize_block(x[i8:i8 + qb]))  # the oldest bf16 rows
+        i8 = i8n
+    qa, sa = Q.quantize_rows(x[:i8], qb)
+    assert len(blocks) == i8 // qb
+    assert np.array_equal(np.concatenate([b[0] for b in blocks]), qa)
+    assert np.array_equal(np.stack([b[1] for b in blocks]), sa)
+
+
+def test_growth_tables_cover_capacity_and_keep_live_lengths():
+    w = make_workload("tiered", B=2, ctx=("fixed", 3000))
+    res = P.reserve(w.head_rank, w.ratio_hi_ppm, w.ratio_lo_ppm, w.n_clusters, w.recent_ppm,
+                    w.quant_block, w.n_comp, w.n_fixed, w.budget_override)
+    T = 500
+    cap = P.capacity(res, T)
+    need_bf, need_i8 = P.pages_needed(cap, w.page_size, w.quant_block)
+    pool = P.Pool(need_bf, need_i8)
+    t = P.build_tables(pool, res, w.page_size, w.quant_block, 256, 512, True, gen_tokens=T)
+    for r in range(w.B):
+        for h in range(w.Hkv):
+            assert t.lens[r][h] == (res.n_i8[r][h], res.n_bf[r][h])
+            assert t.ring[r][0] * w.page_size >= cap.n_bf[r][h]
+    seen = {}
+    for (r, h, tier, t0, t1, slot) in t.work:
+        seen.setdefault((r, h, tier), []).append((t0, t1))
+    for r in range(w.B):
+        for h in range(w.Hkv):
+            for tier, n in ((0, cap.n_i8[r][h]), (1, cap.n_bf[r][h])):
+                assert sorted(seen[(r, h, tier)])[-1][1] == n
+    with pytest.raises(P.OracleError):
+        P.build_tables(P.Pool([100], [0]), res, w.page_size, w.quant_block, 256, 512, True,
+                       [0, 0], [[0], [0]], [0], gen_tokens=T)
