@@ -78,6 +78,54 @@ def _traffic_record(config: str):
         return None
 
 
+def append_bench(w, args, evict, stream):
+    """Decode steps that each append one row per (r, h) first (tg_append_kv,
+    with the ageing of the oldest bf16 block into INT8 where the tier split
+    moves), on a cache built with room for them; the append and the decode
+    are timed separately with HIP events."""
+    import numpy as np
+    import torch
+
+    from non_uniform_paged_amd.runner import Prepared
+
+    K = args.append_steps
+    gp = Prepared(w, chunk_bf=args.chunk_bf, chunk_i8=args.chunk_i8, gen_tokens=K)
+    lens0 = gp.live_lengths().copy()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for k in range(K):
+        evict(k)
+        ev[k][0].record(stream)
+        gp.append(stream=stream)
+        ev[k][1].record(stream)
+        gp.step(stream=stream)
+        ev[k][2].record(stream)
+    torch.cuda.synchronize()
+    app_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    lens = gp.live_lengths()
+    L0 = lens0.sum(-1)
+    # the tier split of the grown lengths (INT8: whole blocks of the rows older
+    # than the recent share)
+    Lk = L0 + K
+    n_i8 = (Lk - (Lk * w.recent_ppm + 999_999) // 1_000_000) // w.quant_block * w.quant_block
+    expect = np.stack([n_i8, Lk - n_i8], -1)
+    d = w.d
+    aged = int((lens[..., 0] - lens0[..., 0]).sum()) // w.quant_block
+    # algorithmic bytes: each new row written (K and V, bf16), and per aged
+    # block its bf16 rows read and its codes and scales written
+    nbytes = K * w.B * w.Hkv * 4 * d + aged * (w.quant_block * 4 * d + w.quant_block * 2 * d + 4 * d)
+    out = {"steps": K, "append_us_mean": round(float(app_ms.mean()) * 1e3, 2),
+           "append_us_median": round(float(np.median(app_ms)) * 1e3, 2),
+           "decode_us_mean_after_append": round(float(dec_ms.mean()) * 1e3, 2),
+           "aged_blocks": aged, "append_bytes": nbytes,
+           "append_GBps": round(nbytes / (app_ms.sum() * 1e-3) / 1e9, 2),
+           "lengths_match_tier_split": bool(np.array_equal(lens, expect)),
+           "capacity_flag": int(gp.status.item())}
+    del gp
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, prep, budget_s: float = 12.0):
     """The oracle, untuned, on this host: fp64 attention of sampled (r, h)
     pairs from their raw rows (row generation excluded from the time)."""
@@ -129,6 +177,8 @@ def main():
     ap.add_argument("--chunk-bf", type=int, default=None, help="bf16 rows per plan item (default per workload)")
     ap.add_argument("--chunk-i8", type=int, default=None, help="INT8 rows per plan item (default per workload)")
     ap.add_argument("--flush", choices=["read", "write", "none"], default="read")
+    ap.add_argument("--append-steps", type=int, default=128,
+                    help="decode steps with tg_append_kv timed on a second cache built for growth (0: skip)")
     ap.add_argument("--group-size", type=int, default=None,
                     help="requests per shared-prefix group item (default 16 / G when pages are shared)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -302,6 +352,8 @@ def main():
             "algorithmic_bytes_per_launch": split_bytes,
         },
     }
+    if args.append_steps > 0 and w.paths is None:
+        result["append"] = append_bench(w, args, evict, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, prep)
     print(json.dumps(result), flush=True)
