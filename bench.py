@@ -126,6 +126,54 @@ def append_bench(w, args, evict, stream):
     return out
 
 
+def host_tier_bench(prep, args, stream, resident_ms):
+    """The same decode step with the INT8 pages in pinned host memory,
+    streamed per request through two HBM staging slots (tg_decode_streamed):
+    step time, INT8 bytes crossing to the device per step, their rate, the
+    plain host-to-device copy rate of the same bytes, the step's rate as a
+    fraction of it, and the time the step spends beyond the copies alone
+    (the compute the pipeline does not hide)."""
+    import numpy as np
+    import torch
+
+    resident_out = prep.output().copy()
+    prep.to_host_i8()
+    nbytes = prep.host_i8_bytes()
+    # plain copy rate: every host pool to a device buffer once, pinned source
+    dst = torch.empty(max(hp.numel() for hp in prep.host_pools), dtype=torch.uint8, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for hp in prep.host_pools:
+        dst[:hp.numel()].copy_(hp, non_blocking=True)
+    e0.record(stream)
+    for hp in prep.host_pools:
+        dst[:hp.numel()].copy_(hp, non_blocking=True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    pool_bytes = sum(hp.numel() for hp in prep.host_pools)
+    copy_gbps = pool_bytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del dst
+    prep.step_streamed(stream=stream)
+    torch.cuda.synchronize()
+    identical = bool(np.array_equal(prep.output(), resident_out))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.host_steps)]
+    for k in range(args.host_steps):
+        ev[k][0].record(stream)
+        prep.step_streamed(stream=stream)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    step_ms = float(np.median(ms))
+    copy_ms = nbytes / (copy_gbps * 1e9) * 1e3
+    return {"steps": args.host_steps, "step_ms_median": round(step_ms, 4),
+            "int8_bytes_to_device_per_step": nbytes,
+            "int8_GBps": round(nbytes / (step_ms * 1e-3) / 1e9, 2),
+            "plain_h2d_copy_GBps": round(copy_gbps, 2),
+            "copy_only_ms": round(copy_ms, 4), "resident_step_ms": round(resident_ms, 4),
+            "fraction_of_copy_rate": round(copy_ms / step_ms, 4),
+            "exposed_ms_beyond_copy": round(step_ms - copy_ms, 4),
+            "bit_identical_to_resident": identical}
+
+
 def cpu_baseline(w, prep, budget_s: float = 12.0):
     """The oracle, untuned, on this host: fp64 attention of sampled (r, h)
     pairs from their raw rows (row generation excluded from the time)."""
@@ -179,6 +227,8 @@ def main():
     ap.add_argument("--flush", choices=["read", "write", "none"], default="read")
     ap.add_argument("--append-steps", type=int, default=128,
                     help="decode steps with tg_append_kv timed on a second cache built for growth (0: skip)")
+    ap.add_argument("--host-steps", type=int, default=10,
+                    help="decode steps with the INT8 tier in pinned host memory, streamed (0: skip)")
     ap.add_argument("--group-size", type=int, default=None,
                     help="requests per shared-prefix group item (default 16 / G when pages are shared)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -356,6 +406,8 @@ def main():
         result["append"] = append_bench(w, args, evict, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, prep)
+    if args.host_steps > 0 and prep.tables.stride_has_i8:
+        result["host_tier"] = host_tier_bench(prep, args, stream, med)
     print(json.dumps(result), flush=True)
 
 

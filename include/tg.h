@@ -375,6 +375,37 @@ int tg_merge_partials(const float* workspace, int32_t n_slots, int32_t n_pairs, 
                       int32_t d, const int32_t* part_off, float* out, void* stream);
 
 /* ------------------------------------------------------------------------
+ * INT8 tier in host DRAM, streamed per step  (host orchestration + device)
+ *
+ * TTKV page, "Tier Layout" (the slow tier sits in DRAM) and its block-wise
+ * streaming of the slow tier: cache->pool[c][TG_TIER_I8] are host pointers
+ * to pinned memory (e.g. hipHostMalloc) holding the INT8 pages; everything
+ * else is as for tg_decode_attn.  Per call, the bf16 items run first on
+ * `stream`; then, request by request, the INT8 pages of request r are copied
+ * (hipMemcpyAsync on the library's own copy stream, one copy per run of
+ * consecutive page ids) into staging slot r mod 2 while the kernels of
+ * request r - 1 run, and the INT8 items of r run on `stream` once their copy
+ * is done; the merge follows.  The results are those of tg_decode_attn bit
+ * for bit.
+ *
+ *   tables     host tables of the cache (the INT8 block table rows name the
+ *              pages to copy)
+ *   args.work  the plan reordered by tg_stream_order (device copy);
+ *   chunk_off  host [B + 1] from tg_stream_order
+ *   staging    device, 256-byte aligned, >= tg_stream_staging_bytes bytes
+ * Calls must not overlap in time (one copy stream per process).  Errors as
+ * tg_decode_attn; TG_EINVAL on a bad chunk_off or staging size. */
+size_t tg_stream_staging_bytes(const tg_cache* cache, const tg_tables* tables);
+int tg_decode_streamed(const tg_cache* cache, const tg_tables* tables, const tg_decode_args* args,
+                       const int32_t* chunk_off, void* staging, size_t staging_bytes, void* stream);
+/* Plan order for tg_decode_streamed (host): bf16 and group items first, in
+ * plan order, then the INT8 items of request 0, 1, ... (plan order within a
+ * request).  work_out [n_items*6]; chunk_off [B + 1]: chunk_off[0] = number
+ * of bf16 items, request r's INT8 items are [chunk_off[r], chunk_off[r+1]).
+ * TG_EINVAL on a malformed plan. */
+int tg_stream_order(const tg_tables* tables, int32_t B, int32_t* work_out, int32_t* chunk_off);
+
+/* ------------------------------------------------------------------------
  * Measurement aid  (device)
  *
  * Streaming read of `bytes` (a multiple of 16) at `src` (16-byte aligned

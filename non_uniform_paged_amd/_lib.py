@@ -108,6 +108,10 @@ SIGNATURES = {
                                          c_void_p, c_void_p]),
     "tg_bench_read": (ctypes.c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
     "tg_append_kv": (ctypes.c_int, [POINTER(Cache), c_void_p, c_void_p, c_void_p]),
+    "tg_stream_staging_bytes": (c_size_t, [POINTER(Cache), POINTER(Tables)]),
+    "tg_decode_streamed": (ctypes.c_int, [POINTER(Cache), POINTER(Tables), POINTER(DecodeArgs), P32, c_void_p,
+                                          c_size_t, c_void_p]),
+    "tg_stream_order": (ctypes.c_int, [POINTER(Tables), c_int32, P32, P32]),
 }
 
 _LIB = None

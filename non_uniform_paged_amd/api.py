@@ -20,6 +20,7 @@ __all__ = [
     "tg_reserve", "tg_size_tables", "tg_build_tables", "tg_release",
     "tg_write_kv", "tg_decode_workspace_bytes", "tg_decode_attn", "tg_decode_split",
     "tg_merge_partials", "tg_bench_read", "TG_BENCH_READ_BLOCKS", "tg_append_kv",
+    "tg_stream_order", "tg_stream_staging_bytes", "tg_decode_streamed",
 ]
 
 
@@ -291,7 +292,7 @@ def tg_write_kv(cache: DeviceCache, rows, index, offsets, stream=None) -> None:
                             _stream_ptr(stream)), "tg_write_kv")
 
 
-def _decode_args(cache, q, out, workspace, n_q_heads, sm_scale):
+def _decode_args(cache, q, out, workspace, n_q_heads, sm_scale, work=None):
     torch = _torch()
     if q.dtype == torch.float32:
         qd = TG_Q_F32
@@ -303,7 +304,7 @@ def _decode_args(cache, q, out, workspace, n_q_heads, sm_scale):
     a.n_q_heads = int(n_q_heads)
     a.q_dtype = qd
     a.q = _ptr(q)
-    a.work = _ptr(cache.work)
+    a.work = _ptr(cache.work if work is None else work)
     a.n_items = int(cache.n_items)
     a.part_off = _ptr(cache.part_off)
     a.gitems = _ptr(cache.gitems)
@@ -358,3 +359,28 @@ def tg_append_kv(cache: DeviceCache, rows, status=None, stream=None) -> None:
     reserved capacity."""
     check(lib().tg_append_kv(ctypes.byref(cache.struct), _ptr(rows), _ptr(status), _stream_ptr(stream)),
           "tg_append_kv")
+
+
+def tg_stream_order(tables: Tables):
+    """(work [n_items][6] int32, chunk_off [B+1] int32): the plan reordered
+    for tg_decode_streamed."""
+    work = np.zeros((max(tables.n_items, 1), 6), np.int32)
+    off = np.zeros(tables.B + 1, np.int32)
+    check(lib().tg_stream_order(ctypes.byref(tables.struct), tables.B, _p32(work), _p32(off)), "tg_stream_order")
+    return work[:tables.n_items], off
+
+
+def tg_stream_staging_bytes(cache: DeviceCache, tables: Tables) -> int:
+    return int(lib().tg_stream_staging_bytes(ctypes.byref(cache.struct), ctypes.byref(tables.struct)))
+
+
+def tg_decode_streamed(cache: DeviceCache, tables: Tables, q, out, workspace, n_q_heads: int, work, chunk_off,
+                       staging, sm_scale: float = 0.0, stream=None) -> None:
+    """Decode step with the INT8 pages in pinned host memory (the cache's
+    INT8 pool pointers), streamed through ``staging``; ``work`` is the device
+    copy of ``tg_stream_order``'s plan, ``chunk_off`` its host offsets."""
+    a = _decode_args(cache, q, out, workspace, n_q_heads, sm_scale, work=work)
+    off = np.ascontiguousarray(chunk_off, dtype=np.int32)
+    check(lib().tg_decode_streamed(ctypes.byref(cache.struct), ctypes.byref(tables.struct), ctypes.byref(a),
+                                   _p32(off), _ptr(staging), int(staging.numel() * staging.element_size()),
+                                   _stream_ptr(stream)), "tg_decode_streamed")

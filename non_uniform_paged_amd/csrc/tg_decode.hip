@@ -9,7 +9,9 @@
 // writes o in fp32.  tg_decode_attn is the two in sequence.
 
 #include <cmath>
+#include <algorithm>
 #include <cstdint>
+#include <vector>
 
 #include "tg_device.h"
 
@@ -177,7 +179,8 @@ extern "C" int tg_merge_partials(const float* workspace, int32_t n_slots, int32_
 
 namespace {
 
-int decode_split(const tg_cache* c, const tg_decode_args* a, void* stream, bool merge) {
+// Validates a decode call and fills the split-kernel arguments.
+int make_split_args(const tg_cache* c, const tg_decode_args* a, bool merge, SplitArgs* out, int32_t* G_out) {
   if (!c || !a) return TG_EINVAL;
   if (c->B < 1 || c->n_kv_heads < 1 || c->n_clusters < 1 || c->n_clusters > TG_MAX_CLUSTERS)
     return TG_EINVAL;
@@ -201,7 +204,9 @@ int decode_split(const tg_cache* c, const tg_decode_args* a, void* stream, bool 
       if (c->page_bytes[cl][t] > INT32_MAX) return TG_EUNSUPPORTED;
       if (reinterpret_cast<uintptr_t>(c->pool[cl][t]) % 16) return TG_EINVAL;
     }
-  SplitArgs s{};
+  if (c->ring != nullptr && c->bf_base == nullptr) return TG_EINVAL;
+  SplitArgs& s = *out;
+  s = SplitArgs{};
   for (int32_t cl = 0; cl < c->n_clusters; ++cl)
     for (int t = 0; t < 2; ++t) {
       s.pool[cl][t] = (gptr)(c->pool[cl][t]);
@@ -213,7 +218,6 @@ int decode_split(const tg_cache* c, const tg_decode_args* a, void* stream, bool 
   s.ring = (const TG_GLOBAL int32_t*)(c->ring);
   s.bf_base = (const TG_GLOBAL int32_t*)(c->bf_base);
   s.n_clusters = c->n_clusters;
-  if (c->ring != nullptr && c->bf_base == nullptr) return TG_EINVAL;
   s.n_fixed = (const TG_GLOBAL int32_t*)(c->n_fixed);
   s.n_kv_heads = c->n_kv_heads;
   s.cluster_of_head = (const TG_GLOBAL int32_t*)(c->cluster_of_head);
@@ -228,6 +232,16 @@ int decode_split(const tg_cache* c, const tg_decode_args* a, void* stream, bool 
   s.n_q_heads = a->n_q_heads;
   const float scale = a->sm_scale != 0.f ? a->sm_scale : 1.f / std::sqrt(static_cast<float>(d));
   s.scale_log2 = scale * kLog2e;
+  *G_out = G;
+  return TG_OK;
+}
+
+int decode_split(const tg_cache* c, const tg_decode_args* a, void* stream, bool merge) {
+  SplitArgs s;
+  int32_t G = 0;
+  const int st_code = make_split_args(c, a, merge, &s, &G);
+  if (st_code) return st_code;
+  const int32_t d = c->head_dim;
   hipStream_t st = static_cast<hipStream_t>(stream);
   // one launch over both tiers when the cache has INT8 pages
   bool has_i8 = false;
@@ -239,6 +253,124 @@ int decode_split(const tg_cache* c, const tg_decode_args* a, void* stream, bool 
                    c->B * c->n_kv_heads, G, d, a->out, a->n_slots, st);
   return e == hipSuccess ? TG_OK : TG_EDEVICE;
 }
+
+// ---------------------------------------------------------------- host-DRAM INT8 tier
+// INT8 pages of request r in cluster c: the leading non-negative entries of
+// its host table row.
+int64_t i8_pages_of(const tg_tables* t, int32_t c, int32_t r) {
+  const int32_t stride = t->stride[c][TG_TIER_I8];
+  if (stride == 0) return 0;
+  const int32_t* row = t->bt[c][TG_TIER_I8] + static_cast<int64_t>(r) * stride;
+  int64_t n = 0;
+  while (n < stride && row[n] >= 0) ++n;
+  return n;
+}
+
+// Staging slot layout: per cluster, room for the INT8 pages of the largest
+// request, clusters one after another; two slots.
+size_t slot_layout(const tg_cache* c, const tg_tables* t, size_t* off /*[C]*/) {
+  size_t at = 0;
+  for (int32_t cl = 0; cl < c->n_clusters; ++cl) {
+    int64_t most = 0;
+    for (int32_t r = 0; r < c->B; ++r) most = std::max(most, i8_pages_of(t, cl, r));
+    off[cl] = at;
+    at += static_cast<size_t>(most) * static_cast<size_t>(c->page_bytes[cl][TG_TIER_I8]);
+    at = (at + 255) & ~static_cast<size_t>(255);
+  }
+  return at;
+}
+
+struct StreamState {
+  hipStream_t copy = nullptr;
+  std::vector<hipEvent_t> events;
+};
+
+int stream_state(int32_t n_events, StreamState** out) {
+  static StreamState state;  // one device per process; calls must not overlap
+  if (state.copy == nullptr &&
+      hipStreamCreateWithFlags(&state.copy, hipStreamNonBlocking) != hipSuccess)
+    return TG_EDEVICE;
+  while (static_cast<int32_t>(state.events.size()) < n_events) {
+    hipEvent_t e;
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return TG_EDEVICE;
+    state.events.push_back(e);
+  }
+  *out = &state;
+  return TG_OK;
+}
+
+}  // namespace
+
+extern "C" size_t tg_stream_staging_bytes(const tg_cache* c, const tg_tables* t) {
+  if (!c || !t || c->n_clusters < 1 || c->n_clusters > TG_MAX_CLUSTERS) return 0;
+  size_t off[TG_MAX_CLUSTERS];
+  return 2 * slot_layout(c, t, off);
+}
+
+extern "C" int tg_decode_streamed(const tg_cache* c, const tg_tables* t, const tg_decode_args* a,
+                                  const int32_t* chunk_off, void* staging, size_t staging_bytes,
+                                  void* stream) {
+  SplitArgs s;
+  int32_t G = 0;
+  int code = make_split_args(c, a, true, &s, &G);
+  if (code) return code;
+  if (!t || !chunk_off || !staging) return TG_EINVAL;
+  const int32_t B = c->B, d = c->head_dim;
+  if (chunk_off[0] < 0 || chunk_off[B] != a->n_items) return TG_EINVAL;
+  for (int32_t r = 0; r < B; ++r)
+    if (chunk_off[r + 1] < chunk_off[r]) return TG_EINVAL;
+  size_t off[TG_MAX_CLUSTERS];
+  const size_t slot_bytes = slot_layout(c, t, off);
+  if (staging_bytes < 2 * slot_bytes || reinterpret_cast<uintptr_t>(staging) % 256) return TG_EINVAL;
+  StreamState* ss = nullptr;
+  if ((code = stream_state(2 * B + 1, &ss))) return code;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipEvent_t ev_start = ss->events[2 * B];
+  const bool qf32 = a->q_dtype == TG_Q_F32;
+  // the staging slots are free once earlier work on the compute stream is done
+  if (hipEventRecord(ev_start, st) != hipSuccess || hipStreamWaitEvent(ss->copy, ev_start, 0) != hipSuccess)
+    return TG_EDEVICE;
+  // bf16 items (HBM-resident pages) first: they run while the first pages cross
+  SplitArgs sb = s;
+  sb.n_items = chunk_off[0];
+  if (launch_split(sb, d, G, qf32, false, st) != hipSuccess) return TG_EDEVICE;
+  char* stage = static_cast<char*>(staging);
+  for (int32_t r = 0; r < B; ++r) {
+    char* slot = stage + (r % 2) * slot_bytes;
+    hipEvent_t copied = ss->events[2 * r], done = ss->events[2 * r + 1];
+    if (r >= 2 && hipStreamWaitEvent(ss->copy, ss->events[2 * (r - 2) + 1], 0) != hipSuccess) return TG_EDEVICE;
+    for (int32_t cl = 0; cl < c->n_clusters; ++cl) {
+      const int64_t n = i8_pages_of(t, cl, r);
+      const int32_t* row = t->bt[cl][TG_TIER_I8] + static_cast<int64_t>(r) * t->stride[cl][TG_TIER_I8];
+      const size_t pb = static_cast<size_t>(c->page_bytes[cl][TG_TIER_I8]);
+      const char* host = static_cast<const char*>(c->pool[cl][TG_TIER_I8]);
+      for (int64_t j0 = 0; j0 < n;) {  // one copy per run of consecutive page ids
+        int64_t j1 = j0 + 1;
+        while (j1 < n && row[j1] == row[j1 - 1] + 1) ++j1;
+        if (hipMemcpyAsync(slot + off[cl] + j0 * pb, host + static_cast<size_t>(row[j0]) * pb, (j1 - j0) * pb,
+                           hipMemcpyHostToDevice, ss->copy) != hipSuccess)
+          return TG_EDEVICE;
+        j0 = j1;
+      }
+    }
+    if (hipEventRecord(copied, ss->copy) != hipSuccess || hipStreamWaitEvent(st, copied, 0) != hipSuccess)
+      return TG_EDEVICE;
+    SplitArgs sr = s;
+    for (int32_t cl = 0; cl < c->n_clusters; ++cl) {
+      sr.pool[cl][TG_TIER_I8] = (gptr)(slot + off[cl]);
+      sr.bt[cl][TG_TIER_I8] = nullptr;  // block j of the request is staged page j
+    }
+    sr.work = s.work + static_cast<int64_t>(chunk_off[r]) * 6;
+    sr.n_items = chunk_off[r + 1] - chunk_off[r];
+    if (launch_split(sr, d, G, qf32, true, st) != hipSuccess) return TG_EDEVICE;
+    if (hipEventRecord(done, st) != hipSuccess) return TG_EDEVICE;
+  }
+  const hipError_t e = launch_merge(a->workspace, a->workspace + static_cast<int64_t>(a->n_slots) * G * d,
+                                    a->part_off, B * c->n_kv_heads, G, d, a->out, a->n_slots, st);
+  return e == hipSuccess ? TG_OK : TG_EDEVICE;
+}
+
+namespace {
 
 }  // namespace
 

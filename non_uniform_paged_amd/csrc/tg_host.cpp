@@ -762,6 +762,31 @@ extern "C" int tg_build_tables(tg_pool* pool, const tg_reservation* live, const 
   return TG_OK;
 }
 
+extern "C" int tg_stream_order(const tg_tables* t, int32_t B, int32_t* work_out, int32_t* chunk_off) {
+  if (!t || B < 1 || !chunk_off || (t->n_items > 0 && (!t->work || !work_out))) return TG_EINVAL;
+  std::vector<int32_t> count(B, 0);
+  int32_t n_bf = 0;
+  for (int32_t k = 0; k < t->n_items; ++k) {
+    const int32_t* w = t->work + int64_t(k) * 6;
+    if (w[2] == TG_TIER_I8) {
+      if (w[0] < 0 || w[0] >= B) return TG_EINVAL;
+      ++count[w[0]];
+    } else {
+      ++n_bf;
+    }
+  }
+  chunk_off[0] = n_bf;
+  for (int32_t r = 0; r < B; ++r) chunk_off[r + 1] = chunk_off[r] + count[r];
+  std::vector<int32_t> at(chunk_off, chunk_off + B);
+  int32_t nb = 0;
+  for (int32_t k = 0; k < t->n_items; ++k) {
+    const int32_t* w = t->work + int64_t(k) * 6;
+    const int32_t dst = w[2] == TG_TIER_I8 ? at[w[0]]++ : nb++;
+    std::memcpy(work_out + int64_t(dst) * 6, w, 6 * sizeof(int32_t));
+  }
+  return TG_OK;
+}
+
 extern "C" int tg_release(tg_pool* pool, tg_tables* t, int32_t r) {
   if (!pool || !t || !t->released || r < 0) return TG_EINVAL;
   // B is implicit in the tables; the caller guarantees r < B.

@@ -105,7 +105,8 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
 
   for (int w0 = 0; w0 < nb; w0 += 64) {
     const int nw = min(64, nb - w0);
-    const int pid_lane = bt_row[b0 + w0 + min(lane, nw - 1)];
+    const int jb = b0 + w0 + min(lane, nw - 1);
+    const int pid_lane = bt_row != nullptr ? bt_row[jb] : jb;  // no table: block j is page j
     auto blk_ptr = [&](int b) {
       const int pid = __builtin_amdgcn_readlane(pid_lane, min(b, nw - 1));
       return pool + static_cast<int64_t>(pid) * pbytes + head_off;
@@ -268,7 +269,9 @@ __device__ __forceinline__ void i8_dispatch(const SplitArgs& a, const TG_GLOBAL 
   }
   const int cl = uniform(a.cluster_of_head[h]);
   const int hs = uniform(a.slot_in_cluster[h]);
-  const TG_GLOBAL int32_t* bt_row = a.bt[cl][TG_TIER_I8] + static_cast<int64_t>(r) * a.stride[cl][TG_TIER_I8];
+  const TG_GLOBAL int32_t* bt_row =
+      a.bt[cl][TG_TIER_I8] != nullptr ? a.bt[cl][TG_TIER_I8] + static_cast<int64_t>(r) * a.stride[cl][TG_TIER_I8]
+                                      : nullptr;
   gptr pool = a.pool[cl][TG_TIER_I8];
   const int64_t pbytes = a.page_bytes[cl][TG_TIER_I8];
   bool shared = false;  // an item that starts on the shared radix path reads through the caches

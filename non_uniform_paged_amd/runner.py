@@ -97,7 +97,46 @@ class Prepared:
 
     # ------------------------------------------------------------------ run
     def step(self, stream=None):
+        if getattr(self, "host_i8", False):
+            raise RuntimeError("the INT8 pages are in host memory: use step_streamed")
         api.tg_decode_attn(self.cache, self.q, self.out, self.workspace, self.w.Hq, 0.0, stream=stream)
+
+    # ------------------------------------------------------------------ INT8 tier in host DRAM
+    def to_host_i8(self):
+        """Move the INT8 pools to pinned host memory and prepare the streamed
+        decode (its reordered plan on the device and its staging buffer);
+        afterwards only ``step_streamed`` decodes."""
+        import torch
+        dev = self.cache.device
+        self.host_pools = []
+        for c in range(self.res.C):
+            dp = self.cache.pools[c][0]
+            if dp is None:
+                continue
+            hp = torch.empty(dp.numel(), dtype=torch.uint8, pin_memory=True)
+            hp.copy_(dp)
+            self.host_pools.append(hp)
+            self.cache.struct.pool[c][0] = hp.data_ptr()
+            self.cache.pools[c][0] = None
+        torch.cuda.synchronize(dev)
+        work, self.chunk_off = api.tg_stream_order(self.tables)
+        self.stream_work = torch.from_numpy(np.ascontiguousarray(work)).to(dev)
+        nbytes = api.tg_stream_staging_bytes(self.cache, self.tables)
+        self.staging = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        self.host_i8 = True
+
+    def step_streamed(self, stream=None):
+        api.tg_decode_streamed(self.cache, self.tables, self.q, self.out, self.workspace, self.w.Hq,
+                               self.stream_work, self.chunk_off, self.staging, stream=stream)
+
+    def host_i8_bytes(self) -> int:
+        """INT8 page bytes one streamed step copies to the device."""
+        t = self.tables
+        n = 0
+        for c in range(self.res.C):
+            if t.stride[c][0]:
+                n += int((t.bt[c][0] >= 0).sum()) * self.pool.page_bytes(c, 0)
+        return n
 
     def append(self, stream=None):
         """Append the next staged row to every (r, h) (tg_append_kv)."""
