@@ -200,7 +200,8 @@ def cpu_baseline(w, prep, budget_s: float = 12.0):
             r, h = divmod(int(i), w.Hkv)
             K16, V16 = w.logical_kv(r, h, res.L[r][h])
             t0 = time.perf_counter()
-            o = A.decode_rows(q[r, h * G:(h + 1) * G], K16, V16, res.n_i8[r][h], w.quant_block, scale)
+            o = A.decode_rows(q[r, h * G:(h + 1) * G], K16, V16, res.n_i8[r][h], w.quant_block, scale,
+                              w.old_bits)
             spent += time.perf_counter() - t0
             n8, nb = res.n_i8[r][h], res.n_bf[r][h]
             nbytes += nb * 4 * w.d + n8 * 2 * w.d + (n8 // w.quant_block) * 4 * w.d

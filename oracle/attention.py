@@ -87,14 +87,14 @@ def q_f64(w) -> np.ndarray:
     return np.asarray(q, np.float64) if w.q_dtype == "f32" else bf16_to_f64(q)
 
 
-def rows_f64(K16: np.ndarray, V16: np.ndarray, n_i8: int, qb: int) -> Tuple[np.ndarray, np.ndarray]:
+def rows_f64(K16: np.ndarray, V16: np.ndarray, n_i8: int, qb: int, bits: int = 8) -> Tuple[np.ndarray, np.ndarray]:
     """fp64 K, V a sequence attends over: its bf16 rows, with the oldest
-    ``n_i8`` rows replaced by their INT8 dequantised values."""
+    ``n_i8`` rows replaced by their ``bits``-bit (8 or 4) dequantised values."""
     K = bf16_to_f64(K16)
     V = bf16_to_f64(V16)
     if n_i8:
-        qk, sk = quant.quantize_rows(K[:n_i8].astype(np.float32), qb)
-        qv, sv = quant.quantize_rows(V[:n_i8].astype(np.float32), qb)
+        qk, sk = quant.quantize_rows(K[:n_i8].astype(np.float32), qb, bits)
+        qv, sv = quant.quantize_rows(V[:n_i8].astype(np.float32), qb, bits)
         K[:n_i8] = quant.dequantize_rows(qk, sk, qb)
         V[:n_i8] = quant.dequantize_rows(qv, sv, qb)
     return K, V
@@ -103,13 +103,13 @@ def rows_f64(K16: np.ndarray, V16: np.ndarray, n_i8: int, qb: int) -> Tuple[np.n
 def head_rows(w, res: planner.Reservation, r: int, h: int) -> Tuple[np.ndarray, np.ndarray]:
     """fp64 K, V rows of (r, h) (see ``rows_f64``)."""
     K16, V16 = w.logical_kv(r, h, res.L[r][h])
-    return rows_f64(K16, V16, res.n_i8[r][h], w.quant_block)
+    return rows_f64(K16, V16, res.n_i8[r][h], w.quant_block, getattr(w, "old_bits", 8))
 
 
 def decode_rows(q_group: np.ndarray, K16: np.ndarray, V16: np.ndarray, n_i8: int, qb: int,
-                scale: float) -> np.ndarray:
+                scale: float, bits: int = 8) -> np.ndarray:
     """Outputs [G][d] of one GQA group from its raw rows (bf16 bits)."""
-    K, V = rows_f64(K16, V16, n_i8, qb)
+    K, V = rows_f64(K16, V16, n_i8, qb, bits)
     return attend(q_group, K, V, scale)
 
 
@@ -122,7 +122,8 @@ def decode_pair(w, res: planner.Reservation, r: int, h: int, q: Optional[np.ndar
     if scale is None:
         scale = 1.0 / math.sqrt(w.d)
     K16, V16 = w.logical_kv(r, h, res.L[r][h])
-    return decode_rows(q[r, h * G:(h + 1) * G], K16, V16, res.n_i8[r][h], w.quant_block, scale)
+    return decode_rows(q[r, h * G:(h + 1) * G], K16, V16, res.n_i8[r][h], w.quant_block, scale,
+                       getattr(w, "old_bits", 8))
 
 
 def decode(w, res: Optional[planner.Reservation] = None,

@@ -1,4 +1,4 @@
-"""Oracle for the slow tier's block-wise INT8 quantiser -- TEST INFRASTRUCTURE.
+"""Oracle for the slow tier's block-wise INT8 / INT4 quantiser -- TEST INFRASTRUCTURE.
 
 TTKV page (arXiv 2604.19769 explainer), "Tier Layout" (slow tier holds older
 KV states at INT8/INT4) and "Tier Interaction" (the slow tier is quantised in
@@ -13,6 +13,8 @@ the design notes) is symmetric absmax per (block, channel):
 
 K and V are quantised separately, each over a block of ``Qb`` consecutive
 logical rows (the oldest rows of a sequence, block k = rows [k*Qb, (k+1)*Qb)).
+The INT4 variant (same page, "INT8/INT4") is the same rule with 7 in place
+of 127: s = fp16_rne(absmax / 7), q4 = clamp(rint(x / s), -7, 7).
 
 The code decision (q8) is taken from fp32 arithmetic, the same precision the
 device kernel uses, so both sides must agree bit for bit.
@@ -28,38 +30,45 @@ import numpy as np
 FP16_MAX = np.float16(65504.0)
 
 
-def block_scale(x: np.ndarray) -> np.ndarray:
+def qmax_of(bits: int) -> int:
+    """Largest code magnitude of a ``bits``-bit symmetric code (127 or 7)."""
+    assert bits in (8, 4)
+    return (1 << (bits - 1)) - 1
+
+
+def block_scale(x: np.ndarray, bits: int = 8) -> np.ndarray:
     """Per-channel fp16 scale of one block ``x`` [Qb][d] (fp32 values)."""
     x = np.asarray(x, dtype=np.float32)
     absmax = np.max(np.abs(x), axis=0)
     with np.errstate(over="ignore"):
-        s = (absmax / np.float32(127.0)).astype(np.float16)
+        s = (absmax / np.float32(qmax_of(bits))).astype(np.float16)
     return np.where(np.isinf(s), FP16_MAX, s).astype(np.float16)
 
 
-def quantize_block(x: np.ndarray):
-    """Quantise one block ``x`` [Qb][d] (fp32 values) -> (q8 int8 [Qb][d], s fp16 [d])."""
+def quantize_block(x: np.ndarray, bits: int = 8):
+    """Quantise one block ``x`` [Qb][d] (fp32 values) -> (codes int8 [Qb][d], s fp16 [d])."""
     x = np.asarray(x, dtype=np.float32)
-    s = block_scale(x)
+    qm = qmax_of(bits)
+    s = block_scale(x, bits)
     sf = s.astype(np.float32)
     pos = sf > 0
     safe = np.where(pos, sf, np.float32(1.0))
     with np.errstate(over="ignore", invalid="ignore"):
         y = np.rint(x / safe)
-    q = np.where(pos, np.clip(y, -127, 127), 0).astype(np.int8)
+    q = np.where(pos, np.clip(y, -qm, qm), 0).astype(np.int8)
     return q, s
 
 
-def quantize_rows(x: np.ndarray, qb: int):
+def quantize_rows(x: np.ndarray, qb: int, bits: int = 8):
     """Quantise rows [n][d] (n a multiple of ``qb``) block by block.
 
-    Returns (q8 [n][d] int8, scales [n/qb][d] fp16)."""
+    Returns (codes [n][d] int8, scales [n/qb][d] fp16)."""
     x = np.asarray(x, dtype=np.float32)
     n = x.shape[0]
     assert n % qb == 0
     qs, ss = [], []
     for k in range(n // qb):
-        q, s = quantize_block(x[k * qb:(k + 1) * qb])
+        q, s = quantize_block(x[k * qb:(k + 1) * qb], bits)
         qs.append(q)
         ss.append(s)
     if not qs:

@@ -160,3 +160,25 @@ def test_gqa_mapping_and_scale_default():
         K16, V16 = w.logical_kv(0, h, 64)
         ref = A.attend(q[0, hq:hq + 1], A.bf16_to_f64(K16), A.bf16_to_f64(V16), 1 / math.sqrt(128))
         assert np.max(np.abs(o[0, hq] - ref[0])) < 1e-14
+
+
+def test_int4_workload_rows_within_half_a_step_and_exact_multiples():
+    w = make_workload("tiered4", B=1, Hkv=2, Hq=4, ctx=("fixed", 1000))
+    assert w.old_bits == 4
+    res = A.reserve_for(w)
+    n8 = res.n_i8[0][0]
+    K, V = A.head_rows(w, res, 0, 0)
+    K16, V16 = w.logical_kv(0, 0, res.L[0][0])
+    Kb, Vb = A.bf16_to_f64(K16), A.bf16_to_f64(V16)
+    assert np.array_equal(K[n8:], Kb[n8:])
+    for X, Xb in ((K, Kb), (V, Vb)):
+        for blk in range(n8 // 64):
+            sl = slice(64 * blk, 64 * blk + 64)
+            step = np.abs(Xb[sl]).max(axis=0) / 7
+            assert np.all(np.abs(X[sl] - Xb[sl]) <= step * (0.5 + 2.0 ** -10) + 1e-30)
+    # rows that are multiples of 2^-3 within +-7 * 2^-3 quantise exactly to 4 bits
+    g = np.random.default_rng(6)
+    k = g.integers(-7, 8, size=(128, 64)); k[0] = 7; k[64] = -7
+    Kx = (k * 2.0 ** -3).astype(np.float32)
+    qk, sk = quant.quantize_rows(Kx, 64, 4)
+    assert np.array_equal(quant.dequantize_rows(qk, sk, 64), Kx.astype(np.float64))

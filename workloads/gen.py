@@ -95,6 +95,11 @@ SPECS: Dict[str, dict] = {
                    ratio_ppm=(1_000_000, 1_000_000), budget=None, n_clusters=1,
                    page_size=16, quant_block=64, q_dtype="bf16", recent_ppm=125_000,
                    rank="seeded", outlier=None, share=None),
+    # The tiered workload with a 4-bit slow tier (same seed, same rows).
+    "tiered4": dict(cfg_id=4, B=4, Hq=32, Hkv=8, d=128, ctx=("fixed", 131072),
+                    ratio_ppm=(1_000_000, 1_000_000), budget=None, n_clusters=1,
+                    page_size=16, quant_block=64, q_dtype="bf16", recent_ppm=125_000,
+                    rank="seeded", outlier=None, share=None, old_bits=4),
     # Prefix-shared radix layout: 256 requests share a 2000-token prefix, then
     # one of 4 shared 500-token branches, then a unique 80..1000-token suffix;
     # budgets (ratio 0.60 -> 0.20) apply to the suffix only.
@@ -134,6 +139,7 @@ class Workload:
     outlier_channels: Optional[np.ndarray]  # int32 [Hkv, n_out] or None
     outlier_scale: float
     spec: dict
+    old_bits: int = 8                # code width of the slow (quantised) tier: 8 or 4
 
     # ------------------------------------------------------------------ Q
     @property
@@ -253,6 +259,7 @@ def make_workload(name: str, **overrides) -> Workload:
     ``ctx=("uniform", 300, 900)``) to make smaller seeded variants for tests.
     """
     spec = dict(SPECS[name])
+    spec.setdefault("old_bits", 8)
     unknown = set(overrides) - set(spec)
     if unknown:
         raise KeyError(f"unknown workload fields: {sorted(unknown)}")
@@ -315,7 +322,7 @@ def make_workload(name: str, **overrides) -> Workload:
         ratio_hi_ppm=int(hi_ppm), ratio_lo_ppm=int(lo_ppm), recent_ppm=int(spec["recent_ppm"]),
         head_rank=rank, n_comp=n_comp, n_fixed=n_fixed, budget_override=override,
         node_len=node_len, paths=paths, outlier_channels=outl, outlier_scale=float(oscale),
-        spec=spec,
+        spec=spec, old_bits=int(spec["old_bits"]),
     )
 
 
