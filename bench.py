@@ -35,13 +35,14 @@ METRIC = "effective KV GB/s (and % of HBM peak) in ragged-paged decode attention
 # the split-kernel time on MI355X: the best length depends on how the item
 # count falls against the ~2048 resident wavefronts and on the length mix.
 PLAN_CHUNKS = {"tiny": (1024, 1024), "llama8b": (1024, 1024), "ragged": (4096, 1024),
-               "tiered": (1024, 1536), "radix": (768, 1024)}
+               "tiered": (1024, 1536), "tiered4": (1024, 1536), "radix": (768, 1024)}
 
 DESCRIPTIONS = {
     "tiny": "tiny: 2 requests, 4/2 heads, d 64, ctx 256, budgets in {32..256}, 2 clusters",
     "llama8b": "Llama-3-8B-shaped layer: batch 64, 32/8 heads, d 128, ctx U[4096,16384], ratio 0.50->0.10 by head rank, 2 clusters, page 16, bf16",
     "ragged": "high raggedness: batch 256, 32/8 heads, d 128, ctx log-U[2048,32768], ratio 0.60->0.05, 8 clusters, 1% K outlier channels x8",
     "tiered": "TTKV tiered: batch 4, ctx 131072, 32/8 heads, d 128, newest 12.5% bf16, rest INT8 64-token blocks",
+    "tiered4": "TTKV tiered, 4-bit slow tier: batch 4, ctx 131072, 32/8 heads, d 128, newest 12.5% bf16, rest INT4 64-token blocks",
     "radix": "prefix-shared radix: batch 256, 2000-token prefix + 1 of 4 500-token branches + 80..1000 suffix, ratio 0.60->0.20 on suffix",
 }
 # HBM bytes per split stage from rocprofv3 counter runs, one file per workload

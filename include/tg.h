@@ -136,15 +136,24 @@ int tg_reserve(const tg_budget_table* table, int32_t B, const int32_t* n_comp,
  *              + ((c>>5)&1)*8 + (c&7)
  *           V: S*d + ((t>>4)*(d/64) + (c>>6))*1024 + (((t>>2)&3)*16 + (c&15))*16
  *              + ((c>>4)&3)*4 + (t&3))
+ *   INT4 : (old_bits 4, d = 128) K codes, V codes     head_bytes = S*d + 4*d
+ *          (S*d/2 bytes each; a code is u = q4 + 8 in 4 bits), then K
+ *          scales [d] fp16, V scales [d] fp16.  In 32-bit words of a block,
+ *          nibble p of a word being bits 4p..4p+3:
+ *           K (t, c): word (((t>>4)*64 + (t&15) + 16*((c>>3)&3))*4 + (c>>5)),
+ *                     nibble ((c&1)<<2) | ((c&7)>>1)
+ *           V (t, c): at +S*d/2, word (((t>>4)*64 + (c&15) + 16*((t>>2)&3))*4
+ *                     + (c>>5)), nibble ((t&1)<<2) | (((c>>4)&1)<<1) | ((t&3)>>1)
  * Pages are handed out lowest free id first; shared pages are
  * reference-counted; a failing allocation changes nothing.
  * ---------------------------------------------------------------------- */
 typedef struct tg_pool tg_pool;
 
-/* cluster_size [C] from tg_reserve; pages_bf / pages_i8 [C] capacities (>= 0).
+/* cluster_size [C] from tg_reserve; pages_bf / pages_i8 [C] capacities (>= 0);
+ * old_bits 8 (INT8 pages) or 4 (INT4 pages) sizes the slow tier's pages.
  * TG_EINVAL on bad geometry, TG_EOVERFLOW if a pool's byte size overflows. */
 int tg_pool_create(int32_t n_clusters, const int32_t* cluster_size, int32_t head_dim,
-                   int32_t page_size, int32_t quant_block, const int64_t* pages_bf,
+                   int32_t page_size, int32_t quant_block, int32_t old_bits, const int64_t* pages_bf,
                    const int64_t* pages_i8, tg_pool** out);
 void tg_pool_destroy(tg_pool* pool);
 /* Bytes of one page of (cluster c, tier), or -1 on a bad index. */
@@ -280,6 +289,7 @@ typedef struct tg_cache {
   int32_t* bf_base;                          /* device [B*H] ring row of logical bf16 row 0
                                                 (zero at admission; updated by tg_append_kv) */
   int32_t recent_ppm;                        /* tier rule of the reservation (tg_append_kv) */
+  int32_t old_bits;                          /* slow-tier codes: 8 (0 = 8) or 4 (d = 128 only) */
 } tg_cache;
 
 /* ------------------------------------------------------------------------

@@ -75,7 +75,8 @@ class Cache(ctypes.Structure):
                 ("bt", (c_void_p * 2) * TG_MAX_CLUSTERS),
                 ("stride", (c_int32 * 2) * TG_MAX_CLUSTERS),
                 ("cluster_of_head", c_void_p), ("slot_in_cluster", c_void_p), ("len", c_void_p),
-                ("n_fixed", c_void_p), ("ring", c_void_p), ("bf_base", c_void_p), ("recent_ppm", c_int32)]
+                ("n_fixed", c_void_p), ("ring", c_void_p), ("bf_base", c_void_p), ("recent_ppm", c_int32),
+                ("old_bits", c_int32)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -89,7 +90,8 @@ class DecodeArgs(ctypes.Structure):
 SIGNATURES = {
     "tg_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "tg_reserve": (ctypes.c_int, [POINTER(BudgetTable), c_int32, P32, P32, P32, POINTER(Reservation)]),
-    "tg_pool_create": (ctypes.c_int, [c_int32, P32, c_int32, c_int32, c_int32, P64, P64, POINTER(c_void_p)]),
+    "tg_pool_create": (ctypes.c_int, [c_int32, P32, c_int32, c_int32, c_int32, c_int32, P64, P64,
+                                      POINTER(c_void_p)]),
     "tg_pool_destroy": (None, [c_void_p]),
     "tg_pool_page_bytes": (c_int64, [c_void_p, c_int32, c_int32]),
     "tg_pool_capacity": (c_int64, [c_void_p, c_int32, c_int32]),

@@ -90,15 +90,17 @@ class Pool:
     """Host bookkeeping of the (cluster, tier) page pools (``tg_pool``)."""
 
     def __init__(self, cluster_size: Sequence[int], head_dim: int, page_size: int, quant_block: int,
-                 pages_bf: Sequence[int], pages_i8: Sequence[int]):
+                 pages_bf: Sequence[int], pages_i8: Sequence[int], old_bits: int = 8):
         cs = _i32(cluster_size)
         self.C = int(cs.size)
         self.head_dim, self.page_size, self.quant_block = int(head_dim), int(page_size), int(quant_block)
+        self.old_bits = int(old_bits)
         pb = np.ascontiguousarray(pages_bf, dtype=np.int64)
         pi = np.ascontiguousarray(pages_i8, dtype=np.int64)
         h = ctypes.c_void_p()
         check(lib().tg_pool_create(self.C, _p32(cs), self.head_dim, self.page_size, self.quant_block,
-                                   pb.ctypes.data_as(L.P64), pi.ctypes.data_as(L.P64), ctypes.byref(h)),
+                                   self.old_bits, pb.ctypes.data_as(L.P64), pi.ctypes.data_as(L.P64),
+                                   ctypes.byref(h)),
               "tg_pool_create")
         self.handle = h
 
@@ -280,6 +282,7 @@ class DeviceCache:
         c_s.ring = _ptr(self.ring)
         c_s.bf_base = _ptr(self.bf_base)
         c_s.recent_ppm = int(res.struct.recent_ppm)
+        c_s.old_bits = pool.old_bits
         self.struct = c_s
         self.B, self.H, self.d = res.B, res.H, pool.head_dim
 

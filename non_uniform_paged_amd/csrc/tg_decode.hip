@@ -179,6 +179,9 @@ extern "C" int tg_merge_partials(const float* workspace, int32_t n_slots, int32_
 
 namespace {
 
+// Code width of the slow tier (0 in an older cache struct means 8).
+int old_bits_of(const tg_cache* c) { return c->old_bits == 4 ? 4 : 8; }
+
 // Validates a decode call and fills the split-kernel arguments.
 int make_split_args(const tg_cache* c, const tg_decode_args* a, bool merge, SplitArgs* out, int32_t* G_out) {
   if (!c || !a) return TG_EINVAL;
@@ -205,6 +208,8 @@ int make_split_args(const tg_cache* c, const tg_decode_args* a, bool merge, Spli
       if (reinterpret_cast<uintptr_t>(c->pool[cl][t]) % 16) return TG_EINVAL;
     }
   if (c->ring != nullptr && c->bf_base == nullptr) return TG_EINVAL;
+  if (c->old_bits != 0 && c->old_bits != 8 && c->old_bits != 4) return TG_EINVAL;
+  if (c->old_bits == 4 && d != 128) return TG_EUNSUPPORTED;
   SplitArgs& s = *out;
   s = SplitArgs{};
   for (int32_t cl = 0; cl < c->n_clusters; ++cl)
@@ -246,7 +251,7 @@ int decode_split(const tg_cache* c, const tg_decode_args* a, void* stream, bool 
   // one launch over both tiers when the cache has INT8 pages
   bool has_i8 = false;
   for (int32_t cl = 0; cl < c->n_clusters; ++cl) has_i8 |= c->stride[cl][TG_TIER_I8] > 0;
-  hipError_t e = launch_split(s, d, G, a->q_dtype == TG_Q_F32, has_i8, st);
+  hipError_t e = launch_split(s, d, G, a->q_dtype == TG_Q_F32, has_i8, old_bits_of(c), st);
   if (e != hipSuccess) return TG_EDEVICE;
   if (!merge) return TG_OK;
   e = launch_merge(a->workspace, a->workspace + static_cast<int64_t>(a->n_slots) * G * d, a->part_off,
@@ -333,7 +338,7 @@ extern "C" int tg_decode_streamed(const tg_cache* c, const tg_tables* t, const t
   // bf16 items (HBM-resident pages) first: they run while the first pages cross
   SplitArgs sb = s;
   sb.n_items = chunk_off[0];
-  if (launch_split(sb, d, G, qf32, false, st) != hipSuccess) return TG_EDEVICE;
+  if (launch_split(sb, d, G, qf32, false, 8, st) != hipSuccess) return TG_EDEVICE;
   char* stage = static_cast<char*>(staging);
   for (int32_t r = 0; r < B; ++r) {
     char* slot = stage + (r % 2) * slot_bytes;
@@ -362,7 +367,7 @@ extern "C" int tg_decode_streamed(const tg_cache* c, const tg_tables* t, const t
     }
     sr.work = s.work + static_cast<int64_t>(chunk_off[r]) * 6;
     sr.n_items = chunk_off[r + 1] - chunk_off[r];
-    if (launch_split(sr, d, G, qf32, true, st) != hipSuccess) return TG_EDEVICE;
+    if (launch_split(sr, d, G, qf32, true, old_bits_of(c), st) != hipSuccess) return TG_EDEVICE;
     if (hipEventRecord(done, st) != hipSuccess) return TG_EDEVICE;
   }
   const hipError_t e = launch_merge(a->workspace, a->workspace + static_cast<int64_t>(a->n_slots) * G * d,

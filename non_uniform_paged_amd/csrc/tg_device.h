@@ -145,9 +145,9 @@ __device__ __forceinline__ f32x4_t mfma_f16_k16(const u32x2_t& a, const u32x2_t&
   return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a), __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
 }
 
-// Split-kernel launch over every plan item; has_i8: the cache has INT8
-// pages.  Returns hipErrorInvalidValue for an unsupported (d, G).
-hipError_t launch_split(const SplitArgs& a, int d, int G, bool qf32, bool has_i8, hipStream_t s);
+// Split-kernel launch over every plan item; has_i8: the cache has INT8 (or,
+// with old_bits 4, INT4) pages.  Returns hipErrorInvalidValue for an unsupported (d, G).
+hipError_t launch_split(const SplitArgs& a, int d, int G, bool qf32, bool has_i8, int old_bits, hipStream_t s);
 
 }  // namespace tg_dev
 

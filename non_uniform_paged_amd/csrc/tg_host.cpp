@@ -189,20 +189,22 @@ extern "C" int tg_reserve(const tg_budget_table* tb, int32_t B, const int32_t* n
 // --------------------------------------------------------------------------
 // pools
 // --------------------------------------------------------------------------
-static int64_t head_bytes(int32_t tier, int32_t d, int32_t ps, int32_t qb) {
-  return tier == TG_TIER_BF16 ? int64_t(4) * ps * d : int64_t(2) * qb * d + int64_t(4) * d;
+static int64_t head_bytes(int32_t tier, int32_t d, int32_t ps, int32_t qb, int32_t bits) {
+  return tier == TG_TIER_BF16 ? int64_t(4) * ps * d : int64_t(2) * qb * d * bits / 8 + int64_t(4) * d;
 }
 
 extern "C" int tg_pool_create(int32_t C, const int32_t* cluster_size, int32_t d, int32_t ps,
-                              int32_t qb, const int64_t* pages_bf, const int64_t* pages_i8,
+                              int32_t qb, int32_t old_bits, const int64_t* pages_bf, const int64_t* pages_i8,
                               tg_pool** out) {
   if (!out || !cluster_size || !pages_bf || !pages_i8) return TG_EINVAL;
   if (C < 1 || C > TG_MAX_CLUSTERS || d < 1 || ps < 1 || qb < 1) return TG_EINVAL;
+  if (old_bits != 8 && old_bits != 4) return TG_EINVAL;
+  if (old_bits == 4 && (qb * d) % 2) return TG_EINVAL;
   for (int32_t c = 0; c < C; ++c)
     if (cluster_size[c] < 1 || pages_bf[c] < 0 || pages_i8[c] < 0) return TG_EINVAL;
   for (int32_t c = 0; c < C; ++c)
     for (int32_t t = 0; t < 2; ++t) {
-      const int64_t pb = head_bytes(t, d, ps, qb) * cluster_size[c];
+      const int64_t pb = head_bytes(t, d, ps, qb, old_bits) * cluster_size[c];
       const int64_t cap = t == TG_TIER_BF16 ? pages_bf[c] : pages_i8[c];
       if (cap > 0 && pb > std::numeric_limits<int64_t>::max() / cap) return TG_EOVERFLOW;
     }
@@ -215,8 +217,8 @@ extern "C" int tg_pool_create(int32_t C, const int32_t* cluster_size, int32_t d,
     p->quant_block = qb;
     p->cluster_size.assign(cluster_size, cluster_size + C);
     for (int32_t c = 0; c < C; ++c) {
-      p->sub[c][TG_TIER_BF16].init(pages_bf[c], head_bytes(TG_TIER_BF16, d, ps, qb) * cluster_size[c]);
-      p->sub[c][TG_TIER_I8].init(pages_i8[c], head_bytes(TG_TIER_I8, d, ps, qb) * cluster_size[c]);
+      p->sub[c][TG_TIER_BF16].init(pages_bf[c], head_bytes(TG_TIER_BF16, d, ps, qb, old_bits) * cluster_size[c]);
+      p->sub[c][TG_TIER_I8].init(pages_i8[c], head_bytes(TG_TIER_I8, d, ps, qb, old_bits) * cluster_size[c]);
     }
   } catch (...) {
     delete p;

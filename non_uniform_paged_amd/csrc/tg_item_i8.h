@@ -28,6 +28,13 @@
 //     ((t>>4)*(d/64) + (c>>6))*1024 + (((t>>2)&3)*16 + (c&15))*16 + ((c>>4)&3)*4 + (t&3)
 //   K scales [d] fp16 at +128*d, V scales [d] fp16 at +130*d
 // so that each contiguous 1 KiB wave load holds matrix-core operands.
+//
+// INT4 page (d = 128): codes u = q4 + 8 in nibbles; K codes of group g (rows
+// 16g..16g+15), lane l, step s (channels 32s + 8(l/16) + e) are 32-bit word
+// (64g + l)*4 + s, nibble ((e&1)<<2) | (e>>1); V codes (at +32d) of lane l
+// (channel l%16 of tile n, rows 16g + 4(l/16) + i) are word (64g + l)*4 + n/2,
+// nibble ((i&1)<<2) | ((n&1)<<1) | (i>>1); scales at +64d (K) and +66d (V).
+// Two bit operations per pair of values turn a word into fp16 operands.
 
 #include <cmath>
 
@@ -36,12 +43,22 @@
 namespace tg_dev {
 
 constexpr uint32_t kF16x2_1152 = 0x64806480u;  // two fp16 1152.0
+constexpr uint32_t kF16x2_24 = 0x4E004E00u;    // two fp16 24.0
 
 // 4 int8 codes (one dword) -> 4 fp16 values 1152 + q8 (two dwords)
 __device__ __forceinline__ u32x2_t codes_to_f16(uint32_t w) {
   const uint32_t x = w ^ 0x80808080u;
   return u32x2_t{__builtin_amdgcn_perm(0x64646464u, x, 0x04010400u),
                  __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u)};
+}
+
+// 8 INT4 codes u = q4 + 8 (one dword, nibble k = bits 4k..4k+3) -> 8 fp16
+// values 16 + u = 24 + q4: word k of the result holds nibbles k and k + 4
+// (placed in mantissa bits 6..9 of fp16 16.0).
+__device__ __forceinline__ u32x4_t nibbles_to_f16(uint32_t x) {
+  constexpr uint32_t kMask = 0x03C003C0u, k16 = 0x4C004C00u;
+  return u32x4_t{((x << 6) & kMask) | k16, ((x << 2) & kMask) | k16, ((x >> 2) & kMask) | k16,
+                 ((x >> 6) & kMask) | k16};
 }
 
 __device__ __forceinline__ float half_lo(uint32_t w) {
@@ -51,11 +68,21 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
 }
 
-template <int D, int G, bool QF32, int DEPTH, bool STREAM>
+// BITS = 4: the INT4 page (include/tg.h): per 16-row group one 16-byte load
+// per lane holds all d = 128 channels of K (and one all of V) as nibbles;
+// values 24 + q4 take the place of 1152 + q8, and the rest is unchanged.
+template <int D, int G, bool QF32, int DEPTH, bool STREAM, int BITS>
 __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0, int t1, int slot,
                                         int hs, const TG_GLOBAL int32_t* bt_row, gptr pool,
                                         int64_t pbytes, float* lds) {
-  constexpr int NL = D / 64;           // 1 KiB loads per 16-row group (K codes, V codes)
+  static_assert(BITS == 8 || (BITS == 4 && D == 128), "INT4 pages are laid out for d = 128");
+  constexpr int NL = BITS == 8 ? D / 64 : 1;  // 1 KiB loads per 16-row group (K codes, V codes)
+  constexpr int CODE_BYTES = kQBlock * D * BITS / 8;  // K (or V) codes of one head's block
+  constexpr uint32_t kBias = BITS == 8 ? kF16x2_1152 : kF16x2_24;
+  // INT8: q' and the weights P enter the matrix cores as fp16 high + low
+  // parts (~22 significant bits).  INT4: one fp16 part each (11 bits, far
+  // finer than the 4-bit codes they multiply), half the matrix-core work.
+  constexpr bool TWO = BITS == 8;
   constexpr int NK = D / 32;           // score steps (32 channels each)
   constexpr int NT = D / 16;           // 16-channel tiles of V
   constexpr int GR = kQBlock / kPage;  // 16-row groups per block
@@ -96,10 +123,10 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
   for (int k = 0; k < NT * 4; ++k) lds[k * 64 + lane] = 0.f;
   float m_ref = -INFINITY;
   float l_run = 0.f;
-  const int64_t head_off = static_cast<int64_t>(hs) * (2 * kQBlock * D + 4 * D);
+  const int64_t head_off = static_cast<int64_t>(hs) * (2 * CODE_BYTES + 4 * D);
   const int lane_off = lane * 16;
-  const u32x4_t c1152x8 = {kF16x2_1152, kF16x2_1152, kF16x2_1152, kF16x2_1152};
-  const u32x2_t c1152x4 = {kF16x2_1152, kF16x2_1152};
+  const u32x4_t c1152x8 = {kBias, kBias, kBias, kBias};  // constant-offset operands
+  const u32x2_t c1152x4 = {kBias, kBias};
   const int b0 = t0 / kQBlock;
   const int nb = (t1 - t0) / kQBlock;
 
@@ -117,12 +144,12 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
 #pragma unroll
       for (int L = 0; L < NL; ++L) kk[L] = ldpage<STREAM>(bp + (k * NL + L) * 1024);
 #pragma unroll
-      for (int L = 0; L < NL; ++L) vv[L] = ldpage<STREAM>(bp + kQBlock * D + (k * NL + L) * 1024);
+      for (int L = 0; L < NL; ++L) vv[L] = ldpage<STREAM>(bp + CODE_BYTES + (k * NL + L) * 1024);
     };
     u32x4_t skraw[NK];  // K scales 32 s + 8 lj .. +8 of the next block to start
     uint32_t svraw[NT];  // V scale of channel 16 n + lg of the current block
     auto load_sk = [&](int b) {
-      gptr bp = blk_ptr(b) + 2 * kQBlock * D;
+      gptr bp = blk_ptr(b) + 2 * CODE_BYTES;
 #pragma unroll
       for (int s = 0; s < NK; ++s) skraw[s] = ldv16(bp + (32 * s + 8 * lj) * 2);
     };
@@ -151,7 +178,7 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
 #pragma unroll
       for (int s = 0; s < NK; ++s) {
         qb = mfma_f16_k32(c1152x8, qop[0][s], qb);
-        qb = mfma_f16_k32(c1152x8, qop[1][s], qb);
+        if constexpr (TWO) qb = mfma_f16_k32(c1152x8, qop[1][s], qb);
       }
       const float qk_bias = qb[0];  // 1152 * sum_c Q'[lg][c], the same in every row
 
@@ -165,7 +192,7 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
         const int kn = k + DEPTH - 1;  // group requested now: block blk + kn/GR, group kn%GR
         issue(kc[kn % DEPTH], vc[kn % DEPTH], blk + kn / GR, kn % GR);
         if (k == 1) {
-          gptr sp = blk_ptr(blk) + 2 * kQBlock * D + 2 * D;
+          gptr sp = blk_ptr(blk) + 2 * CODE_BYTES + 2 * D;
 #pragma unroll
           for (int n = 0; n < NT; ++n) svraw[n] = *(const TG_GLOBAL uint16_t*)(sp + (16 * n + lg) * 2);
         }
@@ -176,12 +203,17 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
         f32x4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < NK; ++s) {
-          const u32x4_t x = kc[u][s / 2];
-          const u32x2_t c0 = codes_to_f16(x[(s % 2) * 2]);
-          const u32x2_t c1 = codes_to_f16(x[(s % 2) * 2 + 1]);
-          const u32x4_t A = {c0[0], c0[1], c1[0], c1[1]};
+          u32x4_t A;
+          if constexpr (BITS == 8) {
+            const u32x4_t x = kc[u][s / 2];
+            const u32x2_t c0 = codes_to_f16(x[(s % 2) * 2]);
+            const u32x2_t c1 = codes_to_f16(x[(s % 2) * 2 + 1]);
+            A = u32x4_t{c0[0], c0[1], c1[0], c1[1]};
+          } else {
+            A = nibbles_to_f16(kc[u][0][s]);  // channels 32 s + 8 lj + e, e < 8
+          }
           sacc = mfma_f16_k32(A, qop[0][s], sacc);
-          sacc = mfma_f16_k32(A, qop[1][s], sacc);
+          if constexpr (TWO) sacc = mfma_f16_k32(A, qop[1][s], sacc);
         }
         float sc[4];
 #pragma unroll
@@ -205,24 +237,30 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
           m_ref = mn;
         }
         float pw[4];
+        uint32_t ph[4], pl[4];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           pw[rr] = __builtin_amdgcn_exp2f(sc[rr] - m_ref);
-          l_run += pw[rr];
+          split_f16(pw[rr], ph[rr], pl[rr]);
+          // with one part, the sum takes the rounded weights the products use
+          l_run += TWO ? pw[rr] : static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ph[rr])));
         }
-        uint32_t ph[4], pl[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) split_f16(pw[rr], ph[rr], pl[rr]);
         const u32x2_t Ph = {ph[0] | (ph[1] << 16), ph[2] | (ph[3] << 16)};
         const u32x2_t Pl = {pl[0] | (pl[1] << 16), pl[2] | (pl[3] << 16)};
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-          const u32x2_t B = codes_to_f16(vc[u][n / 4][n % 4]);
+          u32x2_t B;
+          if constexpr (BITS == 8) {
+            B = codes_to_f16(vc[u][n / 4][n % 4]);
+          } else {  // word n/2 holds tiles n & ~1 (values 0, 1) and n | 1 (values 2, 3)
+            const u32x4_t f = nibbles_to_f16(vc[u][0][n / 2]);
+            B = (n & 1) ? u32x2_t{f[2], f[3]} : u32x2_t{f[0], f[1]};
+          }
           accb[n] = mfma_f16_k16(Ph, B, accb[n]);
-          accb[n] = mfma_f16_k16(Pl, B, accb[n]);
+          if constexpr (TWO) accb[n] = mfma_f16_k16(Pl, B, accb[n]);
         }
         pbias = mfma_f16_k16(Ph, c1152x4, pbias);
-        pbias = mfma_f16_k16(Pl, c1152x4, pbias);
+        if constexpr (TWO) pbias = mfma_f16_k16(Pl, c1152x4, pbias);
         __builtin_amdgcn_sched_barrier(0);
       }
       // end of block: fold in the V scales
@@ -257,7 +295,7 @@ constexpr int kI8LdsFloats = (D / 16) * 4 * 64;
 
 // Runs plan item `w` (an INT8-tier item) with `lds` as the wave's
 // accumulator (kI8LdsFloats<D> floats).
-template <int D, int G, bool QF32, int DEPTH>
+template <int D, int G, bool QF32, int DEPTH, int BITS = 8>
 __device__ __forceinline__ void i8_dispatch(const SplitArgs& a, const TG_GLOBAL int32_t* w, float* lds) {
   const int r = uniform(w[0]), h = uniform(w[1]);
   const int t0 = uniform(w[3]), slot = uniform(w[5]);
@@ -277,9 +315,9 @@ __device__ __forceinline__ void i8_dispatch(const SplitArgs& a, const TG_GLOBAL 
   bool shared = false;  // an item that starts on the shared radix path reads through the caches
   if (a.n_fixed) shared = t0 + kQBlock <= uniform(a.n_fixed[r]);
   if (shared)
-    i8_item<D, G, QF32, DEPTH, false>(a, r, h, t0, t1, slot, hs, bt_row, pool, pbytes, lds);
+    i8_item<D, G, QF32, DEPTH, false, BITS>(a, r, h, t0, t1, slot, hs, bt_row, pool, pbytes, lds);
   else
-    i8_item<D, G, QF32, DEPTH, true>(a, r, h, t0, t1, slot, hs, bt_row, pool, pbytes, lds);
+    i8_item<D, G, QF32, DEPTH, true, BITS>(a, r, h, t0, t1, slot, hs, bt_row, pool, pbytes, lds);
 }
 
 }  // namespace tg_dev

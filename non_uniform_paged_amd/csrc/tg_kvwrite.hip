@@ -108,6 +108,67 @@ __global__ __launch_bounds__(2 * D) void write_i8_kernel(WriteArgs a) {
   reinterpret_cast<_Float16*>(head + 2 * kQBlock * D + kv * D * 2)[ch] = s16;
 }
 
+// Packs the codes of one head's block (LDS, int8 [2][kQBlock][D], K then V,
+// values in [-7, 7]) into the INT4 page layout of include/tg.h at `head`:
+// 32-bit words, nibble p = bits 4p..4p+3 holding u = q4 + 8.  Called by all
+// 2*D threads of the workgroup after the codes are in LDS.
+template <int D>
+__device__ void store_i4_words(const int8_t (*codes)[kQBlock][D], char* head) {
+  constexpr int WORDS = kQBlock * D / 8;  // per K (and per V)
+  for (int wi = threadIdx.x; wi < 2 * WORDS; wi += 2 * D) {
+    const int kv = wi / WORDS, x = wi % WORDS;
+    const int g = x / 256, l = (x % 256) / 4, m = x % 4;
+    uint32_t word = 0;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      int t, c;
+      if (kv == 0) {  // K: row 16g + l%16, channel 32m + 8(l/16) + e
+        t = 16 * g + (l & 15);
+        c = 32 * m + 8 * (l >> 4) + (((p & 3) << 1) | (p >> 2));
+      } else {        // V: rows 16g + 4(l/16) + i, channel l%16 of tile 2m + q
+        t = 16 * g + 4 * (l >> 4) + (((p & 1) << 1) | (p >> 2));
+        c = (l & 15) + 16 * (2 * m + ((p >> 1) & 1));
+      }
+      word |= static_cast<uint32_t>(codes[kv][t][c] + 8) << (4 * p);
+    }
+    *reinterpret_cast<uint32_t*>(head + kv * (kQBlock * D / 2) + x * 4) = word;
+  }
+}
+
+// One block of 2*D threads per (r, h, 64-row block), thread = (K|V, channel):
+// the INT4 slow tier (codes in [-7, 7], scale absmax / 7).
+template <int D>
+__global__ __launch_bounds__(2 * D) void write_i4_kernel(WriteArgs a) {
+  __shared__ int8_t codes[2][kQBlock][D];
+  const int rh = blockIdx.y;
+  const int r = rh / a.H, h = rh % a.H;
+  const int n_i8 = a.len[2 * rh];
+  const int b = blockIdx.x;
+  if (b * kQBlock >= n_i8) return;
+  const int kv = threadIdx.x / D, ch = threadIdx.x % D;
+  const int cl = a.cluster_of_head[h], hs = a.slot_in_cluster[h];
+  const int64_t base = a.offsets[rh] + static_cast<int64_t>(b) * kQBlock;
+  float amax = 0.f;
+  for (int t = 0; t < kQBlock; ++t) {
+    const int64_t row = a.index[base + t];
+    amax = fmaxf(amax, fabsf(__uint_as_float(static_cast<uint32_t>(a.rows[row * 2 * D + kv * D + ch]) << 16)));
+  }
+  _Float16 s16 = static_cast<_Float16>(amax / 7.0f);
+  if (__builtin_isinf(static_cast<float>(s16))) s16 = static_cast<_Float16>(65504.0f);
+  const float sf = static_cast<float>(s16);
+  for (int t = 0; t < kQBlock; ++t) {
+    const int64_t row = a.index[base + t];
+    const float x = __uint_as_float(static_cast<uint32_t>(a.rows[row * 2 * D + kv * D + ch]) << 16);
+    codes[kv][t][ch] = sf > 0.f ? static_cast<int8_t>(fminf(fmaxf(__builtin_rintf(x / sf), -7.f), 7.f)) : 0;
+  }
+  const int pid = a.bt[cl][TG_TIER_I8][static_cast<int64_t>(r) * a.stride[cl][TG_TIER_I8] + b];
+  char* head = a.pool[cl][TG_TIER_I8] + static_cast<int64_t>(pid) * a.page_bytes[cl][TG_TIER_I8] +
+               static_cast<int64_t>(hs) * (kQBlock * D + 4 * D);
+  reinterpret_cast<_Float16*>(head + kQBlock * D + kv * D * 2)[ch] = s16;
+  __syncthreads();
+  store_i4_words<D>(codes, head);
+}
+
 // ---------------------------------------------------------------- decode-step append
 struct AppendArgs {
   char* pool[TG_MAX_CLUSTERS][2];
@@ -141,8 +202,9 @@ __device__ __forceinline__ int bf16_offset(int kv, int t, int c) {
 // the new row as the newest bf16 row (ring row base + n_bf) and, when the
 // tier split of the new length moves the INT8 boundary, quantises the oldest
 // kQBlock bf16 rows into INT8 block n_i8 / kQBlock and advances the ring.
-template <int D>
+template <int D, int BITS>
 __global__ __launch_bounds__(2 * D) void append_kernel(AppendArgs a) {
+  __shared__ int8_t lcodes[BITS == 4 ? 2 : 1][BITS == 4 ? kQBlock : 1][BITS == 4 ? D : 1];
   const int rh = blockIdx.x;
   const int r = rh / a.H, h = rh % a.H;
   const int kv = threadIdx.x / D, ch = threadIdx.x % D;
@@ -180,26 +242,35 @@ __global__ __launch_bounds__(2 * D) void append_kernel(AppendArgs a) {
     const uint16_t x = *reinterpret_cast<const uint16_t*>(bf_head(pos) + bf16_offset<D>(kv, pos % kPage, ch));
     return __uint_as_float(static_cast<uint32_t>(x) << 16);
   };
+  constexpr float kQMax = BITS == 8 ? 127.f : 7.f;
+  constexpr int CODE_BYTES = kQBlock * D * BITS / 8;
   float amax = 0.f;
   for (int t = 0; t < kQBlock; ++t) amax = fmaxf(amax, fabsf(value(t)));
-  _Float16 s16 = static_cast<_Float16>(amax / 127.0f);
+  _Float16 s16 = static_cast<_Float16>(amax / kQMax);
   if (__builtin_isinf(static_cast<float>(s16))) s16 = static_cast<_Float16>(65504.0f);
   const float sf = static_cast<float>(s16);
   char* head = a.pool[cl][TG_TIER_I8] + static_cast<int64_t>(bt_i8[blk]) * a.page_bytes[cl][TG_TIER_I8] +
-               static_cast<int64_t>(hs) * (2 * kQBlock * D + 4 * D);
-  int8_t* codes = reinterpret_cast<int8_t*>(head + kv * kQBlock * D);
+               static_cast<int64_t>(hs) * (2 * CODE_BYTES + 4 * D);
   constexpr int NL = D / 64;
   for (int t = 0; t < kQBlock; ++t) {
     const float x = value(t);
     int q = 0;
-    if (sf > 0.f) q = static_cast<int>(fminf(fmaxf(__builtin_rintf(x / sf), -127.f), 127.f));
-    const int c = ch;
-    const int off = kv == 0
-        ? ((t >> 4) * NL + (c >> 6)) * 1024 + (((c >> 3) & 3) * 16 + (t & 15)) * 16 + ((c >> 5) & 1) * 8 + (c & 7)
-        : ((t >> 4) * NL + (c >> 6)) * 1024 + (((t >> 2) & 3) * 16 + (c & 15)) * 16 + ((c >> 4) & 3) * 4 + (t & 3);
-    codes[off] = static_cast<int8_t>(q);
+    if (sf > 0.f) q = static_cast<int>(fminf(fmaxf(__builtin_rintf(x / sf), -kQMax), kQMax));
+    if constexpr (BITS == 4) {
+      lcodes[kv][t][ch] = static_cast<int8_t>(q);
+    } else {
+      const int c = ch;
+      const int off = kv == 0
+          ? ((t >> 4) * NL + (c >> 6)) * 1024 + (((c >> 3) & 3) * 16 + (t & 15)) * 16 + ((c >> 5) & 1) * 8 + (c & 7)
+          : ((t >> 4) * NL + (c >> 6)) * 1024 + (((t >> 2) & 3) * 16 + (c & 15)) * 16 + ((c >> 4) & 3) * 4 + (t & 3);
+      reinterpret_cast<int8_t*>(head + kv * CODE_BYTES)[off] = static_cast<int8_t>(q);
+    }
   }
-  reinterpret_cast<_Float16*>(head + 2 * kQBlock * D + kv * D * 2)[ch] = s16;
+  reinterpret_cast<_Float16*>(head + 2 * CODE_BYTES + kv * D * 2)[ch] = s16;
+  if constexpr (BITS == 4) {
+    __syncthreads();
+    store_i4_words<D>(lcodes, head);
+  }
   if (threadIdx.x == 0) {
     a.len[2 * rh] = n_i8 + kQBlock;
     a.len[2 * rh + 1] = n_bf + 1 - kQBlock;
@@ -239,10 +310,15 @@ extern "C" int tg_append_kv(const tg_cache* c, const uint16_t* rows, int32_t* st
   const int64_t pairs = static_cast<int64_t>(c->B) * c->n_kv_heads;
   if (pairs > INT32_MAX) return TG_EUNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (c->head_dim == 128)
-    hipLaunchKernelGGL(append_kernel<128>, dim3(static_cast<unsigned>(pairs)), dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(append_kernel<64>, dim3(static_cast<unsigned>(pairs)), dim3(128), 0, st, a);
+  const dim3 grid(static_cast<unsigned>(pairs));
+  if (c->old_bits == 4) {
+    if (c->head_dim != 128) return TG_EUNSUPPORTED;
+    hipLaunchKernelGGL((append_kernel<128, 4>), grid, dim3(256), 0, st, a);
+  } else if (c->head_dim == 128) {
+    hipLaunchKernelGGL((append_kernel<128, 8>), grid, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((append_kernel<64, 8>), grid, dim3(128), 0, st, a);
+  }
   return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
 }
 
@@ -287,8 +363,14 @@ extern "C" int tg_write_kv(const tg_cache* c, const uint16_t* rows, const int32_
   }
   if (max_i8 > 0) {
     const dim3 grid(static_cast<unsigned>(max_i8), static_cast<unsigned>(pairs));
-    if (d == 128) hipLaunchKernelGGL(write_i8_kernel<128>, grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(write_i8_kernel<64>, grid, dim3(128), 0, st, a);
+    if (c->old_bits == 4) {
+      if (d != 128) return TG_EUNSUPPORTED;
+      hipLaunchKernelGGL(write_i4_kernel<128>, grid, dim3(256), 0, st, a);
+    } else if (d == 128) {
+      hipLaunchKernelGGL(write_i8_kernel<128>, grid, dim3(256), 0, st, a);
+    } else {
+      hipLaunchKernelGGL(write_i8_kernel<64>, grid, dim3(128), 0, st, a);
+    }
     if (hipGetLastError() != hipSuccess) return TG_EDEVICE;
   }
   return TG_OK;

@@ -57,7 +57,8 @@ class Prepared:
         C = self.res.C
         extra = slack_pages + shift_pages
         self.pool = api.Pool(self.res.cluster_size, w.d, w.page_size, w.quant_block,
-                             [need[c][1] + extra for c in range(C)], [need[c][0] + extra for c in range(C)])
+                             [need[c][1] + extra for c in range(C)], [need[c][0] + extra for c in range(C)],
+                             getattr(w, "old_bits", 8))
         if shift_pages:
             # occupy the lowest pages first so that this batch lands elsewhere
             filler = api.tg_reserve(w.head_rank, 10**6, 10**6, C, 10**6, w.quant_block,
@@ -161,8 +162,8 @@ class Prepared:
         """Algorithmic bytes of one step.
 
         ``effective``: every (r, h) pays for the rows it attends over (a row
-        is 4d bytes bf16, 2d bytes INT8, plus 4d bytes of scales per INT8
-        block), plus q, o and the tables it reads.  ``roofline``: the same, but
+        is 4d bytes bf16, 2d bytes INT8 or d bytes INT4, plus 4d bytes of
+        scales per quantised block), plus q, o and the tables it reads.  ``roofline``: the same, but
         a shared page's head block counts once however many sequences read
         it.  Flops: 4 * d * G per retained row per KV-head.
         """
@@ -171,7 +172,8 @@ class Prepared:
         qbytes = 4 if w.q_dtype == "f32" else 2
         n_i8 = res.n_i8.astype(np.int64)
         n_bf = res.n_bf.astype(np.int64)
-        kv_eff = int((n_bf * 4 * d).sum() + (n_i8 * 2 * d).sum() + (n_i8 // w.quant_block * 4 * d).sum())
+        bits = getattr(w, "old_bits", 8)
+        kv_eff = int((n_bf * 4 * d).sum() + (n_i8 * 2 * d * bits // 8).sum() + (n_i8 // w.quant_block * 4 * d).sum())
         # unique page blocks: (cluster, tier, page id, head slot) -> rows read
         seen = {}
         for r in range(w.B):
@@ -188,7 +190,7 @@ class Prepared:
                             seen[key] = rows
         kv_roof = 0
         for (c, tier, pid, s), rows in seen.items():
-            kv_roof += rows * 4 * d if tier == 1 else rows * 2 * d + 4 * d
+            kv_roof += rows * 4 * d if tier == 1 else rows * 2 * d * bits // 8 + 4 * d
         q_o = w.B * w.Hq * d * (qbytes + 4)
         tables = t.n_items * 24 + t.n_gitems * 128 + (w.B * w.Hkv + 1) * 4 + sum(
             int(-(-n_bf[r, h] // w.page_size) + n_i8[r, h] // w.quant_block) * 4
@@ -206,5 +208,6 @@ def allocated_bytes(w, n_clusters: int, chunk_bf: int = 1024, chunk_i8: int = 10
     res = api.tg_reserve(w.head_rank, w.ratio_hi_ppm, w.ratio_lo_ppm, n_clusters, w.recent_ppm,
                          w.quant_block, w.n_comp, w.n_fixed, w.budget_override)
     need = api.tg_size_tables(res, w.page_size, w.quant_block, share_of(w), chunk_bf, chunk_i8)["pages_needed"]
-    pool = api.Pool(res.cluster_size, w.d, w.page_size, w.quant_block, [0] * res.C, [0] * res.C)
+    pool = api.Pool(res.cluster_size, w.d, w.page_size, w.quant_block, [0] * res.C, [0] * res.C,
+                    getattr(w, "old_bits", 8))
     return sum(need[c][t] * pool.page_bytes(c, t) for c in range(res.C) for t in range(2))
