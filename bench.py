@@ -79,6 +79,51 @@ def _traffic_record(config: str):
         return None
 
 
+def codec_bench(prep, args, stream):
+    """The lossless bf16 exponent codec over the whole bf16 page pool of the
+    cache (the KV pages as they sit in HBM): compressed size, encode and
+    decode rates (input and output bytes of bf16 per second), and a
+    bit-exact check of the round trip."""
+    import numpy as np
+    import torch
+
+    from non_uniform_paged_amd import api
+
+    pools = [p[1] for p in prep.cache.pools if p[1] is not None]
+    src = pools[0].view(torch.int16) if len(pools) == 1 else torch.cat([p.view(torch.int16) for p in pools])
+    n = src.numel() - src.numel() % 8
+    src = src[:n]
+    dst = torch.empty(api.tg_zip_bound(n), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(api.tg_zip_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(src)
+    api.tg_zip_encode(src, dst, ws, stream=stream)
+    api.tg_zip_decode(dst, n, out, stream=stream)
+    torch.cuda.synchronize()
+    exact = bool(torch.equal(out, src))
+    size = api.zip_compressed_bytes(dst)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    enc, dec = [], []
+    for _ in range(args.zip_reps):
+        ev[0].record(stream)
+        api.tg_zip_encode(src, dst, ws, stream=stream)
+        ev[1].record(stream)
+        api.tg_zip_decode(dst, n, out, stream=stream)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        enc.append(ev[0].elapsed_time(ev[1]))
+        dec.append(ev[1].elapsed_time(ev[2]))
+    e_ms, d_ms = float(np.median(enc)), float(np.median(dec))
+    n_esc = (size - 256 - n - n // 2) // 5
+    res = {"values": n, "bf16_bytes": 2 * n, "compressed_bytes": size, "ratio": round(2 * n / size, 4),
+           "escapes": n_esc, "encode_ms": round(e_ms, 4), "decode_ms": round(d_ms, 4),
+           "encode_GBps": round(2 * n / (e_ms * 1e-3) / 1e9, 1), "decode_GBps": round(2 * n / (d_ms * 1e-3) / 1e9, 1),
+           "round_trip_bit_exact": exact,
+           "pages_quote_GBps": {"encode": 613, "decode": 2181, "hardware": "not stated"}}
+    del dst, ws, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def append_bench(w, args, evict, stream):
     """Decode steps that each append one row per (r, h) first (tg_append_kv,
     with the ageing of the oldest bf16 block into INT8 where the tier split
@@ -231,6 +276,8 @@ def main():
                     help="decode steps with tg_append_kv timed on a second cache built for growth (0: skip)")
     ap.add_argument("--host-steps", type=int, default=10,
                     help="decode steps with the INT8 tier in pinned host memory, streamed (0: skip)")
+    ap.add_argument("--zip-reps", type=int, default=5,
+                    help="timed encode/decode passes of the lossless codec over the bf16 pool (0: skip)")
     ap.add_argument("--group-size", type=int, default=None,
                     help="requests per shared-prefix group item (default 16 / G when pages are shared)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -406,6 +453,8 @@ def main():
     }
     if args.append_steps > 0 and w.paths is None:
         result["append"] = append_bench(w, args, evict, stream)
+    if args.zip_reps > 0:
+        result["codec"] = codec_bench(prep, args, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, prep)
     if args.host_steps > 0 and prep.tables.stride_has_i8:

@@ -416,6 +416,31 @@ int tg_decode_streamed(const tg_cache* cache, const tg_tables* tables, const tg_
 int tg_stream_order(const tg_tables* tables, int32_t B, int32_t* work_out, int32_t* chunk_off);
 
 /* ------------------------------------------------------------------------
+ * Lossless bf16 exponent codec  (device)
+ *
+ * SplitZip page ("Die SplitZip-Strategie"): the 16 most frequent exponents
+ * of the input get 4-bit codes, two per byte; sign and mantissa take one
+ * byte per value; values with another exponent are listed in an escape
+ * stream that decoding writes over its first result.  Codebook: exponents by
+ * count descending, ties to the smaller exponent.  Compressed buffer (n a
+ * multiple of 8, little endian):
+ *   [0, 8) n (int64), [8, 16) n_esc (int64), [16, 32) codebook (uint8, rank
+ *   order), [32, 256) zero, [256, 256 + n) sign << 7 | mantissa per value,
+ *   [256 + n, 256 + 3n/2) codes (value i in bits 4(i%2).. of byte i/2, an
+ *   escaped value's code is 0), then n_esc uint32 escape positions
+ *   (ascending) and n_esc uint8 escape exponents.
+ *   Size 256 + 3n/2 + 5 n_esc (read n_esc from the header).
+ * src, dst, workspace: device, 16-byte aligned; dst of tg_zip_bound(n) bytes,
+ * workspace of tg_zip_workspace_bytes(n).  TG_EINVAL on a bad size or
+ * pointer; n <= 2^32.
+ * ---------------------------------------------------------------------- */
+size_t tg_zip_bound(int64_t n);
+size_t tg_zip_workspace_bytes(int64_t n);
+int tg_zip_encode(const uint16_t* src, int64_t n, void* dst, size_t dst_bytes, void* workspace,
+                  size_t workspace_bytes, void* stream);
+int tg_zip_decode(const void* src, int64_t n, uint16_t* dst, void* stream);
+
+/* ------------------------------------------------------------------------
  * Measurement aid  (device)
  *
  * Streaming read of `bytes` (a multiple of 16) at `src` (16-byte aligned

@@ -114,6 +114,10 @@ SIGNATURES = {
     "tg_decode_streamed": (ctypes.c_int, [POINTER(Cache), POINTER(Tables), POINTER(DecodeArgs), P32, c_void_p,
                                           c_size_t, c_void_p]),
     "tg_stream_order": (ctypes.c_int, [POINTER(Tables), c_int32, P32, P32]),
+    "tg_zip_bound": (c_size_t, [c_int64]),
+    "tg_zip_workspace_bytes": (c_size_t, [c_int64]),
+    "tg_zip_encode": (ctypes.c_int, [c_void_p, c_int64, c_void_p, c_size_t, c_void_p, c_size_t, c_void_p]),
+    "tg_zip_decode": (ctypes.c_int, [c_void_p, c_int64, c_void_p, c_void_p]),
 }
 
 _LIB = None

@@ -21,6 +21,7 @@ __all__ = [
     "tg_write_kv", "tg_decode_workspace_bytes", "tg_decode_attn", "tg_decode_split",
     "tg_merge_partials", "tg_bench_read", "TG_BENCH_READ_BLOCKS", "tg_append_kv",
     "tg_stream_order", "tg_stream_staging_bytes", "tg_decode_streamed",
+    "tg_zip_bound", "tg_zip_workspace_bytes", "tg_zip_encode", "tg_zip_decode", "zip_compressed_bytes",
 ]
 
 
@@ -387,3 +388,30 @@ def tg_decode_streamed(cache: DeviceCache, tables: Tables, q, out, workspace, n_
     check(lib().tg_decode_streamed(ctypes.byref(cache.struct), ctypes.byref(tables.struct), ctypes.byref(a),
                                    _p32(off), _ptr(staging), int(staging.numel() * staging.element_size()),
                                    _stream_ptr(stream)), "tg_decode_streamed")
+
+
+# --------------------------------------------------------------------------- lossless codec
+def tg_zip_bound(n: int) -> int:
+    return int(lib().tg_zip_bound(int(n)))
+
+
+def tg_zip_workspace_bytes(n: int) -> int:
+    return int(lib().tg_zip_workspace_bytes(int(n)))
+
+
+def tg_zip_encode(src, dst, workspace, stream=None) -> None:
+    """Compress ``src`` (device int16/uint16 tensor of bf16 bits, size a
+    multiple of 8) into ``dst`` (device, >= tg_zip_bound bytes)."""
+    check(lib().tg_zip_encode(_ptr(src), int(src.numel()), _ptr(dst), int(dst.numel() * dst.element_size()),
+                              _ptr(workspace), int(workspace.numel() * workspace.element_size()),
+                              _stream_ptr(stream)), "tg_zip_encode")
+
+
+def tg_zip_decode(src, n: int, dst, stream=None) -> None:
+    check(lib().tg_zip_decode(_ptr(src), int(n), _ptr(dst), _stream_ptr(stream)), "tg_zip_decode")
+
+
+def zip_compressed_bytes(buf) -> int:
+    """Size of a compressed buffer from its header (reads 16 bytes back)."""
+    h = buf[:16].cpu().numpy().view(np.int64)
+    return 256 + int(h[0]) + int(h[0]) // 2 + 5 * int(h[1])

@@ -32,7 +32,7 @@ HIP_FLAGS = [
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-I", INCLUDE, "-Wall", "-Wextra"]
 
-HIP_SOURCES = ["tg_decode.hip", "tg_split.hip", "tg_kvwrite.hip", "tg_bench.hip"]
+HIP_SOURCES = ["tg_decode.hip", "tg_split.hip", "tg_kvwrite.hip", "tg_bench.hip", "tg_zip.hip"]
 CXX_SOURCES = ["tg_host.cpp"]
 
 

@@ -1,0 +1,269 @@
+// Lossless bf16 exponent codec (gfx950), SplitZip page ("Die SplitZip-
+// Strategie", "Warum es schnell ist"): the 16 most frequent exponents get
+// 4-bit codes packed two per byte, sign and mantissa go to one byte per value,
+// and values with any other exponent are listed in an escape stream
+// (position, exponent) that decoding writes over its first result.  Buffer
+// format in include/tg.h.
+//
+// Encode: exponent histogram (LDS per workgroup, then global atomics) ->
+// codebook (one workgroup ranks the 256 counts) -> streams + escape count per
+// workgroup -> exclusive scan of the counts -> escape records in position
+// order.  Decode: one pass over the streams, then one thread per escape.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "tg.h"
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kPerThread = 8;                           // values per thread and step (16 bytes)
+constexpr int kSteps = 4;                               // steps per workgroup
+constexpr int64_t kPerBlock = kThreads * kPerThread * kSteps;  // values per encode workgroup
+constexpr int64_t kHeader = 256;
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+struct Work {  // device workspace
+  uint32_t hist[256];
+  uint32_t code_of[256];  // code, or 16 for an escaped exponent
+  int64_t n_esc;
+  // then block counts [n_blocks], block offsets [n_blocks] (uint32 each)
+};
+
+__global__ void zero_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = 0;
+}
+
+__device__ __forceinline__ uint32_t exp_of(uint32_t v) { return (v >> 7) & 0xFFu; }
+
+__global__ __launch_bounds__(kThreads) void hist_kernel(const u32x4_t* __restrict__ src, int64_t n16,
+                                                        Work* __restrict__ ws) {
+  __shared__ uint32_t h[256];
+  h[threadIdx.x] = 0;
+  __syncthreads();
+  for (int64_t i = blockIdx.x * int64_t(kThreads) + threadIdx.x; i < n16; i += int64_t(gridDim.x) * kThreads) {
+    const u32x4_t x = __builtin_nontemporal_load(src + i);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      atomicAdd(&h[exp_of(x[k])], 1u);
+      atomicAdd(&h[exp_of(x[k] >> 16)], 1u);
+    }
+  }
+  __syncthreads();
+  if (h[threadIdx.x]) atomicAdd(&ws->hist[threadIdx.x], h[threadIdx.x]);
+}
+
+// Rank of exponent e: count descending, then exponent ascending.
+__global__ __launch_bounds__(256) void book_kernel(Work* __restrict__ ws, uint8_t* __restrict__ dst, int64_t n) {
+  __shared__ uint32_t c[256];
+  const int e = threadIdx.x;
+  c[e] = ws->hist[e];
+  __syncthreads();
+  int rank = 0;
+  for (int f = 0; f < 256; ++f) rank += (c[f] > c[e]) || (c[f] == c[e] && f < e);
+  ws->code_of[e] = rank < 16 ? rank : 16;
+  if (rank < 16) dst[16 + rank] = static_cast<uint8_t>(e);
+  if (e < 224) dst[32 + e] = 0;
+  if (e == 0) {
+    ws->n_esc = 0;
+    *reinterpret_cast<int64_t*>(dst) = n;
+  }
+}
+
+// Streams of kPerBlock values per workgroup; escape count per workgroup.
+__global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4_t* __restrict__ src, int64_t n,
+                                                          const Work* __restrict__ ws, uint8_t* __restrict__ dst,
+                                                          uint32_t* __restrict__ block_count) {
+  __shared__ uint32_t code_of[256];
+  __shared__ uint32_t red[kThreads / 64];
+  code_of[threadIdx.x] = ws->code_of[threadIdx.x];
+  __syncthreads();
+  uint32_t esc = 0;
+  const int64_t base16 = blockIdx.x * (kPerBlock / kPerThread);
+  for (int step = 0; step < kSteps; ++step) {
+    const int64_t i = base16 + step * kThreads + threadIdx.x;  // 8-value group
+    if (i * kPerThread >= n) break;
+    const u32x4_t x = __builtin_nontemporal_load(src + i);
+    uint32_t sm[2] = {0, 0}, codes = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t v = (x[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+      const uint32_t c = code_of[exp_of(v)];
+      esc += c >> 4;
+      codes |= (c & 15u) << (4 * k);
+      sm[k >> 2] |= (((v >> 15) << 7) | (v & 0x7Fu)) << (8 * (k & 3));
+    }
+    *reinterpret_cast<u32x2_t*>(dst + kHeader + i * 8) = u32x2_t{sm[0], sm[1]};
+    *reinterpret_cast<uint32_t*>(dst + kHeader + n + i * 4) = codes;
+  }
+  // escapes of the workgroup
+  for (int o = 32; o > 0; o >>= 1) esc += __shfl_xor(esc, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = esc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t t = 0;
+    for (int w = 0; w < kThreads / 64; ++w) t += red[w];
+    block_count[blockIdx.x] = t;
+  }
+}
+
+// Exclusive scan of the block counts (one workgroup), total into the header.
+__global__ __launch_bounds__(1024) void scan_kernel(const uint32_t* __restrict__ count, uint32_t* __restrict__ off,
+                                                    int64_t nb, Work* __restrict__ ws, uint8_t* __restrict__ dst) {
+  __shared__ uint32_t part[1024];
+  const int64_t per = (nb + 1023) / 1024;
+  const int64_t lo = threadIdx.x * per, hi = lo + per < nb ? lo + per : nb;
+  uint32_t s = 0;
+  for (int64_t b = lo; b < hi; ++b) s += count[b];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int k = 1; k < 1024; k <<= 1) {  // inclusive scan of the 1024 partial sums
+    const uint32_t v = threadIdx.x >= static_cast<unsigned>(k) ? part[threadIdx.x - k] : 0u;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  uint32_t run = part[threadIdx.x] - s;
+  for (int64_t b = lo; b < hi; ++b) {
+    off[b] = run;
+    run += count[b];
+  }
+  if (threadIdx.x == 1023) {
+    ws->n_esc = part[1023];
+    *reinterpret_cast<int64_t*>(dst + 8) = part[1023];
+  }
+}
+
+// Escape records of a workgroup's values, in position order.
+__global__ __launch_bounds__(kThreads) void escape_kernel(const u32x4_t* __restrict__ src, int64_t n,
+                                                          const Work* __restrict__ ws,
+                                                          const uint32_t* __restrict__ block_count,
+                                                          const uint32_t* __restrict__ block_off,
+                                                          uint8_t* __restrict__ dst) {
+  if (block_count[blockIdx.x] == 0) return;
+  __shared__ uint32_t code_of[256];
+  __shared__ uint32_t scan[kThreads];
+  code_of[threadIdx.x] = ws->code_of[threadIdx.x];
+  const int64_t n_esc = ws->n_esc;
+  uint32_t* pos = reinterpret_cast<uint32_t*>(dst + kHeader + n + n / 2);
+  uint8_t* exps = reinterpret_cast<uint8_t*>(pos + n_esc);
+  uint32_t at = block_off[blockIdx.x];
+  __syncthreads();
+  const int64_t base16 = blockIdx.x * (kPerBlock / kPerThread);
+  for (int step = 0; step < kSteps; ++step) {
+    const int64_t i = base16 + step * kThreads + threadIdx.x;
+    u32x4_t x = {0, 0, 0, 0};
+    const bool in = i * kPerThread < n;
+    if (in) x = src[i];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mine += in ? code_of[exp_of(x[k >> 1] >> (16 * (k & 1)))] >> 4 : 0;
+    scan[threadIdx.x] = mine;
+    __syncthreads();
+    for (int k = 1; k < kThreads; k <<= 1) {
+      const uint32_t v = threadIdx.x >= static_cast<unsigned>(k) ? scan[threadIdx.x - k] : 0u;
+      __syncthreads();
+      scan[threadIdx.x] += v;
+      __syncthreads();
+    }
+    uint32_t w = at + scan[threadIdx.x] - mine;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t e = exp_of(x[k >> 1] >> (16 * (k & 1)));
+      if (in && code_of[e] == 16) {
+        pos[w] = static_cast<uint32_t>(i * kPerThread + k);
+        exps[w] = static_cast<uint8_t>(e);
+        ++w;
+      }
+    }
+    at += scan[kThreads - 1];
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void decode_kernel(const uint8_t* __restrict__ src, int64_t n,
+                                                          u32x4_t* __restrict__ out) {
+  __shared__ uint32_t book[16];
+  if (threadIdx.x < 16) book[threadIdx.x] = src[16 + threadIdx.x];
+  __syncthreads();
+  for (int64_t i = blockIdx.x * int64_t(kThreads) + threadIdx.x; i * kPerThread < n;
+       i += int64_t(gridDim.x) * kThreads) {
+    const u32x2_t sm = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(src + kHeader) + i);
+    const uint32_t codes = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src + kHeader + n) + i);
+    uint32_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t b = (sm[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+      v[k] = ((b >> 7) << 15) | (book[(codes >> (4 * k)) & 15u] << 7) | (b & 0x7Fu);
+    }
+    out[i] = u32x4_t{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void patch_kernel(const uint8_t* __restrict__ src, int64_t n,
+                                                         uint16_t* __restrict__ out) {
+  const int64_t n_esc = *reinterpret_cast<const int64_t*>(src + 8);
+  const uint32_t* pos = reinterpret_cast<const uint32_t*>(src + kHeader + n + n / 2);
+  const uint8_t* exps = reinterpret_cast<const uint8_t*>(pos + n_esc);
+  for (int64_t j = blockIdx.x * int64_t(kThreads) + threadIdx.x; j < n_esc; j += int64_t(gridDim.x) * kThreads) {
+    const uint32_t p = pos[j];
+    if (p < n) out[p] = static_cast<uint16_t>((out[p] & 0x807Fu) | (static_cast<uint32_t>(exps[j]) << 7));
+  }
+}
+
+int64_t n_blocks(int64_t n) { return (n + kPerBlock - 1) / kPerBlock; }
+
+}  // namespace
+
+extern "C" size_t tg_zip_bound(int64_t n) {
+  return n < 0 ? 0 : static_cast<size_t>(kHeader + n + n / 2 + 5 * n);
+}
+
+extern "C" size_t tg_zip_workspace_bytes(int64_t n) {
+  return n < 0 ? 0 : sizeof(Work) + 8 * static_cast<size_t>(n_blocks(n));
+}
+
+extern "C" int tg_zip_encode(const uint16_t* src, int64_t n, void* dst, size_t dst_bytes, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (!src || !dst || !workspace || n < 8 || n % 8 || n > (int64_t(1) << 32)) return TG_EINVAL;
+  if (dst_bytes < tg_zip_bound(n) || workspace_bytes < tg_zip_workspace_bytes(n)) return TG_EINVAL;
+  if (reinterpret_cast<uintptr_t>(src) % 16 || reinterpret_cast<uintptr_t>(dst) % 16 ||
+      reinterpret_cast<uintptr_t>(workspace) % 16)
+    return TG_EINVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Work* ws = static_cast<Work*>(workspace);
+  const int64_t nb = n_blocks(n);
+  uint32_t* count = reinterpret_cast<uint32_t*>(ws + 1);
+  uint32_t* off = count + nb;
+  uint8_t* out = static_cast<uint8_t*>(dst);
+  const u32x4_t* in = reinterpret_cast<const u32x4_t*>(src);
+  const int64_t n16 = n / 8;
+  hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<uint32_t*>(ws->hist), int64_t(256));
+  const int64_t hb = (n16 + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(hist_kernel, dim3(static_cast<unsigned>(hb < 4096 ? hb : 4096)), dim3(kThreads), 0, st, in, n16,
+                     ws);
+  hipLaunchKernelGGL(book_kernel, dim3(1), dim3(256), 0, st, ws, out, n);
+  hipLaunchKernelGGL(encode_kernel, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0, st, in, n, ws, out, count);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, count, off, nb, ws, out);
+  hipLaunchKernelGGL(escape_kernel, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0, st, in, n, ws, count, off,
+                     out);
+  return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
+}
+
+extern "C" int tg_zip_decode(const void* src, int64_t n, uint16_t* dst, void* stream) {
+  if (!src || !dst || n < 8 || n % 8 || n > (int64_t(1) << 32)) return TG_EINVAL;
+  if (reinterpret_cast<uintptr_t>(src) % 16 || reinterpret_cast<uintptr_t>(dst) % 16) return TG_EINVAL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint8_t* in = static_cast<const uint8_t*>(src);
+  const int64_t groups = n / 8;
+  const int64_t gb = (groups + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(decode_kernel, dim3(static_cast<unsigned>(gb < 8192 ? gb : 8192)), dim3(kThreads), 0, st, in, n,
+                     reinterpret_cast<u32x4_t*>(dst));
+  hipLaunchKernelGGL(patch_kernel, dim3(256), dim3(kThreads), 0, st, in, n, dst);
+  return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
+}
