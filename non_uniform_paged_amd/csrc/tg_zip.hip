@@ -5,10 +5,14 @@
 // (position, exponent) that decoding writes over its first result.  Buffer
 // format in include/tg.h.
 //
-// Encode: exponent histogram (LDS per workgroup, then global atomics) ->
-// codebook (one workgroup ranks the 256 counts) -> streams + escape count per
-// workgroup -> exclusive scan of the counts -> escape records in position
-// order.  Decode: one pass over the streams, then one thread per escape.
+// Encode: exponent histogram (16 LDS copies per workgroup so that lanes with
+// the same exponent rarely hit the same counter, then global atomics) ->
+// codebook (one workgroup ranks the 256 counts) -> streams, with each
+// workgroup's escapes staged in the workspace (up to kStage of them) ->
+// exclusive scan of the per-workgroup counts -> escape records placed in
+// position order (staged ones sorted by position; a workgroup with more
+// re-reads its values).  Decode: one pass over the streams, then one thread
+// per escape.
 
 #include <hip/hip_runtime.h>
 
@@ -20,7 +24,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kPerThread = 8;                           // values per thread and step (16 bytes)
-constexpr int kSteps = 4;                               // steps per workgroup
+constexpr int kSteps = 16;                              // steps per workgroup
+constexpr int kStage = 128;                             // escapes staged per workgroup
+constexpr int kCopies = 16;                             // LDS histogram copies
 constexpr int64_t kPerBlock = kThreads * kPerThread * kSteps;  // values per encode workgroup
 constexpr int64_t kHeader = 256;
 
@@ -31,7 +37,8 @@ struct Work {  // device workspace
   uint32_t hist[256];
   uint32_t code_of[256];  // code, or 16 for an escaped exponent
   int64_t n_esc;
-  // then block counts [n_blocks], block offsets [n_blocks] (uint32 each)
+  // then block counts [nb], block offsets [nb] (uint32), staged escape
+  // positions [nb][kStage] (uint32) and exponents [nb][kStage] (uint8)
 };
 
 __global__ void zero_kernel(uint32_t* p, int64_t n) {
@@ -43,19 +50,22 @@ __device__ __forceinline__ uint32_t exp_of(uint32_t v) { return (v >> 7) & 0xFFu
 
 __global__ __launch_bounds__(kThreads) void hist_kernel(const u32x4_t* __restrict__ src, int64_t n16,
                                                         Work* __restrict__ ws) {
-  __shared__ uint32_t h[256];
-  h[threadIdx.x] = 0;
+  __shared__ uint32_t h[kCopies][257];  // padded so that copies sit on different banks
+  for (int k = threadIdx.x; k < kCopies * 257; k += kThreads) (&h[0][0])[k] = 0;
   __syncthreads();
+  uint32_t* mine = h[threadIdx.x % kCopies];
   for (int64_t i = blockIdx.x * int64_t(kThreads) + threadIdx.x; i < n16; i += int64_t(gridDim.x) * kThreads) {
     const u32x4_t x = __builtin_nontemporal_load(src + i);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      atomicAdd(&h[exp_of(x[k])], 1u);
-      atomicAdd(&h[exp_of(x[k] >> 16)], 1u);
+      atomicAdd(&mine[exp_of(x[k])], 1u);
+      atomicAdd(&mine[exp_of(x[k] >> 16)], 1u);
     }
   }
   __syncthreads();
-  if (h[threadIdx.x]) atomicAdd(&ws->hist[threadIdx.x], h[threadIdx.x]);
+  uint32_t t = 0;
+  for (int c = 0; c < kCopies; ++c) t += h[c][threadIdx.x];
+  if (t) atomicAdd(&ws->hist[threadIdx.x], t);
 }
 
 // Rank of exponent e: count descending, then exponent ascending.
@@ -78,12 +88,16 @@ __global__ __launch_bounds__(256) void book_kernel(Work* __restrict__ ws, uint8_
 // Streams of kPerBlock values per workgroup; escape count per workgroup.
 __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4_t* __restrict__ src, int64_t n,
                                                           const Work* __restrict__ ws, uint8_t* __restrict__ dst,
-                                                          uint32_t* __restrict__ block_count) {
+                                                          uint32_t* __restrict__ block_count,
+                                                          uint32_t* __restrict__ stage_pos,
+                                                          uint8_t* __restrict__ stage_exp) {
   __shared__ uint32_t code_of[256];
-  __shared__ uint32_t red[kThreads / 64];
+  __shared__ uint32_t n_staged;
   code_of[threadIdx.x] = ws->code_of[threadIdx.x];
+  if (threadIdx.x == 0) n_staged = 0;
   __syncthreads();
-  uint32_t esc = 0;
+  uint32_t* spos = stage_pos + static_cast<int64_t>(blockIdx.x) * kStage;
+  uint8_t* sexp = stage_exp + static_cast<int64_t>(blockIdx.x) * kStage;
   const int64_t base16 = blockIdx.x * (kPerBlock / kPerThread);
   for (int step = 0; step < kSteps; ++step) {
     const int64_t i = base16 + step * kThreads + threadIdx.x;  // 8-value group
@@ -94,22 +108,21 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4_t* __restr
     for (int k = 0; k < 8; ++k) {
       const uint32_t v = (x[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
       const uint32_t c = code_of[exp_of(v)];
-      esc += c >> 4;
+      if (c == 16) {  // rare: stage (position, exponent), in any order
+        const uint32_t at = atomicAdd(&n_staged, 1u);
+        if (at < kStage) {
+          spos[at] = static_cast<uint32_t>(i * kPerThread + k);
+          sexp[at] = static_cast<uint8_t>(exp_of(v));
+        }
+      }
       codes |= (c & 15u) << (4 * k);
       sm[k >> 2] |= (((v >> 15) << 7) | (v & 0x7Fu)) << (8 * (k & 3));
     }
     *reinterpret_cast<u32x2_t*>(dst + kHeader + i * 8) = u32x2_t{sm[0], sm[1]};
     *reinterpret_cast<uint32_t*>(dst + kHeader + n + i * 4) = codes;
   }
-  // escapes of the workgroup
-  for (int o = 32; o > 0; o >>= 1) esc += __shfl_xor(esc, o, 64);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = esc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t t = 0;
-    for (int w = 0; w < kThreads / 64; ++w) t += red[w];
-    block_count[blockIdx.x] = t;
-  }
+  if (threadIdx.x == 0) block_count[blockIdx.x] = n_staged;
 }
 
 // Exclusive scan of the block counts (one workgroup), total into the header.
@@ -139,20 +152,38 @@ __global__ __launch_bounds__(1024) void scan_kernel(const uint32_t* __restrict__
   }
 }
 
-// Escape records of a workgroup's values, in position order.
+// Escape records of a workgroup's values, in position order: the staged
+// ones ranked by position, or (more than kStage) found again by re-reading.
 __global__ __launch_bounds__(kThreads) void escape_kernel(const u32x4_t* __restrict__ src, int64_t n,
                                                           const Work* __restrict__ ws,
                                                           const uint32_t* __restrict__ block_count,
                                                           const uint32_t* __restrict__ block_off,
+                                                          const uint32_t* __restrict__ stage_pos,
+                                                          const uint8_t* __restrict__ stage_exp,
                                                           uint8_t* __restrict__ dst) {
-  if (block_count[blockIdx.x] == 0) return;
+  const uint32_t count = block_count[blockIdx.x];
+  if (count == 0) return;
   __shared__ uint32_t code_of[256];
   __shared__ uint32_t scan[kThreads];
-  code_of[threadIdx.x] = ws->code_of[threadIdx.x];
   const int64_t n_esc = ws->n_esc;
   uint32_t* pos = reinterpret_cast<uint32_t*>(dst + kHeader + n + n / 2);
   uint8_t* exps = reinterpret_cast<uint8_t*>(pos + n_esc);
   uint32_t at = block_off[blockIdx.x];
+  if (count <= kStage) {
+    const uint32_t* sp = stage_pos + static_cast<int64_t>(blockIdx.x) * kStage;
+    const uint8_t* se = stage_exp + static_cast<int64_t>(blockIdx.x) * kStage;
+    if (threadIdx.x < count) scan[threadIdx.x] = sp[threadIdx.x];
+    __syncthreads();
+    if (threadIdx.x < count) {
+      const uint32_t p = scan[threadIdx.x];
+      uint32_t rank = 0;  // positions are distinct
+      for (uint32_t j = 0; j < count; ++j) rank += scan[j] < p;
+      pos[at + rank] = p;
+      exps[at + rank] = se[threadIdx.x];
+    }
+    return;
+  }
+  code_of[threadIdx.x] = ws->code_of[threadIdx.x];
   __syncthreads();
   const int64_t base16 = blockIdx.x * (kPerBlock / kPerThread);
   for (int step = 0; step < kSteps; ++step) {
@@ -225,7 +256,7 @@ extern "C" size_t tg_zip_bound(int64_t n) {
 }
 
 extern "C" size_t tg_zip_workspace_bytes(int64_t n) {
-  return n < 0 ? 0 : sizeof(Work) + 8 * static_cast<size_t>(n_blocks(n));
+  return n < 0 ? 0 : sizeof(Work) + (8 + 5 * kStage) * static_cast<size_t>(n_blocks(n));
 }
 
 extern "C" int tg_zip_encode(const uint16_t* src, int64_t n, void* dst, size_t dst_bytes, void* workspace,
@@ -240,6 +271,8 @@ extern "C" int tg_zip_encode(const uint16_t* src, int64_t n, void* dst, size_t d
   const int64_t nb = n_blocks(n);
   uint32_t* count = reinterpret_cast<uint32_t*>(ws + 1);
   uint32_t* off = count + nb;
+  uint32_t* spos = off + nb;
+  uint8_t* sexp = reinterpret_cast<uint8_t*>(spos + nb * kStage);
   uint8_t* out = static_cast<uint8_t*>(dst);
   const u32x4_t* in = reinterpret_cast<const u32x4_t*>(src);
   const int64_t n16 = n / 8;
@@ -248,10 +281,11 @@ extern "C" int tg_zip_encode(const uint16_t* src, int64_t n, void* dst, size_t d
   hipLaunchKernelGGL(hist_kernel, dim3(static_cast<unsigned>(hb < 4096 ? hb : 4096)), dim3(kThreads), 0, st, in, n16,
                      ws);
   hipLaunchKernelGGL(book_kernel, dim3(1), dim3(256), 0, st, ws, out, n);
-  hipLaunchKernelGGL(encode_kernel, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0, st, in, n, ws, out, count);
+  hipLaunchKernelGGL(encode_kernel, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0, st, in, n, ws, out, count,
+                     spos, sexp);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, st, count, off, nb, ws, out);
   hipLaunchKernelGGL(escape_kernel, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0, st, in, n, ws, count, off,
-                     out);
+                     spos, sexp, out);
   return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
 }
 
