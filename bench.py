@@ -34,8 +34,8 @@ METRIC = "effective KV GB/s (and % of HBM peak) in ragged-paged decode attention
 # Plan item lengths (bf16 rows, INT8 rows) per workload, chosen by sweeping
 # the split-kernel time on MI355X: the best length depends on how the item
 # count falls against the ~2048 resident wavefronts and on the length mix.
-PLAN_CHUNKS = {"tiny": (1024, 1024), "llama8b": (1024, 1024), "ragged": (4096, 1024),
-               "tiered": (1024, 1536), "tiered4": (1024, 1536), "radix": (768, 1024)}
+PLAN_CHUNKS = {"tiny": (1024, 1024), "llama8b": (896, 1024), "ragged": (4096, 1024),
+               "tiered": (512, 1792), "tiered4": (512, 2048), "radix": (768, 1024)}
 
 DESCRIPTIONS = {
     "tiny": "tiny: 2 requests, 4/2 heads, d 64, ctx 256, budgets in {32..256}, 2 clusters",

@@ -187,7 +187,9 @@ int32_t tg_pool_refcount(const tg_pool* pool, int32_t c, int32_t tier, int64_t p
  *           k = ceil(u / (chunk / unit)) near-equal items, item i starting at
  *           unit floor(i * u / k).  slot = index of the item's partial;
  *           part_off [B*H + 1] = first slot of each (r, h).  With lpt != 0 the
- *           items are stably sorted by descending (t1 - t0) * (2 bf16 | 1 INT8).
+ *           items are stably sorted by descending (t1 - t0) * w, w in
+ *           proportion to a row's HBM bytes: 16 qb for bf16, old_bits * qb + 16
+ *           for the quantised tier (old_bits of the pool).
  *   groups  with group_size > 1 and `share`, the leading shared bf16 pages of
  *           each (r, h) are cut into runs of one radix node; requests whose
  *           run has the same (node, first row, pages, n_i8) are taken in

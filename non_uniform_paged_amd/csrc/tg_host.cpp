@@ -91,7 +91,7 @@ struct SubPool {
 }  // namespace
 
 struct tg_pool {
-  int32_t C = 0, d = 0, page_size = 0, quant_block = 0;
+  int32_t C = 0, d = 0, page_size = 0, quant_block = 0, old_bits = 8;
   std::vector<int32_t> cluster_size;
   SubPool sub[TG_MAX_CLUSTERS][2];
   std::unordered_map<ShareKey, int64_t, ShareKeyHash> registry;
@@ -215,6 +215,7 @@ extern "C" int tg_pool_create(int32_t C, const int32_t* cluster_size, int32_t d,
     p->d = d;
     p->page_size = ps;
     p->quant_block = qb;
+    p->old_bits = old_bits;
     p->cluster_size.assign(cluster_size, cluster_size + C);
     for (int32_t c = 0; c < C; ++c) {
       p->sub[c][TG_TIER_BF16].init(pages_bf[c], head_bytes(TG_TIER_BF16, d, ps, qb, old_bits) * cluster_size[c]);
@@ -480,8 +481,14 @@ struct RunIdentHash {
   }
 };
 
+// Longest-first cost of one row of tier t: its HBM bytes (4d for bf16; codes
+// 2d * bits / 8 plus 4d / qb of scales for the quantised tier) times 4 qb / d.
+int64_t lpt_weight(int32_t t, int32_t qb, int32_t bits) {
+  return t == TG_TIER_BF16 ? 16 * int64_t(qb) : int64_t(bits) * qb + 16;
+}
+
 int make_plan(const tg_reservation* res, const Geometry& g, const Paths& paths, const tg_plan_opts* o,
-              Plan* p) {
+              int32_t old_bits, Plan* p) {
   int64_t bound = 0;
   int st = count_plan(res, g, o, &bound);
   if (st) return st;
@@ -574,7 +581,7 @@ int make_plan(const tg_reservation* res, const Geometry& g, const Paths& paths, 
     for (int32_t k = 0; k < n; ++k) order[k] = k;
     auto cost = [&](int32_t k) {
       const int32_t* w = p->work.data() + int64_t(k) * 6;
-      return int64_t(w[4] - w[3]) * (w[2] == TG_TIER_BF16 ? 2 : 1);
+      return int64_t(w[4] - w[3]) * lpt_weight(w[2], g.qb, old_bits);
     };
     std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return cost(a) > cost(b); });
     std::vector<int32_t> tmp(p->work);
@@ -609,7 +616,8 @@ extern "C" int tg_size_tables(const tg_reservation* live, int32_t ps, int32_t qb
   }
   Plan plan;
   try {
-    if ((st = make_plan(res, g, paths, opts, &plan))) return st;
+    // (the longest-first order, the only use of the code width, changes no size)
+    if ((st = make_plan(res, g, paths, opts, 8, &plan))) return st;
   } catch (...) {
     return TG_ENOMEM;
   }
@@ -666,7 +674,7 @@ extern "C" int tg_build_tables(tg_pool* pool, const tg_reservation* live, const 
     return TG_EINVAL;
   Plan plan;
   try {
-    if ((st = make_plan(res, g, paths, opts, &plan))) return st;
+    if ((st = make_plan(res, g, paths, opts, pool->old_bits, &plan))) return st;
   } catch (...) {
     return TG_ENOMEM;
   }

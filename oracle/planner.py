@@ -46,8 +46,11 @@ R-plan   items (r, h, tier, t0, t1, slot) in order r, h, tier (INT8 first).
          partial) is cut into k = ceil(u / (chunk / unit)) items as equal as
          whole units allow: item i starts at unit floor(i * u / k).  slot is
          the natural index; part_off is the CSR of slots per (r, h).  With lpt,
-         items are stably sorted by descending cost (t1 - t0) * (2 for bf16,
-         1 for INT8).
+         items are stably sorted by descending cost (t1 - t0) * w_tier, w_tier
+         proportional to the HBM bytes one row of the tier costs: a bf16 row is
+         4d bytes, a quantised row 2d * bits / 8 bytes of codes plus 4d / Qb of
+         scales, so w = 16 Qb (bf16) and bits * Qb + 16 (INT8 or INT4), the
+         common factor d / (4 Qb) dropped.
 R-step   (decode-step growth) an appended row becomes the newest bf16 row
          and R-tier is applied to the new length; when the INT8 boundary moves
          (by one block) the oldest Qb bf16 rows are quantised (R-q) into the
@@ -423,8 +426,15 @@ def split_range(lo: int, hi: int, unit: int, chunk: int):
     return [(lo + (i * u // k) * unit, min(lo + ((i + 1) * u // k) * unit, hi)) for i in range(k)]
 
 
+def lpt_weight(tier: int, quant_block: int, old_bits: int) -> int:
+    """Cost of one row of ``tier`` in the longest-first order (R-plan): its
+    HBM bytes times 4 Qb / d."""
+    return 16 * quant_block if tier == TIER_BF else old_bits * quant_block + 16
+
+
 def plan(res: Reservation, chunk_bf: int, chunk_i8: int, lpt: bool, group_size: int = 0,
-         page_size: int = 16, quant_block: int = 64, n_fixed=None, paths=None, node_len=None):
+         page_size: int = 16, quant_block: int = 64, n_fixed=None, paths=None, node_len=None,
+         old_bits: int = 8):
     """Split plan, partial CSR and group-item member table (R-plan, R-group).
 
     Returns (work, part_off, gitems).  A work item is (r, h, tier, t0, t1,
@@ -486,14 +496,14 @@ def plan(res: Reservation, chunk_bf: int, chunk_i8: int, lpt: bool, group_size: 
     gitems = [[(m, gslot[gi][k]) for k, m in enumerate(grp)] + [(-1, -1)] * (GROUP_WIDTH - len(grp))
               for gi, grp in enumerate(gitems_members)]
     if lpt:
-        work = sorted(work, key=lambda it: -(it[4] - it[3]) * (2 if it[2] == TIER_BF else 1))
+        work = sorted(work, key=lambda it: -(it[4] - it[3]) * lpt_weight(it[2], quant_block, old_bits))
     return work, part_off, gitems
 
 
 def build_tables(pool: Pool, res: Reservation, page_size: int, quant_block: int,
                  chunk_bf: int, chunk_i8: int, lpt: bool,
                  n_fixed=None, paths=None, node_len=None, group_size: int = 0,
-                 gen_tokens: int = 0) -> Tables:
+                 gen_tokens: int = 0, old_bits: int = 8) -> Tables:
     """Allocate pages and emit block tables, lengths and the plan (R-alloc,
     R-page, R-plan, R-group).  With gen_tokens > 0 pages and plan cover the
     capacity for that many appended rows (R-step); lengths stay the live ones
@@ -518,7 +528,7 @@ def build_tables(pool: Pool, res: Reservation, page_size: int, quant_block: int,
     lens = [[(live.n_i8[r][h], live.n_bf[r][h]) for h in range(H)] for r in range(B)]
     nf = [0] * B if n_fixed is None else list(n_fixed)
     work, part_off, gitems = plan(res, chunk_bf, chunk_i8, lpt, group_size, page_size, quant_block,
-                                  nf, paths, node_len)
+                                  nf, paths, node_len, old_bits)
     t = Tables(bt, stride, lens, work, part_off, pages)
     t.gitems = gitems
     t.ring = [[len(pages[r][c][TIER_BF]) for c in range(C)] for r in range(B)]

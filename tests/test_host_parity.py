@@ -68,11 +68,11 @@ def _tables_parity(w, chunk_bf=512, chunk_i8=1024, lpt=True, slack=3, group_size
     assert [row[1] for row in sizes["pages_needed"]] == need_bf
     assert [row[0] for row in sizes["pages_needed"]] == need_i8
     pool_g = tg.Pool(res_g.cluster_size, w.d, w.page_size, w.quant_block,
-                     [x + slack for x in need_bf], [x + slack for x in need_i8])
+                     [x + slack for x in need_bf], [x + slack for x in need_i8], old_bits=w.old_bits)
     pool_o = P.Pool([x + slack for x in need_bf], [x + slack for x in need_i8])
     t_g = tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt, group_size, gen)
     t_o = P.build_tables(pool_o, res_o, w.page_size, w.quant_block, chunk_bf, chunk_i8, lpt, *sh_o,
-                         **({"group_size": group_size} if sh_o else {"gen_tokens": gen}))
+                         **({"group_size": group_size} if sh_o else {"gen_tokens": gen}), old_bits=w.old_bits)
     for c in range(w.n_clusters):
         for t in range(2):
             assert t_g.stride[c][t] == t_o.stride[c][t]
@@ -95,7 +95,8 @@ def test_growth_tables_bit_exact(name, gen):
     assert np.array_equal(t_g.len[..., 0], np.array(res_o.n_i8)) and np.array_equal(t_g.len[..., 1], np.array(res_o.n_bf))
 
 
-@pytest.mark.parametrize("name,gs", [("tiny", 0), ("llama8b", 0), ("ragged", 0), ("tiered", 0), ("radix", 0),
+@pytest.mark.parametrize("name,gs", [("tiny", 0), ("llama8b", 0), ("ragged", 0), ("tiered", 0), ("tiered4", 0),
+                                     ("radix", 0),
                                      ("radix", 2), ("radix", 8), ("radix", 32)])
 def test_full_size_configs_bit_exact(name, gs):
     w = make_workload(name)
@@ -170,10 +171,11 @@ def test_randomised_small_cases_bit_exact():
         cap_i8 = [n + rnd.randint(-1, 2) for n in need_i8]
         cap_bf = [max(0, x) for x in cap_bf]
         cap_i8 = [max(0, x) for x in cap_i8]
-        pool_g = tg.Pool(res_g.cluster_size, 16, ps, qb, cap_bf, cap_i8)
+        bits = rnd.choice([8, 4])
+        pool_g = tg.Pool(res_g.cluster_size, 16, ps, qb, cap_bf, cap_i8, old_bits=bits)
         pool_o = P.Pool(cap_bf, cap_i8)
         try:
-            t_o = P.build_tables(pool_o, res_o, ps, qb, chunk_bf, chunk_i8, lpt, *sh_o, **grp)
+            t_o = P.build_tables(pool_o, res_o, ps, qb, chunk_bf, chunk_i8, lpt, *sh_o, **grp, old_bits=bits)
         except P.OracleError as e:
             assert e.code == "ENOMEM"
             with pytest.raises(tg.TGError) as ge:

@@ -264,6 +264,30 @@ def test_invariants(name):
     assert not pool.registry
 
 
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("chunks", [(64, 128), (128, 192), (256, 64), (48, 320)])
+def test_longest_first_order_follows_bytes_read(bits, chunks):
+    """The longest-first order ranks items by the HBM bytes they read, priced
+    from the page layout itself: a bf16 head page is ps rows of K and V at 2
+    bytes a value; a quantised head block is qb rows of K and V codes at
+    bits / 8 bytes a value plus one 2-byte scale per channel for K and for V.
+    Equal bytes keep the natural (slot) order."""
+    from fractions import Fraction
+    w = make_workload("tiered", B=3, ctx=("fixed", 2900), recent_ppm=300_000)
+    res = P.reserve(w.head_rank, w.ratio_hi_ppm, w.ratio_lo_ppm, w.n_clusters, w.recent_ppm,
+                    w.quant_block, w.n_comp, w.n_fixed, w.budget_override)
+    need_bf, need_i8 = P.pages_needed(res, w.page_size, w.quant_block)
+    t = P.build_tables(P.Pool(need_bf, need_i8), res, w.page_size, w.quant_block, chunks[0], chunks[1], True,
+                       old_bits=bits)
+    d, ps, qb = w.d, w.page_size, w.quant_block
+    per_row = {P.TIER_BF: Fraction(ps * 2 * d * 2, ps),
+               P.TIER_I8: Fraction(qb * 2 * d * bits // 8 + 2 * d * 2, qb)}
+    key = [(-(t1 - t0) * per_row[tier], slot) for (r, h, tier, t0, t1, slot) in t.work]
+    assert key == sorted(key)
+    # both tiers and several lengths take part, so the order is not trivial
+    assert len({it[2] for it in t.work}) == 2 and len({it[4] - it[3] for it in t.work}) > 3
+
+
 def test_rejects_bad_admission_inputs():
     with pytest.raises(P.OracleError):
         P.reserve([0, 0], 10, 10, 1, 10**6, 64, [5])
