@@ -31,12 +31,6 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "effective KV GB/s (and % of HBM peak) in ragged-paged decode attention"
-# Plan item lengths (bf16 rows, INT8 rows) per workload, chosen by sweeping
-# the split-kernel time on MI355X: the best length depends on how the item
-# count falls against the ~2048 resident wavefronts and on the length mix.
-PLAN_CHUNKS = {"tiny": (1024, 1024), "llama8b": (896, 1024), "ragged": (4096, 1024),
-               "tiered": (512, 1792), "tiered4": (512, 2048), "radix": (768, 1024)}
-
 DESCRIPTIONS = {
     "tiny": "tiny: 2 requests, 4/2 heads, d 64, ctx 256, budgets in {32..256}, 2 clusters",
     "llama8b": "Llama-3-8B-shaped layer: batch 64, 32/8 heads, d 128, ctx U[4096,16384], ratio 0.50->0.10 by head rank, 2 clusters, page 16, bf16",
@@ -309,7 +303,7 @@ def main():
         return
 
     from non_uniform_paged_amd import api
-    from non_uniform_paged_amd.runner import Prepared, allocated_bytes
+    from non_uniform_paged_amd.runner import PLAN_CHUNKS, Prepared, allocated_bytes
     from workloads import make_workload
 
     torch.cuda.set_device(0)

@@ -15,6 +15,13 @@ import numpy as np
 
 from . import api
 
+# Plan item lengths (bf16 rows, quantised-tier rows) per workload, chosen by
+# sweeping the split-kernel time on MI355X: the best length depends on how
+# the item count falls against the ~2048 resident wavefronts and on the
+# length mix.  The benchmark and the full-size parity tests both use them.
+PLAN_CHUNKS = {"tiny": (1024, 1024), "llama8b": (896, 1024), "ragged": (4096, 1024),
+               "tiered": (512, 1792), "tiered4": (512, 2048), "radix": (768, 1024)}
+
 
 def reserve_workload(w) -> api.Reservation:
     return api.tg_reserve(w.head_rank, w.ratio_hi_ppm, w.ratio_lo_ppm, w.n_clusters, w.recent_ppm,

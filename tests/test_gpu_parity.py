@@ -94,11 +94,16 @@ def _sample_pairs(w, k, seed):
     return sorted((int(i) // w.Hkv, int(i) % w.Hkv) for i in idx)
 
 
-@pytest.mark.parametrize("name,k", [("llama8b", 24), ("ragged", 24), ("tiered", 8), ("radix", 24)])
+@pytest.mark.parametrize("name,k", [("llama8b", 24), ("ragged", 24), ("tiered", 8), ("tiered4", 8),
+                                    ("radix", 24)])
 def test_full_size_configs_sampled(name, k):
+    """Full sizes in the benchmark's launch configuration (its plan item
+    lengths and group size), sampled (r, h) pairs against the oracle."""
     _need_gpu()
+    from non_uniform_paged_amd.runner import PLAN_CHUNKS
     w = make_workload(name)
-    _run_and_compare(w, pairs=_sample_pairs(w, k, 11), what=f"{name}-full")
+    chunk_bf, chunk_i8 = PLAN_CHUNKS[name]
+    _run_and_compare(w, pairs=_sample_pairs(w, k, 11), what=f"{name}-full", chunk_bf=chunk_bf, chunk_i8=chunk_i8)
 
 
 def test_single_row_returns_value_row_exactly():
