@@ -447,11 +447,13 @@ int tg_zip_decode(const void* src, int64_t n, uint16_t* dst, void* stream);
  *
  * Streaming read of `bytes` (a multiple of 16) at `src` (16-byte aligned
  * device memory) with non-temporal loads over TG_BENCH_READ_BLOCKS
- * workgroups; each writes one fold of what it read to sink[block] (device
+ * workgroups sweeping the buffer together (pass k of workgroup b reads the
+ * 16 KiB tile k * TG_BENCH_READ_BLOCKS + b); each writes one fold of what it
+ * read to sink[block] (device
  * uint32 [TG_BENCH_READ_BLOCKS]) so that no load is elided.  Timing it gives
  * the device's achievable read rate.  TG_EINVAL on a bad size or pointer.
  * ---------------------------------------------------------------------- */
-#define TG_BENCH_READ_BLOCKS 2048
+#define TG_BENCH_READ_BLOCKS 4096
 int tg_bench_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus

@@ -23,7 +23,7 @@ STATUS_NAMES = {0: "TG_OK", -1: "TG_EINVAL", -2: "TG_ENOMEM", -3: "TG_EOVERFLOW"
 TG_TIER_I8 = 0
 TG_TIER_BF16 = 1
 TG_GROUP_WIDTH = 32
-TG_BENCH_READ_BLOCKS = 2048
+TG_BENCH_READ_BLOCKS = 4096
 TG_MAX_CLUSTERS = 16
 TG_Q_F32 = 0
 TG_Q_BF16 = 1

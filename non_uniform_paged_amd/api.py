@@ -98,6 +98,8 @@ class Pool:
         self.old_bits = int(old_bits)
         pb = np.ascontiguousarray(pages_bf, dtype=np.int64)
         pi = np.ascontiguousarray(pages_i8, dtype=np.int64)
+        if pb.size != self.C or pi.size != self.C:
+            raise ValueError("pages_bf and pages_i8 need one entry per cluster")
         h = ctypes.c_void_p()
         check(lib().tg_pool_create(self.C, _p32(cs), self.head_dim, self.page_size, self.quant_block,
                                    self.old_bits, pb.ctypes.data_as(L.P64), pi.ctypes.data_as(L.P64),

@@ -1,9 +1,11 @@
 // Measurement aid (gfx950): the achievable streaming-read rate of the device,
 // the ceiling the decode split kernels are compared with besides the HBM
-// peak.  Workgroup b reads its own contiguous 1/nblocks of the buffer, 16 KiB
-// per step (each wavefront 1 KiB contiguous per load, four loads in flight per
-// thread), with non-temporal loads, and folds the words into one per
-// workgroup so that no load can be dropped.
+// peak.  The grid sweeps the buffer together: pass k of workgroup b reads the
+// 16 KiB tile (k * gridDim.x + b) (each wavefront 1 KiB contiguous per load,
+// four loads in flight per thread) with non-temporal loads, so that the
+// addresses in flight at any moment stay close (on MI355X this reads ~5 %
+// faster than giving each workgroup its own contiguous range); each workgroup
+// folds the words it read into one so that no load can be dropped.
 
 #include "tg_device.h"
 
@@ -12,22 +14,19 @@ namespace {
 
 __global__ __launch_bounds__(256) void read_kernel(const TG_GLOBAL u32x4_t* __restrict__ src, int64_t n16,
                                                    TG_GLOBAL uint32_t* __restrict__ sink) {
-  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
-  const int64_t lo = static_cast<int64_t>(blockIdx.x) * per;
-  const int64_t hi = lo + per < n16 ? lo + per : n16;
+  constexpr int kLoads = 4;  // 16-byte loads in flight per thread
+  const int64_t tile = 256 * kLoads;
+  const int64_t step = static_cast<int64_t>(gridDim.x) * tile;
   uint32_t acc = 0;
-  int64_t i = lo + threadIdx.x;
-  for (; i + 3 * 256 < hi; i += 4 * 256) {
-    const u32x4_t a = __builtin_nontemporal_load(src + i);
-    const u32x4_t b = __builtin_nontemporal_load(src + i + 256);
-    const u32x4_t c = __builtin_nontemporal_load(src + i + 512);
-    const u32x4_t d = __builtin_nontemporal_load(src + i + 768);
-    acc ^= (a[0] ^ a[1] ^ a[2] ^ a[3]) ^ (b[0] ^ b[1] ^ b[2] ^ b[3]) ^ (c[0] ^ c[1] ^ c[2] ^ c[3]) ^
-           (d[0] ^ d[1] ^ d[2] ^ d[3]);
-  }
-  for (; i < hi; i += 256) {
-    const u32x4_t a = __builtin_nontemporal_load(src + i);
-    acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * tile + threadIdx.x; base < n16; base += step) {
+    u32x4_t v[kLoads];
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      const int64_t j = base + u * 256;
+      v[u] = j < n16 ? __builtin_nontemporal_load(src + j) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
   __shared__ uint32_t red[256];
   red[threadIdx.x] = acc;
