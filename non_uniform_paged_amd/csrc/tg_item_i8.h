@@ -34,7 +34,7 @@
 // (64g + l)*4 + s, nibble ((e&1)<<2) | (e>>1); V codes (at +32d) of lane l
 // (channel l%16 of tile n, rows 16g + 4(l/16) + i) are word (64g + l)*4 + n/2,
 // nibble ((i&1)<<2) | ((n&1)<<1) | (i>>1); scales at +64d (K) and +66d (V).
-// Two bit operations per pair of values turn a word into fp16 operands.
+// Five bit operations turn a word of 8 codes into four fp16 operand words.
 
 #include <cmath>
 
@@ -43,7 +43,8 @@
 namespace tg_dev {
 
 constexpr uint32_t kF16x2_1152 = 0x64806480u;  // two fp16 1152.0
-constexpr uint32_t kF16x2_24 = 0x4E004E00u;    // two fp16 24.0
+constexpr uint32_t kF16x2_1032 = 0x64086408u;  // two fp16 1032.0
+constexpr uint32_t kF16x2_72 = 0x54805480u;    // two fp16 72.0
 
 // 4 int8 codes (one dword) -> 4 fp16 values 1152 + q8 (two dwords)
 __device__ __forceinline__ u32x2_t codes_to_f16(uint32_t w) {
@@ -52,13 +53,16 @@ __device__ __forceinline__ u32x2_t codes_to_f16(uint32_t w) {
                  __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u)};
 }
 
-// 8 INT4 codes u = q4 + 8 (one dword, nibble k = bits 4k..4k+3) -> 8 fp16
-// values 16 + u = 24 + q4: word k of the result holds nibbles k and k + 4
-// (placed in mantissa bits 6..9 of fp16 16.0).
+// 8 INT4 codes u = q4 + 8 (one dword, nibble k = bits 4k..4k+3) -> 8 exact
+// fp16 values; word k of the result holds nibbles k and k + 4.  A nibble in
+// bits 0..3 of a 16-bit half is the low mantissa of fp16 1024 (value
+// 1024 + u = 1032 + q4); one in bits 4..7 sits in mantissa bits 4..7 of fp16
+// 64 (value 64 + u = 72 + q4); a byte shift brings nibbles 2, 3, 6, 7 to
+// those places.  Words 0 and 2 are offset by 1032, words 1 and 3 by 72.
 __device__ __forceinline__ u32x4_t nibbles_to_f16(uint32_t x) {
-  constexpr uint32_t kMask = 0x03C003C0u, k16 = 0x4C004C00u;
-  return u32x4_t{((x << 6) & kMask) | k16, ((x << 2) & kMask) | k16, ((x >> 2) & kMask) | k16,
-                 ((x >> 6) & kMask) | k16};
+  const uint32_t y = x >> 8;
+  return u32x4_t{(x & 0x000F000Fu) | 0x64006400u, (x & 0x00F000F0u) | 0x54005400u,
+                 (y & 0x000F000Fu) | 0x64006400u, (y & 0x00F000F0u) | 0x54005400u};
 }
 
 __device__ __forceinline__ float half_lo(uint32_t w) {
@@ -70,7 +74,9 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
 
 // BITS = 4: the INT4 page (include/tg.h): per 16-row group one 16-byte load
 // per lane holds all d = 128 channels of K (and one all of V) as nibbles;
-// values 24 + q4 take the place of 1152 + q8, and the rest is unchanged.
+// values 1032 + q4 or 72 + q4 (by operand word, nibbles_to_f16) take the
+// place of 1152 + q8, the constant tiles carry the same per-word offsets,
+// and the rest is unchanged.
 template <int D, int G, bool QF32, int DEPTH, bool STREAM, int BITS>
 __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0, int t1, int slot,
                                         int hs, const TG_GLOBAL int32_t* bt_row, gptr pool,
@@ -78,7 +84,6 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
   static_assert(BITS == 8 || (BITS == 4 && D == 128), "INT4 pages are laid out for d = 128");
   constexpr int NL = BITS == 8 ? D / 64 : 1;  // 1 KiB loads per 16-row group (K codes, V codes)
   constexpr int CODE_BYTES = kQBlock * D * BITS / 8;  // K (or V) codes of one head's block
-  constexpr uint32_t kBias = BITS == 8 ? kF16x2_1152 : kF16x2_24;
   // INT8: q' and the weights P enter the matrix cores as fp16 high + low
   // parts (~22 significant bits).  INT4: one fp16 part each (11 bits, far
   // finer than the 4-bit codes they multiply), half the matrix-core work.
@@ -125,8 +130,12 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
   float l_run = 0.f;
   const int64_t head_off = static_cast<int64_t>(hs) * (2 * CODE_BYTES + 4 * D);
   const int lane_off = lane * 16;
-  const u32x4_t c1152x8 = {kBias, kBias, kBias, kBias};  // constant-offset operands
-  const u32x2_t c1152x4 = {kBias, kBias};
+  // constant-offset operands: 1152 for every INT8 value; for INT4 the offsets
+  // of the operand words (K: words 0-3 of a step; V: the two words of a tile)
+  constexpr uint32_t kOffA = BITS == 8 ? kF16x2_1152 : kF16x2_1032;
+  constexpr uint32_t kOffB = BITS == 8 ? kF16x2_1152 : kF16x2_72;
+  const u32x4_t c1152x8 = {kOffA, kOffB, kOffA, kOffB};
+  const u32x2_t c1152x4 = {kOffA, kOffB};
   const int b0 = t0 / kQBlock;
   const int nb = (t1 - t0) / kQBlock;
 
