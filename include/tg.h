@@ -189,7 +189,11 @@ int32_t tg_pool_refcount(const tg_pool* pool, int32_t c, int32_t tier, int64_t p
  *           part_off [B*H + 1] = first slot of each (r, h).  With lpt != 0 the
  *           items are stably sorted by descending (t1 - t0) * w, w in
  *           proportion to a row's HBM bytes: 16 qb for bf16, old_bits * qb + 16
- *           for the quantised tier (old_bits of the pool).
+ *           for the quantised tier (old_bits of the pool); group items stay
+ *           ahead of the others.  The split kernel runs each of the leading
+ *           n_gitems entries on a whole workgroup (four wavefronts sharing the
+ *           page loads); a plan in another order still decodes correctly,
+ *           more slowly.
  *   groups  with group_size > 1 and `share`, the leading shared bf16 pages of
  *           each (r, h) are cut into runs of one radix node; requests whose
  *           run has the same (node, first row, pages, n_i8) are taken in

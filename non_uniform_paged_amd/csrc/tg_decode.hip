@@ -367,6 +367,7 @@ extern "C" int tg_decode_streamed(const tg_cache* c, const tg_tables* t, const t
     }
     sr.work = s.work + static_cast<int64_t>(chunk_off[r]) * 6;
     sr.n_items = chunk_off[r + 1] - chunk_off[r];
+    sr.n_gitems = 0;  // INT8 items only: no cooperative workgroups
     if (launch_split(sr, d, G, qf32, true, old_bits_of(c), st) != hipSuccess) return TG_EDEVICE;
     if (hipEventRecord(done, st) != hipSuccess) return TG_EDEVICE;
   }

@@ -13,6 +13,8 @@
 // pointers read from a struct are otherwise generic, and flat loads also count
 // against lgkmcnt, which serialises the waits of the streaming loops.
 #define TG_GLOBAL __attribute__((address_space(1)))
+// LDS pointers are kept in the local address space for the same reason.
+#define TG_LDS __attribute__((address_space(3)))
 
 namespace tg_dev {
 

@@ -583,7 +583,12 @@ int make_plan(const tg_reservation* res, const Geometry& g, const Paths& paths, 
       const int32_t* w = p->work.data() + int64_t(k) * 6;
       return int64_t(w[4] - w[3]) * lpt_weight(w[2], g.qb, old_bits);
     };
-    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return cost(a) > cost(b); });
+    // group items (r < 0) stay ahead of the rest; each part longest first
+    auto group = [&](int32_t k) { return p->work[int64_t(k) * 6] < 0; };
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+      if (group(a) != group(b)) return group(a);
+      return cost(a) > cost(b);
+    });
     std::vector<int32_t> tmp(p->work);
     for (int64_t k = 0; k < n; ++k)
       std::memcpy(p->work.data() + k * 6, tmp.data() + int64_t(order[k]) * 6, 6 * sizeof(int32_t));

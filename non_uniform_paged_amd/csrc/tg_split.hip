@@ -1,8 +1,10 @@
-// Split kernels of the decode step (gfx950): one wavefront per plan item,
-// four wavefronts per workgroup.  A cache with an INT8 tier runs every item
-// of both tiers in one launch (the longest-first plan then balances the two
+// Split kernels of the decode step (gfx950).  The plan's leading n_gitems
+// entries are group items: workgroup b < n_gitems runs entry b on all four
+// wavefronts together (bf16_group_coop); every later workgroup runs four
+// entries, one per wavefront.  A cache with an INT8 tier runs every item of
+// both tiers in one launch (the longest-first plan then balances the two
 // tiers together, and there is one tail instead of two); a bf16-only cache
-// runs the bf16 kernel, which needs no LDS.
+// runs the bf16 kernel.
 
 #include <cstdlib>
 
@@ -13,21 +15,60 @@
 namespace tg_dev {
 namespace {
 
+// Plan entry of wavefront `wave` of workgroup `b` outside the cooperative
+// workgroups (ng of them), or -1 past the plan.
+__device__ __forceinline__ int single_item(const SplitArgs& a, int ng, int b, int wave) {
+  const int item = ng + (b - ng) * kWavesPerBlock + wave;
+  return item < a.n_items ? item : -1;
+}
+
 template <int D, int G, bool QF32, int DEPTH>
-__global__ __launch_bounds__(64 * kWavesPerBlock) void split_bf16_kernel(SplitArgs a) {
-  const int item = uniform(static_cast<int>(blockIdx.x) * kWavesPerBlock + (static_cast<int>(threadIdx.x) >> 6));
-  if (item >= a.n_items) return;
+__global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_per_eu(2))) void split_bf16_kernel(
+    SplitArgs a) {
+  __shared__ __attribute__((aligned(16))) char coop[kCoopLdsBytes<D>];
+  const int b = static_cast<int>(blockIdx.x);
+  const int wave = uniform(static_cast<int>(threadIdx.x) >> 6);
+  const int ng = min(a.n_gitems, a.n_items);
+  if (b < ng) {
+    const TG_GLOBAL int32_t* w = a.work + static_cast<int64_t>(b) * 6;
+    if (uniform(w[0]) < 0) {
+      bf16_group_coop<D, G, QF32>(a, w, (TG_LDS char*)coop);
+    } else if (wave == 0 && uniform(w[2]) == TG_TIER_BF16) {
+      bf16_dispatch<D, G, QF32, DEPTH>(a, w);  // not a group item: one wavefront runs it
+    }
+    return;
+  }
+  const int item = uniform(single_item(a, ng, b, wave));
+  if (item < 0) return;
   const TG_GLOBAL int32_t* w = a.work + static_cast<int64_t>(item) * 6;
   if (uniform(w[2]) != TG_TIER_BF16) return;  // no INT8 pages in this cache
   bf16_dispatch<D, G, QF32, DEPTH>(a, w);
 }
 
 template <int D, int G, bool QF32, int BITS>
-__global__ __launch_bounds__(64 * kWavesPerBlock) void split_tiered_kernel(SplitArgs a) {
-  __shared__ float lds[kWavesPerBlock][kI8LdsFloats<D>];
+__global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_per_eu(2))) void split_tiered_kernel(
+    SplitArgs a) {
+  // LDS: the INT8 items' accumulators, or the pages of a cooperative group item
+  constexpr int kI8Bytes = kWavesPerBlock * kI8LdsFloats<D> * 4;
+  __shared__ __attribute__((aligned(16))) char smem[kI8Bytes > kCoopLdsBytes<D> ? kI8Bytes : kCoopLdsBytes<D>];
+  float(*lds)[kI8LdsFloats<D>] = reinterpret_cast<float(*)[kI8LdsFloats<D>]>(smem);
+  const int b = static_cast<int>(blockIdx.x);
   const int wave = uniform(static_cast<int>(threadIdx.x) >> 6);
-  const int item = uniform(static_cast<int>(blockIdx.x) * kWavesPerBlock + wave);
-  if (item >= a.n_items) return;
+  const int ng = min(a.n_gitems, a.n_items);
+  if (b < ng) {
+    const TG_GLOBAL int32_t* w = a.work + static_cast<int64_t>(b) * 6;
+    if (uniform(w[0]) < 0) {
+      bf16_group_coop<D, G, QF32>(a, w, (TG_LDS char*)smem);
+    } else if (wave == 0) {  // not a group item: one wavefront runs it
+      if (uniform(w[2]) == TG_TIER_I8)
+        i8_dispatch<D, G, QF32, 2, BITS>(a, w, lds[0]);
+      else
+        bf16_dispatch<D, G, QF32, 2>(a, w);
+    }
+    return;
+  }
+  const int item = uniform(single_item(a, ng, b, wave));
+  if (item < 0) return;
   const TG_GLOBAL int32_t* w = a.work + static_cast<int64_t>(item) * 6;
   if (uniform(w[2]) == TG_TIER_I8)
     i8_dispatch<D, G, QF32, 2, BITS>(a, w, lds[wave]);
@@ -37,7 +78,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void split_tiered_kernel(Split
 
 template <int D, int G, bool QF32>
 hipError_t launch(const SplitArgs& a, bool has_i8, int old_bits, hipStream_t s) {
-  const int blocks = (a.n_items + kWavesPerBlock - 1) / kWavesPerBlock;
+  const int ng = a.n_gitems < a.n_items ? a.n_gitems : a.n_items;
+  const int blocks = ng + (a.n_items - ng + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks == 0) return hipSuccess;
   const dim3 grid(blocks), block(64 * kWavesPerBlock);
   if (has_i8) {

@@ -43,8 +43,9 @@ class Prepared:
                  slack_pages: int = 0, shift_pages: int = 0, device: str = "cuda",
                  group_size: Optional[int] = None, gen_tokens: int = 0):
         """``group_size`` None: group shared-prefix pages for as many requests
-        as fill two 16-column score tiles (32 / G) when the batch shares a radix
-        prefix, else no groups.  ``gen_tokens`` > 0 reserves room for that
+        as a workgroup's four wavefronts score at once (two 16-column tiles
+        each: 128 / G, at most 32) when the batch shares a radix prefix, else
+        no groups.  ``gen_tokens`` > 0 reserves room for that
         many appended rows per (r, h) and stages them (the continuation of
         each sequence) on the device for ``append``."""
         import torch
@@ -55,7 +56,7 @@ class Prepared:
         self.share = share_of(w)
         G = w.Hq // w.Hkv
         if group_size is None:
-            group_size = min(32 // G, api.TG_GROUP_WIDTH) if self.share is not None else 0
+            group_size = min(128 // G, api.TG_GROUP_WIDTH) if self.share is not None else 0
         self.group_size = group_size
         self.gen_tokens = gen_tokens
         sizes = api.tg_size_tables(self.res, w.page_size, w.quant_block, self.share, chunk_bf, chunk_i8, lpt,

@@ -50,7 +50,8 @@ R-plan   items (r, h, tier, t0, t1, slot) in order r, h, tier (INT8 first).
          proportional to the HBM bytes one row of the tier costs: a bf16 row is
          4d bytes, a quantised row 2d * bits / 8 bytes of codes plus 4d / Qb of
          scales, so w = 16 Qb (bf16) and bits * Qb + 16 (INT8 or INT4), the
-         common factor d / (4 Qb) dropped.
+         common factor d / (4 Qb) dropped; group items (R-group) stay ahead of
+         all other items, each part sorted on its own.
 R-step   (decode-step growth) an appended row becomes the newest bf16 row
          and R-tier is applied to the new length; when the INT8 boundary moves
          (by one block) the oldest Qb bf16 rows are quantised (R-q) into the
@@ -495,8 +496,9 @@ def plan(res: Reservation, chunk_bf: int, chunk_i8: int, lpt: bool, group_size: 
     work = [(-1 - gi, h, TIER_BF, t0, t1, -1) for gi, (h, t0, t1) in enumerate(gitem_rows)] + own
     gitems = [[(m, gslot[gi][k]) for k, m in enumerate(grp)] + [(-1, -1)] * (GROUP_WIDTH - len(grp))
               for gi, grp in enumerate(gitems_members)]
-    if lpt:
-        work = sorted(work, key=lambda it: -(it[4] - it[3]) * lpt_weight(it[2], quant_block, old_bits))
+    if lpt:  # group items stay ahead of the rest (R-plan)
+        key = lambda it: (it[0] >= 0, -(it[4] - it[3]) * lpt_weight(it[2], quant_block, old_bits))
+        work = sorted(work, key=key)
     return work, part_off, gitems
 
 

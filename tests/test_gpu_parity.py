@@ -308,11 +308,49 @@ def test_all_int8_and_empty_bf16_tier():
                                             (16, 2, 10**6, "bf16"), (3, 8, 250_000, "bf16"),
                                             (4, 8, 10**6, "f32")])
 def test_group_items(gs, G, recent, qd):
-    """Shared-prefix group items (one pass over a shared page for up to 32 / G
-    requests, in one or two 16-column score tiles) against the oracle, for
-    several group sizes and head shapes."""
+    """Shared-prefix group items (one pass over a shared page for all members,
+    the four wavefronts of a workgroup scoring 32 / G members each) against
+    the oracle, for several group sizes and head shapes."""
     _need_gpu()
     w = make_workload("radix", B=40, Hq=2 * G, Hkv=2, recent_ppm=recent, q_dtype=qd,
                       share=dict(prefix=200, branch=50, n_branches=3, suffix=(8, 300)))
     p, _ = _run_and_compare(w, what=f"group{gs}-G{G}-{recent}-{qd}", chunk_bf=48, group_size=gs)
     assert (p.tables.n_gitems > 0) == (gs > 1)
+
+
+@pytest.mark.parametrize("gs,G,d,qd", [(32, 4, 128, "bf16"), (32, 8, 128, "bf16"), (24, 2, 128, "f32"),
+                                        (13, 4, 128, "bf16"), (32, 4, 64, "bf16"), (32, 8, 64, "f32"),
+                                        (32, 1, 64, "bf16")])
+def test_group_items_wide(gs, G, d, qd):
+    """Wide groups: every wavefront of the workgroup has members (G = 4, 32
+    members), two passes over the pages (G = 8 takes 16 members a pass), a
+    ragged last wavefront, and d = 64 (one page block per wavefront)."""
+    _need_gpu()
+    w = make_workload("radix", B=70, Hq=2 * G, Hkv=2, d=d, q_dtype=qd,
+                      share=dict(prefix=230, branch=60, n_branches=2, suffix=(8, 200)))
+    p, _ = _run_and_compare(w, what=f"wide{gs}-G{G}-d{d}-{qd}", chunk_bf=64, group_size=gs)
+    assert p.tables.n_gitems > 0
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_group_items_in_any_plan_order(seed):
+    """A plan whose group items do not lead (shuffled on the host) still
+    decodes correctly: the leading workgroups hand ordinary items to one
+    wavefront, and group items met later run on one wavefront, a tile of
+    members at a time."""
+    torch = _need_gpu()
+    from non_uniform_paged_amd import api
+    G = 4
+    w = make_workload("radix", B=24, Hq=2 * G, Hkv=2,
+                      share=dict(prefix=120, branch=40, n_branches=3, suffix=(8, 150)))
+    p = _prep(w, chunk_bf=48, group_size=32)
+    assert p.tables.n_gitems > 0
+    plan = p.tables.plan.copy()
+    perm = np.random.default_rng(seed).permutation(len(plan))
+    assert (plan[perm][:p.tables.n_gitems, 0] >= 0).any()  # some leading entries are ordinary items
+    p.cache.work.copy_(torch.from_numpy(np.ascontiguousarray(plan[perm])).to(p.cache.work.device))
+    p.step()
+    got = p.output()
+    res_o = A.reserve_for(w)
+    pairs = [(r, h) for r in range(w.B) for h in range(w.Hkv)]
+    _check(got, A.decode(w, res_o, pairs), pairs, G, f"shuffled-plan-{seed}")

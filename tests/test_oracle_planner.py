@@ -379,6 +379,8 @@ def test_group_invariants(gs, recent_ppm):
         _group_check(w, res, t, gs)
         n_group = sum(1 for it in t.work if it[0] < 0)
         assert n_group == len(t.gitems) and (n_group > 0) == (gs > 1)
+        # the longest-first order keeps the group items ahead of all others
+        assert all(it[0] < 0 for it in t.work[:n_group]) and all(it[0] >= 0 for it in t.work[n_group:])
 
 
 # ---------------------------------------------------------------- decode-step growth (R-step)
