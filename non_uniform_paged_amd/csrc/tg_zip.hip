@@ -27,6 +27,7 @@ constexpr int kPerThread = 8;                           // values per thread and
 constexpr int kSteps = 16;                              // steps per workgroup
 constexpr int kStage = 128;                             // escapes staged per workgroup
 constexpr int kCopies = 16;                             // LDS histogram copies
+constexpr int kLoads = 4;                               // 16-byte loads in flight per thread
 constexpr int64_t kPerBlock = kThreads * kPerThread * kSteps;  // values per encode workgroup
 constexpr int64_t kHeader = 256;
 
@@ -54,12 +55,22 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const u32x4_t* __restric
   for (int k = threadIdx.x; k < kCopies * 257; k += kThreads) (&h[0][0])[k] = 0;
   __syncthreads();
   uint32_t* mine = h[threadIdx.x % kCopies];
-  for (int64_t i = blockIdx.x * int64_t(kThreads) + threadIdx.x; i < n16; i += int64_t(gridDim.x) * kThreads) {
-    const u32x4_t x = __builtin_nontemporal_load(src + i);
+  // workgroup b reads tiles b, b + grid, ... of kLoads * 256 words, kLoads
+  // loads in flight per thread
+  const int64_t tile = int64_t(kThreads) * kLoads;
+  for (int64_t base = blockIdx.x * tile + threadIdx.x; base < n16; base += int64_t(gridDim.x) * tile) {
+    u32x4_t x[kLoads];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      atomicAdd(&mine[exp_of(x[k])], 1u);
-      atomicAdd(&mine[exp_of(x[k] >> 16)], 1u);
+    for (int u = 0; u < kLoads; ++u)
+      if (base + u * kThreads < n16) x[u] = __builtin_nontemporal_load(src + base + u * kThreads);
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      if (base + u * kThreads >= n16) break;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        atomicAdd(&mine[exp_of(x[u][k])], 1u);
+        atomicAdd(&mine[exp_of(x[u][k] >> 16)], 1u);
+      }
     }
   }
   __syncthreads();
@@ -99,10 +110,19 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4_t* __restr
   uint32_t* spos = stage_pos + static_cast<int64_t>(blockIdx.x) * kStage;
   uint8_t* sexp = stage_exp + static_cast<int64_t>(blockIdx.x) * kStage;
   const int64_t base16 = blockIdx.x * (kPerBlock / kPerThread);
-  for (int step = 0; step < kSteps; ++step) {
-    const int64_t i = base16 + step * kThreads + threadIdx.x;  // 8-value group
+  static_assert(kSteps % kLoads == 0, "steps go in groups of kLoads");
+  for (int step0 = 0; step0 < kSteps; step0 += kLoads) {
+    u32x4_t xs[kLoads];  // the group's loads first: kLoads in flight per thread
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      const int64_t i = base16 + (step0 + u) * kThreads + threadIdx.x;
+      if (i * kPerThread < n) xs[u] = __builtin_nontemporal_load(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+    const int64_t i = base16 + (step0 + u) * kThreads + threadIdx.x;  // 8-value group
     if (i * kPerThread >= n) break;
-    const u32x4_t x = __builtin_nontemporal_load(src + i);
+    const u32x4_t x = xs[u];
     uint32_t sm[2] = {0, 0}, codes = 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -120,35 +140,66 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const u32x4_t* __restr
     }
     *reinterpret_cast<u32x2_t*>(dst + kHeader + i * 8) = u32x2_t{sm[0], sm[1]};
     *reinterpret_cast<uint32_t*>(dst + kHeader + n + i * 4) = codes;
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0) block_count[blockIdx.x] = n_staged;
 }
 
-// Exclusive scan of the block counts (one workgroup), total into the header.
+// Exclusive scan of the block counts (one workgroup of 16 wavefronts), total
+// into the header.  Wavefront w owns a contiguous segment of the counts and
+// walks it 64 at a time with coalesced loads and a wavefront scan; the 16
+// segment totals are scanned in LDS, and a second walk writes the offsets.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
 __global__ __launch_bounds__(1024) void scan_kernel(const uint32_t* __restrict__ count, uint32_t* __restrict__ off,
                                                     int64_t nb, Work* __restrict__ ws, uint8_t* __restrict__ dst) {
-  __shared__ uint32_t part[1024];
-  const int64_t per = (nb + 1023) / 1024;
-  const int64_t lo = threadIdx.x * per, hi = lo + per < nb ? lo + per : nb;
-  uint32_t s = 0;
-  for (int64_t b = lo; b < hi; ++b) s += count[b];
-  part[threadIdx.x] = s;
-  __syncthreads();
-  for (int k = 1; k < 1024; k <<= 1) {  // inclusive scan of the 1024 partial sums
-    const uint32_t v = threadIdx.x >= static_cast<unsigned>(k) ? part[threadIdx.x - k] : 0u;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    __syncthreads();
+  __shared__ uint32_t seg_total[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t per = ((nb + 15) / 16 + 63) / 64 * 64;  // segment length, a multiple of 64
+  const int64_t lo = wave * per, hi = lo + per < nb ? lo + per : nb;
+  constexpr int U = 8;  // loads in flight per lane
+  uint32_t total = 0;
+  for (int64_t b0 = lo + lane; b0 - lane < hi; b0 += 64 * U) {
+    uint32_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = b0 + 64 * u < hi ? count[b0 + 64 * u] : 0u;
+    uint32_t t = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) t += v[u];
+    total += t;
   }
-  uint32_t run = part[threadIdx.x] - s;
-  for (int64_t b = lo; b < hi; ++b) {
-    off[b] = run;
-    run += count[b];
+  // a wavefront sum: every lane's partial folded
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) total += __shfl_xor(total, d, 64);
+  if (lane == 0) seg_total[wave] = total;
+  __syncthreads();
+  uint32_t base = 0;
+  for (int k = 0; k < wave; ++k) base += seg_total[k];
+  for (int64_t b0 = lo + lane; b0 - lane < hi; b0 += 64 * U) {
+    uint32_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = b0 + 64 * u < hi ? count[b0 + 64 * u] : 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t inc = wave_inclusive_scan(v[u]);
+      if (b0 + 64 * u < hi) off[b0 + 64 * u] = base + inc - v[u];
+      base += __shfl(inc, 63, 64);
+    }
   }
   if (threadIdx.x == 1023) {
-    ws->n_esc = part[1023];
-    *reinterpret_cast<int64_t*>(dst + 8) = part[1023];
+    uint32_t all = 0;
+    for (int k = 0; k < 16; ++k) all += seg_total[k];
+    ws->n_esc = all;
+    *reinterpret_cast<int64_t*>(dst + 8) = all;
   }
 }
 
@@ -222,17 +273,33 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(const uint8_t* __restr
   __shared__ uint32_t book[16];
   if (threadIdx.x < 16) book[threadIdx.x] = src[16 + threadIdx.x];
   __syncthreads();
-  for (int64_t i = blockIdx.x * int64_t(kThreads) + threadIdx.x; i * kPerThread < n;
-       i += int64_t(gridDim.x) * kThreads) {
-    const u32x2_t sm = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(src + kHeader) + i);
-    const uint32_t codes = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src + kHeader + n) + i);
-    uint32_t v[8];
+  const int64_t groups = n / kPerThread;
+  const int64_t tile = int64_t(kThreads) * kLoads;
+  for (int64_t base = blockIdx.x * tile + threadIdx.x; base < groups; base += int64_t(gridDim.x) * tile) {
+    u32x2_t sms[kLoads];
+    uint32_t cs[kLoads];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t b = (sm[k >> 2] >> (8 * (k & 3))) & 0xFFu;
-      v[k] = ((b >> 7) << 15) | (book[(codes >> (4 * k)) & 15u] << 7) | (b & 0x7Fu);
+    for (int u = 0; u < kLoads; ++u) {
+      const int64_t i = base + u * kThreads;
+      if (i < groups) {
+        sms[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(src + kHeader) + i);
+        cs[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(src + kHeader + n) + i);
+      }
     }
-    out[i] = u32x4_t{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      const int64_t i = base + u * kThreads;
+      if (i >= groups) break;
+      const u32x2_t sm = sms[u];
+      const uint32_t codes = cs[u];
+      uint32_t v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t b = (sm[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+        v[k] = ((b >> 7) << 15) | (book[(codes >> (4 * k)) & 15u] << 7) | (b & 0x7Fu);
+      }
+      out[i] = u32x4_t{v[0] | (v[1] << 16), v[2] | (v[3] << 16), v[4] | (v[5] << 16), v[6] | (v[7] << 16)};
+    }
   }
 }
 
@@ -277,7 +344,7 @@ extern "C" int tg_zip_encode(const uint16_t* src, int64_t n, void* dst, size_t d
   const u32x4_t* in = reinterpret_cast<const u32x4_t*>(src);
   const int64_t n16 = n / 8;
   hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<uint32_t*>(ws->hist), int64_t(256));
-  const int64_t hb = (n16 + kThreads - 1) / kThreads;
+  const int64_t hb = (n16 + kThreads * kLoads - 1) / (kThreads * kLoads);
   hipLaunchKernelGGL(hist_kernel, dim3(static_cast<unsigned>(hb < 4096 ? hb : 4096)), dim3(kThreads), 0, st, in, n16,
                      ws);
   hipLaunchKernelGGL(book_kernel, dim3(1), dim3(256), 0, st, ws, out, n);
@@ -295,8 +362,8 @@ extern "C" int tg_zip_decode(const void* src, int64_t n, uint16_t* dst, void* st
   hipStream_t st = static_cast<hipStream_t>(stream);
   const uint8_t* in = static_cast<const uint8_t*>(src);
   const int64_t groups = n / 8;
-  const int64_t gb = (groups + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL(decode_kernel, dim3(static_cast<unsigned>(gb < 8192 ? gb : 8192)), dim3(kThreads), 0, st, in, n,
+  const int64_t gb = (groups + kThreads * kLoads - 1) / (kThreads * kLoads);
+  hipLaunchKernelGGL(decode_kernel, dim3(static_cast<unsigned>(gb < 4096 ? gb : 4096)), dim3(kThreads), 0, st, in, n,
                      reinterpret_cast<u32x4_t*>(dst));
   hipLaunchKernelGGL(patch_kernel, dim3(256), dim3(kThreads), 0, st, in, n, dst);
   return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
