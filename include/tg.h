@@ -230,8 +230,9 @@ typedef struct tg_plan_opts {
   int32_t chunk_bf;  /* bf16 item length, a positive multiple of page_size */
   int32_t chunk_i8;  /* INT8 item length, a positive multiple of quant_block */
   int32_t lpt;       /* nonzero: longest items first */
-  int32_t group_size; /* 0 or 1: no group items; at most TG_GROUP_WIDTH.  The
-                         decode kernels take group_size * G <= 32 */
+  int32_t group_size; /* 0 or 1: no group items; at most TG_GROUP_WIDTH (a
+                         workgroup scores 128 / G members a pass over the
+                         pages, so 128 / G or less is one pass) */
   int32_t gen_tokens; /* >= 0: rows each (r, h) may still gain by tg_append_kv
                          (see growth below); 0 with `share` only */
 } tg_plan_opts;
@@ -352,10 +353,9 @@ int tg_append_kv(const tg_cache* cache, const uint16_t* rows, int32_t* status, v
  *   sm_scale  score scale; 0 means 1/sqrt(d)
  * TG_EUNSUPPORTED unless d in {64, 128}, G in {1, 2, 4, 8}, page_size 16 and
  * quant_block 64; TG_EINVAL on inconsistent arguments; TG_EDEVICE on a
- * failed launch.  A group item computes the partials of all its members in
- * one pass (G columns of the score tile per member); its members must fit
- * two score tiles: members * G <= 32, else the result is undefined (plan
- * with group_size <= 32 / G).
+ * failed launch.  A group item computes the partials of all its members (G
+ * score columns each); a leading group item runs on a whole workgroup, 128 /
+ * G members (64 / G for G = 8 with fp32 q) per pass over its pages.
  * ---------------------------------------------------------------------- */
 size_t tg_decode_workspace_bytes(int32_t n_slots, int32_t G, int32_t d);
 

@@ -5,7 +5,7 @@
 // q-heads of KV-head h over rows [t0, t1) of the bf16 tier.  A group item
 // does the same for the requests that share those pages (radix prefix), one
 // set of G score columns per member, in one pass over the pages: the four
-// wavefronts of a workgroup take 32 / G members each (two 16-column score
+// wavefronts of a workgroup take up to 32 / G members each (two 16-column score
 // tiles) and share the page loads through LDS (bf16_group_coop).
 //
 // The maths is the online normaliser (CAP survey page, section 2.4.3
