@@ -401,6 +401,9 @@ __device__ __forceinline__ void bf16_group_coop(const SplitArgs& a, const TG_GLO
 
   for (int pass = 0; pass < TG_GROUP_WIDTH; pass += kWavesPerBlock * M) {
     if (pass > 0 && uniform(gm[2 * pass]) < 0) break;  // no members left (same in every wavefront)
+    // the previous pass's partial stores share the vector-memory counter with
+    // the page loads: let them drain so that the counts below cover loads only
+    wait_vmcnt<0>();
     int col_r[CT], col_slot[CT];
     tile_members<G, CT>(r0, -1, gm, pass + wave * M, col_r, col_slot);
     // a wavefront without members only helps load the pages (uniform)
