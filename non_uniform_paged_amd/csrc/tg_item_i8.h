@@ -88,6 +88,12 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
   // parts (~22 significant bits).  INT4: one fp16 part each (11 bits, far
   // finer than the 4-bit codes they multiply), half the matrix-core work.
   constexpr bool TWO = BITS == 8;
+  // INT4: two 16-row groups form one 32-row step (one reference max, K = 32
+  // products for P V), with DEPTH groups in the register pipeline, one pair
+  // ahead.  (For INT8 the pair step measured slower: its two-part operands
+  // already keep the matrix cores busier.)
+  constexpr bool PAIR = BITS == 4;
+  static_assert(!PAIR || (DEPTH % 2 == 0 && (kQBlock / kPage) % 2 == 0), "groups go in pairs");
   constexpr int NK = D / 32;           // score steps (32 channels each)
   constexpr int NT = D / 16;           // 16-channel tiles of V
   constexpr int GR = kQBlock / kPage;  // 16-row groups per block
@@ -164,7 +170,7 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
     };
     load_sk(0);
 #pragma unroll
-    for (int u = 0; u < DEPTH - 1; ++u) issue(kc[u], vc[u], 0, u);
+    for (int u = 0; u < DEPTH - (PAIR ? 2 : 1); ++u) issue(kc[u], vc[u], 0, u);
 
     for (int blk = 0; blk < nw; ++blk) {
       // Q' = q * s_K as fp16 high + low parts, and the score bias of the block
@@ -196,6 +202,95 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
       for (int n = 0; n < NT; ++n) accb[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       f32x4_t pbias = {0.f, 0.f, 0.f, 0.f};
 
+      if constexpr (PAIR) {
+#pragma unroll
+      for (int k = 0; k < GR; k += 2) {  // groups k, k + 1 as one 32-row step
+        const int kn = k + DEPTH - 2;    // groups requested now: kn, kn + 1
+        issue(kc[kn % DEPTH], vc[kn % DEPTH], blk + kn / GR, kn % GR);
+        issue(kc[(kn + 1) % DEPTH], vc[(kn + 1) % DEPTH], blk + (kn + 1) / GR, (kn + 1) % GR);
+        if (k == 0) {
+          gptr sp = blk_ptr(blk) + 2 * CODE_BYTES + 2 * D;
+#pragma unroll
+          for (int n = 0; n < NT; ++n) svraw[n] = *(const TG_GLOBAL uint16_t*)(sp + (16 * n + lg) * 2);
+        }
+        if (k == 2) load_sk(blk + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int u0 = k % DEPTH, u1 = (k + 1) % DEPTH;
+        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NK; ++s) {
+          u32x4_t A0, A1;
+          if constexpr (BITS == 8) {
+            const u32x4_t x0 = kc[u0][s / 2], x1 = kc[u1][s / 2];
+            const u32x2_t c00 = codes_to_f16(x0[(s % 2) * 2]), c01 = codes_to_f16(x0[(s % 2) * 2 + 1]);
+            const u32x2_t c10 = codes_to_f16(x1[(s % 2) * 2]), c11 = codes_to_f16(x1[(s % 2) * 2 + 1]);
+            A0 = u32x4_t{c00[0], c00[1], c01[0], c01[1]};
+            A1 = u32x4_t{c10[0], c10[1], c11[0], c11[1]};
+          } else {
+            A0 = nibbles_to_f16(kc[u0][0][s]);
+            A1 = nibbles_to_f16(kc[u1][0][s]);
+          }
+          s0 = mfma_f16_k32(A0, qop[0][s], s0);
+          s1 = mfma_f16_k32(A1, qop[0][s], s1);
+          if constexpr (TWO) {
+            s0 = mfma_f16_k32(A0, qop[1][s], s0);
+            s1 = mfma_f16_k32(A1, qop[1][s], s1);
+          }
+        }
+        float sc[8];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          sc[rr] = (s0[rr] - qk_bias) * a.scale_log2;
+          sc[4 + rr] = (s1[rr] - qk_bias) * a.scale_log2;
+        }
+        float pm = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+        pm = xor32_max(xor16_max(pm));
+        if (__builtin_amdgcn_ballot_w64(pm > m_ref + kSlack) != 0) {
+          const float mn = fmaxf(m_ref, pm);
+          const float alpha = __builtin_amdgcn_exp2f(m_ref - mn);
+          l_run *= alpha;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const float ar = __shfl(alpha, 4 * lj + rr, 64);  // alpha of head 4lj+rr
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+              accb[n][rr] *= ar;
+              lds[(4 * n + rr) * 64 + lane] *= ar;
+            }
+            pbias[rr] *= ar;
+          }
+          m_ref = mn;
+        }
+        uint32_t ph[8], pl[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pw = __builtin_amdgcn_exp2f(sc[e] - m_ref);
+          split_f16(pw, ph[e], pl[e]);
+          l_run += TWO ? pw : static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(ph[e])));
+        }
+        const u32x4_t Ph = {ph[0] | (ph[1] << 16), ph[2] | (ph[3] << 16), ph[4] | (ph[5] << 16), ph[6] | (ph[7] << 16)};
+        const u32x4_t Pl = {pl[0] | (pl[1] << 16), pl[2] | (pl[3] << 16), pl[4] | (pl[5] << 16), pl[6] | (pl[7] << 16)};
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+          u32x2_t B0, B1;
+          if constexpr (BITS == 8) {
+            B0 = codes_to_f16(vc[u0][n / 4][n % 4]);
+            B1 = codes_to_f16(vc[u1][n / 4][n % 4]);
+          } else {
+            const u32x4_t f0 = nibbles_to_f16(vc[u0][0][n / 2]), f1 = nibbles_to_f16(vc[u1][0][n / 2]);
+            B0 = (n & 1) ? u32x2_t{f0[2], f0[3]} : u32x2_t{f0[0], f0[1]};
+            B1 = (n & 1) ? u32x2_t{f1[2], f1[3]} : u32x2_t{f1[0], f1[1]};
+          }
+          const u32x4_t B = {B0[0], B0[1], B1[0], B1[1]};
+          accb[n] = mfma_f16_k32(Ph, B, accb[n]);
+          if constexpr (TWO) accb[n] = mfma_f16_k32(Pl, B, accb[n]);
+        }
+        const u32x4_t c2 = {c1152x4[0], c1152x4[1], c1152x4[0], c1152x4[1]};
+        pbias = mfma_f16_k32(Ph, c2, pbias);
+        if constexpr (TWO) pbias = mfma_f16_k32(Pl, c2, pbias);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      } else {
 #pragma unroll
       for (int k = 0; k < GR; ++k) {
         const int kn = k + DEPTH - 1;  // group requested now: block blk + kn/GR, group kn%GR
@@ -271,6 +366,7 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
         pbias = mfma_f16_k16(Ph, c1152x4, pbias);
         if constexpr (TWO) pbias = mfma_f16_k16(Pl, c1152x4, pbias);
         __builtin_amdgcn_sched_barrier(0);
+      }
       }
       // end of block: fold in the V scales
 #pragma unroll

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
       bf16_group_coop<D, G, QF32>(a, w, (TG_LDS char*)smem);
     } else if (wave == 0) {  // not a group item: one wavefront runs it
       if (uniform(w[2]) == TG_TIER_I8)
-        i8_dispatch<D, G, QF32, 2, BITS>(a, w, lds[0]);
+        i8_dispatch<D, G, QF32, BITS == 4 ? 4 : 2, BITS>(a, w, lds[0]);
       else
         bf16_dispatch<D, G, QF32, 2>(a, w);
     }
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
   if (item < 0) return;
   const TG_GLOBAL int32_t* w = a.work + static_cast<int64_t>(item) * 6;
   if (uniform(w[2]) == TG_TIER_I8)
-    i8_dispatch<D, G, QF32, 2, BITS>(a, w, lds[wave]);
+    i8_dispatch<D, G, QF32, BITS == 4 ? 4 : 2, BITS>(a, w, lds[wave]);
   else
     bf16_dispatch<D, G, QF32, 2>(a, w);
 }
