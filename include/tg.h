@@ -214,8 +214,11 @@ int32_t tg_pool_refcount(const tg_pool* pool, int32_t c, int32_t tier, int64_t p
  *           block) the oldest Qb bf16 rows become the next INT8 block.  Pages
  *           are reserved now for the largest sizes on the way (INT8 rows of
  *           L + T, the most bf16 rows at any length from L to L + T), and the
- *           plan covers those capacities; the decode kernels clip every item
- *           to the live lengths.  The bf16 tier turns over its ring[r][c]
+ *           plan covers those capacities with as many items per range as the
+ *           live rows give (k = ceil(u_live / c) for u_live units of chunk c
+ *           units), more only where items would pass 2 c units (k =
+ *           ceil(u / 2c)); the decode kernels clip every item to the live
+ *           lengths.  The bf16 tier turns over its ring[r][c]
  *           pages (logical bf16 row j of (r, h) lives at ring row
  *           (bf_base[r][h] + j) mod (16 ring[r][c])).
  * ---------------------------------------------------------------------- */

@@ -426,13 +426,21 @@ int count_plan(const tg_reservation* res, const Geometry& g, const tg_plan_opts*
 }
 
 // Rows [lo, hi) as near-equal items of whole units (pages or INT8 blocks),
-// at most `chunk` rows each: k = ceil(u / (chunk / unit)) items over u units,
-// item i starting at unit floor(i * u / k).
+// at most `chunk` rows each: k = ceil(u / c) items over u units (c = chunk /
+// unit), item i starting at unit floor(i * u / k).  In a plan with room for
+// appended rows, rows up to hi_live are live and the rest reserved: the item
+// count then follows the live rows, k = max(1, ceil(u_live / c), ceil(u /
+// 2c)), so that the room adds no items (items stay under 2 chunk rows).
 template <typename F>
-void split_range(int64_t lo, int64_t hi, int64_t unit, int64_t chunk, F&& emit) {
+void split_range(int64_t lo, int64_t hi, int64_t hi_live, int64_t unit, int64_t chunk, F&& emit) {
   const int64_t u = ceil_div(hi - lo, unit);
   if (u <= 0) return;
-  const int64_t k = ceil_div(u, chunk / unit);
+  const int64_t c = chunk / unit;
+  int64_t k = ceil_div(u, c);
+  if (hi_live < hi) {
+    const int64_t u_live = ceil_div(std::max<int64_t>(hi_live - lo, 0), unit);
+    k = std::max<int64_t>({1, ceil_div(u_live, c), ceil_div(u, 2 * c)});
+  }
   for (int64_t i = 0; i < k; ++i)
     emit(lo + (i * u / k) * unit, std::min(lo + ((i + 1) * u / k) * unit, hi));
 }
@@ -487,8 +495,10 @@ int64_t lpt_weight(int32_t t, int32_t qb, int32_t bits) {
   return t == TG_TIER_BF16 ? 16 * int64_t(qb) : int64_t(bits) * qb + 16;
 }
 
-int make_plan(const tg_reservation* res, const Geometry& g, const Paths& paths, const tg_plan_opts* o,
-              int32_t old_bits, Plan* p) {
+// `res` holds the rows the plan tiles (the reserved capacity for growth),
+// `live` the live rows (the same reservation without growth).
+int make_plan(const tg_reservation* res, const tg_reservation* live, const Geometry& g, const Paths& paths,
+              const tg_plan_opts* o, int32_t old_bits, Plan* p) {
   int64_t bound = 0;
   int st = count_plan(res, g, o, &bound);
   if (st) return st;
@@ -531,7 +541,7 @@ int make_plan(const tg_reservation* res, const Geometry& g, const Paths& paths, 
         const int64_t lo = grp.ja * g.ps, hi = (grp.ja + grp.id.npages) * g.ps;
         for (size_t k = 0; k < grp.members.size(); k += o->group_size) {
           const size_t e = std::min(grp.members.size(), k + size_t(o->group_size));
-          split_range(lo, hi, g.ps, o->chunk_bf, [&](int64_t t0, int64_t t1) {
+          split_range(lo, hi, hi, g.ps, o->chunk_bf, [&](int64_t t0, int64_t t1) {
             gi.push_back(GItem{h, t0, t1, std::vector<int32_t>(grp.members.begin() + k, grp.members.begin() + e)});
           });
         }
@@ -564,10 +574,11 @@ int make_plan(const tg_reservation* res, const Geometry& g, const Paths& paths, 
       }
       for (int32_t t : {TG_TIER_I8, TG_TIER_BF16}) {
         const int64_t len = t == TG_TIER_BF16 ? res->n_bf[i] : res->n_i8[i];
+        const int64_t len_live = t == TG_TIER_BF16 ? live->n_bf[i] : live->n_i8[i];
         const int64_t lo = t == TG_TIER_BF16 ? shared_rows[i] : 0;
         const int32_t ch = t == TG_TIER_BF16 ? o->chunk_bf : o->chunk_i8;
         const int32_t unit = t == TG_TIER_BF16 ? g.ps : g.qb;
-        split_range(lo, len, unit, ch, [&](int64_t t0, int64_t t1) {
+        split_range(lo, len, len_live, unit, ch, [&](int64_t t0, int64_t t1) {
           const int32_t w[6] = {r, h, t, int32_t(t0), int32_t(t1), int32_t(slot++)};
           p->work.insert(p->work.end(), w, w + 6);
         });
@@ -622,7 +633,7 @@ extern "C" int tg_size_tables(const tg_reservation* live, int32_t ps, int32_t qb
   Plan plan;
   try {
     // (the longest-first order, the only use of the code width, changes no size)
-    if ((st = make_plan(res, g, paths, opts, 8, &plan))) return st;
+    if ((st = make_plan(res, live, g, paths, opts, 8, &plan))) return st;
   } catch (...) {
     return TG_ENOMEM;
   }
@@ -679,7 +690,7 @@ extern "C" int tg_build_tables(tg_pool* pool, const tg_reservation* live, const 
     return TG_EINVAL;
   Plan plan;
   try {
-    if ((st = make_plan(res, g, paths, opts, pool->old_bits, &plan))) return st;
+    if ((st = make_plan(res, live, g, paths, opts, pool->old_bits, &plan))) return st;
   } catch (...) {
     return TG_ENOMEM;
   }

@@ -58,7 +58,10 @@ R-step   (decode-step growth) an appended row becomes the newest bf16 row
          next INT8 block.  Pages for gen_tokens appended rows are reserved at
          admission: INT8 rows of the final length, and the most bf16 rows held
          at any length on the way; the bf16 tier turns over its pages as a
-         ring.  Not combined with shared radix pages.
+         ring.  Not combined with shared radix pages.  The plan tiles the
+         reserved rows; its item count per range follows the live rows
+         (k = ceil(u_live / c), raised only to keep items at most 2 chunk
+         rows), so that room for appended rows adds no items.
 R-group  (only with a group size > 1 and radix paths) the leading shared bf16
          pages of each (r, h) are cut into runs with the same radix node;
          requests whose run has the same (node, first row, page count, INT8
@@ -417,13 +420,21 @@ def page_counts_row(res: Reservation, r: int, c: int, page_size: int) -> int:
     return _ceil_div(max(res.n_bf[r][h] for h in hs), page_size)
 
 
-def split_range(lo: int, hi: int, unit: int, chunk: int):
+def split_range(lo: int, hi: int, unit: int, chunk: int, hi_live=None):
     """Rows [lo, hi) as near-equal items of whole units, at most chunk rows
-    each (R-plan)."""
+    each (R-plan).  With hi_live (a plan with room for appended rows, R-step:
+    rows up to hi_live are live, the rest reserved) the item count follows the
+    live rows, k = ceil(u_live / c), raised only as far as keeps the items at
+    most 2 chunk rows, while the items tile the whole reserved range."""
     u = _ceil_div(hi - lo, unit)
     if u <= 0:
         return []
-    k = _ceil_div(u, chunk // unit)
+    c = chunk // unit
+    if hi_live is None:
+        k = _ceil_div(u, c)
+    else:
+        u_live = _ceil_div(max(hi_live - lo, 0), unit)
+        k = max(1, _ceil_div(u_live, c), _ceil_div(u, 2 * c))
     return [(lo + (i * u // k) * unit, min(lo + ((i + 1) * u // k) * unit, hi)) for i in range(k)]
 
 
@@ -435,7 +446,7 @@ def lpt_weight(tier: int, quant_block: int, old_bits: int) -> int:
 
 def plan(res: Reservation, chunk_bf: int, chunk_i8: int, lpt: bool, group_size: int = 0,
          page_size: int = 16, quant_block: int = 64, n_fixed=None, paths=None, node_len=None,
-         old_bits: int = 8):
+         old_bits: int = 8, live=None):
     """Split plan, partial CSR and group-item member table (R-plan, R-group).
 
     Returns (work, part_off, gitems).  A work item is (r, h, tier, t0, t1,
@@ -489,7 +500,8 @@ def plan(res: Reservation, chunk_bf: int, chunk_i8: int, lpt: bool, group_size: 
                 slot += 1
             for t, lo, n, unit, ch in ((TIER_I8, 0, res.n_i8[r][h], quant_block, chunk_i8),
                                        (TIER_BF, shared_rows[r][h], res.n_bf[r][h], page_size, chunk_bf)):
-                for t0, t1 in split_range(lo, n, unit, ch):
+                n_live = None if live is None else (live.n_i8 if t == TIER_I8 else live.n_bf)[r][h]
+                for t0, t1 in split_range(lo, n, unit, ch, n_live):
                     own.append((r, h, t, t0, t1, slot))
                     slot += 1
     part_off.append(slot)
@@ -530,7 +542,8 @@ def build_tables(pool: Pool, res: Reservation, page_size: int, quant_block: int,
     lens = [[(live.n_i8[r][h], live.n_bf[r][h]) for h in range(H)] for r in range(B)]
     nf = [0] * B if n_fixed is None else list(n_fixed)
     work, part_off, gitems = plan(res, chunk_bf, chunk_i8, lpt, group_size, page_size, quant_block,
-                                  nf, paths, node_len, old_bits)
+                                  nf, paths, node_len, old_bits,
+                                  live if gen_tokens > 0 else None)
     t = Tables(bt, stride, lens, work, part_off, pages)
     t.gitems = gitems
     t.ring = [[len(pages[r][c][TIER_BF]) for c in range(C)] for r in range(B)]

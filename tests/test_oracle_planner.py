@@ -438,6 +438,50 @@ def test_incremental_blocks_equal_blocks_of_the_whole_sequence():
     assert np.array_equal(np.stack([b[1] for b in blocks]), sa)
 
 
+@pytest.mark.parametrize("T,chunks", [(1, (256, 512)), (128, (512, 1792)), (500, (256, 512)), (5000, (256, 512))])
+def test_growth_plan_item_counts_follow_the_live_rows(T, chunks):
+    """Room for T appended rows adds no items while it is small: each tier
+    range of the growth plan has as many items as the same range of the plan
+    of the live rows alone, unless that would make items longer than twice
+    the chunk (then more, up to that bound); the items tile the reserved rows,
+    near-equal in whole units, in order."""
+    w = make_workload("tiered", B=3, ctx=("fixed", 2900), recent_ppm=200_000)
+    res = P.reserve(w.head_rank, w.ratio_hi_ppm, w.ratio_lo_ppm, w.n_clusters, w.recent_ppm,
+                    w.quant_block, w.n_comp, w.n_fixed, w.budget_override)
+    cap = P.capacity(res, T)
+    need_bf, need_i8 = P.pages_needed(cap, w.page_size, w.quant_block)
+    g = P.build_tables(P.Pool(need_bf, need_i8), res, w.page_size, w.quant_block, chunks[0], chunks[1], False,
+                       gen_tokens=T)
+    need_bf, need_i8 = P.pages_needed(res, w.page_size, w.quant_block)
+    plain = P.build_tables(P.Pool(need_bf, need_i8), res, w.page_size, w.quant_block, chunks[0], chunks[1], False)
+
+    def ranges(t):
+        out = {}
+        for (r, h, tier, t0, t1, slot) in t.work:
+            out.setdefault((r, h, tier), []).append((t0, t1))
+        return out
+
+    gi, pi = ranges(g), ranges(plain)
+    grew = 0
+    for (r, h, tier), its in gi.items():
+        unit = w.page_size if tier == P.TIER_BF else w.quant_block
+        c = (chunks[0] if tier == P.TIER_BF else chunks[1]) // unit
+        full = cap.n_bf[r][h] if tier == P.TIER_BF else cap.n_i8[r][h]
+        assert its[0][0] == 0 and its[-1][1] == full
+        assert all(a[1] == b[0] for a, b in zip(its, its[1:]))
+        sizes = [-(-(b - a) // unit) for a, b in its]
+        assert max(sizes) - min(sizes) <= 1 and max(sizes) <= 2 * c
+        n_plain = len(pi.get((r, h, tier), []))
+        if len(its) != max(n_plain, 1):
+            # only where keeping the live count would pass twice the chunk, and
+            # then no more items than that bound needs
+            u = -(-full // unit)
+            assert u > 2 * c * max(n_plain, 1) and 2 * c * (len(its) - 1) < u
+            grew += 1
+    if T <= 500:
+        assert grew == 0
+
+
 def test_growth_tables_cover_capacity_and_keep_live_lengths():
     w = make_workload("tiered", B=2, ctx=("fixed", 3000))
     res = P.reserve(w.head_rank, w.ratio_hi_ppm, w.ratio_lo_ppm, w.n_clusters, w.recent_ppm,
