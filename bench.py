@@ -214,9 +214,11 @@ def host_tier_bench(prep, args, stream, resident_ms):
             "bit_identical_to_resident": identical}
 
 
-def cpu_baseline(w, prep, budget_s: float = 12.0):
+def cpu_baseline(w, prep, budget_s: float = 12.0, min_s: float = 10.0):
     """The oracle, untuned, on this host: fp64 attention of sampled (r, h)
-    pairs from their raw rows (row generation excluded from the time)."""
+    pairs from their raw rows (row generation excluded from the time).  When
+    one pass over every pair takes less than min_s, the pairs are decoded
+    again (their rows kept, up to 2 GB of them) until min_s of oracle time."""
     import numpy as np
     try:
         from threadpoolctl import threadpool_limits
@@ -235,6 +237,8 @@ def cpu_baseline(w, prep, budget_s: float = 12.0):
     done = 0
     worst = 0.0
     ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    kept, kept_bytes = [], 0
+    distinct = 0
     try:
         for i in order:
             r, h = divmod(int(i), w.Hkv)
@@ -244,17 +248,31 @@ def cpu_baseline(w, prep, budget_s: float = 12.0):
                               w.old_bits)
             spent += time.perf_counter() - t0
             n8, nb = res.n_i8[r][h], res.n_bf[r][h]
-            nbytes += nb * 4 * w.d + n8 * 2 * w.d + (n8 // w.quant_block) * 4 * w.d
+            pair_bytes = nb * 4 * w.d + n8 * 2 * w.d + (n8 // w.quant_block) * 4 * w.d
+            nbytes += pair_bytes
             worst = max(worst, float(np.abs(gpu_out[r, h * G:(h + 1) * G] - o).max()))
             done += 1
+            distinct += 1
+            if kept_bytes < 2e9:
+                kept.append((r, h, K16, V16, pair_bytes))
+                kept_bytes += K16.nbytes + V16.nbytes
             if spent > budget_s:
                 break
+        while kept and spent < min_s:  # one pass was short: decode the kept pairs again
+            for r, h, K16, V16, pair_bytes in kept:
+                t0 = time.perf_counter()
+                A.decode_rows(q[r, h * G:(h + 1) * G], K16, V16, res.n_i8[r][h], w.quant_block, scale, w.old_bits)
+                spent += time.perf_counter() - t0
+                nbytes += pair_bytes
+                done += 1
+                if spent >= min_s:
+                    break
     finally:
         if ctx is not None:
             ctx.unregister() if hasattr(ctx, "unregister") else None
     return {"value": round(nbytes / spent / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {w.B * w.Hkv} (request, KV-head) pairs of the same step, fp64 numpy, "
-                      f"1 BLAS thread, {spent:.1f} s", "max_abs_err_vs_gpu": worst}
+            "sample": f"{done} pair decodes over {distinct} of the {w.B * w.Hkv} (request, KV-head) pairs of "
+                      f"the same step, fp64 numpy, 1 BLAS thread, {spent:.1f} s", "max_abs_err_vs_gpu": worst}
 
 
 def main():
@@ -273,7 +291,7 @@ def main():
     ap.add_argument("--zip-reps", type=int, default=5,
                     help="timed encode/decode passes of the lossless codec over the bf16 pool (0: skip)")
     ap.add_argument("--group-size", type=int, default=None,
-                    help="requests per shared-prefix group item (default 16 / G when pages are shared)")
+                    help="requests per shared-prefix group item (default min(32, 128 / G) when pages are shared)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (counter calibration)")
