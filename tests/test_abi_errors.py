@@ -1,0 +1,116 @@
+"""Argument checks of the device entry points, on the CPU: each call below is
+rejected by the library's host-side validation before anything reaches the
+GPU, so these run without one.  The returned code is the one include/tg.h
+documents for that mistake."""
+import ctypes
+
+import numpy as np
+
+from non_uniform_paged_amd import _lib as L
+
+
+def _cache(d=128, B=2, H=2, C=1, page=16, qb=64, old_bits=8):
+    c = L.Cache()
+    c.B, c.n_kv_heads, c.head_dim = B, H, d
+    c.page_size, c.quant_block, c.n_clusters = page, qb, C
+    c.old_bits = old_bits
+    c.recent_ppm = 1_000_000
+    return c
+
+
+def _args(**kw):
+    a = L.DecodeArgs()
+    a.n_q_heads = kw.get("n_q_heads", 4)
+    a.q_dtype = kw.get("q_dtype", L.TG_Q_BF16)
+    for k, v in kw.items():
+        if k not in ("n_q_heads", "q_dtype"):
+            setattr(a, k, v)
+    return a
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def test_decode_rejects_missing_and_unsupported_arguments():
+    lib = L.lib()
+    assert lib.tg_decode_attn(None, None, None) == L.TG_EINVAL
+    c = _cache()
+    # no cluster tables, no q
+    assert lib.tg_decode_attn(ctypes.byref(c), ctypes.byref(_args()), None) == L.TG_EINVAL
+    # q-heads not a multiple of the KV-heads
+    c.cluster_of_head = c.slot_in_cluster = c.len = FAKE.value
+    a = _args(n_q_heads=3, q=FAKE.value, out=FAKE.value, part_off=FAKE.value)
+    assert lib.tg_decode_attn(ctypes.byref(c), ctypes.byref(a), None) == L.TG_EINVAL
+    # head size and group size outside the supported set
+    for d, nq in ((96, 4), (128, 6), (128, 32)):
+        c2 = _cache(d=d)
+        c2.cluster_of_head = c2.slot_in_cluster = c2.len = FAKE.value
+        a = _args(n_q_heads=nq, q=FAKE.value, out=FAKE.value, part_off=FAKE.value)
+        assert lib.tg_decode_attn(ctypes.byref(c2), ctypes.byref(a), None) == L.TG_EUNSUPPORTED, (d, nq)
+    # INT4 is laid out for d = 128 only
+    c3 = _cache(d=64, old_bits=4)
+    c3.cluster_of_head = c3.slot_in_cluster = c3.len = FAKE.value
+    a = _args(q=FAKE.value, out=FAKE.value, part_off=FAKE.value)
+    assert lib.tg_decode_attn(ctypes.byref(c3), ctypes.byref(a), None) == L.TG_EUNSUPPORTED
+    # bad q dtype; items without a workspace; a workspace too small for the slots
+    a = _args(q_dtype=7, q=FAKE.value, out=FAKE.value, part_off=FAKE.value)
+    assert lib.tg_decode_attn(ctypes.byref(c), ctypes.byref(a), None) == L.TG_EINVAL
+    a = _args(q=FAKE.value, out=FAKE.value, part_off=FAKE.value, n_items=5, work=FAKE.value, n_slots=5)
+    assert lib.tg_decode_attn(ctypes.byref(c), ctypes.byref(a), None) == L.TG_EINVAL
+    need = lib.tg_decode_workspace_bytes(5, 2, 128)
+    assert need == 5 * 2 * (128 + 2) * 4
+    a = _args(q=FAKE.value, out=FAKE.value, part_off=FAKE.value, n_items=5, work=FAKE.value, n_slots=5,
+              workspace=FAKE.value, workspace_bytes=need - 4)
+    assert lib.tg_decode_attn(ctypes.byref(c), ctypes.byref(a), None) == L.TG_EINVAL
+    # group items without their member table
+    a = _args(q=FAKE.value, out=FAKE.value, part_off=FAKE.value, n_gitems=1)
+    assert lib.tg_decode_attn(ctypes.byref(c), ctypes.byref(a), None) == L.TG_EINVAL
+
+
+def test_merge_write_append_reject_bad_arguments():
+    lib = L.lib()
+    assert lib.tg_merge_partials(None, 4, 2, 4, 96, None, None, None) == L.TG_EUNSUPPORTED
+    assert lib.tg_merge_partials(None, 4, 2, 4, 128, None, None, None) == L.TG_EINVAL
+    assert lib.tg_merge_partials(None, -1, 0, 4, 128, None, None, None) == L.TG_EINVAL
+    assert lib.tg_write_kv(None, None, None, None, None) == L.TG_EINVAL
+    c = _cache()
+    c.cluster_of_head = c.slot_in_cluster = c.len = FAKE.value
+    assert lib.tg_write_kv(ctypes.byref(c), None, None, None, None) == L.TG_EINVAL
+    c64 = _cache(d=96)
+    c64.cluster_of_head = c64.slot_in_cluster = c64.len = FAKE.value
+    assert lib.tg_write_kv(ctypes.byref(c64), FAKE, FAKE, FAKE, None) == L.TG_EUNSUPPORTED
+    # appending needs the growth ring
+    assert lib.tg_append_kv(ctypes.byref(c), FAKE, None, None) == L.TG_EINVAL
+    c.ring = c.bf_base = FAKE.value
+    c.recent_ppm = 2_000_000
+    assert lib.tg_append_kv(ctypes.byref(c), FAKE, None, None) == L.TG_EINVAL
+
+
+def test_codec_and_read_aid_reject_bad_sizes():
+    lib = L.lib()
+    assert lib.tg_zip_bound(-1) == 0 and lib.tg_zip_workspace_bytes(-1) == 0
+    n = 1 << 12
+    assert lib.tg_zip_bound(n) >= 256 + n + n // 2
+    for bad_n in (0, 7, 12, (1 << 32) + 8):
+        assert lib.tg_zip_encode(FAKE, bad_n, FAKE, 1 << 40, FAKE, 1 << 40, None) == L.TG_EINVAL, bad_n
+        assert lib.tg_zip_decode(FAKE, bad_n, FAKE, None) == L.TG_EINVAL, bad_n
+    # destination or workspace smaller than the bounds
+    assert lib.tg_zip_encode(FAKE, n, FAKE, lib.tg_zip_bound(n) - 1, FAKE, 1 << 40, None) == L.TG_EINVAL
+    assert lib.tg_zip_encode(FAKE, n, FAKE, 1 << 40, FAKE, lib.tg_zip_workspace_bytes(n) - 1, None) == L.TG_EINVAL
+    # misaligned pointers
+    odd = ctypes.c_void_p(0x1008)
+    assert lib.tg_zip_encode(odd, n, FAKE, 1 << 40, FAKE, 1 << 40, None) == L.TG_EINVAL
+    assert lib.tg_zip_decode(FAKE, n, odd, None) == L.TG_EINVAL
+    assert lib.tg_bench_read(FAKE, 24, FAKE, None) == L.TG_EINVAL
+    assert lib.tg_bench_read(None, 32, FAKE, None) == L.TG_EINVAL
+
+
+def test_status_strings_cover_every_code():
+    lib = L.lib()
+    lib.tg_strerror.restype = ctypes.c_char_p
+    seen = set()
+    for code in L.STATUS_NAMES:
+        s = lib.tg_strerror(code)
+        assert s and s not in seen
+        seen.add(s)
+    assert np.all([isinstance(x, bytes) for x in seen])
