@@ -293,6 +293,8 @@ def main():
     ap.add_argument("--group-size", type=int, default=None,
                     help="requests per shared-prefix group item (default min(32, 128 / G) when pages are shared)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tune", action="store_true",
+                    help="time candidate plan item lengths on the device first and keep the fastest")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (counter calibration)")
     args = ap.parse_args()
@@ -321,7 +323,7 @@ def main():
         return
 
     from non_uniform_paged_amd import api
-    from non_uniform_paged_amd.runner import PLAN_CHUNKS, Prepared, allocated_bytes
+    from non_uniform_paged_amd.runner import PLAN_CHUNKS, Prepared, allocated_bytes, tune_candidates
     from workloads import make_workload
 
     torch.cuda.set_device(0)
@@ -343,6 +345,13 @@ def main():
             torch.amax(flush)
         elif args.flush == "write":
             flush.fill_(i & 0xFF)
+
+    tuned = None
+    if args.tune:  # outside the timed region: pick the plan item lengths on the device
+        cands = tune_candidates(w, prep.tables.stride_has_i8)
+        tuned = sorted(prep.tune_chunks(cands, evict=lambda: evict(0), stream=stream), key=lambda x: x[2])
+        args.chunk_bf, args.chunk_i8 = prep.chunks
+        tr = prep.traffic()
 
     def one_step(evs=None):
         # the decode step: tg_decode_attn (split kernel(s), then the merge)
@@ -434,6 +443,7 @@ def main():
                    "page": w.page_size, "chunk_bf": args.chunk_bf, "chunk_i8": args.chunk_i8,
                    "plan_items": prep.tables.n_items, "group_items": prep.tables.n_gitems,
                    "group_size": prep.group_size, "retained_head_rows": tr["head_rows"],
+                   "chunks_tuned": None if tuned is None else [[a, b, round(c, 1)] for a, b, c in tuned[:5]],
                    "parallelism": "single GPU"},
         "hbm_frac_roofline_bytes": round(tr["roofline"] / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "effective_bytes": tr["effective"],

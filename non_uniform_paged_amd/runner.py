@@ -15,6 +15,16 @@ import numpy as np
 
 from . import api
 
+def tune_candidates(w, has_quantised: bool):
+    """(chunk_bf, chunk_i8) pairs tune_chunks tries: bf16 item lengths from
+    256 to 6144 rows, and with a quantised tier INT8 / INT4 lengths from 1024
+    to 3072 rows against the shorter bf16 lengths."""
+    if not has_quantised:
+        return [(cb, 1024) for cb in (256, 384, 512, 640, 768, 832, 896, 960, 1024, 1280, 1536, 2048, 3072,
+                                      4096, 6144)]
+    return [(cb, ci) for cb in (384, 512, 768, 1024) for ci in (1024, 1536, 1792, 2048, 2304, 2560, 3072)]
+
+
 # Plan item lengths (bf16 rows, quantised-tier rows) per workload, chosen by
 # sweeping the split-kernel time on MI355X: the best length depends on how
 # the item count falls against the ~2048 resident wavefronts and on the
@@ -74,6 +84,7 @@ class Prepared:
             ftab = api.tg_build_tables(self.pool, filler, None, w.page_size * 4, w.quant_block, False)
         self.tables = api.tg_build_tables(self.pool, self.res, self.share, chunk_bf, chunk_i8, lpt, group_size,
                                           gen_tokens)
+        self.chunks = (chunk_bf, chunk_i8)
         if shift_pages:
             api.tg_release(self.pool, ftab, 0)
         self.cache = api.DeviceCache(self.pool, self.res, self.tables, dev, self.share)
@@ -103,6 +114,61 @@ class Prepared:
         self.out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
         ws = api.tg_decode_workspace_bytes(self.tables.n_slots, G, w.d)
         self.workspace = torch.empty(max(ws // 4, 1), dtype=torch.float32, device=dev)
+
+    # ------------------------------------------------------------------ plan
+    def replan(self, chunk_bf: int, chunk_i8: int, lpt: bool = True) -> None:
+        """Swap in the plan of other item lengths over the same pages: the
+        tables are rebuilt on a fresh host pool of the same capacities (page
+        allocation does not depend on the item lengths, so the block tables
+        come out identical, which is checked) and the plan, its slot CSR and
+        member table replace the device ones."""
+        import torch
+        w, C = self.w, self.res.C
+        pool = api.Pool(self.res.cluster_size, w.d, w.page_size, w.quant_block,
+                        [self.pool.capacity(c, api.TG_TIER_BF16) for c in range(C)],
+                        [self.pool.capacity(c, api.TG_TIER_I8) for c in range(C)], getattr(w, "old_bits", 8))
+        t = api.tg_build_tables(pool, self.res, self.share, chunk_bf, chunk_i8, lpt, self.group_size,
+                                self.gen_tokens)
+        for c in range(C):
+            for tier in range(2):
+                if not np.array_equal(t.bt[c][tier], self.tables.bt[c][tier]):
+                    raise RuntimeError("replan: the block tables differ (pool not built from empty)")
+        dev = self.cache.device
+        self.cache.work = torch.from_numpy(t.plan.copy()).to(dev)
+        self.cache.part_off = torch.from_numpy(t.part_off).to(dev)
+        self.cache.gitems = torch.from_numpy(t.gitems.reshape(-1).copy()).to(dev) if t.n_gitems else None
+        self.cache.n_items, self.cache.n_gitems, self.cache.n_slots = t.n_items, t.n_gitems, t.n_slots
+        G = w.Hq // w.Hkv
+        need = api.tg_decode_workspace_bytes(t.n_slots, G, w.d) // 4
+        if need > self.workspace.numel():
+            self.workspace = torch.empty(need, dtype=torch.float32, device=dev)
+        self.tables = t
+        self.chunks = (chunk_bf, chunk_i8)
+
+    def tune_chunks(self, candidates, evict=None, steps: int = 8, stream=None):
+        """Time the split stage for each (chunk_bf, chunk_i8) candidate over
+        the same pages (``evict()`` runs before every timed step) and keep
+        the fastest plan.  Returns [(chunk_bf, chunk_i8, median us)]."""
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream()
+        G = self.w.Hq // self.w.Hkv
+        out = []
+        for cb, ci in candidates:
+            self.replan(cb, ci)
+            ts = []
+            for i in range(steps + 2):
+                if evict is not None:
+                    evict()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(s)
+                api.tg_decode_split(self.cache, self.q, self.workspace, self.w.Hq, stream=s)
+                e1.record(s)
+                ts.append((e0, e1))
+            torch.cuda.synchronize()
+            out.append((cb, ci, float(np.median([a.elapsed_time(b) for a, b in ts[2:]])) * 1e3))
+        best = min(out, key=lambda x: x[2])
+        self.replan(best[0], best[1])
+        return out
 
     # ------------------------------------------------------------------ run
     def step(self, stream=None):

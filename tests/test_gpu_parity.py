@@ -354,3 +354,26 @@ def test_group_items_in_any_plan_order(seed):
     res_o = A.reserve_for(w)
     pairs = [(r, h) for r in range(w.B) for h in range(w.Hkv)]
     _check(got, A.decode(w, res_o, pairs), pairs, G, f"shuffled-plan-{seed}")
+
+
+def test_replan_over_the_same_pages():
+    """The runner's replan swaps in plans of other item lengths over the same
+    pages (and tune_chunks picks the fastest of them): every plan decodes to
+    the oracle's result, on an INT8-tier batch and a radix batch."""
+    torch = _need_gpu()
+    for w in (make_workload("tiered", B=2, Hq=8, Hkv=2, ctx=("fixed", 3000)),
+              make_workload("radix", B=12, Hq=8, Hkv=2, share=dict(prefix=150, branch=40, n_branches=2,
+                                                                     suffix=(8, 120)))):
+        p = _prep(w, chunk_bf=64, chunk_i8=128)
+        res_o = A.reserve_for(w)
+        pairs = [(r, h) for r in range(w.B) for h in range(w.Hkv)]
+        ref = A.decode(w, res_o, pairs)
+        for cb, ci in ((16, 64), (48, 192), (4096, 4096)):
+            p.replan(cb, ci)
+            p.step()
+            _check(p.output(), ref, pairs, w.Hq // w.Hkv, f"replan-{w.name}-{cb}-{ci}")
+        out = p.tune_chunks([(32, 64), (96, 256)], steps=2)
+        assert {(a, b) for a, b, _ in out} == {(32, 64), (96, 256)}
+        assert p.chunks == min(out, key=lambda x: x[2])[:2]
+        p.step()
+        _check(p.output(), ref, pairs, w.Hq // w.Hkv, f"tuned-{w.name}")
