@@ -214,6 +214,20 @@ def host_tier_bench(prep, args, stream, resident_ms):
             "bit_identical_to_resident": identical}
 
 
+def _device_record(torch) -> dict:
+    """What the runtime reports about the GPU (to check the published
+    figures the roofline uses: compute units, memory, caches)."""
+    p = torch.cuda.get_device_properties(0)
+    out = {}
+    for k in ("name", "gcnArchName", "multi_processor_count", "total_memory", "L2_cache_size",
+              "max_threads_per_multi_processor", "warp_size", "clock_rate", "memory_clock_rate",
+              "memory_bus_width"):
+        v = getattr(p, k, None)
+        if v is not None:
+            out[k] = v if isinstance(v, (int, float, str)) else str(v)
+    return out
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -478,6 +492,7 @@ def main():
         "cache_eviction_between_steps": args.flush,
         "wall_s_timed_region": round(wall, 4),
         "prepare_s": round(t_prep, 2),
+        "device": _device_record(torch),
         "read_ceiling_GBps": round(read_gbps, 1),
         "split_frac_of_read_ceiling": round(achieved / read_gbps, 4),
         "fragmentation": {"retained_bytes": tr["kv_roofline"], "allocated_bytes_by_clusters": alloc,
