@@ -353,7 +353,7 @@ int tg_append_kv(const tg_cache* cache, const uint16_t* rows, int32_t* status, v
  *             acc [n_slots][G][d] then (m, l) [n_slots][G][2] (m in natural
  *             log units of the scaled score)
  *   out       device fp32 [B][Hq][d]
- *   sm_scale  score scale; 0 means 1/sqrt(d)
+ *   sm_scale  score scale, finite and >= 0; 0 means 1/sqrt(d)
  * TG_EUNSUPPORTED unless d in {64, 128}, G in {1, 2, 4, 8}, page_size 16 and
  * quant_block 64; TG_EINVAL on inconsistent arguments; TG_EDEVICE on a
  * failed launch.  A group item computes the partials of all its members (G

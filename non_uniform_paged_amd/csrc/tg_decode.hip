@@ -192,6 +192,7 @@ int make_split_args(const tg_cache* c, const tg_decode_args* a, bool merge, Spli
   const int32_t d = c->head_dim;
   if (!supported(d, G) || c->page_size != kPage || c->quant_block != kQBlock) return TG_EUNSUPPORTED;
   if (a->q_dtype != TG_Q_F32 && a->q_dtype != TG_Q_BF16) return TG_EINVAL;
+  if (!(a->sm_scale >= 0.f) || !std::isfinite(a->sm_scale)) return TG_EINVAL;
   if (a->n_items < 0 || a->n_gitems < 0 || a->n_slots < 0 || !a->q || !c->cluster_of_head ||
       !c->slot_in_cluster || !c->len)
     return TG_EINVAL;

@@ -55,6 +55,10 @@ def test_decode_rejects_missing_and_unsupported_arguments():
     # bad q dtype; items without a workspace; a workspace too small for the slots
     a = _args(q_dtype=7, q=FAKE.value, out=FAKE.value, part_off=FAKE.value)
     assert lib.tg_decode_attn(ctypes.byref(c), ctypes.byref(a), None) == L.TG_EINVAL
+    # the score scale must be finite and non-negative (0 = 1/sqrt(d))
+    for bad in (-0.125, float("nan"), float("inf")):
+        a = _args(q=FAKE.value, out=FAKE.value, part_off=FAKE.value, sm_scale=bad)
+        assert lib.tg_decode_attn(ctypes.byref(c), ctypes.byref(a), None) == L.TG_EINVAL, bad
     a = _args(q=FAKE.value, out=FAKE.value, part_off=FAKE.value, n_items=5, work=FAKE.value, n_slots=5)
     assert lib.tg_decode_attn(ctypes.byref(c), ctypes.byref(a), None) == L.TG_EINVAL
     need = lib.tg_decode_workspace_bytes(5, 2, 128)
