@@ -171,10 +171,11 @@ class Prepared:
         return out
 
     # ------------------------------------------------------------------ run
-    def step(self, stream=None):
+    def step(self, stream=None, sm_scale: float = 0.0):
+        """One decode step over the uploaded plan; ``sm_scale`` 0 means 1/sqrt(d)."""
         if getattr(self, "host_i8", False):
             raise RuntimeError("the INT8 pages are in host memory: use step_streamed")
-        api.tg_decode_attn(self.cache, self.q, self.out, self.workspace, self.w.Hq, 0.0, stream=stream)
+        api.tg_decode_attn(self.cache, self.q, self.out, self.workspace, self.w.Hq, sm_scale, stream=stream)
 
     # ------------------------------------------------------------------ INT8 tier in host DRAM
     def to_host_i8(self):

@@ -377,3 +377,21 @@ def test_replan_over_the_same_pages():
         assert p.chunks == min(out, key=lambda x: x[2])[:2]
         p.step()
         _check(p.output(), ref, pairs, w.Hq // w.Hkv, f"tuned-{w.name}")
+
+
+@pytest.mark.parametrize("scale", [0.02, 0.3])
+def test_custom_score_scale(scale):
+    """A caller's score scale (instead of 1/sqrt(d)) reaches every path: bf16
+    items, INT8 items (where the block's K scale is folded into q) and
+    shared-prefix group items, against the oracle at the same scale."""
+    _need_gpu()
+    for w, kw in ((make_workload("tiered", B=2, Hq=8, Hkv=2, ctx=("fixed", 2500)), dict(chunk_bf=64, chunk_i8=192)),
+                  (make_workload("radix", B=20, Hq=8, Hkv=2, share=dict(prefix=150, branch=40, n_branches=2,
+                                                                         suffix=(8, 120))),
+                   dict(chunk_bf=48, group_size=32))):
+        p = _prep(w, **kw)
+        p.step(sm_scale=scale)
+        res_o = A.reserve_for(w)
+        pairs = [(r, h) for r in range(w.B) for h in range(w.Hkv)]
+        ref = A.decode(w, res_o, pairs, scale=scale)
+        _check(p.output(), ref, pairs, w.Hq // w.Hkv, f"scale-{scale}-{w.name}")
