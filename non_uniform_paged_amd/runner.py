@@ -77,15 +77,19 @@ class Prepared:
         self.pool = api.Pool(self.res.cluster_size, w.d, w.page_size, w.quant_block,
                              [need[c][1] + extra for c in range(C)], [need[c][0] + extra for c in range(C)],
                              getattr(w, "old_bits", 8))
+        fillers = []
         if shift_pages:
-            # occupy the lowest pages first so that this batch lands elsewhere
-            filler = api.tg_reserve(w.head_rank, 10**6, 10**6, C, 10**6, w.quant_block,
-                                    [shift_pages * w.page_size], None, None)
-            ftab = api.tg_build_tables(self.pool, filler, None, w.page_size * 4, w.quant_block, False)
+            # occupy the lowest shift_pages pages of both tiers first so that
+            # this batch lands elsewhere: one all-bf16 and one all-INT8 request
+            for recent, rows in ((10**6, w.page_size), (0, w.quant_block)):
+                filler = api.tg_reserve(w.head_rank, 10**6, 10**6, C, recent, w.quant_block,
+                                        [shift_pages * rows], None, None)
+                fillers.append(api.tg_build_tables(self.pool, filler, None, w.page_size * 4, w.quant_block * 4,
+                                                   False))
         self.tables = api.tg_build_tables(self.pool, self.res, self.share, chunk_bf, chunk_i8, lpt, group_size,
                                           gen_tokens)
         self.chunks = (chunk_bf, chunk_i8)
-        if shift_pages:
+        for ftab in fillers:
             api.tg_release(self.pool, ftab, 0)
         self.cache = api.DeviceCache(self.pool, self.res, self.tables, dev, self.share)
 

@@ -395,3 +395,22 @@ def test_custom_score_scale(scale):
         pairs = [(r, h) for r in range(w.B) for h in range(w.Hkv)]
         ref = A.decode(w, res_o, pairs, scale=scale)
         _check(p.output(), ref, pairs, w.Hq // w.Hkv, f"scale-{scale}-{w.name}")
+
+
+def test_pages_beyond_4_gib():
+    """Pages placed past byte 2^32 of their pools (bf16 and INT8 alike) give
+    the same outputs, bit for bit, as the same batch in the lowest pages:
+    page addresses are formed in 64 bits on every path (~13 GB of pools)."""
+    _need_gpu()
+    w = make_workload("tiered", B=1, Hq=8, Hkv=2, ctx=("fixed", 3000), n_clusters=1)
+    a = _prep(w, chunk_bf=64, chunk_i8=192)
+    a.step()
+    ga = a.output()
+    del a
+    shift = (1 << 32) // (2 * 8192) + 64  # bf16 pages of 2 heads x 8 KiB: past 4 GiB
+    b = _prep(w, chunk_bf=64, chunk_i8=192, shift_pages=shift)
+    for tier in (0, 1):
+        bt = b.tables.bt[0][tier]
+        assert int(bt[bt >= 0].min()) * b.pool.page_bytes(0, tier) >= 1 << 32, tier
+    b.step()
+    assert np.array_equal(ga, b.output())
