@@ -214,6 +214,45 @@ def host_tier_bench(prep, args, stream, resident_ms):
             "bit_identical_to_resident": identical}
 
 
+def stream_read_bench(w, prep, evict, stream, reps: int = 5) -> dict:
+    """Time tg_bench_streams over the chunk counts of the plan: the rate the
+    split kernels' access pattern (independent per-item page streams, two
+    pages in flight) allows on this device, with no arithmetic."""
+    import numpy as np
+    import torch
+
+    from non_uniform_paged_amd import api
+    plan = prep.tables.plan
+    t0, t1 = plan[:, 3].astype(np.int64), plan[:, 4].astype(np.int64)
+    page = 4 * w.page_size * w.d                              # K and V of one head's bf16 page
+    block = 2 * w.quant_block * w.d * getattr(w, "old_bits", 8) // 8 + 4 * w.d  # one INT8 block
+    bf = plan[:, 2] == api.TG_TIER_BF16
+    nbytes = np.where(bf, (-(-t1 // w.page_size) - t0 // w.page_size) * page,
+                      (-(-t1 // w.quant_block) - t0 // w.quant_block) * block)
+    n_chunks = -(-nbytes // 8192)
+    total = int(n_chunks.sum())
+    off = np.zeros(len(n_chunks) + 1, np.int32)
+    off[1:] = np.cumsum(n_chunks)
+    ids = np.random.default_rng(0).permutation(total).astype(np.int32)
+    buf = torch.ones(total * 8192, dtype=torch.uint8, device="cuda")
+    d_ids, d_off = torch.from_numpy(ids).cuda(), torch.from_numpy(off).cuda()
+    sink = torch.empty(len(n_chunks), dtype=torch.int32, device="cuda")
+    api.tg_bench_streams(buf, d_ids, d_off, sink, stream=stream)
+    ts = []
+    for i in range(reps):
+        evict(i)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        api.tg_bench_streams(buf, d_ids, d_off, sink, stream=stream)
+        ev[1].record(stream)
+        ts.append(ev)
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ts]))
+    del buf
+    return {"streams": int(len(n_chunks)), "bytes": total * 8192, "ms": round(ms, 5),
+            "GBps": round(total * 8192 / (ms * 1e-3) / 1e9, 1)}
+
+
 def _device_record(torch) -> dict:
     """What the runtime reports about the GPU (to check the published
     figures the roofline uses: compute units, memory, caches)."""
@@ -454,6 +493,11 @@ def main():
     read_gbps = rbuf.numel() / (read_ms * 1e-3) / 1e9
     del rbuf
 
+    # the same access pattern with no arithmetic: one stream per plan item, in
+    # plan order, each reading as many 8 KiB chunks as the item reads bytes
+    # (pages of shared runs once), chunks placed at random in a fresh buffer
+    streams = stream_read_bench(w, prep, evict, stream)
+
     # pool bytes the batch needs at the configured cluster count, one cluster
     # and one cluster per KV-head, against the bytes it retains
     alloc = {str(C): allocated_bytes(w, C, args.chunk_bf, args.chunk_i8)
@@ -495,11 +539,11 @@ def main():
         "device": _device_record(torch),
         "read_ceiling_GBps": round(read_gbps, 1),
         "split_frac_of_read_ceiling": round(achieved / read_gbps, 4),
+        "stream_read": dict(streams, split_time_frac=round(streams["ms"] / split_ms, 4)),
         "fragmentation": {"retained_bytes": tr["kv_roofline"], "allocated_bytes_by_clusters": alloc,
                           "ratio_by_clusters": {k: round(v / tr["kv_roofline"], 4) for k, v in alloc.items()}},
         "roofline": {
-            "kernel": "split_bf16_kernel" if not prep.tables.stride_has_i8 else
-                      "split_i8_kernel + split_bf16_kernel",
+            "kernel": "split_bf16_kernel" if not prep.tables.stride_has_i8 else "split_tiered_kernel",
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,

@@ -463,6 +463,22 @@ int tg_zip_decode(const void* src, int64_t n, uint16_t* dst, void* stream);
 #define TG_BENCH_READ_BLOCKS 4096
 int tg_bench_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
+/* Streaming read in the decode split kernels' own access pattern: n_streams
+ * independent streams, one wavefront each (four to a workgroup), stream w
+ * reading the 8 KiB chunks chunk[off[w]] .. chunk[off[w + 1] - 1] of `src`
+ * (chunk c = bytes [8192 c, 8192 c + 8192)) in list order, in 1 KiB wave
+ * loads with two chunks in flight, non-temporal -- as a decode item reads its
+ * pages.  Chunk ids are taken modulo bytes / 8192, so any list stays inside
+ * `src`.  sink[w] (device uint32 [n_streams]) receives the XOR of every
+ * 32-bit word stream w read (a chunk listed twice cancels).  Timing it over
+ * the chunk counts of a plan gives the rate that pattern allows, with no
+ * arithmetic.  src: 16-byte aligned device memory, `bytes` a positive
+ * multiple of 8192; chunk, off (n_streams + 1 entries, non-decreasing):
+ * device int32.  TG_EINVAL on a bad size or pointer; TG_EDEVICE on a failed
+ * launch. */
+int tg_bench_streams(const void* src, size_t bytes, const int32_t* chunk, const int32_t* off, int32_t n_streams,
+                     uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

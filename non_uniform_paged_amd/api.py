@@ -19,7 +19,7 @@ __all__ = [
     "Reservation", "Share", "Pool", "Tables", "DeviceCache",
     "tg_reserve", "tg_size_tables", "tg_build_tables", "tg_release",
     "tg_write_kv", "tg_decode_workspace_bytes", "tg_decode_attn", "tg_decode_split",
-    "tg_merge_partials", "tg_bench_read", "TG_BENCH_READ_BLOCKS", "tg_append_kv",
+    "tg_merge_partials", "tg_bench_read", "tg_bench_streams", "TG_BENCH_READ_BLOCKS", "tg_append_kv",
     "tg_stream_order", "tg_stream_staging_bytes", "tg_decode_streamed",
     "tg_zip_bound", "tg_zip_workspace_bytes", "tg_zip_encode", "tg_zip_decode", "zip_compressed_bytes",
 ]
@@ -356,6 +356,19 @@ def tg_bench_read(src, sink, stream=None) -> None:
         raise ValueError("sink too small")
     check(lib().tg_bench_read(_ptr(src), int(src.numel() * src.element_size()), _ptr(sink),
                               _stream_ptr(stream)), "tg_bench_read")
+
+
+def tg_bench_streams(src, chunk, off, sink, stream=None) -> None:
+    """Independent streams of 8 KiB chunks of ``src`` (device tensor, size a
+    multiple of 8192 bytes): stream w reads chunk[off[w]:off[w + 1]] (device
+    int32 tensors) one wavefront at a time, as a decode item reads its pages;
+    ``sink`` (device int32, len(off) - 1 elements) receives each stream's XOR
+    fold."""
+    n = int(off.numel()) - 1
+    if n < 0 or sink.numel() < n:
+        raise ValueError("off must have n_streams + 1 entries and sink n_streams")
+    check(lib().tg_bench_streams(_ptr(src), int(src.numel() * src.element_size()), _ptr(chunk), _ptr(off), n,
+                                 _ptr(sink), _stream_ptr(stream)), "tg_bench_streams")
 
 
 def tg_append_kv(cache: DeviceCache, rows, status=None, stream=None) -> None:

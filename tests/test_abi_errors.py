@@ -107,6 +107,12 @@ def test_codec_and_read_aid_reject_bad_sizes():
     assert lib.tg_zip_decode(FAKE, n, odd, None) == L.TG_EINVAL
     assert lib.tg_bench_read(FAKE, 24, FAKE, None) == L.TG_EINVAL
     assert lib.tg_bench_read(None, 32, FAKE, None) == L.TG_EINVAL
+    # the paged-stream read: buffer of whole 8 KiB chunks, aligned, tables present
+    for args in ((FAKE, 8192 + 16, FAKE, FAKE, 1), (FAKE, 0, FAKE, FAKE, 1), (odd, 8192, FAKE, FAKE, 1),
+                 (FAKE, 8192, None, FAKE, 1), (FAKE, 8192, FAKE, None, 1), (FAKE, 8192, FAKE, FAKE, -1)):
+        assert lib.tg_bench_streams(*args, FAKE, None) == L.TG_EINVAL, args
+    assert lib.tg_bench_streams(FAKE, 8192, FAKE, FAKE, 1, None, None) == L.TG_EINVAL
+    assert lib.tg_bench_streams(FAKE, 8192, None, None, 0, None, None) == L.TG_OK  # nothing to read
 
 
 def test_status_strings_cover_every_code():
