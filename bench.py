@@ -13,7 +13,7 @@ bracketed by HIP events on the stream the kernels run on; the K steps together
 are bracketed by device synchronisation.
 
 Prints one JSON line (see the ``result`` dict at the end).  ``--gpus`` above 1
-is refused: this build measures one GPU.
+is refused: the measurement runs on one GPU.
 """
 from __future__ import annotations
 
@@ -374,8 +374,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the decode step shards by request with no exchange; see the design notes)",
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(the decode step would shard by request with no exchange)",
               file=sys.stderr)
         sys.exit(2)
 
