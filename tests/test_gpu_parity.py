@@ -414,3 +414,45 @@ def test_pages_beyond_4_gib():
         assert int(bt[bt >= 0].min()) * b.pool.page_bytes(0, tier) >= 1 << 32, tier
     b.step()
     assert np.array_equal(ga, b.output())
+
+
+def test_decode_step_replays_from_a_graph():
+    """The decode step (split kernels, then the merge; no memory-set nodes)
+    captured once in a HIP graph and replayed: every replay, with eager work
+    and synchronisations between replays and new queries copied into the
+    captured q buffer, equals the eager step bit for bit."""
+    torch = _need_gpu()
+    for w, kw in ((make_workload("tiered", B=2, Hq=8, Hkv=2, ctx=("fixed", 2500)), dict(chunk_bf=64, chunk_i8=192)),
+                  (make_workload("radix", B=20, Hq=8, Hkv=2, share=dict(prefix=150, branch=40, n_branches=2,
+                                                                         suffix=(8, 120))),
+                   dict(chunk_bf=48, group_size=32))):
+        p = _prep(w, **kw)
+        q0 = p.q.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # warm-up off the default stream, as capture requires
+            p.step(stream=side)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            p.step()
+        gen = torch.Generator(device="cpu").manual_seed(5)
+        for k in range(4):
+            qk = q0 if k == 0 else (q0.float() + 0.25 * torch.randn(q0.shape, generator=gen).to(q0.device)).to(q0.dtype)
+            p.q.copy_(qk)
+            p.step()  # eager reference with the same q
+            want = p.output().copy()
+            p.out.zero_()
+            junk = torch.randn(1 << 20, device=q0.device).sum()  # eager work between replays
+            g.replay()
+            torch.cuda.synchronize()
+            got = p.output()
+            assert np.isfinite(float(junk))
+            assert np.array_equal(got, want), (w.name, k)
+        # a replay with the workload's own q against the oracle
+        p.q.copy_(q0)
+        g.replay()
+        res_o = A.reserve_for(w)
+        pairs = [(r, h) for r in range(w.B) for h in range(w.Hkv)]
+        _check(p.output(), A.decode(w, res_o, pairs), pairs, w.Hq // w.Hkv, f"graph-{w.name}")
