@@ -294,8 +294,29 @@ class DeviceCache:
 
 
 def tg_write_kv(cache: DeviceCache, rows, index, offsets, stream=None) -> None:
+    torch = _torch()
+    _dev(rows, "rows")
+    _dev(index, "index", 0, (torch.int32,))
+    _dev(offsets, "offsets", (int(cache.B) * int(cache.H) + 1) * 8, (torch.int64,))
     check(lib().tg_write_kv(ctypes.byref(cache.struct), _ptr(rows), _ptr(index), _ptr(offsets),
                             _stream_ptr(stream)), "tg_write_kv")
+
+
+def _dev(t, name: str, min_bytes: int = 0, dtypes=None):
+    """Check that ``t`` is a contiguous device tensor of at least
+    ``min_bytes`` bytes (and of one of ``dtypes``): the C calls take raw
+    pointers and cannot see a buffer's size, so a short buffer would be read
+    or written past its end on the device."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} must be one of {[str(d) for d in dtypes]}, not {t.dtype}")
+    if t.numel() * t.element_size() < min_bytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {min_bytes}")
+    return t
 
 
 def _decode_args(cache, q, out, workspace, n_q_heads, sm_scale, work=None):
@@ -306,6 +327,12 @@ def _decode_args(cache, q, out, workspace, n_q_heads, sm_scale, work=None):
         qd = TG_Q_BF16
     else:
         raise TypeError("q must be float32 or bfloat16")
+    rows = int(cache.B) * int(n_q_heads) * int(cache.d)
+    _dev(q, "q", rows * q.element_size())
+    if out is not None:
+        _dev(out, "out", rows * 4, (torch.float32,))
+    _dev(workspace, "workspace")
+    _dev(cache.work if work is None else work, "work", int(cache.n_items) * 24, (torch.int32,))
     a = L.DecodeArgs()
     a.n_q_heads = int(n_q_heads)
     a.q_dtype = qd
@@ -344,6 +371,10 @@ def tg_decode_split(cache: DeviceCache, q, workspace, n_q_heads: int, sm_scale: 
 
 def tg_merge_partials(workspace, n_slots: int, n_pairs: int, G: int, d: int, part_off, out,
                       stream=None) -> None:
+    torch = _torch()
+    _dev(workspace, "workspace", int(n_slots) * int(G) * (int(d) + 2) * 4)
+    _dev(part_off, "part_off", (int(n_pairs) + 1) * 4, (torch.int32,))
+    _dev(out, "out", int(n_pairs) * int(G) * int(d) * 4, (torch.float32,))
     check(lib().tg_merge_partials(_ptr(workspace), int(n_slots), int(n_pairs), int(G), int(d),
                                   _ptr(part_off), _ptr(out), _stream_ptr(stream)), "tg_merge_partials")
 
@@ -364,9 +395,14 @@ def tg_bench_streams(src, chunk, off, sink, stream=None) -> None:
     int32 tensors) one wavefront at a time, as a decode item reads its pages;
     ``sink`` (device int32, len(off) - 1 elements) receives each stream's XOR
     fold."""
+    torch = _torch()
     n = int(off.numel()) - 1
     if n < 0 or sink.numel() < n:
         raise ValueError("off must have n_streams + 1 entries and sink n_streams")
+    _dev(src, "src")
+    _dev(chunk, "chunk", 0, (torch.int32,))
+    _dev(off, "off", 0, (torch.int32,))
+    _dev(sink, "sink", 4 * n)
     check(lib().tg_bench_streams(_ptr(src), int(src.numel() * src.element_size()), _ptr(chunk), _ptr(off), n,
                                  _ptr(sink), _stream_ptr(stream)), "tg_bench_streams")
 
@@ -376,6 +412,9 @@ def tg_append_kv(cache: DeviceCache, rows, status=None, stream=None) -> None:
     and age the oldest bf16 block into INT8 where the tier split says so;
     ``status`` (device int32, optional) gets bit 0 if a (r, h) ran out of the
     reserved capacity."""
+    _dev(rows, "rows", int(cache.B) * int(cache.H) * 2 * int(cache.d) * 2)
+    if status is not None:
+        _dev(status, "status", 4)
     check(lib().tg_append_kv(ctypes.byref(cache.struct), _ptr(rows), _ptr(status), _stream_ptr(stream)),
           "tg_append_kv")
 
@@ -417,12 +456,17 @@ def tg_zip_workspace_bytes(n: int) -> int:
 def tg_zip_encode(src, dst, workspace, stream=None) -> None:
     """Compress ``src`` (device int16/uint16 tensor of bf16 bits, size a
     multiple of 8) into ``dst`` (device, >= tg_zip_bound bytes)."""
+    _dev(src, "src")
+    _dev(dst, "dst")
+    _dev(workspace, "workspace")
     check(lib().tg_zip_encode(_ptr(src), int(src.numel()), _ptr(dst), int(dst.numel() * dst.element_size()),
                               _ptr(workspace), int(workspace.numel() * workspace.element_size()),
                               _stream_ptr(stream)), "tg_zip_encode")
 
 
 def tg_zip_decode(src, n: int, dst, stream=None) -> None:
+    _dev(src, "src")
+    _dev(dst, "dst", int(n) * 2)
     check(lib().tg_zip_decode(_ptr(src), int(n), _ptr(dst), _stream_ptr(stream)), "tg_zip_decode")
 
 

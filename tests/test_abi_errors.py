@@ -5,6 +5,7 @@ documents for that mistake."""
 import ctypes
 
 import numpy as np
+import pytest
 
 from non_uniform_paged_amd import _lib as L
 
@@ -124,3 +125,29 @@ def test_status_strings_cover_every_code():
         assert s and s not in seen
         seen.add(s)
     assert np.all([isinstance(x, bytes) for x in seen])
+
+
+def test_python_binding_refuses_unfit_buffers():
+    """The binding checks what the C calls cannot see behind a raw pointer:
+    device placement, contiguity, dtype and size of every buffer, so that a
+    short or host buffer is refused before any launch (CPU only: every case
+    fails before the library is called)."""
+    torch = pytest.importorskip("torch")
+    from types import SimpleNamespace
+    from non_uniform_paged_amd import api
+    cache = SimpleNamespace(B=2, H=2, d=64, work=torch.zeros(6, dtype=torch.int32), n_items=1, part_off=None,
+                            gitems=None, n_gitems=0, n_slots=1)
+    q = torch.zeros(2 * 4 * 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="q must be a device tensor"):
+        api._decode_args(cache, q, None, q, 4, 0.0)
+    with pytest.raises(TypeError, match="q must be float32 or bfloat16"):
+        api._decode_args(cache, q.to(torch.float16), None, q, 4, 0.0)
+    with pytest.raises(ValueError, match="rows must be a device tensor"):
+        api.tg_append_kv(cache, torch.zeros(8, dtype=torch.int16))
+    with pytest.raises(ValueError, match="workspace must be a device tensor"):
+        api.tg_merge_partials(torch.zeros(4), 1, 1, 2, 64, torch.zeros(2, dtype=torch.int32), torch.zeros(128))
+    with pytest.raises(ValueError, match="src must be a device tensor"):
+        api.tg_zip_decode(torch.zeros(8, dtype=torch.int16), 8, torch.zeros(8, dtype=torch.int16))
+    with pytest.raises(ValueError, match="rows must be a device tensor"):
+        api.tg_write_kv(cache, torch.zeros(4, dtype=torch.int16), torch.zeros(1, dtype=torch.int32),
+                        torch.zeros(5, dtype=torch.int64))
