@@ -8,12 +8,12 @@ through PyTorch.  ``w`` is any object with the fields of
 """
 from __future__ import annotations
 
-import math
 from typing import Optional
 
 import numpy as np
 
 from . import api
+
 
 def tune_candidates(w, has_quantised: bool):
     """(chunk_bf, chunk_i8) pairs tune_chunks tries: bf16 item lengths from

@@ -3,14 +3,12 @@
 Tolerance (stated by the workload specification): every fp32 output element
 satisfies |gpu - oracle| <= 2e-3 + 1e-2 * |oracle|.  Integer work (budgets,
 tables, INT8 codes and scales) must match bit for bit."""
-import math
 import sys
 
 import numpy as np
 import pytest
 
 from oracle import attention as A
-from oracle import planner as P
 from oracle import quant as Q
 from workloads import make_workload
 

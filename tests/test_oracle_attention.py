@@ -9,7 +9,6 @@ import pytest
 import torch
 
 from oracle import attention as A
-from oracle import planner as P
 from oracle import quant
 from workloads import make_workload
 

@@ -28,7 +28,7 @@ import concurrent.futures as _cf
 import dataclasses
 import math
 import os
-from typing import Dict, List, Optional, Sequence, Tuple
+from typing import Dict, List, Optional, Tuple
 
 import numpy as np
 
