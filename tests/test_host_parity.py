@@ -229,3 +229,12 @@ def test_error_codes():
     with pytest.raises(tg.TGError) as e:
         tg.tg_size_tables(rr, 16, 64, tg.Share(n_nodes, ids, node_len), gen_tokens=8)
     assert e.value.name == "TG_EINVAL"
+
+
+def test_rounding_directions_match_the_hand_worked_cases():
+    """The library's reservation on the oracle pins' hand-worked rounding
+    cases (rank step floored, budget and bf16 share ceiled)."""
+    r = tg.tg_reserve([0, 1, 2, 3], 500_000, 100_000, 1, 1_000_000, 64, [3000], None, None)
+    assert r.budget.tolist() == [[1500, 1101, 701, 300]]
+    r = tg.tg_reserve([0], 1_000_000, 1_000_000, 1, 125_000, 64, [585], None, None)
+    assert (r.n_i8.tolist(), r.n_bf.tolist()) == ([[448]], [[137]])

@@ -1,0 +1,224 @@
+"""Mistakes planted in the oracle are caught by its pins.
+
+Each case below replaces one oracle function (for that test only, on the
+CPU) with a plausible mistake: a dropped term, a wrong sign, index or axis,
+a transposed or swapped operand, a wrong rounding, an off-by-one.  Then it
+runs the oracle's own pin tests unchanged and requires at least one of them
+to fail.  A mutant no pin catches would mean that part of the oracle is not
+really pinned."""
+import heapq
+import importlib.util
+import os
+
+import numpy as np
+import pytest
+
+from oracle import attention as A
+from oracle import planner as P
+from oracle import quant as Q
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _load(name):
+    spec = importlib.util.spec_from_file_location(f"_pins_{name}", os.path.join(HERE, name + ".py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+TA = _load("test_oracle_attention")
+TQ = _load("test_oracle_quant")
+TP = _load("test_oracle_planner")
+
+ATTENTION_PINS = [
+    lambda: TA.test_uniform_budgets_equal_dense_sdpa(
+        "llama8b", dict(B=2, ctx=("uniform", 200, 500), ratio_ppm=(1_000_000, 1_000_000), n_clusters=1)),
+    TA.test_single_row_returns_its_value_row,
+    TA.test_closed_forms,
+    TA.test_matches_pure_python_brute_force,
+    TA.test_lse_merge_split_invariance,
+    TA.test_int8_rows_equal_attention_over_same_bf16_values,
+    TA.test_workload_tier_rows_oldest_quantised_newest_exact,
+    TA.test_gqa_mapping_and_scale_default,
+]
+QUANT_PINS = [TQ.test_error_bounded_by_half_step_and_absmax_hits_127,
+              TQ.test_integer_multiples_of_power_of_two_step_round_trip_exactly,
+              TQ.test_ties_round_to_even, TQ.test_zero_block_and_sign_symmetry_and_saturation,
+              TQ.test_rows_are_quantised_block_by_block]
+PLANNER_PINS = [TP.test_hand_worked_budgets_clusters_tables_plan, TP.test_hand_worked_tier_split,
+                TP.test_hand_worked_rounding_directions,
+                TP.test_tiered_128k_split_matches_workload_statement, TP.test_hand_worked_sharing_and_release,
+                TP.test_radix_lesson_block_counts, TP.test_hand_worked_group_items]
+
+
+def _caught(pins) -> bool:
+    for pin in pins:
+        try:
+            pin()
+        except Exception:  # an assertion, or the mutant breaking a shape
+            return True
+    return False
+
+
+# ------------------------------------------------------------------ attention mutants
+def _attend_no_scale(q, K, V, scale):
+    s = np.asarray(K, np.float64) @ np.asarray(q, np.float64).T
+    p = np.exp(s - s.max(axis=0))
+    return (p.T @ np.asarray(V, np.float64)) / p.sum(axis=0)[:, None]
+
+
+def _attend_wrong_axis(q, K, V, scale):  # softmax over the heads instead of the rows
+    s = (np.asarray(K, np.float64) @ np.asarray(q, np.float64).T) * scale
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    return p.T @ np.asarray(V, np.float64)
+
+
+def _attend_keys_as_values(q, K, V, scale):
+    return TA_ORIG_ATTEND(q, K, K, scale)
+
+
+def _attend_no_normaliser(q, K, V, scale):
+    s = (np.asarray(K, np.float64) @ np.asarray(q, np.float64).T) * scale
+    p = np.exp(s - s.max(axis=0))
+    return p.T @ np.asarray(V, np.float64)
+
+
+def _merge_sign(m, l, acc):
+    m = np.asarray(m, np.float64)
+    w = np.exp(m.max(axis=0) - m)
+    return (w[:, :, None] * np.asarray(acc, np.float64)).sum(axis=0) / (w * np.asarray(l, np.float64)).sum(axis=0)[:, None]
+
+
+def _merge_unweighted_l(m, l, acc):
+    m = np.asarray(m, np.float64)
+    w = np.exp(m - m.max(axis=0))
+    return (w[:, :, None] * np.asarray(acc, np.float64)).sum(axis=0) / np.asarray(l, np.float64).sum(axis=0)[:, None]
+
+
+def _rows_off_by_one(K16, V16, n_i8, qb, bits=8):
+    return TA_ORIG_ROWS(K16, V16, max(n_i8 - 1, 0), qb, bits)
+
+
+def _rows_k_only(K16, V16, n_i8, qb, bits=8):
+    K, _ = TA_ORIG_ROWS(K16, V16, n_i8, qb, bits)
+    return K, A.bf16_to_f64(V16)
+
+
+TA_ORIG_ATTEND = A.attend
+TA_ORIG_ROWS = A.rows_f64
+
+
+@pytest.mark.parametrize("target,mutant", [
+    ("attend", _attend_no_scale), ("attend", _attend_wrong_axis), ("attend", _attend_keys_as_values),
+    ("attend", _attend_no_normaliser), ("lse_merge", _merge_sign), ("lse_merge", _merge_unweighted_l),
+    ("rows_f64", _rows_off_by_one), ("rows_f64", _rows_k_only),
+], ids=["no-scale", "softmax-over-heads", "keys-as-values", "no-normaliser", "merge-sign", "merge-unweighted-l",
+        "int8-rows-off-by-one", "int8-values-not-dequantised"])
+def test_attention_mutants_are_caught(monkeypatch, target, mutant):
+    monkeypatch.setattr(A, target, mutant)
+    assert _caught(ATTENTION_PINS), f"no pin catches the {mutant.__name__} mutant of {target}"
+
+
+# ------------------------------------------------------------------ quantiser mutants
+QB_ORIG = Q.quantize_block
+BS_ORIG = Q.block_scale
+
+
+def _scale_over_128(x, bits=8):
+    x = np.asarray(x, np.float32)
+    return (np.max(np.abs(x), axis=0) / np.float32(128 if bits == 8 else 8)).astype(np.float16)
+
+
+def _scale_not_fp16(x, bits=8):  # the scale kept in fp32, so a code is not the stored scale's
+    s = np.max(np.abs(np.asarray(x, np.float32)), axis=0) / np.float32(Q.qmax_of(bits))
+    return s.astype(np.float32).view(np.float32)
+
+
+def _round_half_up(x, bits=8):
+    x = np.asarray(x, np.float32)
+    qm = Q.qmax_of(bits)
+    s = Q.block_scale(x, bits)
+    sf = s.astype(np.float32)
+    safe = np.where(sf > 0, sf, np.float32(1))
+    y = np.floor(x / safe + np.float32(0.5))
+    return np.where(sf > 0, np.clip(y, -qm, qm), 0).astype(np.int8), s
+
+
+def _clamp_128(x, bits=8):
+    x = np.asarray(x, np.float32)
+    s = Q.block_scale(x, bits)
+    sf = s.astype(np.float32)
+    safe = np.where(sf > 0, sf, np.float32(1))
+    y = np.rint(x / safe * np.float32(1.004))  # saturates just past the code range
+    return np.where(sf > 0, np.clip(y, -128, 127), 0).astype(np.int8), s
+
+
+@pytest.mark.parametrize("target,mutant", [
+    ("block_scale", _scale_over_128), ("block_scale", _scale_not_fp16),
+    ("quantize_block", _round_half_up), ("quantize_block", _clamp_128),
+], ids=["scale-over-128", "scale-not-fp16", "round-half-up", "overshoot-and-clamp-128"])
+def test_quantiser_mutants_are_caught(monkeypatch, target, mutant):
+    monkeypatch.setattr(Q, target, mutant)
+    assert _caught(QUANT_PINS), f"no pin catches the {mutant.__name__} mutant of {target}"
+
+
+# ------------------------------------------------------------------ planner mutants
+RATIO_ORIG = P.ratio_ppm
+ALLOC_ORIG = P.Pool.alloc
+
+
+def _ratio_reversed_rank(k, H, hi, lo):
+    return RATIO_ORIG(H - 1 - k, H, hi, lo)
+
+
+def _ratio_rounds_up(k, H, hi, lo):
+    return hi if H == 1 else hi - (-((-(hi - lo) * k) // (H - 1)))
+
+
+def _tier_floor(L, recent_ppm, quant_block):
+    old = L - (L * recent_ppm) // P.PPM
+    i8 = (old // quant_block) * quant_block
+    return i8, L - i8
+
+
+def _tier_unaligned(L, recent_ppm, quant_block):
+    i8 = L - P._ceil_div(L * recent_ppm, P.PPM)
+    return i8, L - i8
+
+
+def _alloc_reversed(self, c, t):
+    # hand out the highest page id first instead of the lowest
+    free = [p for p in range(self.cap[c][t]) if self.ref[c][t].get(p, 0) == 0]
+    if not free:
+        raise P.OracleError("ENOMEM", "exhausted")
+    pid = free[-1]
+    self.ref[c][t][pid] = 1
+    if pid >= self.top[c][t]:
+        self.top[c][t] = pid + 1
+    h = self.heap[c][t]
+    if pid in h:
+        h.remove(pid)
+        heapq.heapify(h)
+    return pid
+
+
+@pytest.mark.parametrize("target,mutant", [
+    ("ratio_ppm", _ratio_reversed_rank), ("ratio_ppm", _ratio_rounds_up),
+    ("tier_split", _tier_floor), ("tier_split", _tier_unaligned),
+], ids=["rank-reversed", "ratio-rounded-up", "tier-floor", "tier-not-block-aligned"])
+def test_planner_mutants_are_caught(monkeypatch, target, mutant):
+    monkeypatch.setattr(P, target, mutant)
+    assert _caught(PLANNER_PINS), f"no pin catches the {mutant.__name__} mutant of {target}"
+
+
+def test_allocation_order_mutant_is_caught(monkeypatch):
+    monkeypatch.setattr(P.Pool, "alloc", _alloc_reversed)
+    assert _caught(PLANNER_PINS), "no pin catches highest-free-first allocation"
+
+
+def test_pins_pass_on_the_oracle_as_it_is():
+    """The control: unmutated, every pin used above passes."""
+    for pins in (ATTENTION_PINS, QUANT_PINS, PLANNER_PINS):
+        assert not _caught(pins)

@@ -50,6 +50,29 @@ def test_hand_worked_tier_split():
     assert [row[0] for row in res.n_bf] == g["expect_n_bf"]
 
 
+def test_hand_worked_rounding_directions():
+    """Two cases worked by hand where the rounding direction of the rules
+    decides the result (R-rank, R-round, R-tier).
+
+    Ratio band 0.5 .. 0.1 over H = 4 heads: rank 1 gets
+    500000 - floor(400000 * 1 / 3) = 500000 - 133333 = 366667 ppm (rounding
+    the step up would give 366666); for n = 3000 compressible tokens its
+    budget is ceil(366667 * 3000 / 1e6) = ceil(1100.001) = 1101 (1100 with
+    the other rounding).  Ranks 0, 2, 3: 500000, 233334, 100000 ppm ->
+    1500, ceil(700.002) = 701, 300.
+
+    Tier split of L = 585 rows keeping 12.5 % bf16 in 64-row blocks:
+    n_bf0 = ceil(585 / 8) = ceil(73.125) = 74, the older 511 rows hold 7
+    whole blocks, so n_i8 = 448 and n_bf = 137 (rounding n_bf0 down would
+    leave 512 older rows: 8 blocks, n_i8 = 512)."""
+    assert [P.ratio_ppm(k, 4, 500_000, 100_000) for k in range(4)] == [500_000, 366_667, 233_334, 100_000]
+    res = P.reserve([0, 1, 2, 3], 500_000, 100_000, 1, 1_000_000, 64, [3000], None, None)
+    assert res.budget == [[1500, 1101, 701, 300]]
+    assert P.tier_split(585, 125_000, 64) == (448, 137)
+    res = P.reserve([0], 1_000_000, 1_000_000, 1, 125_000, 64, [585], None, None)
+    assert (res.n_i8, res.n_bf) == ([[448]], [[137]])
+
+
 def test_tiered_128k_split_matches_workload_statement():
     g = _gold("planner_hand.json")["case_ttkv_128k"]
     res = P.reserve([0], 1_000_000, 1_000_000, 1, g["recent_ppm"], g["quant_block"], [g["L"]])
