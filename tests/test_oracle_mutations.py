@@ -16,6 +16,7 @@ import pytest
 from oracle import attention as A
 from oracle import planner as P
 from oracle import quant as Q
+from oracle import splitzip as Z
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -30,6 +31,7 @@ def _load(name):
 TA = _load("test_oracle_attention")
 TQ = _load("test_oracle_quant")
 TP = _load("test_oracle_planner")
+TZ = _load("test_oracle_splitzip")
 
 ATTENTION_PINS = [
     lambda: TA.test_uniform_budgets_equal_dense_sdpa(
@@ -221,4 +223,80 @@ def test_allocation_order_mutant_is_caught(monkeypatch):
 def test_pins_pass_on_the_oracle_as_it_is():
     """The control: unmutated, every pin used above passes."""
     for pins in (ATTENTION_PINS, QUANT_PINS, PLANNER_PINS):
+        assert not _caught(pins)
+
+
+# ------------------------------------------------------------------ plan, growth and codec mutants
+PLAN_PINS = [TP.test_hand_worked_budgets_clusters_tables_plan, TP.test_hand_worked_group_items,
+             lambda: TP.test_invariants("llama8b"), lambda: TP.test_invariants("radix"),
+             lambda: TP.test_longest_first_order_follows_bytes_read(8, (64, 128)),
+             lambda: TP.test_longest_first_order_follows_bytes_read(4, (128, 192))]
+GROWTH_PINS = [lambda: TP.test_append_steps_follow_the_tier_split(125_000, 64),
+               lambda: TP.test_append_steps_follow_the_tier_split(300_000, 64),
+               TP.test_capacity_is_the_largest_split_on_the_way,
+               TP.test_incremental_blocks_equal_blocks_of_the_whole_sequence,
+               lambda: TP.test_growth_plan_item_counts_follow_the_live_rows(128, (512, 1792)),
+               TP.test_growth_tables_cover_capacity_and_keep_live_lengths]
+CODEC_PINS = [TZ.test_hand_worked_buffer, TZ.test_round_trips_bit_exact, TZ.test_codebook_is_the_sixteen_most_frequent]
+SPLIT_ORIG = P.split_range
+CODEBOOK_ORIG = Z.codebook
+
+
+def _split_one_more(lo, hi, unit, chunk, hi_live=None):  # one item too many
+    u = P._ceil_div(hi - lo, unit)
+    if u <= 0:
+        return []
+    k = P._ceil_div(u, chunk // unit) + 1
+    k = min(k, u)
+    return [(lo + (i * u // k) * unit, min(lo + ((i + 1) * u // k) * unit, hi)) for i in range(k)]
+
+
+def _split_ceil_starts(lo, hi, unit, chunk, hi_live=None):  # item i starts at ceil(i u / k)
+    u = P._ceil_div(hi - lo, unit)
+    if u <= 0:
+        return []
+    k = P._ceil_div(u, chunk // unit) if hi_live is None else max(
+        1, P._ceil_div(P._ceil_div(max(hi_live - lo, 0), unit), chunk // unit), P._ceil_div(u, 2 * (chunk // unit)))
+    st = [lo + P._ceil_div(i * u, k) * unit for i in range(k)] + [hi]
+    return [(st[i], min(st[i + 1], hi)) for i in range(k)]
+
+
+def _lpt_swapped(tier, quant_block, old_bits):
+    return old_bits * quant_block + 16 if tier == P.TIER_BF else 16 * quant_block
+
+
+def _append_ages_a_row(n_i8, n_bf, recent_ppm, quant_block):  # ages when the boundary passes a row, not a block
+    n_bf += 1
+    old = n_i8 + n_bf - P._ceil_div((n_i8 + n_bf) * recent_ppm, P.PPM)
+    if old - n_i8 >= 1 and n_bf > quant_block:
+        return n_i8 + quant_block, n_bf - quant_block, True
+    return n_i8, n_bf, False
+
+
+def _codebook_ties_to_larger(x):
+    counts = np.bincount(Z.exponents(x), minlength=256)
+    order = sorted(range(256), key=lambda e: (-counts[e], -e))
+    return np.array(order[:16], dtype=np.uint8)
+
+
+def _codebook_least_frequent(x):
+    counts = np.bincount(Z.exponents(x), minlength=256)
+    seen = [e for e in range(256) if counts[e] > 0]
+    order = sorted(seen, key=lambda e: (counts[e], e)) + [e for e in range(256) if counts[e] == 0]
+    return np.array(order[:16], dtype=np.uint8)
+
+
+@pytest.mark.parametrize("module,target,mutant,pins", [
+    (P, "split_range", _split_one_more, PLAN_PINS), (P, "split_range", _split_ceil_starts, PLAN_PINS),
+    (P, "lpt_weight", _lpt_swapped, PLAN_PINS), (P, "append_step", _append_ages_a_row, GROWTH_PINS),
+    (Z, "codebook", _codebook_ties_to_larger, CODEC_PINS), (Z, "codebook", _codebook_least_frequent, CODEC_PINS),
+], ids=["plan-one-item-too-many", "plan-starts-rounded-up", "lpt-weights-swapped", "ageing-by-row",
+        "codebook-ties-to-larger", "codebook-least-frequent"])
+def test_plan_growth_codec_mutants_are_caught(monkeypatch, module, target, mutant, pins):
+    monkeypatch.setattr(module, target, mutant)
+    assert _caught(pins), f"no pin catches the {mutant.__name__} mutant of {target}"
+
+
+def test_plan_growth_codec_pins_pass_unmutated():
+    for pins in (PLAN_PINS, GROWTH_PINS, CODEC_PINS):
         assert not _caught(pins)
