@@ -157,6 +157,20 @@ def _clamp_128(x, bits=8):
     return np.where(sf > 0, np.clip(y, -128, 127), 0).astype(np.int8), s
 
 
+def _qmax_int4_as_8(bits):  # a 4-bit code taken as 0..15 magnitude 8
+    return 127 if bits == 8 else 8
+
+
+INT4_PINS = [TQ.test_int4_error_bounded_and_absmax_hits_7, TQ.test_int4_exact_round_trip_and_ties,
+             TQ.test_int4_is_coarser_than_int8_on_the_same_block,
+             TA.test_int4_workload_rows_within_half_a_step_and_exact_multiples]
+
+
+def test_int4_code_range_mutant_is_caught(monkeypatch):
+    monkeypatch.setattr(Q, "qmax_of", _qmax_int4_as_8)
+    assert _caught(INT4_PINS), "no pin catches an INT4 code range of +-8"
+
+
 @pytest.mark.parametrize("target,mutant", [
     ("block_scale", _scale_over_128), ("block_scale", _scale_not_fp16),
     ("quantize_block", _round_half_up), ("quantize_block", _clamp_128),
@@ -222,7 +236,7 @@ def test_allocation_order_mutant_is_caught(monkeypatch):
 
 def test_pins_pass_on_the_oracle_as_it_is():
     """The control: unmutated, every pin used above passes."""
-    for pins in (ATTENTION_PINS, QUANT_PINS, PLANNER_PINS):
+    for pins in (ATTENTION_PINS, QUANT_PINS, INT4_PINS, PLANNER_PINS):
         assert not _caught(pins)
 
 
