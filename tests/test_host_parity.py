@@ -238,3 +238,28 @@ def test_rounding_directions_match_the_hand_worked_cases():
     assert r.budget.tolist() == [[1500, 1101, 701, 300]]
     r = tg.tg_reserve([0], 1_000_000, 1_000_000, 1, 125_000, 64, [585], None, None)
     assert (r.n_i8.tolist(), r.n_bf.tolist()) == ([[448]], [[137]])
+
+
+def test_binding_signatures_follow_the_header():
+    """Every ctypes signature has the header prototype's number of
+    parameters, and a return type of the same size and kind, so that no
+    argument is dropped or widened between Python and the library."""
+    import ctypes
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    protos = {}
+    for m in re.finditer(r"\b([A-Za-z_][A-Za-z_0-9 ]*?\**)\s*\b(tg_[a-z_0-9]+)\s*\(([^;{]*?)\)\s*;", text, flags=re.S):
+        ret, name, params = m.group(1).strip(), m.group(2), " ".join(m.group(3).split())
+        n = 0 if params in ("", "void") else params.count(",") + 1
+        protos[name] = (ret, n)
+    kinds = {"int": ctypes.c_int, "int32_t": ctypes.c_int32, "int64_t": ctypes.c_int64, "size_t": ctypes.c_size_t,
+             "void": None, "const char*": ctypes.c_char_p}
+    assert set(protos) == set(_lib.SIGNATURES), set(protos) ^ set(_lib.SIGNATURES)
+    for name, (ret, n) in protos.items():
+        res, args = _lib.SIGNATURES[name]
+        assert len(args) == n, (name, n, len(args))
+        want = kinds[ret.replace(" *", "*")]
+        if want is None:
+            assert res is None, name
+        else:
+            assert res is not None and ctypes.sizeof(res) == ctypes.sizeof(want), (name, ret, res)
