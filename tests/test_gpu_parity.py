@@ -104,6 +104,19 @@ def test_full_size_configs_sampled(name, k):
     _run_and_compare(w, pairs=_sample_pairs(w, k, 11), what=f"{name}-full", chunk_bf=chunk_bf, chunk_i8=chunk_i8)
 
 
+@pytest.mark.parametrize("name,k", [("ragged", 12), ("tiered", 6)])
+def test_full_size_with_one_page_items(name, k):
+    """The largest plans at full size: every item one bf16 page or one INT8
+    block (ragged: 428369 items and partials, 107093 workgroups, ~209
+    partials a pair through the four-wavefront merge), sampled pairs
+    against the oracle."""
+    _need_gpu()
+    w = make_workload(name)
+    p, _ = _run_and_compare(w, pairs=_sample_pairs(w, k, 5), what=f"{name}-one-page-items", chunk_bf=16,
+                            chunk_i8=64)
+    assert p.tables.n_items == p.tables.n_slots and p.tables.n_items > (400_000 if name == "ragged" else 90_000)
+
+
 def test_single_row_returns_value_row_exactly():
     torch = _need_gpu()
     w = make_workload("llama8b", B=3, ctx=("uniform", 20, 40), budget=None)
