@@ -343,6 +343,19 @@ def test_group_items_wide(gs, G, d, qd):
     assert p.tables.n_gitems > 0
 
 
+@pytest.mark.parametrize("G,qd", [(4, "bf16"), (8, "f32")])
+def test_group_items_past_one_page_window(G, qd):
+    """Group items longer than the 64 pages whose ids a wavefront holds at
+    once (a 1500-row prefix in one item: two windows, the second ending in a
+    short pair) on the cooperative path."""
+    _need_gpu()
+    w = make_workload("radix", B=40, Hq=2 * G, Hkv=2, q_dtype=qd,
+                      share=dict(prefix=1500, branch=200, n_branches=2, suffix=(8, 100)))
+    p, _ = _run_and_compare(w, what=f"long-group-items-G{G}-{qd}", chunk_bf=4096, group_size=32)
+    rows = p.tables.plan[:p.tables.n_gitems, 4] - p.tables.plan[:p.tables.n_gitems, 3]
+    assert rows.max() > 64 * 16
+
+
 @pytest.mark.parametrize("seed", [1, 2])
 def test_group_items_in_any_plan_order(seed):
     """A plan whose group items do not lead (shuffled on the host) still
