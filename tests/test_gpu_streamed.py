@@ -22,6 +22,10 @@ CASES = {
     "tiered-b3": ("tiered", dict(B=3, Hq=8, Hkv=2, ctx=("fixed", 3000))),
     "two-clusters-b5": ("llama8b", dict(B=5, ctx=("uniform", 600, 2500), recent_ppm=250_000)),
     "d64-g8-f32": ("tiered", dict(B=4, Hq=16, Hkv=2, d=64, q_dtype="f32", ctx=("fixed", 1500))),
+    # shared radix pages in both tiers: group items run before the streamed
+    # INT8 items, and shared INT8 pages are staged once per request
+    "radix-int8": ("radix", dict(B=12, Hq=8, Hkv=2, recent_ppm=250_000,
+                                 share=dict(prefix=300, branch=80, n_branches=2, suffix=(8, 300)))),
 }
 
 
