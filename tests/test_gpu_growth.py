@@ -72,6 +72,9 @@ CASES = {
     "bf16": (dict(B=3, Hq=8, Hkv=4, d=64, ctx=("uniform", 200, 900), recent_ppm=10**6), 150, [0, 150]),
     # q in fp32, G 8
     "g8": (dict(B=2, Hq=16, Hkv=2, q_dtype="f32", ctx=("fixed", 1000), recent_ppm=250_000), 130, [0, 130]),
+    # ragged budgets in two clusters (each cluster its own bf16 ring) with ageing
+    "clusters-ageing": (dict(B=3, Hq=8, Hkv=4, ctx=("uniform", 300, 1200), recent_ppm=250_000), 200,
+                        [0, 37, 200]),
 }
 
 
@@ -79,7 +82,7 @@ CASES = {
 def test_append_and_age_match_fresh_admission(case):
     torch = _need_gpu()
     from non_uniform_paged_amd.runner import Prepared
-    base = "llama8b" if case == "bf16" else "tiered"
+    base = "llama8b" if case in ("bf16", "clusters-ageing") else "tiered"
     over, T, checks = CASES[case]
     w = make_workload(base, **over)
     print(f"case {case}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} d={w.d} T={T}", flush=True)
