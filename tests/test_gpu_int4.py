@@ -98,6 +98,20 @@ def test_int4_head_shapes(G, qd):
     _check(p.output(), A.decode(w, A.reserve_for(w)), f"int4 G{G} {qd}")
 
 
+@pytest.mark.parametrize("C", [1, 2])
+def test_int4_under_shared_radix_pages(C):
+    """The INT4 tier beside shared radix pages: group items over the shared
+    bf16 pages, shared INT4 blocks referenced by many tables, and ragged
+    clusters, against the oracle (which quantises the same rows to 4 bits)."""
+    _need_gpu()
+    w = make_workload("radix", B=24, Hq=8, Hkv=2, old_bits=4, recent_ppm=250_000, n_clusters=C,
+                      share=dict(prefix=300, branch=80, n_branches=3, suffix=(8, 300)))
+    p = _prep(w, chunk_bf=64, chunk_i8=128)
+    assert p.tables.n_gitems > 0 and p.tables.stride_has_i8
+    p.step()
+    _check(p.output(), A.decode(w, A.reserve_for(w)), f"int4 radix C{C}")
+
+
 class _ExactRows(Workload):
     """Rows that are multiples of 2^-3 within +-7 * 2^-3, with +-7 * 2^-3 in
     every 64-row block and channel: exact in bf16 and in INT4."""
