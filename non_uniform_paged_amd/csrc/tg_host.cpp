@@ -199,7 +199,7 @@ extern "C" int tg_pool_create(int32_t C, const int32_t* cluster_size, int32_t d,
   if (!out || !cluster_size || !pages_bf || !pages_i8) return TG_EINVAL;
   if (C < 1 || C > TG_MAX_CLUSTERS || d < 1 || ps < 1 || qb < 1) return TG_EINVAL;
   if (old_bits != 8 && old_bits != 4) return TG_EINVAL;
-  if (old_bits == 4 && (qb * d) % 2) return TG_EINVAL;
+  if (old_bits == 4 && qb % 2 && d % 2) return TG_EINVAL;  // two codes a byte: qb * d must be even
   for (int32_t c = 0; c < C; ++c)
     if (cluster_size[c] < 1 || pages_bf[c] < 0 || pages_i8[c] < 0) return TG_EINVAL;
   for (int32_t c = 0; c < C; ++c)
