@@ -26,7 +26,19 @@ def _inputs():
         "normal-1M": normal,
         "cauchy-ragged": (g.standard_cauchy(8192 * 3 + 8).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16),
         "one-exponent": np.full(4096, 0x4049, np.uint16),
+        # seventeen exponents, 512 values each: the tie at rank 16 goes to the
+        # smaller exponent and the largest one is escaped
+        "seventeen-tied": _tied(g),
+        # escapes only in the last 1000 values of a long buffer
+        "late-escapes": np.concatenate([normal[:1 << 19], ((np.arange(1000) % 50 + 200) << 7).astype(np.uint16),
+                                        normal[:24]]),
     }
+
+
+def _tied(g):
+    e = np.repeat(np.arange(100, 117), 512)
+    x = (g.integers(0, 2, e.size) << 15) | (e << 7) | g.integers(0, 128, e.size)
+    return x[g.permutation(e.size)].astype(np.uint16)
 
 
 @pytest.mark.parametrize("name", list(_inputs()))
