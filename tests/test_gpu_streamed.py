@@ -21,6 +21,9 @@ def _need_gpu():
 CASES = {
     "tiered-b3": ("tiered", dict(B=3, Hq=8, Hkv=2, ctx=("fixed", 3000))),
     "two-clusters-b5": ("llama8b", dict(B=5, ctx=("uniform", 600, 2500), recent_ppm=250_000)),
+    # INT4 codes in host memory: half the bytes cross per block
+    "int4-b3": ("tiered4", dict(B=3, Hq=8, Hkv=2, ctx=("fixed", 3000))),
+    "int4-two-clusters-b4": ("tiered4", dict(B=4, Hq=16, Hkv=4, n_clusters=2, ctx=("uniform", 700, 2600))),
     "d64-g8-f32": ("tiered", dict(B=4, Hq=16, Hkv=2, d=64, q_dtype="f32", ctx=("fixed", 1500))),
     # shared radix pages in both tiers: group items run before the streamed
     # INT8 items, and shared INT8 pages are staged once per request
