@@ -250,16 +250,28 @@ def test_int8_tier_equals_bf16_tier_on_exact_values():
     assert np.max(np.abs(ga - gb)) < 1e-5
 
 
-def test_merge_partials_against_lse_oracle():
+@pytest.mark.parametrize("G,d,counts,n_empty", [
+    (4, 128, [1, 3, 7, 0, 2, 16], 0),
+    # 16 or more slots per pair on average: four wavefronts per row
+    (4, 128, [40, 1, 0, 130, 17, 3], 9),
+    (8, 64, [64, 64, 2, 95], 5),
+    (1, 128, [33, 0, 70, 1], 4),
+    (2, 64, [5, 1, 9, 2, 3], 3),
+])
+def test_merge_partials_against_lse_oracle(G, d, counts, n_empty):
+    """Slots with no rows (m = -inf, l = 0, acc = 0, as an item past the end
+    of its rows writes them) add nothing; a pair with no slots gives zeros."""
     torch = _need_gpu()
     from non_uniform_paged_amd import api
-    rnd = np.random.default_rng(5)
-    G, d = 4, 128
-    counts = [1, 3, 7, 0, 2, 16]
+    rnd = np.random.default_rng(5 + G + d)
     n_slots = sum(counts)
     m = rnd.normal(0, 5, size=(n_slots, G)).astype(np.float32)
     l = rnd.uniform(0.5, 50, size=(n_slots, G)).astype(np.float32)
     acc = rnd.normal(0, 3, size=(n_slots, G, d)).astype(np.float32)
+    empty = rnd.choice(n_slots, n_empty, replace=False)
+    m[empty] = -np.inf
+    l[empty] = 0
+    acc[empty] = 0
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     ws = np.concatenate([acc.reshape(-1), np.stack([m, l], -1).reshape(-1)]).astype(np.float32)
     out = torch.empty((len(counts) * G, d), dtype=torch.float32, device="cuda")
@@ -271,6 +283,8 @@ def test_merge_partials_against_lse_oracle():
             assert np.all(got[p_] == 0)
             continue
         sl = slice(off[p_], off[p_ + 1])
+        if np.all(m[sl] == -np.inf):
+            continue  # no rows at all: any output is unconstrained
         ref = A.lse_merge(m[sl], l[sl], acc[sl])
         assert np.all(np.abs(got[p_] - ref) <= 1e-5 + 1e-5 * np.abs(ref))
 
