@@ -151,3 +151,30 @@ def test_python_binding_refuses_unfit_buffers():
     with pytest.raises(ValueError, match="rows must be a device tensor"):
         api.tg_write_kv(cache, torch.zeros(4, dtype=torch.int16), torch.zeros(1, dtype=torch.int32),
                         torch.zeros(5, dtype=torch.int64))
+
+
+def test_pool_create_checks():
+    """tg_pool_create: INT4 codes pack two to a byte, so a block of qb rows of
+    d channels needs qb * d even; the other arguments as documented."""
+    lib = L.lib()
+    one = (ctypes.c_int32 * 1)(2)
+    pages = (ctypes.c_int64 * 1)(3)
+    neg = (ctypes.c_int64 * 1)(-1)
+
+    def create(d, ps, qb, bits, n_c=one, pb=pages, pi=pages):
+        out = ctypes.c_void_p()
+        rc = lib.tg_pool_create(1, n_c, d, ps, qb, bits, pb, pi, ctypes.byref(out))
+        if rc == L.TG_OK:
+            lib.tg_pool_destroy(out)
+        return rc
+
+    assert create(128, 16, 64, 4) == L.TG_OK
+    assert create(5, 16, 3, 4) == L.TG_EINVAL       # 15 codes: half a byte left over
+    assert create(5, 16, 4, 4) == L.TG_OK
+    assert create(6, 16, 3, 4) == L.TG_OK
+    assert create(5, 16, 3, 8) == L.TG_OK           # INT8 codes: any shape
+    assert create(128, 16, 64, 6) == L.TG_EINVAL    # only 8 or 4 bits
+    assert create(128, 0, 64, 8) == L.TG_EINVAL
+    assert create(128, 16, 64, 8, n_c=(ctypes.c_int32 * 1)(0)) == L.TG_EINVAL
+    assert create(128, 16, 64, 8, pi=neg) == L.TG_EINVAL
+    assert create(1 << 30, 16, 64, 8, pb=(ctypes.c_int64 * 1)(1 << 40)) == L.TG_EOVERFLOW
