@@ -386,6 +386,15 @@ int tg_decode_attn(const tg_cache* cache, const tg_decode_args* args, void* stre
  * B*H pairs of `part_off`.  Same errors as tg_decode_attn. */
 int tg_decode_split(const tg_cache* cache, const tg_decode_args* args, void* stream);
 
+/* Measurement aid: tg_decode_split with the split kernel's own start and end
+ * recorded into start_event and stop_event (hipEvent_t, created by the
+ * caller with timing enabled), so that their elapsed time is the kernel's
+ * execution without the dispatch latency that a separately recorded event
+ * adds.  A plan with no items launches nothing and records neither event.
+ * TG_EINVAL on a null event; otherwise the errors of tg_decode_split. */
+int tg_decode_split_timed(const tg_cache* cache, const tg_decode_args* args, void* start_event, void* stop_event,
+                          void* stream);
+
 /* Merge stage alone (also the merge of partials computed on different
  * shards).  For each pair p in [0, n_pairs) and g < G, merges slots
  * [part_off[p], part_off[p+1]) of `workspace` (layout as above, n_slots
@@ -458,10 +467,12 @@ int tg_zip_decode(const void* src, int64_t n, uint16_t* dst, void* stream);
  * 16 KiB tile k * TG_BENCH_READ_BLOCKS + b); each writes one fold of what it
  * read to sink[block] (device
  * uint32 [TG_BENCH_READ_BLOCKS]) so that no load is elided.  Timing it gives
- * the device's achievable read rate.  TG_EINVAL on a bad size or pointer.
+ * the device's achievable read rate.  start_event, stop_event: null, or
+ * hipEvent_t that receive the kernel's own start and end.  TG_EINVAL on a
+ * bad size or pointer.
  * ---------------------------------------------------------------------- */
 #define TG_BENCH_READ_BLOCKS 4096
-int tg_bench_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
+int tg_bench_read(const void* src, size_t bytes, uint32_t* sink, void* start_event, void* stop_event, void* stream);
 
 /* Streaming read in the decode split kernels' own access pattern: n_streams
  * independent streams, one wavefront each (four to a workgroup), stream w
@@ -474,10 +485,10 @@ int tg_bench_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
  * the chunk counts of a plan gives the rate that pattern allows, with no
  * arithmetic.  src: 16-byte aligned device memory, `bytes` a positive
  * multiple of 8192; chunk, off (n_streams + 1 entries, non-decreasing):
- * device int32.  TG_EINVAL on a bad size or pointer; TG_EDEVICE on a failed
- * launch. */
+ * device int32.  start_event, stop_event: as for tg_bench_read.  TG_EINVAL
+ * on a bad size or pointer; TG_EDEVICE on a failed launch. */
 int tg_bench_streams(const void* src, size_t bytes, const int32_t* chunk, const int32_t* off, int32_t n_streams,
-                     uint32_t* sink, void* stream);
+                     uint32_t* sink, void* start_event, void* stop_event, void* stream);
 
 #ifdef __cplusplus
 }

@@ -108,8 +108,10 @@ SIGNATURES = {
     "tg_decode_split": (ctypes.c_int, [POINTER(Cache), POINTER(DecodeArgs), c_void_p]),
     "tg_merge_partials": (ctypes.c_int, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                          c_void_p, c_void_p]),
-    "tg_bench_read": (ctypes.c_int, [c_void_p, c_size_t, c_void_p, c_void_p]),
-    "tg_bench_streams": (ctypes.c_int, [c_void_p, c_size_t, c_void_p, c_void_p, c_int32, c_void_p, c_void_p]),
+    "tg_decode_split_timed": (ctypes.c_int, [POINTER(Cache), POINTER(DecodeArgs), c_void_p, c_void_p, c_void_p]),
+    "tg_bench_read": (ctypes.c_int, [c_void_p, c_size_t, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "tg_bench_streams": (ctypes.c_int, [c_void_p, c_size_t, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+                                        c_void_p, c_void_p]),
     "tg_append_kv": (ctypes.c_int, [POINTER(Cache), c_void_p, c_void_p, c_void_p]),
     "tg_stream_staging_bytes": (c_size_t, [POINTER(Cache), POINTER(Tables)]),
     "tg_decode_streamed": (ctypes.c_int, [POINTER(Cache), POINTER(Tables), POINTER(DecodeArgs), P32, c_void_p,

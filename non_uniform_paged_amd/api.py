@@ -18,7 +18,7 @@ __all__ = [
     "TGError", "TG_TIER_I8", "TG_TIER_BF16", "TG_Q_F32", "TG_Q_BF16", "TG_GROUP_WIDTH",
     "Reservation", "Share", "Pool", "Tables", "DeviceCache",
     "tg_reserve", "tg_size_tables", "tg_build_tables", "tg_release",
-    "tg_write_kv", "tg_decode_workspace_bytes", "tg_decode_attn", "tg_decode_split",
+    "tg_write_kv", "tg_decode_workspace_bytes", "tg_decode_attn", "tg_decode_split", "tg_decode_split_timed",
     "tg_merge_partials", "tg_bench_read", "tg_bench_streams", "TG_BENCH_READ_BLOCKS", "tg_append_kv",
     "tg_stream_order", "tg_stream_staging_bytes", "tg_decode_streamed",
     "tg_zip_bound", "tg_zip_workspace_bytes", "tg_zip_encode", "tg_zip_decode", "zip_compressed_bytes",
@@ -369,6 +369,33 @@ def tg_decode_split(cache: DeviceCache, q, workspace, n_q_heads: int, sm_scale: 
           "tg_decode_split")
 
 
+def _event_ptr(ev, stream):
+    """Raw hipEvent_t of a torch.cuda.Event (created by a first record on
+    ``stream`` if it has none yet), for the launches that record a kernel's own
+    start and end into it."""
+    if ev.cuda_event == 0:
+        ev.record(stream)
+    return ctypes.c_void_p(ev.cuda_event)
+
+
+def _events(events, stream):
+    if events is None:
+        return None, None
+    start, stop = events
+    return _event_ptr(start, stream), _event_ptr(stop, stream)
+
+
+def tg_decode_split_timed(cache: DeviceCache, q, workspace, n_q_heads: int, events, sm_scale: float = 0.0,
+                          stream=None) -> None:
+    """tg_decode_split with the split kernel's own start and end recorded
+    into ``events`` (two torch.cuda.Event with timing enabled), so that
+    ``events[0].elapsed_time(events[1])`` is the kernel's execution alone."""
+    a = _decode_args(cache, q, None, workspace, n_q_heads, sm_scale)
+    e0, e1 = _events(events, _torch().cuda.current_stream() if stream is None else stream)
+    check(lib().tg_decode_split_timed(ctypes.byref(cache.struct), ctypes.byref(a), e0, e1, _stream_ptr(stream)),
+          "tg_decode_split_timed")
+
+
 def tg_merge_partials(workspace, n_slots: int, n_pairs: int, G: int, d: int, part_off, out,
                       stream=None) -> None:
     torch = _torch()
@@ -379,22 +406,24 @@ def tg_merge_partials(workspace, n_slots: int, n_pairs: int, G: int, d: int, par
                                   _ptr(part_off), _ptr(out), _stream_ptr(stream)), "tg_merge_partials")
 
 
-def tg_bench_read(src, sink, stream=None) -> None:
+def tg_bench_read(src, sink, stream=None, events=None) -> None:
     """Streaming read of the whole of ``src`` (a device tensor, size a
     multiple of 16 bytes); ``sink`` is a device int32 tensor of at least
-    TG_BENCH_READ_BLOCKS elements."""
+    TG_BENCH_READ_BLOCKS elements.  ``events``: None, or two torch.cuda.Event
+    that receive the kernel's own start and end."""
     if sink.numel() * sink.element_size() < 4 * TG_BENCH_READ_BLOCKS:
         raise ValueError("sink too small")
-    check(lib().tg_bench_read(_ptr(src), int(src.numel() * src.element_size()), _ptr(sink),
+    e0, e1 = _events(events, _torch().cuda.current_stream() if stream is None else stream)
+    check(lib().tg_bench_read(_ptr(src), int(src.numel() * src.element_size()), _ptr(sink), e0, e1,
                               _stream_ptr(stream)), "tg_bench_read")
 
 
-def tg_bench_streams(src, chunk, off, sink, stream=None) -> None:
+def tg_bench_streams(src, chunk, off, sink, stream=None, events=None) -> None:
     """Independent streams of 8 KiB chunks of ``src`` (device tensor, size a
     multiple of 8192 bytes): stream w reads chunk[off[w]:off[w + 1]] (device
     int32 tensors) one wavefront at a time, as a decode item reads its pages;
     ``sink`` (device int32, len(off) - 1 elements) receives each stream's XOR
-    fold."""
+    fold.  ``events``: as for ``tg_bench_read``."""
     torch = _torch()
     n = int(off.numel()) - 1
     if n < 0 or sink.numel() < n:
@@ -403,8 +432,9 @@ def tg_bench_streams(src, chunk, off, sink, stream=None) -> None:
     _dev(chunk, "chunk", 0, (torch.int32,))
     _dev(off, "off", 0, (torch.int32,))
     _dev(sink, "sink", 4 * n)
+    e0, e1 = _events(events, torch.cuda.current_stream() if stream is None else stream)
     check(lib().tg_bench_streams(_ptr(src), int(src.numel() * src.element_size()), _ptr(chunk), _ptr(off), n,
-                                 _ptr(sink), _stream_ptr(stream)), "tg_bench_streams")
+                                 _ptr(sink), e0, e1, _stream_ptr(stream)), "tg_bench_streams")
 
 
 def tg_append_kv(cache: DeviceCache, rows, status=None, stream=None) -> None:

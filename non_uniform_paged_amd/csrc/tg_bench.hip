@@ -13,6 +13,7 @@
 // reads its pages.  Timing it over the chunk counts of a plan gives the rate
 // that pattern allows on this device, with no arithmetic at all.
 
+#include <hip/hip_ext.h>
 #include "tg_device.h"
 
 namespace tg_dev {
@@ -90,22 +91,26 @@ __global__ __launch_bounds__(256) void streams_kernel(const TG_GLOBAL u32x4_t* _
 
 using namespace tg_dev;
 
-extern "C" int tg_bench_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+extern "C" int tg_bench_read(const void* src, size_t bytes, uint32_t* sink, void* start_event, void* stop_event,
+                             void* stream) {
   if (!src || !sink || bytes % 16 || reinterpret_cast<uintptr_t>(src) % 16) return TG_EINVAL;
   if (bytes == 0) return TG_OK;
-  hipLaunchKernelGGL(read_kernel, dim3(TG_BENCH_READ_BLOCKS), dim3(256), 0, static_cast<hipStream_t>(stream),
+  hipExtLaunchKernelGGL(read_kernel, dim3(TG_BENCH_READ_BLOCKS), dim3(256), 0, static_cast<hipStream_t>(stream),
+                        static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event), 0,
                      (const TG_GLOBAL u32x4_t*)(src), static_cast<int64_t>(bytes / 16),
                      (TG_GLOBAL uint32_t*)(sink));
   return hipGetLastError() == hipSuccess ? TG_OK : TG_EDEVICE;
 }
 
 extern "C" int tg_bench_streams(const void* src, size_t bytes, const int32_t* chunk, const int32_t* off,
-                                int32_t n_streams, uint32_t* sink, void* stream) {
+                                int32_t n_streams, uint32_t* sink, void* start_event, void* stop_event,
+                                void* stream) {
   if (!src || reinterpret_cast<uintptr_t>(src) % 16 || bytes == 0 || bytes % 8192 || n_streams < 0) return TG_EINVAL;
   if (n_streams == 0) return TG_OK;
   if (!chunk || !off || !sink) return TG_EINVAL;
   const int blocks = (n_streams + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL(streams_kernel, dim3(blocks), dim3(64 * kWavesPerBlock), 0, static_cast<hipStream_t>(stream),
+  hipExtLaunchKernelGGL(streams_kernel, dim3(blocks), dim3(64 * kWavesPerBlock), 0, static_cast<hipStream_t>(stream),
+                        static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event), 0,
                      (const TG_GLOBAL u32x4_t*)(src), static_cast<int64_t>(bytes / 8192),
                      (const TG_GLOBAL int32_t*)(chunk), (const TG_GLOBAL int32_t*)(off), n_streams,
                      (TG_GLOBAL uint32_t*)(sink));

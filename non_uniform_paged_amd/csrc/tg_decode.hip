@@ -242,7 +242,8 @@ int make_split_args(const tg_cache* c, const tg_decode_args* a, bool merge, Spli
   return TG_OK;
 }
 
-int decode_split(const tg_cache* c, const tg_decode_args* a, void* stream, bool merge) {
+int decode_split(const tg_cache* c, const tg_decode_args* a, void* stream, bool merge, hipEvent_t e0 = nullptr,
+                 hipEvent_t e1 = nullptr) {
   SplitArgs s;
   int32_t G = 0;
   const int st_code = make_split_args(c, a, merge, &s, &G);
@@ -252,7 +253,7 @@ int decode_split(const tg_cache* c, const tg_decode_args* a, void* stream, bool 
   // one launch over both tiers when the cache has INT8 pages
   bool has_i8 = false;
   for (int32_t cl = 0; cl < c->n_clusters; ++cl) has_i8 |= c->stride[cl][TG_TIER_I8] > 0;
-  hipError_t e = launch_split(s, d, G, a->q_dtype == TG_Q_F32, has_i8, old_bits_of(c), st);
+  hipError_t e = launch_split(s, d, G, a->q_dtype == TG_Q_F32, has_i8, old_bits_of(c), st, e0, e1);
   if (e != hipSuccess) return TG_EDEVICE;
   if (!merge) return TG_OK;
   e = launch_merge(a->workspace, a->workspace + static_cast<int64_t>(a->n_slots) * G * d, a->part_off,
@@ -387,4 +388,10 @@ extern "C" int tg_decode_attn(const tg_cache* c, const tg_decode_args* a, void* 
 
 extern "C" int tg_decode_split(const tg_cache* c, const tg_decode_args* a, void* stream) {
   return decode_split(c, a, stream, false);
+}
+
+extern "C" int tg_decode_split_timed(const tg_cache* c, const tg_decode_args* a, void* start_event,
+                                     void* stop_event, void* stream) {
+  if (!start_event || !stop_event) return TG_EINVAL;
+  return decode_split(c, a, stream, false, static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event));
 }

@@ -149,7 +149,8 @@ __device__ __forceinline__ f32x4_t mfma_f16_k16(const u32x2_t& a, const u32x2_t&
 
 // Split-kernel launch over every plan item; has_i8: the cache has INT8 (or,
 // with old_bits 4, INT4) pages.  Returns hipErrorInvalidValue for an unsupported (d, G).
-hipError_t launch_split(const SplitArgs& a, int d, int G, bool qf32, bool has_i8, int old_bits, hipStream_t s);
+hipError_t launch_split(const SplitArgs& a, int d, int G, bool qf32, bool has_i8, int old_bits, hipStream_t s,
+                        hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 
 }  // namespace tg_dev
 

@@ -4,9 +4,13 @@
 // entries, one per wavefront.  A cache with an INT8 tier runs every item of
 // both tiers in one launch (the longest-first plan then balances the two
 // tiers together, and there is one tail instead of two); a bf16-only cache
-// runs the bf16 kernel.
+// runs the bf16 kernel.  Launches go through hipExtLaunchKernelGGL so that a
+// measurement can have the kernel's own start and end recorded into two
+// events (null events: an ordinary launch).
 
 #include <cstdlib>
+
+#include <hip/hip_ext.h>
 
 #include "tg_device.h"
 #include "tg_item_bf16.h"
@@ -77,7 +81,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_pe
 }
 
 template <int D, int G, bool QF32>
-hipError_t launch(const SplitArgs& a, bool has_i8, int old_bits, hipStream_t s) {
+hipError_t launch(const SplitArgs& a, bool has_i8, int old_bits, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int ng = a.n_gitems < a.n_items ? a.n_gitems : a.n_items;
   const int blocks = ng + (a.n_items - ng + kWavesPerBlock - 1) / kWavesPerBlock;
   if (blocks == 0) return hipSuccess;
@@ -85,11 +89,11 @@ hipError_t launch(const SplitArgs& a, bool has_i8, int old_bits, hipStream_t s) 
   if (has_i8) {
     if (old_bits == 4) {
       if constexpr (D == 128)
-        hipLaunchKernelGGL((split_tiered_kernel<D, G, QF32, 4>), grid, block, 0, s, a);
+        hipExtLaunchKernelGGL((split_tiered_kernel<D, G, QF32, 4>), grid, block, 0, s, e0, e1, 0, a);
       else
         return hipErrorInvalidValue;
     } else {
-      hipLaunchKernelGGL((split_tiered_kernel<D, G, QF32, 8>), grid, block, 0, s, a);
+      hipExtLaunchKernelGGL((split_tiered_kernel<D, G, QF32, 8>), grid, block, 0, s, e0, e1, 0, a);
     }
     return hipGetLastError();
   }
@@ -98,32 +102,34 @@ hipError_t launch(const SplitArgs& a, bool has_i8, int old_bits, hipStream_t s) 
     return (e && atoi(e) == 3) ? 3 : 2;
   }();
   if (depth == 3)
-    hipLaunchKernelGGL((split_bf16_kernel<D, G, QF32, 3>), grid, block, 0, s, a);
+    hipExtLaunchKernelGGL((split_bf16_kernel<D, G, QF32, 3>), grid, block, 0, s, e0, e1, 0, a);
   else
-    hipLaunchKernelGGL((split_bf16_kernel<D, G, QF32, 2>), grid, block, 0, s, a);
+    hipExtLaunchKernelGGL((split_bf16_kernel<D, G, QF32, 2>), grid, block, 0, s, e0, e1, 0, a);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const SplitArgs& a, int G, bool qf32, bool has_i8, int old_bits, hipStream_t s) {
+hipError_t launch_d(const SplitArgs& a, int G, bool qf32, bool has_i8, int old_bits, hipStream_t s, hipEvent_t e0,
+                    hipEvent_t e1) {
   switch (G * 2 + (qf32 ? 1 : 0)) {
-    case 2: return launch<D, 1, false>(a, has_i8, old_bits, s);
-    case 3: return launch<D, 1, true>(a, has_i8, old_bits, s);
-    case 4: return launch<D, 2, false>(a, has_i8, old_bits, s);
-    case 5: return launch<D, 2, true>(a, has_i8, old_bits, s);
-    case 8: return launch<D, 4, false>(a, has_i8, old_bits, s);
-    case 9: return launch<D, 4, true>(a, has_i8, old_bits, s);
-    case 16: return launch<D, 8, false>(a, has_i8, old_bits, s);
-    case 17: return launch<D, 8, true>(a, has_i8, old_bits, s);
+    case 2: return launch<D, 1, false>(a, has_i8, old_bits, s, e0, e1);
+    case 3: return launch<D, 1, true>(a, has_i8, old_bits, s, e0, e1);
+    case 4: return launch<D, 2, false>(a, has_i8, old_bits, s, e0, e1);
+    case 5: return launch<D, 2, true>(a, has_i8, old_bits, s, e0, e1);
+    case 8: return launch<D, 4, false>(a, has_i8, old_bits, s, e0, e1);
+    case 9: return launch<D, 4, true>(a, has_i8, old_bits, s, e0, e1);
+    case 16: return launch<D, 8, false>(a, has_i8, old_bits, s, e0, e1);
+    case 17: return launch<D, 8, true>(a, has_i8, old_bits, s, e0, e1);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_split(const SplitArgs& a, int d, int G, bool qf32, bool has_i8, int old_bits, hipStream_t s) {
-  if (d == 128) return launch_d<128>(a, G, qf32, has_i8, old_bits, s);
-  if (d == 64) return launch_d<64>(a, G, qf32, has_i8, old_bits, s);
+hipError_t launch_split(const SplitArgs& a, int d, int G, bool qf32, bool has_i8, int old_bits, hipStream_t s,
+                        hipEvent_t e0, hipEvent_t e1) {
+  if (d == 128) return launch_d<128>(a, G, qf32, has_i8, old_bits, s, e0, e1);
+  if (d == 64) return launch_d<64>(a, G, qf32, has_i8, old_bits, s, e0, e1);
   return hipErrorInvalidValue;
 }
 

@@ -106,14 +106,18 @@ def test_codec_and_read_aid_reject_bad_sizes():
     odd = ctypes.c_void_p(0x1008)
     assert lib.tg_zip_encode(odd, n, FAKE, 1 << 40, FAKE, 1 << 40, None) == L.TG_EINVAL
     assert lib.tg_zip_decode(FAKE, n, odd, None) == L.TG_EINVAL
-    assert lib.tg_bench_read(FAKE, 24, FAKE, None) == L.TG_EINVAL
-    assert lib.tg_bench_read(None, 32, FAKE, None) == L.TG_EINVAL
+    assert lib.tg_bench_read(FAKE, 24, FAKE, None, None, None) == L.TG_EINVAL
+    # the timed split needs both events (checked before the arguments)
+    c, a = _cache(), _args()
+    assert lib.tg_decode_split_timed(ctypes.byref(c), ctypes.byref(a), None, FAKE, None) == L.TG_EINVAL
+    assert lib.tg_decode_split_timed(ctypes.byref(c), ctypes.byref(a), FAKE, None, None) == L.TG_EINVAL
+    assert lib.tg_bench_read(None, 32, FAKE, None, None, None) == L.TG_EINVAL
     # the paged-stream read: buffer of whole 8 KiB chunks, aligned, tables present
     for args in ((FAKE, 8192 + 16, FAKE, FAKE, 1), (FAKE, 0, FAKE, FAKE, 1), (odd, 8192, FAKE, FAKE, 1),
                  (FAKE, 8192, None, FAKE, 1), (FAKE, 8192, FAKE, None, 1), (FAKE, 8192, FAKE, FAKE, -1)):
-        assert lib.tg_bench_streams(*args, FAKE, None) == L.TG_EINVAL, args
-    assert lib.tg_bench_streams(FAKE, 8192, FAKE, FAKE, 1, None, None) == L.TG_EINVAL
-    assert lib.tg_bench_streams(FAKE, 8192, None, None, 0, None, None) == L.TG_OK  # nothing to read
+        assert lib.tg_bench_streams(*args, FAKE, None, None, None) == L.TG_EINVAL, args
+    assert lib.tg_bench_streams(FAKE, 8192, FAKE, FAKE, 1, None, None, None, None) == L.TG_EINVAL
+    assert lib.tg_bench_streams(FAKE, 8192, None, None, 0, None, None, None, None) == L.TG_OK  # nothing to read
 
 
 def test_status_strings_cover_every_code():

@@ -16,8 +16,10 @@ def test_read_kernel_covers_every_word(nbytes):
     host = rng.integers(0, 2**32, size=nbytes // 4, dtype=np.uint32)
     src = torch.from_numpy(host.view(np.int32)).cuda()
     sink = torch.zeros(api.TG_BENCH_READ_BLOCKS, dtype=torch.int32, device="cuda")
-    api.tg_bench_read(src, sink)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    api.tg_bench_read(src, sink, events=ev)  # with the kernel's start and end recorded
     torch.cuda.synchronize()
+    assert ev[0].elapsed_time(ev[1]) > 0
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     assert got == np.bitwise_xor.reduce(host)
 
@@ -42,8 +44,10 @@ def test_stream_kernel_reads_each_listed_chunk():
     flat = np.concatenate(chunks).astype(np.int32)
     src = torch.from_numpy(host.view(np.int32)).cuda()
     sink = torch.zeros(len(lengths), dtype=torch.int32, device="cuda")
-    api.tg_bench_streams(src, torch.from_numpy(flat).cuda(), torch.from_numpy(off).cuda(), sink)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    api.tg_bench_streams(src, torch.from_numpy(flat).cuda(), torch.from_numpy(off).cuda(), sink, events=ev)
     torch.cuda.synchronize()
+    assert ev[0].elapsed_time(ev[1]) > 0
     got = sink.cpu().numpy().view(np.uint32)
     for w, ids in enumerate(chunks):
         want = np.uint32(0)

@@ -494,3 +494,31 @@ def test_decode_step_replays_from_a_graph():
         res_o = A.reserve_for(w)
         pairs = [(r, h) for r in range(w.B) for h in range(w.Hkv)]
         _check(p.output(), A.decode(w, res_o, pairs), pairs, w.Hq // w.Hkv, f"graph-{w.name}")
+
+
+def test_timed_split_equals_split_and_times_the_kernel():
+    """tg_decode_split_timed writes the same partials as tg_decode_split, bit
+    for bit, and its events bracket the kernel alone: a positive time no
+    longer than that of an event pair recorded around the launch."""
+    torch = _need_gpu()
+    from non_uniform_paged_amd import api
+    from non_uniform_paged_amd.runner import Prepared
+    for name in ("llama8b", "tiered"):
+        w = make_workload(name, B=4, ctx=("uniform", 1000, 3000)) if name == "llama8b" else \
+            make_workload(name, B=2, Hq=8, Hkv=2, ctx=("fixed", 5000))
+        p = Prepared(w, chunk_bf=256, chunk_i8=512)
+        ws = torch.full_like(p.workspace, float("nan"))
+        api.tg_decode_split(p.cache, p.q, ws, w.Hq)
+        ref = ws.clone()
+        ws.fill_(float("nan"))
+        outer = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        inner = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        outer[0].record()
+        api.tg_decode_split_timed(p.cache, p.q, ws, w.Hq, inner)
+        outer[1].record()
+        torch.cuda.synchronize()
+        used = p.tables.n_slots * (w.Hq // w.Hkv) * (w.d + 2)
+        assert torch.equal(ws[:used], ref[:used]), name
+        t_in, t_out = inner[0].elapsed_time(inner[1]), outer[0].elapsed_time(outer[1])
+        print(f"{name}: kernel {t_in * 1e3:.1f} us, event pair {t_out * 1e3:.1f} us", flush=True)
+        assert 0 < t_in <= t_out, (t_in, t_out)
