@@ -181,3 +181,19 @@ def test_int4_workload_rows_within_half_a_step_and_exact_multiples():
     Kx = (k * 2.0 ** -3).astype(np.float32)
     qk, sk = quant.quantize_rows(Kx, 64, 4)
     assert np.array_equal(quant.dequantize_rows(qk, sk, 64), Kx.astype(np.float64))
+
+
+def test_lse_merge_ignores_partials_with_no_rows():
+    # a partial over no rows (m = -inf, l = 0, acc = 0) leaves the merge
+    # unchanged, wherever it sits among the others
+    g = np.random.default_rng(7)
+    q = g.standard_normal((2, 16))
+    K = g.standard_normal((90, 16))
+    V = g.standard_normal((90, 16))
+    parts = [A.partial(q, K[a:b], V[a:b], 0.25) for a, b in ((0, 30), (30, 31), (31, 90))]
+    empty = (np.full(2, -np.inf), np.zeros(2), np.zeros((2, 16)))
+    full = A.attend(q, K, V, 0.25)
+    for at in (0, 2, 3):
+        ps = parts[:at] + [empty] + parts[at:]
+        o = A.lse_merge(np.stack([p[0] for p in ps]), np.stack([p[1] for p in ps]), np.stack([p[2] for p in ps]))
+        assert np.max(np.abs(o - full)) < 1e-13
