@@ -503,10 +503,13 @@ def test_timed_split_equals_split_and_times_the_kernel():
     torch = _need_gpu()
     from non_uniform_paged_amd import api
     from non_uniform_paged_amd.runner import Prepared
-    for name in ("llama8b", "tiered"):
-        w = make_workload(name, B=4, ctx=("uniform", 1000, 3000)) if name == "llama8b" else \
-            make_workload(name, B=2, Hq=8, Hkv=2, ctx=("fixed", 5000))
+    for name, w in (("llama8b", make_workload("llama8b", B=4, ctx=("uniform", 1000, 3000))),
+                    ("tiered", make_workload("tiered", B=2, Hq=8, Hkv=2, ctx=("fixed", 5000))),
+                    ("tiered4", make_workload("tiered4", B=2, Hq=8, Hkv=2, ctx=("fixed", 3000))),
+                    ("radix", make_workload("radix", B=24, Hq=8, Hkv=2,
+                                            share=dict(prefix=300, branch=80, n_branches=3, suffix=(8, 300))))):
         p = Prepared(w, chunk_bf=256, chunk_i8=512)
+        assert name != "radix" or p.tables.n_gitems > 0
         ws = torch.full_like(p.workspace, float("nan"))
         api.tg_decode_split(p.cache, p.q, ws, w.Hq)
         ref = ws.clone()
