@@ -28,7 +28,10 @@ from torch on dense tensors (uniform budgets), the single-row identity, closed
 forms (equal keys -> mean of V; equal values; a 3:1 two-row mix), row
 permutation invariance, pure-Python brute force with math.fsum on tiny
 shapes, INT8 rows equal to bf16 rows of the same value, and split
-invariance of ``lse_merge``.
+invariance of ``lse_merge``.  ``bf16_to_f64`` and ``q_f64`` are pinned by
+hand-checked bit patterns, by all 65536 patterns read field by field from
+the bf16 format, and end to end by the dense-SDPA pin, whose rows and
+queries are decoded from those fields rather than by this module.
 """
 from __future__ import annotations
 
@@ -83,6 +86,8 @@ def reserve_for(w) -> planner.Reservation:
 
 
 def q_f64(w) -> np.ndarray:
+    """Queries [B][Hq][d] in fp64: fp32 queries as they are, bf16 queries
+    decoded exactly."""
     q = w.q()
     return np.asarray(q, np.float64) if w.q_dtype == "f32" else bf16_to_f64(q)
 

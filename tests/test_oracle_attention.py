@@ -13,17 +13,47 @@ from oracle import quant
 from workloads import make_workload
 
 
+def _bf16_value_from_fields(u: int) -> float:
+    """Value of one bf16 bit pattern read from the format's fields: bit 15
+    the sign, bits 14..7 the exponent (bias 127; 0 = subnormal, 255 = inf or
+    NaN), bits 6..0 the fraction -- built with math.ldexp, not by moving the
+    pattern into an fp32 word, so that it checks the oracle's decoder rather
+    than restating it."""
+    sign = -1.0 if (u >> 15) & 1 else 1.0
+    e = (u >> 7) & 0xFF
+    f = u & 0x7F
+    if e == 0xFF:
+        return sign * math.inf if f == 0 else math.nan
+    if e == 0:
+        return sign * math.ldexp(f, -126 - 7)
+    return sign * math.ldexp(128 + f, e - 127 - 7)
+
+
+_BF16_TABLE = np.array([_bf16_value_from_fields(u) for u in range(1 << 16)])
+
+
+def _bf16_table(u):
+    return _BF16_TABLE[np.asarray(u, dtype=np.uint16).astype(np.int64)]
+
+
+def _q_from_fields(w):
+    q = w.q()
+    return np.asarray(q, np.float64) if w.q_dtype == "f32" else _bf16_table(q)
+
+
 def _sdpa_dense(w, res):
-    """torch fp64 scaled_dot_product_attention over the full logical rows."""
-    q = torch.from_numpy(A.q_f64(w))
+    """torch fp64 scaled_dot_product_attention over the full logical rows.
+    Rows and queries are decoded from the bf16 fields (``_bf16_table``), not
+    by the oracle's own decoder, so this pin also covers that decoder."""
+    q = torch.from_numpy(_q_from_fields(w))
     G = w.Hq // w.Hkv
     out = np.zeros((w.B, w.Hq, w.d))
     for r in range(w.B):
         Ks, Vs = [], []
         for h in range(w.Hkv):
             K16, V16 = w.logical_kv(r, h, res.L[r][h])
-            Ks.append(torch.from_numpy(A.bf16_to_f64(K16)))
-            Vs.append(torch.from_numpy(A.bf16_to_f64(V16)))
+            Ks.append(torch.from_numpy(_bf16_table(K16)))
+            Vs.append(torch.from_numpy(_bf16_table(V16)))
         K = torch.stack(Ks).repeat_interleave(G, dim=0)      # [Hq, L, d]
         V = torch.stack(Vs).repeat_interleave(G, dim=0)
         o = torch.nn.functional.scaled_dot_product_attention(q[r][:, None, :], K, V)
@@ -197,3 +227,58 @@ def test_lse_merge_ignores_partials_with_no_rows():
         ps = parts[:at] + [empty] + parts[at:]
         o = A.lse_merge(np.stack([p[0] for p in ps]), np.stack([p[1] for p in ps]), np.stack([p[2] for p in ps]))
         assert np.max(np.abs(o - full)) < 1e-13
+
+
+def test_bf16_decoder_on_fixed_patterns():
+    """Hand-checked patterns of the bf16 format (sign, 8-bit exponent with
+    bias 127, 7-bit fraction): the K/V bf16 rows of the fast tier (TTKV page,
+    "Tier Layout") and bf16 queries enter the oracle through this decoder."""
+    cases = {
+        0x3F80: 1.0, 0xC040: -3.0, 0x4049: 3.140625, 0x3E80: 0.25, 0xBF00: -0.5,
+        0x0001: 2.0 ** -133,                      # smallest subnormal
+        0x0080: 2.0 ** -126,                      # smallest normal
+        0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127,   # largest finite
+        0xFF7F: -(2.0 - 2.0 ** -7) * 2.0 ** 127,
+        0x7F80: math.inf, 0xFF80: -math.inf, 0x0000: 0.0,
+    }
+    pats = np.array(list(cases), dtype=np.uint16)
+    got = A.bf16_to_f64(pats)
+    assert got.dtype == np.float64
+    for u, g in zip(cases, got):
+        assert g == cases[u], hex(u)
+    neg0 = A.bf16_to_f64(np.array([0x8000], dtype=np.uint16))[0]
+    assert neg0 == 0.0 and math.copysign(1.0, neg0) == -1.0
+    assert math.isnan(A.bf16_to_f64(np.array([0x7FC0], dtype=np.uint16))[0])
+
+
+def test_bf16_decoder_on_every_pattern():
+    """All 65536 patterns against the field-by-field reading of the format
+    (NaN patterns must decode to NaN), and against the generator's fp32
+    decoder, which must agree with it exactly."""
+    allp = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):  # signalling-NaN patterns widen to NaN
+        got = A.bf16_to_f64(allp)
+    ref = _BF16_TABLE
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    from workloads import bf16_bits_to_f32
+    with np.errstate(invalid="ignore"):
+        g32 = bf16_bits_to_f32(allp).astype(np.float64)
+    assert np.array_equal(g32[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama8b", "tiered"])
+def test_q_f64_decodes_the_query_bits(name):
+    """q_f64: fp32 queries (Tiny) pass through unchanged, bf16 queries decode
+    through the format fields."""
+    w = make_workload(name, B=2) if name != "tiny" else make_workload(name)
+    q = A.q_f64(w)
+    assert q.dtype == np.float64 and q.shape == (w.B, w.Hq, w.d)
+    raw = w.q()
+    if w.q_dtype == "f32":
+        assert np.array_equal(q, np.asarray(raw, np.float64))
+    else:
+        assert raw.dtype == np.uint16
+        assert np.array_equal(q, _bf16_table(raw))

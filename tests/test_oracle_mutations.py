@@ -112,6 +112,53 @@ TA_ORIG_ATTEND = A.attend
 TA_ORIG_ROWS = A.rows_f64
 
 
+# ------------------------------------------------------------------ bf16 decoder mutants
+def _bf16_shift_15(u):  # the pattern moved one bit short of the fp32 high half
+    return (np.asarray(u, dtype=np.uint16).astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
+
+
+def _bf16_as_fp16(u):  # the bits read as IEEE half precision
+    return np.asarray(u, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def _bf16_sign_dropped(u):  # the sign bit masked off
+    return (((np.asarray(u, dtype=np.uint16) & np.uint16(0x7FFF)).astype(np.uint32)) << np.uint32(16)).view(
+        np.float32).astype(np.float64)
+
+
+def _bf16_fraction_truncated(u):  # the lowest fraction bit lost
+    return (((np.asarray(u, dtype=np.uint16) & np.uint16(0xFFFE)).astype(np.uint32)) << np.uint32(16)).view(
+        np.float32).astype(np.float64)
+
+
+BF16_PINS = [TA.test_bf16_decoder_on_fixed_patterns, TA.test_bf16_decoder_on_every_pattern,
+             lambda: TA.test_q_f64_decodes_the_query_bits("llama8b"),
+             lambda: TA.test_uniform_budgets_equal_dense_sdpa(
+                 "llama8b", dict(B=2, ctx=("uniform", 200, 500), ratio_ppm=(1_000_000, 1_000_000), n_clusters=1))]
+
+
+@pytest.mark.parametrize("mutant", [_bf16_shift_15, _bf16_as_fp16, _bf16_sign_dropped, _bf16_fraction_truncated],
+                         ids=["shift-15", "read-as-fp16", "sign-dropped", "fraction-bit-lost"])
+def test_bf16_decoder_mutants_are_caught(monkeypatch, mutant):
+    """A wrong bf16 decoder is caught by its own pins and, through q_f64 and
+    the row decoding, by the dense-SDPA pin (whose rows are decoded from the
+    format's fields, not by this function)."""
+    monkeypatch.setattr(A, "bf16_to_f64", mutant)
+    with np.errstate(all="ignore"):
+        assert _caught(BF16_PINS), f"no pin catches the {mutant.__name__} mutant of bf16_to_f64"
+        # the end-to-end pin alone must catch it too: it never calls the decoder under test for its reference
+        assert _caught(BF16_PINS[3:]), f"the dense-SDPA pin misses the {mutant.__name__} mutant"
+
+
+def test_q_f64_mutant_is_caught(monkeypatch):
+    """q_f64 reading bf16 queries as fp16 is caught by the query pin and by
+    the dense-SDPA pin."""
+    monkeypatch.setattr(A, "q_f64", lambda w: np.asarray(w.q(), np.float64) if w.q_dtype == "f32"
+                        else _bf16_as_fp16(w.q()))
+    with np.errstate(all="ignore"):
+        assert _caught(BF16_PINS[2:3]) and _caught(BF16_PINS[3:])
+
+
 @pytest.mark.parametrize("target,mutant", [
     ("attend", _attend_no_scale), ("attend", _attend_wrong_axis), ("attend", _attend_keys_as_values),
     ("attend", _attend_no_normaliser), ("lse_merge", _merge_sign), ("lse_merge", _merge_unweighted_l),
@@ -236,7 +283,7 @@ def test_allocation_order_mutant_is_caught(monkeypatch):
 
 def test_pins_pass_on_the_oracle_as_it_is():
     """The control: unmutated, every pin used above passes."""
-    for pins in (ATTENTION_PINS, QUANT_PINS, INT4_PINS, PLANNER_PINS):
+    for pins in (ATTENTION_PINS, QUANT_PINS, INT4_PINS, PLANNER_PINS, BF16_PINS):
         assert not _caught(pins)
 
 
