@@ -265,6 +265,9 @@ typedef struct tg_tables {
   int32_t* gitems;                     /* host [n_gitems][TG_GROUP_WIDTH][2] (may be NULL if 0) */
   int32_t n_gitems;                    /* in: must equal tg_size_tables' value */
   int32_t* ring;                       /* host [B][C]: bf16 pages of (r, c) (nullable) */
+  int32_t B;                           /* out: requests the tables hold (written by
+                                          tg_build_tables; tg_release refuses r outside
+                                          [0, B)) */
 } tg_tables;
 
 /* Allocate every page of the batch from `pool` (all or nothing) and fill the
@@ -272,8 +275,34 @@ typedef struct tg_tables {
 int tg_build_tables(tg_pool* pool, const tg_reservation* res, const tg_share_desc* share,
                     const tg_plan_opts* opts, tg_tables* out);
 
+/* Consistency check of tables against the reservation and the pool they
+ * were built from (host; a debugging aid for tables that were edited, copied
+ * or made elsewhere before they go to the device).  Released requests are
+ * skipped.  Checks, in this order:
+ *   - block tables: each row lists page ids in [0, capacity) of its
+ *     (cluster, tier) pool, then -1 only; no page appears in more rows than
+ *     its reference count;
+ *   - lengths: n_i8 a multiple of Qb, n_i8 <= (INT8 pages of the row) * Qb,
+ *     n_bf <= (bf16 pages, or ring pages when `ring` is set) * page_size;
+ *   - slots: part_off starts at 0 and never decreases; every item's slot (and
+ *     every group member's) lies in its (r, h)'s range and each slot is used
+ *     exactly once;
+ *   - plan items: a valid head and tier, 0 <= t0 < t1 within the rows the
+ *     pages hold; group items bf16, listed once, members in ascending request
+ *     order then (-1, -1) padding, every member's pages over the item's rows
+ *     the very pages of its first member;
+ *   - cover: the items of each (r, h, tier) tile rows 0, 1, ... once each, up
+ *     to at least the live length.
+ * Returns TG_OK, or TG_EINVAL with a description of the first failed check
+ * written to msg (nullable; msg_bytes including the terminating zero);
+ * TG_ENOMEM if the check's own bookkeeping cannot be allocated. */
+int tg_check_tables(const tg_pool* pool, const tg_reservation* res, const tg_tables* tables, char* msg,
+                    size_t msg_bytes);
+
 /* Drop request r's page references; pages reaching zero become free and their
- * share keys are forgotten.  TG_EINVAL if r was already released. */
+ * share keys are forgotten.  TG_EINVAL if r is outside [0, tables->B), if r
+ * was already released, or if a page of r's rows is not live in `pool`
+ * (nothing changes then). */
 int tg_release(tg_pool* pool, tg_tables* tables, int32_t r);
 
 /* ------------------------------------------------------------------------
@@ -313,7 +342,9 @@ typedef struct tg_cache {
  *   q8 = s > 0 ? clamp(rint_even(x / s), -127, 127) : 0       (fp32 math)
  * Shared pages may be written by several sequences with identical data.
  * rows: device uint16 [n_rows][2][d]; index: device int32 [offsets[B*H]];
- * offsets: device int64 [B*H + 1].  TG_EINVAL on a bad shape.
+ * offsets: device int64 [B*H + 1].  TG_EINVAL on a bad shape; TG_EOVERFLOW
+ * if B*H exceeds int32 (any B*H below that is one launch per tier: the grid
+ * strides over pairs past the 65535 workgroups of one grid dimension).
  * ---------------------------------------------------------------------- */
 int tg_write_kv(const tg_cache* cache, const uint16_t* rows, const int32_t* index,
                 const int64_t* offsets, void* stream);

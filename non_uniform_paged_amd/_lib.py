@@ -9,7 +9,9 @@ import ctypes
 import os
 from ctypes import POINTER, c_float, c_int32, c_int64, c_size_t, c_void_p
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtg.so")
+# TG_LIB_PATH names another build of the same library (the sanitizer build
+# of the CPU tests); by default the in-tree libtg.so is loaded.
+LIB_PATH = os.environ.get("TG_LIB_PATH") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtg.so")
 
 TG_OK = 0
 TG_EINVAL = -1
@@ -63,7 +65,7 @@ class TableSizes(ctypes.Structure):
 class Tables(ctypes.Structure):
     _fields_ = [("bt", (P32 * 2) * TG_MAX_CLUSTERS), ("stride", (c_int32 * 2) * TG_MAX_CLUSTERS),
                 ("len", P32), ("work", P32), ("n_items", c_int32), ("part_off", P32),
-                ("released", P32), ("gitems", P32), ("n_gitems", c_int32), ("ring", P32)]
+                ("released", P32), ("gitems", P32), ("n_gitems", c_int32), ("ring", P32), ("B", c_int32)]
 
 
 class Cache(ctypes.Structure):
@@ -102,6 +104,8 @@ SIGNATURES = {
     "tg_build_tables": (ctypes.c_int, [c_void_p, POINTER(Reservation), POINTER(ShareDesc),
                                        POINTER(PlanOpts), POINTER(Tables)]),
     "tg_release": (ctypes.c_int, [c_void_p, POINTER(Tables), c_int32]),
+    "tg_check_tables": (ctypes.c_int, [c_void_p, POINTER(Reservation), POINTER(Tables), ctypes.c_char_p,
+                                       c_size_t]),
     "tg_write_kv": (ctypes.c_int, [POINTER(Cache), c_void_p, c_void_p, c_void_p, c_void_p]),
     "tg_decode_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
     "tg_decode_attn": (ctypes.c_int, [POINTER(Cache), POINTER(DecodeArgs), c_void_p]),

@@ -17,7 +17,7 @@ from ._lib import TG_BENCH_READ_BLOCKS, TG_GROUP_WIDTH, TG_Q_BF16, TG_Q_F32, TG_
 __all__ = [
     "TGError", "TG_TIER_I8", "TG_TIER_BF16", "TG_Q_F32", "TG_Q_BF16", "TG_GROUP_WIDTH",
     "Reservation", "Share", "Pool", "Tables", "DeviceCache",
-    "tg_reserve", "tg_size_tables", "tg_build_tables", "tg_release",
+    "tg_reserve", "tg_size_tables", "tg_build_tables", "tg_release", "tg_check_tables",
     "tg_write_kv", "tg_decode_workspace_bytes", "tg_decode_attn", "tg_decode_split", "tg_decode_split_timed",
     "tg_merge_partials", "tg_bench_read", "tg_bench_streams", "TG_BENCH_READ_BLOCKS", "tg_append_kv",
     "tg_stream_order", "tg_stream_staging_bytes", "tg_decode_streamed",
@@ -209,6 +209,16 @@ def tg_release(pool: Pool, tables: Tables, r: int) -> None:
     if not 0 <= r < tables.B:
         raise IndexError(r)
     check(lib().tg_release(pool.handle, ctypes.byref(tables.struct), int(r)), "tg_release")
+
+
+def tg_check_tables(pool: Pool, res: Reservation, tables: Tables) -> None:
+    """Host consistency check of built (or edited) tables; raises TGError
+    with the library's description of the first failed check."""
+    buf = ctypes.create_string_buffer(512)
+    st = lib().tg_check_tables(pool.handle, ctypes.byref(res.struct), ctypes.byref(tables.struct), buf,
+                               ctypes.sizeof(buf))
+    if st != L.TG_OK:
+        raise L.TGError(st, "tg_check_tables: " + buf.value.decode())
 
 
 def tg_decode_workspace_bytes(n_slots: int, G: int, d: int) -> int:

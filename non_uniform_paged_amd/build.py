@@ -66,17 +66,25 @@ def _run_checking_scratch(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link ``libtg.so``; returns its path."""
+    """Compile every source (the translation units in parallel) and link
+    ``libtg.so``; returns its path."""
+    from concurrent.futures import ThreadPoolExecutor
+
     os.makedirs(BUILD, exist_ok=True)
-    objs = []
+    jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        _run_checking_scratch([HIPCC, *HIP_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+        jobs.append((_run_checking_scratch,
+                     [HIPCC, *HIP_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj], obj))
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
-        _run(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
-        objs.append(obj)
+        jobs.append((_run, ["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], obj))
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        futures = [ex.submit(fn, cmd, verbose) for fn, cmd, _ in jobs]
+        for f in futures:
+            f.result()
+    objs = [obj for _, _, obj in jobs]
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)

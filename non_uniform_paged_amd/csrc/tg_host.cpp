@@ -11,7 +11,9 @@
 // integer rules are the ones documented in include/tg.h.
 
 #include <algorithm>
+#include <cstdarg>
 #include <cstdint>
+#include <cstdio>
 #include <cstring>
 #include <limits>
 #include <new>
@@ -785,6 +787,7 @@ extern "C" int tg_build_tables(tg_pool* pool, const tg_reservation* live, const 
       for (int32_t c = 0; c < g.C; ++c)
         out->ring[int64_t(r) * g.C + c] = static_cast<int32_t>(pages_of(res, g, r, c, TG_TIER_BF16));
   for (int32_t r = 0; r < g.B; ++r) out->released[r] = 0;
+  out->B = g.B;
   return TG_OK;
 }
 
@@ -814,8 +817,7 @@ extern "C" int tg_stream_order(const tg_tables* t, int32_t B, int32_t* work_out,
 }
 
 extern "C" int tg_release(tg_pool* pool, tg_tables* t, int32_t r) {
-  if (!pool || !t || !t->released || r < 0) return TG_EINVAL;
-  // B is implicit in the tables; the caller guarantees r < B.
+  if (!pool || !t || !t->released || r < 0 || r >= t->B) return TG_EINVAL;
   if (t->released[r]) return TG_EINVAL;
   for (int32_t c = 0; c < pool->C; ++c)
     for (int32_t tier = 0; tier < 2; ++tier) {
@@ -846,5 +848,211 @@ extern "C" int tg_release(tg_pool* pool, tg_tables* t, int32_t r) {
       }
     }
   t->released[r] = 1;
+  return TG_OK;
+}
+
+// --------------------------------------------------------------------------
+// table check (debugging aid)
+// --------------------------------------------------------------------------
+namespace {
+
+int check_fail(char* msg, size_t msg_bytes, const char* fmt, ...) {
+  if (msg && msg_bytes > 0) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(msg, msg_bytes, fmt, ap);
+    va_end(ap);
+  }
+  return TG_EINVAL;
+}
+
+}  // namespace
+
+extern "C" int tg_check_tables(const tg_pool* pool, const tg_reservation* res, const tg_tables* t, char* msg,
+                               size_t msg_bytes) {
+  if (msg && msg_bytes > 0) msg[0] = '\0';
+  if (!pool || !res || !t) return check_fail(msg, msg_bytes, "null argument");
+  Geometry g;
+  if (check_reservation(res, pool->page_size, pool->quant_block, &g))
+    return check_fail(msg, msg_bytes, "malformed reservation");
+  if (g.C != pool->C) return check_fail(msg, msg_bytes, "reservation has %d clusters, the pool %d", g.C, pool->C);
+  for (int32_t c = 0; c < g.C; ++c)
+    if (pool->cluster_size[c] != res->cluster_size[c])
+      return check_fail(msg, msg_bytes, "cluster %d: %d heads in the reservation, %d in the pool", c,
+                        res->cluster_size[c], pool->cluster_size[c]);
+  if (t->B != g.B) return check_fail(msg, msg_bytes, "tables hold %d requests, the reservation %d", t->B, g.B);
+  if (!t->len || !t->part_off || t->n_items < 0 || t->n_gitems < 0 || (t->n_items > 0 && !t->work) ||
+      (t->n_gitems > 0 && !t->gitems))
+    return check_fail(msg, msg_bytes, "missing table array or negative count");
+  const int64_t BH = int64_t(g.B) * g.H;
+  try {
+    // block tables: page ids first, then -1; ids inside the pool, referenced
+    // no more often than their reference counts allow
+    std::vector<int64_t> pages(size_t(g.B) * g.C * 2, 0);  // pages in row (r, c, tier)
+    auto npages = [&](int32_t r, int32_t c, int32_t tier) -> int64_t& {
+      return pages[(size_t(r) * g.C + c) * 2 + tier];
+    };
+    for (int32_t c = 0; c < g.C; ++c)
+      for (int32_t tier = 0; tier < 2; ++tier) {
+        const int32_t stride = t->stride[c][tier];
+        if (stride < 0) return check_fail(msg, msg_bytes, "negative stride of (%d, %d)", c, tier);
+        if (stride == 0) continue;
+        if (!t->bt[c][tier]) return check_fail(msg, msg_bytes, "no block table for (%d, %d)", c, tier);
+        const SubPool& sp = pool->sub[c][tier];
+        std::vector<int32_t> uses(size_t(sp.cap), 0);
+        for (int32_t r = 0; r < g.B; ++r) {
+          if (t->released && t->released[r]) continue;
+          const int32_t* row = t->bt[c][tier] + int64_t(r) * stride;
+          int32_t j = 0;
+          for (; j < stride && row[j] >= 0; ++j) {
+            if (row[j] >= sp.cap)
+              return check_fail(msg, msg_bytes, "bt[%d][%d] row %d entry %d: page %d past the capacity %lld", c,
+                                tier, r, j, row[j], static_cast<long long>(sp.cap));
+            ++uses[row[j]];
+          }
+          npages(r, c, tier) = j;
+          for (; j < stride; ++j)
+            if (row[j] != -1)
+              return check_fail(msg, msg_bytes, "bt[%d][%d] row %d entry %d: %d after the row's last page", c,
+                                tier, r, j, row[j]);
+        }
+        for (int64_t pid = 0; pid < sp.cap; ++pid)
+          if (uses[pid] > sp.ref[pid])
+            return check_fail(msg, msg_bytes, "(%d, %d) page %lld: %d table entries, reference count %d", c, tier,
+                              static_cast<long long>(pid), uses[pid], sp.ref[pid]);
+      }
+    // lengths within the rows the pages (or the bf16 ring) hold
+    auto cap_rows = [&](int32_t r, int32_t c, int32_t tier) -> int64_t {
+      if (tier == TG_TIER_I8) return npages(r, c, tier) * g.qb;
+      if (t->ring) return int64_t(t->ring[int64_t(r) * g.C + c]) * g.ps;
+      return npages(r, c, tier) * g.ps;
+    };
+    for (int32_t r = 0; r < g.B; ++r) {
+      if (t->released && t->released[r]) continue;
+      if (t->ring)
+        for (int32_t c = 0; c < g.C; ++c) {
+          const int32_t ring = t->ring[int64_t(r) * g.C + c];
+          if (ring < 0 || ring > npages(r, c, TG_TIER_BF16))
+            return check_fail(msg, msg_bytes, "ring of (%d, %d) is %d pages, the row has %lld", r, c, ring,
+                              static_cast<long long>(npages(r, c, TG_TIER_BF16)));
+        }
+      for (int32_t h = 0; h < g.H; ++h) {
+        const int64_t i = int64_t(r) * g.H + h;
+        const int32_t c = res->cluster_of_head[h];
+        const int32_t n8 = t->len[2 * i], nb = t->len[2 * i + 1];
+        if (n8 < 0 || nb < 0 || n8 % g.qb)
+          return check_fail(msg, msg_bytes, "len of (%d, %d) is (%d, %d)", r, h, n8, nb);
+        if (n8 > cap_rows(r, c, TG_TIER_I8) || nb > cap_rows(r, c, TG_TIER_BF16))
+          return check_fail(msg, msg_bytes, "len of (%d, %d) = (%d, %d) passes its pages (%lld, %lld rows)", r, h,
+                            n8, nb, static_cast<long long>(cap_rows(r, c, TG_TIER_I8)),
+                            static_cast<long long>(cap_rows(r, c, TG_TIER_BF16)));
+      }
+    }
+    // slots
+    if (t->part_off[0] != 0) return check_fail(msg, msg_bytes, "part_off[0] is %d", t->part_off[0]);
+    for (int64_t i = 0; i < BH; ++i)
+      if (t->part_off[i + 1] < t->part_off[i])
+        return check_fail(msg, msg_bytes, "part_off decreases at %lld", static_cast<long long>(i));
+    const int64_t n_slots = t->part_off[BH];
+    std::vector<uint8_t> slot_used(size_t(n_slots), 0);
+    auto take_slot = [&](int64_t rh, int32_t slot, int64_t item) -> int {
+      if (slot < t->part_off[rh] || slot >= t->part_off[rh + 1])
+        return check_fail(msg, msg_bytes, "item %lld: slot %d outside [%d, %d) of pair %lld",
+                          static_cast<long long>(item), slot, t->part_off[rh], t->part_off[rh + 1],
+                          static_cast<long long>(rh));
+      if (slot_used[slot]++)
+        return check_fail(msg, msg_bytes, "item %lld: slot %d used twice", static_cast<long long>(item), slot);
+      return TG_OK;
+    };
+    // plan: ranges of every (r, h, tier), group items once each
+    std::vector<std::vector<std::pair<int32_t, int32_t>>> ranges(size_t(BH) * 2);
+    std::vector<uint8_t> gseen(size_t(t->n_gitems), 0);
+    for (int64_t k = 0; k < t->n_items; ++k) {
+      const int32_t* w = t->work + k * 6;
+      const int32_t h = w[1], tier = w[2], t0 = w[3], t1 = w[4];
+      if (h < 0 || h >= g.H || (tier != TG_TIER_I8 && tier != TG_TIER_BF16) || t0 < 0 || t1 <= t0)
+        return check_fail(msg, msg_bytes, "item %lld: (h %d, tier %d, rows %d..%d)", static_cast<long long>(k), h,
+                          tier, t0, t1);
+      const int32_t c = res->cluster_of_head[h];
+      if (w[0] >= 0) {
+        const int32_t r = w[0];
+        if (r >= g.B) return check_fail(msg, msg_bytes, "item %lld: request %d", static_cast<long long>(k), r);
+        if (t->released && t->released[r]) continue;
+        const int64_t rh = int64_t(r) * g.H + h;
+        if (int st = take_slot(rh, w[5], k)) return st;
+        if (t1 > cap_rows(r, c, tier))
+          return check_fail(msg, msg_bytes, "item %lld: rows %d..%d pass the %lld rows of its pages",
+                            static_cast<long long>(k), t0, t1, static_cast<long long>(cap_rows(r, c, tier)));
+        ranges[size_t(rh) * 2 + tier].push_back({t0, t1});
+        continue;
+      }
+      const int64_t gk = -1 - int64_t(w[0]);
+      if (gk >= t->n_gitems || tier != TG_TIER_BF16 || w[5] != -1)
+        return check_fail(msg, msg_bytes, "item %lld: group item %lld (tier %d, slot %d)", static_cast<long long>(k),
+                          static_cast<long long>(gk), tier, w[5]);
+      if (gseen[gk]++)
+        return check_fail(msg, msg_bytes, "group item %lld listed twice", static_cast<long long>(gk));
+      const int32_t* gm = t->gitems + gk * 2 * TG_GROUP_WIDTH;
+      if (gm[0] < 0) return check_fail(msg, msg_bytes, "group item %lld has no member", static_cast<long long>(gk));
+      const int32_t r0 = gm[0];
+      for (int32_t m = 0; m < TG_GROUP_WIDTH; ++m) {
+        const int32_t r = gm[2 * m], slot = gm[2 * m + 1];
+        if (r < 0) {
+          for (int32_t e = m; e < TG_GROUP_WIDTH; ++e)
+            if (gm[2 * e] != -1 || gm[2 * e + 1] != -1)
+              return check_fail(msg, msg_bytes, "group item %lld: member entry %d after the padding",
+                                static_cast<long long>(gk), e);
+          break;
+        }
+        if (r >= g.B || (m > 0 && r <= gm[2 * m - 2]))
+          return check_fail(msg, msg_bytes, "group item %lld: member %d is request %d (not ascending or out of range)",
+                            static_cast<long long>(gk), m, r);
+        if (t->released && t->released[r]) continue;
+        const int64_t rh = int64_t(r) * g.H + h;
+        if (int st = take_slot(rh, slot, k)) return st;
+        if (t1 > cap_rows(r, c, TG_TIER_BF16))
+          return check_fail(msg, msg_bytes, "group item %lld: rows %d..%d pass request %d's pages",
+                            static_cast<long long>(gk), t0, t1, r);
+        // the members read the very same pages
+        const int32_t stride = t->stride[c][TG_TIER_BF16];
+        for (int64_t pg = t0 / g.ps; pg < ceil_div(t1, g.ps); ++pg)
+          if (t->bt[c][TG_TIER_BF16][int64_t(r) * stride + pg] != t->bt[c][TG_TIER_BF16][int64_t(r0) * stride + pg])
+            return check_fail(msg, msg_bytes, "group item %lld: request %d's page %lld differs from request %d's",
+                              static_cast<long long>(gk), r, static_cast<long long>(pg), r0);
+        ranges[size_t(rh) * 2 + TG_TIER_BF16].push_back({t0, t1});
+      }
+    }
+    for (int64_t gk = 0; gk < t->n_gitems; ++gk)
+      if (!gseen[gk]) return check_fail(msg, msg_bytes, "group item %lld is in no plan entry", static_cast<long long>(gk));
+    for (int64_t sl = 0; sl < n_slots; ++sl)
+      if (!slot_used[sl]) {
+        // a released request's slots are not checked
+        int64_t rh = std::upper_bound(t->part_off, t->part_off + BH + 1, int32_t(sl)) - t->part_off - 1;
+        if (t->released && t->released[rh / g.H]) continue;
+        return check_fail(msg, msg_bytes, "slot %lld is written by no item", static_cast<long long>(sl));
+      }
+    // every tier range is tiled once from row 0 past its live rows
+    for (int64_t rh = 0; rh < BH; ++rh) {
+      if (t->released && t->released[rh / g.H]) continue;
+      for (int32_t tier = 0; tier < 2; ++tier) {
+        auto& v = ranges[size_t(rh) * 2 + tier];
+        std::sort(v.begin(), v.end());
+        const int32_t live = t->len[2 * rh + tier];
+        int64_t at = 0;
+        for (const auto& x : v) {
+          if (x.first != at)
+            return check_fail(msg, msg_bytes, "pair %lld tier %d: items leave rows %lld..%d %s",
+                              static_cast<long long>(rh), tier, static_cast<long long>(at), x.first,
+                              x.first > at ? "uncovered" : "covered twice");
+          at = x.second;
+        }
+        if (at < live)
+          return check_fail(msg, msg_bytes, "pair %lld tier %d: items end at row %lld, %d rows are live",
+                            static_cast<long long>(rh), tier, static_cast<long long>(at), live);
+      }
+    }
+  } catch (...) {
+    return TG_ENOMEM;
+  }
   return TG_OK;
 }

@@ -34,14 +34,14 @@ struct WriteArgs {
   const int32_t* index;
   const int64_t* offsets;
   int32_t H;
+  int32_t pairs;  // B * H; the grid's y dimension strides over them
 };
 
 // One thread per 8 channels of one bf16-tier row; 256 threads = 256/(D/8) rows.
 template <int D>
-__global__ __launch_bounds__(256) void write_bf16_kernel(WriteArgs a) {
+__device__ __forceinline__ void write_bf16_rows(const WriteArgs& a, int rh) {
   constexpr int LPR = D / 8;
   constexpr int RPB = 256 / LPR;
-  const int rh = blockIdx.y;
   const int r = rh / a.H, h = rh % a.H;
   const int n_i8 = a.len[2 * rh], n_bf = a.len[2 * rh + 1];
   const int u = blockIdx.x * RPB + threadIdx.x / LPR;
@@ -67,11 +67,14 @@ __global__ __launch_bounds__(256) void write_bf16_kernel(WriteArgs a) {
     vblk[off] = vsrc[e];
   }
 }
+template <int D>
+__global__ __launch_bounds__(256) void write_bf16_kernel(WriteArgs a) {
+  for (int rh = blockIdx.y; rh < a.pairs; rh += gridDim.y) write_bf16_rows<D>(a, rh);
+}
 
 // One block of 2*D threads per (r, h, 64-row INT8 block): thread = (K|V, channel).
 template <int D>
-__global__ __launch_bounds__(2 * D) void write_i8_kernel(WriteArgs a) {
-  const int rh = blockIdx.y;
+__device__ __forceinline__ void write_i8_block(const WriteArgs& a, int rh) {
   const int r = rh / a.H, h = rh % a.H;
   const int n_i8 = a.len[2 * rh];
   const int b = blockIdx.x;
@@ -107,6 +110,10 @@ __global__ __launch_bounds__(2 * D) void write_i8_kernel(WriteArgs a) {
   }
   reinterpret_cast<_Float16*>(head + 2 * kQBlock * D + kv * D * 2)[ch] = s16;
 }
+template <int D>
+__global__ __launch_bounds__(2 * D) void write_i8_kernel(WriteArgs a) {
+  for (int rh = blockIdx.y; rh < a.pairs; rh += gridDim.y) write_i8_block<D>(a, rh);
+}
 
 // Packs the codes of one head's block (LDS, int8 [2][kQBlock][D], K then V,
 // values in [-7, 7]) into the INT4 page layout of include/tg.h at `head`:
@@ -138,9 +145,7 @@ __device__ void store_i4_words(const int8_t (*codes)[kQBlock][D], char* head) {
 // One block of 2*D threads per (r, h, 64-row block), thread = (K|V, channel):
 // the INT4 slow tier (codes in [-7, 7], scale absmax / 7).
 template <int D>
-__global__ __launch_bounds__(2 * D) void write_i4_kernel(WriteArgs a) {
-  __shared__ int8_t codes[2][kQBlock][D];
-  const int rh = blockIdx.y;
+__device__ __forceinline__ void write_i4_block(const WriteArgs& a, int rh, int8_t (*codes)[kQBlock][D]) {
   const int r = rh / a.H, h = rh % a.H;
   const int n_i8 = a.len[2 * rh];
   const int b = blockIdx.x;
@@ -167,6 +172,14 @@ __global__ __launch_bounds__(2 * D) void write_i4_kernel(WriteArgs a) {
   reinterpret_cast<_Float16*>(head + kQBlock * D + kv * D * 2)[ch] = s16;
   __syncthreads();
   store_i4_words<D>(codes, head);
+  __syncthreads();  // the codes are read before the next pair overwrites them
+}
+template <int D>
+__global__ __launch_bounds__(2 * D) void write_i4_kernel(WriteArgs a) {
+  __shared__ int8_t codes[2][kQBlock][D];
+  // (rh, blockIdx.x) is uniform over the workgroup, so are the early exits
+  // of write_i4_block and its barriers
+  for (int rh = blockIdx.y; rh < a.pairs; rh += gridDim.y) write_i4_block<D>(a, rh, codes);
 }
 
 // ---------------------------------------------------------------- decode-step append
@@ -209,8 +222,19 @@ __global__ __launch_bounds__(2 * D) void append_kernel(AppendArgs a) {
   const int r = rh / a.H, h = rh % a.H;
   const int kv = threadIdx.x / D, ch = threadIdx.x % D;
   const int cl = a.cluster_of_head[h], hs = a.slot_in_cluster[h];
-  const int n_i8 = a.len[2 * rh], n_bf = a.len[2 * rh + 1];
-  const int base = a.bf_base[rh];
+  // Thread 0 reads the lengths and the ring base into LDS and every thread
+  // takes them from there after the barrier: thread 0 updates them in memory
+  // at the end of the step, and a wavefront reading memory itself could see
+  // the new values (no order holds between wavefronts without the barrier).
+  __shared__ int state[3];
+  if (threadIdx.x == 0) {
+    state[0] = a.len[2 * rh];
+    state[1] = a.len[2 * rh + 1];
+    state[2] = a.bf_base[rh];
+  }
+  __syncthreads();
+  const int n_i8 = state[0], n_bf = state[1];
+  const int base = state[2];
   const int ring_rows = a.ring[r * a.C + cl] * kPage;
   const bool age = i8_rows(static_cast<int64_t>(n_i8) + n_bf + 1, a.recent_ppm) > n_i8;
   const int blk = n_i8 / kQBlock;
@@ -350,19 +374,21 @@ extern "C" int tg_write_kv(const tg_cache* c, const uint16_t* rows, const int32_
   a.offsets = offsets;
   a.H = c->n_kv_heads;
   const int64_t pairs = static_cast<int64_t>(c->B) * c->n_kv_heads;
-  if (pairs > 65535) return TG_EUNSUPPORTED;
+  if (pairs > INT32_MAX) return TG_EOVERFLOW;
+  a.pairs = static_cast<int32_t>(pairs);
+  // gridDim.y is at most 65535: the kernels stride over the pairs past it
+  const unsigned gy = static_cast<unsigned>(pairs < 65535 ? pairs : 65535);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int d = c->head_dim;
   const int rpb = 256 / (d / 8);
   if (max_bf > 0) {
-    const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(max_bf) * kPage + rpb - 1) / rpb),
-                    static_cast<unsigned>(pairs));
+    const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(max_bf) * kPage + rpb - 1) / rpb), gy);
     if (d == 128) hipLaunchKernelGGL(write_bf16_kernel<128>, grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL(write_bf16_kernel<64>, grid, dim3(256), 0, st, a);
     if (hipGetLastError() != hipSuccess) return TG_EDEVICE;
   }
   if (max_i8 > 0) {
-    const dim3 grid(static_cast<unsigned>(max_i8), static_cast<unsigned>(pairs));
+    const dim3 grid(static_cast<unsigned>(max_i8), gy);
     if (c->old_bits == 4) {
       if (d != 128) return TG_EUNSUPPORTED;
       hipLaunchKernelGGL(write_i4_kernel<128>, grid, dim3(256), 0, st, a);

@@ -113,6 +113,11 @@ int main(void) {
   CHECK(tg_release(pool, &t, 0) == TG_OK);
   CHECK(tg_pool_free_pages(pool, 0, TG_TIER_BF16) == 4 && tg_pool_free_pages(pool, 1, TG_TIER_BF16) == 2);
   CHECK(tg_release(pool, &t, 0) == TG_EINVAL);
+  /* requests outside [0, B) are refused, and change nothing */
+  CHECK(t.B == B);
+  CHECK(tg_release(pool, &t, B) == TG_EINVAL && tg_release(pool, &t, -1) == TG_EINVAL);
+  CHECK(tg_release(pool, &t, 1 << 30) == TG_EINVAL);
+  CHECK(tg_pool_free_pages(pool, 0, TG_TIER_BF16) == 4 && tg_pool_free_pages(pool, 1, TG_TIER_BF16) == 2);
   CHECK(tg_pool_refcount(pool, 0, TG_TIER_BF16, 4) == 1 && tg_pool_refcount(pool, 0, TG_TIER_BF16, 0) == 0);
   tg_pool_destroy(pool);
 

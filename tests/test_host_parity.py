@@ -85,6 +85,7 @@ def _tables_parity(w, chunk_bf=512, chunk_i8=1024, lpt=True, slack=3, group_size
     assert t_g.n_slots == t_o.part_off[-1] and t_g.n_gitems == len(t_o.gitems)
     assert np.array_equal(t_g.gitems, _gitems_of(t_o))
     assert np.array_equal(t_g.ring, np.array(t_o.ring, dtype=np.int32))
+    tg.tg_check_tables(pool_g, res_g, t_g)  # the library's own consistency check agrees
     return res_o, res_g, pool_o, pool_g, t_o, t_g
 
 
@@ -123,6 +124,7 @@ def test_release_and_reallocation_bit_exact():
         for c in range(w.n_clusters):
             for t in range(2):
                 assert pool_g.free_pages(c, t) == pool_o.free_pages(c, t)
+        tg.tg_check_tables(pool_g, res_g, t_g)  # released rows are skipped, the rest stays consistent
     with pytest.raises(tg.TGError) as e:
         tg.tg_release(pool_g, t_g, order[0])
     assert e.value.name == "TG_EINVAL"
@@ -194,6 +196,7 @@ def test_randomised_small_cases_bit_exact():
         assert np.array_equal(t_g.plan, np.array(t_o.work, dtype=np.int32).reshape(-1, 6)), case
         assert list(t_g.part_off) == t_o.part_off
         assert np.array_equal(t_g.gitems, _gitems_of(t_o)), case
+        tg.tg_check_tables(pool_g, res_g, t_g)
 
 
 def test_error_codes():
