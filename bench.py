@@ -1,11 +1,15 @@
 #!/usr/bin/env python3
 """Benchmark: effective KV GB/s of one ragged-paged decode step on one GPU.
 
-    python bench.py [--steps K] [--warmup W] [--config llama8b]
+    python bench.py [--steps K] [--warmup W] [--config ragged] [--configs tiny,llama8b,...]
 
 One step = the whole decode hot path over one batch: the split-K kernel over
 every plan item (bf16 pages and INT8 blocks) and the log-sum-exp merge, on a
-cache that is already resident in HBM.  Before every timed step a 1 GiB
+cache that is already resident in HBM.  The headline line is the largest
+workload that fits one GPU (``ragged``: batch 256, context 2K-32K); every
+other workload is measured the same way after it and listed under
+``configs``, each with its split kernel's roofline and an oracle check of
+every output it computed.  Before every timed step a 1 GiB
 device read evicts L2 and the 256 MB last-level cache with clean lines
 (outside the timed events; ``--flush write`` uses a 1 GiB write instead, whose
 dirty lines then drain to HBM during the timed kernels).  Each step is
@@ -276,13 +280,25 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+def _threads() -> int:
+    try:
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except AttributeError:  # pragma: no cover
+        return max(1, min(16, os.cpu_count() or 1))
+
+
 def cpu_baseline(w, prep, min_s: float = 10.0, keep_bytes: float = 2e9):
-    """The oracle, untuned, on this host's cores: fp64 attention of the (r, h)
-    pairs of the step from their raw rows, one pair per task on a pool of N
-    threads (N = the cores this process may use, at most 16; numpy releases
-    the interpreter lock in its kernels) with BLAS pinned to one thread each.
-    Rows are generated first (not timed), up to keep_bytes of them; the pairs
-    are decoded again until min_s of wall time, which is what is timed."""
+    """The oracle, untuned, on this host's cores, in two parts.
+
+    Check: every (r, h) pair of the step is decoded by the fp64 oracle from
+    its raw rows and compared with the GPU output element by element, pass
+    iff |g - r| <= 2e-3 + 1e-2 |r| everywhere (max-abs, and max-rel over
+    |r| >= 1e-3, reported).  Timing: a bounded sample of the pairs (rows
+    generated first and not timed, up to keep_bytes of them) is decoded again
+    until min_s of wall time; GB/s over the rows decoded.  One pair per task
+    on a pool of N threads (N = the cores this process may use, at most 16;
+    numpy releases the interpreter lock in its kernels) with BLAS pinned to
+    one thread each."""
     import concurrent.futures as cf
 
     import numpy as np
@@ -296,134 +312,97 @@ def cpu_baseline(w, prep, min_s: float = 10.0, keep_bytes: float = 2e9):
     q = A.q_f64(w)
     G = w.Hq // w.Hkv
     scale = 1.0 / math.sqrt(w.d)
-    try:
-        n_threads = max(1, min(16, len(os.sched_getaffinity(0))))
-    except AttributeError:  # pragma: no cover
-        n_threads = max(1, min(16, os.cpu_count() or 1))
+    n_threads = _threads()
+    gpu_out = prep.output()
+    bits = getattr(w, "old_bits", 8)
+
+    def nbytes_of(r, h):
+        n8, nb = res.n_i8[r][h], res.n_bf[r][h]
+        return nb * 4 * w.d + n8 * 2 * w.d * bits // 8 + (n8 // w.quant_block) * 4 * w.d
+
+    def check(rh):
+        r, h = rh
+        K16, V16 = w.logical_kv(r, h, res.L[r][h])
+        ref = A.decode_rows(q[r, h * G:(h + 1) * G], K16, V16, res.n_i8[r][h], w.quant_block, scale, bits)
+        got = gpu_out[r, h * G:(h + 1) * G]
+        err = np.abs(got - ref)
+        big = np.abs(ref) >= 1e-3
+        rel = float((err[big] / np.abs(ref[big])).max()) if big.any() else 0.0
+        ok = bool(np.all(err <= 2e-3 + 1e-2 * np.abs(ref)))
+        return ok, float(err.max()), rel
+
     order = np.random.default_rng(7).permutation(w.B * w.Hkv)
-    pairs, total = [], 0
+    sample, total = [], 0
     for i in order:
         r, h = divmod(int(i), w.Hkv)
         size = int(res.L[r][h]) * 4 * w.d
-        if pairs and total + size > keep_bytes:
+        if sample and total + size > keep_bytes:
             break
-        pairs.append((r, h))
+        sample.append((r, h))
         total += size
 
     def gen(rh):
         r, h = rh
         K16, V16 = w.logical_kv(r, h, res.L[r][h])
-        n8, nb = res.n_i8[r][h], res.n_bf[r][h]
-        return r, h, K16, V16, nb * 4 * w.d + n8 * 2 * w.d + (n8 // w.quant_block) * 4 * w.d
+        return r, h, K16, V16, nbytes_of(r, h)
 
     def run(task):
         r, h, K16, V16, _ = task
-        return A.decode_rows(q[r, h * G:(h + 1) * G], K16, V16, res.n_i8[r][h], w.quant_block, scale, w.old_bits)
+        return A.decode_rows(q[r, h * G:(h + 1) * G], K16, V16, res.n_i8[r][h], w.quant_block, scale, bits)
 
-    gpu_out = prep.output()
     ctx = threadpool_limits(limits=1) if threadpool_limits else None
     try:
         with cf.ThreadPoolExecutor(max_workers=n_threads) as ex:
-            tasks = list(ex.map(gen, pairs))
             t0 = time.perf_counter()
-            outs = list(ex.map(run, tasks))
-            wall = time.perf_counter() - t0
-            worst = max(float(np.abs(gpu_out[r, h * G:(h + 1) * G] - o).max())
-                        for (r, h, *_), o in zip(tasks, outs))
-            passes = 1
-            while wall < min_s:
+            checks = list(ex.map(check, [(r, h) for r in range(w.B) for h in range(w.Hkv)]))
+            check_s = time.perf_counter() - t0
+            tasks = list(ex.map(gen, sample))
+            wall, passes = 0.0, 0
+            while passes == 0 or wall < min_s:
                 t0 = time.perf_counter()
                 list(ex.map(run, tasks))
                 wall += time.perf_counter() - t0
                 passes += 1
     finally:
-        if ctx is not None:
-            ctx.unregister() if hasattr(ctx, "unregister") else None
+        if ctx is not None and hasattr(ctx, "unregister"):
+            ctx.unregister()
     nbytes = passes * sum(t[4] for t in tasks)
     return {"value": round(nbytes / wall / 1e9, 4), "unit": "GB/s", "cores": n_threads, "kind": "oracle",
             "cpu_model": _cpu_model(),
-            "sample": f"{passes} pass(es) over {len(tasks)} of the {w.B * w.Hkv} (request, KV-head) pairs of the "
-                      f"same step, fp64 numpy, {n_threads} threads with one BLAS thread each, {wall:.1f} s wall",
-            "max_abs_err_vs_gpu": worst}
+            "sample": f"timing: {passes} pass(es) over {len(tasks)} of the {w.B * w.Hkv} (request, KV-head) pairs "
+                      f"of the step, fp64 numpy, {n_threads} threads with one BLAS thread each, {wall:.1f} s wall",
+            "check": {"pairs": len(checks), "of_pairs": w.B * w.Hkv,
+                      "criterion": "|gpu - oracle| <= 2e-3 + 1e-2 |oracle| for every output element",
+                      "pass": all(c[0] for c in checks), "max_abs": max(c[1] for c in checks),
+                      "max_rel": max(c[2] for c in checks), "wall_s": round(check_s, 2)}}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="llama8b", choices=sorted(DESCRIPTIONS))
-    ap.add_argument("--chunk-bf", type=int, default=None, help="bf16 rows per plan item (default per workload)")
-    ap.add_argument("--chunk-i8", type=int, default=None, help="INT8 rows per plan item (default per workload)")
-    ap.add_argument("--flush", choices=["read", "write", "none"], default="read")
-    ap.add_argument("--append-steps", type=int, default=128,
-                    help="decode steps with tg_append_kv timed on a second cache built for growth (0: skip)")
-    ap.add_argument("--host-steps", type=int, default=10,
-                    help="decode steps with the INT8 tier in pinned host memory, streamed (0: skip)")
-    ap.add_argument("--zip-reps", type=int, default=5,
-                    help="timed encode/decode passes of the lossless codec over the bf16 pool (0: skip)")
-    ap.add_argument("--group-size", type=int, default=None,
-                    help="requests per shared-prefix group item (default min(32, 128 / G) when pages are shared)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--tune", action="store_true",
-                    help="time candidate plan item lengths on the device first and keep the fastest")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device-to-device copy 5 times (counter calibration)")
-    args = ap.parse_args()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the library has no multi-GPU path "
-              "(the decode step would shard by request with no exchange)",
-              file=sys.stderr)
-        sys.exit(2)
-
+def measure(name, args, evict, stream, read_gbps=None, headline=False):
+    """Time one workload's decode step (split kernel(s) + merge) and return
+    its record: step times, the split kernel timed alone, its roofline on the
+    algorithmic bytes, the page-stream read of its plan, and the oracle check
+    and baseline.  Extra measurements of the path's other parts (append,
+    codec, host-DRAM tier) go into the records that exercise them."""
     import numpy as np
     import torch
-
-    if args.copy_calibration:
-        n = 1 << 30
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        dt = (time.perf_counter() - t0) / 5
-        print(json.dumps({"copy_bytes_each_way": n, "copies": 5, "ms_per_copy": round(dt * 1e3, 4),
-                          "GBps_read_plus_write": round(2 * n / dt / 1e9, 1)}), flush=True)
-        return
 
     from non_uniform_paged_amd import api
     from non_uniform_paged_amd.runner import PLAN_CHUNKS, Prepared, allocated_bytes, tune_candidates
     from workloads import make_workload
 
-    torch.cuda.set_device(0)
-    w = make_workload(args.config)
+    w = make_workload(name)
+    chunk_bf = args.chunk_bf if (headline and args.chunk_bf) else PLAN_CHUNKS[name][0]
+    chunk_i8 = args.chunk_i8 if (headline and args.chunk_i8) else PLAN_CHUNKS[name][1]
     t_prep = time.perf_counter()
-    if args.chunk_bf is None:
-        args.chunk_bf = PLAN_CHUNKS[args.config][0]
-    if args.chunk_i8 is None:
-        args.chunk_i8 = PLAN_CHUNKS[args.config][1]
-    prep = Prepared(w, chunk_bf=args.chunk_bf, chunk_i8=args.chunk_i8, group_size=args.group_size)
+    prep = Prepared(w, chunk_bf=chunk_bf, chunk_i8=chunk_i8, group_size=args.group_size if headline else None)
     t_prep = time.perf_counter() - t_prep
-    tr = prep.traffic()
     G = w.Hq // w.Hkv
-    stream = torch.cuda.current_stream()
-    flush = None if args.flush == "none" else torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
-
-    def evict(i):
-        if args.flush == "read":
-            torch.amax(flush)
-        elif args.flush == "write":
-            flush.fill_(i & 0xFF)
-
     tuned = None
-    if args.tune:  # outside the timed region: pick the plan item lengths on the device
+    if headline and args.tune:  # outside the timed region: pick the plan item lengths on the device
         cands = tune_candidates(w, prep.tables.stride_has_i8)
         tuned = sorted(prep.tune_chunks(cands, evict=lambda: evict(0), stream=stream), key=lambda x: x[2])
-        args.chunk_bf, args.chunk_i8 = prep.chunks
-        tr = prep.traffic()
+        chunk_bf, chunk_i8 = prep.chunks
+    tr = prep.traffic()
 
     def one_step(evs=None):
         # the decode step: tg_decode_attn (split kernel(s), then the merge)
@@ -467,13 +446,140 @@ def main():
     split_ms_all = np.array([e[0].elapsed_time(e[1]) for e in kev])
     merge_ms_all = np.array([e[1].elapsed_time(e[2]) for e in kev])
 
-    # algorithmic bytes of the split kernel(s) (the dominant kernels): retained
-    # rows (shared pages once), q, tables, partials written; timed alone in
-    # the kernel-timing steps
-    split_bytes = tr["kv_roofline"] + w.B * w.Hq * w.d * (4 if w.q_dtype == "f32" else 2) + tr["tables"] \
-        + prep.tables.n_slots * G * (w.d + 2) * 4
+    # algorithmic bytes of the split kernel(s), the dominant kernels: retained
+    # rows (each page block once), q and the tables they read.  The partials
+    # they write for the merge are overhead of the split, not algorithmic
+    # bytes, and are listed apart.
+    q_bytes = w.B * w.Hq * w.d * (4 if w.q_dtype == "f32" else 2)
+    split_bytes = tr["kv_roofline"] + q_bytes + tr["tables"]
+    partial_bytes = prep.tables.n_slots * G * (w.d + 2) * 4
     split_ms = float(split_ms_all.mean())
     achieved = split_bytes / (split_ms * 1e-3) / 1e9
+    streams = stream_read_bench(w, prep, evict, stream)
+    traffic = _traffic_record(name)
+    rec = {
+        "name": name,
+        "workload": DESCRIPTIONS[name],
+        "config": {"batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "clusters": w.n_clusters,
+                   "page": w.page_size, "chunk_bf": chunk_bf, "chunk_i8": chunk_i8,
+                   "plan_items": prep.tables.n_items, "group_items": prep.tables.n_gitems,
+                   "group_size": prep.group_size, "slots": prep.tables.n_slots,
+                   "retained_head_rows": tr["head_rows"],
+                   "chunks_tuned": None if tuned is None else [[a, b, round(c, 1)] for a, b, c in tuned[:5]]},
+        "effective_bytes": tr["effective"],
+        "roofline_bytes": tr["roofline"],
+        "effective_GBps": round(tr["effective"] / (ms * 1e-3) / 1e9, 2),
+        "step_ms_mean": round(ms, 5),
+        "step_ms_median": round(med, 5),
+        "p10_ms": round(float(np.percentile(step_ms, 10)), 5),
+        "p90_ms": round(float(np.percentile(step_ms, 90)), 5),
+        "steps_per_s": round(1e3 / med, 2),
+        "step_frac_roofline_bytes": round(tr["roofline"] / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "split_ms": round(split_ms, 5),
+        "merge_ms": round(float(merge_ms_all.mean()), 5),
+        "partials_bytes_written": partial_bytes,
+        "wall_s_timed_region": round(wall, 4),
+        "prepare_s": round(t_prep, 2),
+        "stream_read": dict(streams, split_time_frac=round(streams["ms"] / split_ms, 4)),
+        "roofline": {
+            "kernel": "split_bf16_kernel" if not prep.tables.stride_has_i8 else "split_tiered_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": split_bytes,
+        },
+    }
+    if read_gbps:
+        rec["split_frac_of_read_ceiling"] = round(achieved / read_gbps, 4)
+    if headline:
+        # pool bytes the batch needs at the configured cluster count, one
+        # cluster and one cluster per KV-head, against the bytes it retains
+        alloc = {str(C): allocated_bytes(w, C, chunk_bf, chunk_i8) for C in sorted({w.n_clusters, 1, w.Hkv})}
+        rec["fragmentation"] = {"retained_bytes": tr["kv_roofline"], "allocated_bytes_by_clusters": alloc,
+                                "ratio_by_clusters": {k: round(v / tr["kv_roofline"], 4) for k, v in alloc.items()}}
+        if args.append_steps > 0 and w.paths is None:
+            args_a = argparse.Namespace(**vars(args))
+            args_a.chunk_bf, args_a.chunk_i8 = chunk_bf, chunk_i8
+            rec["append"] = append_bench(w, args_a, evict, stream)
+        if args.zip_reps > 0:
+            rec["codec"] = codec_bench(prep, args, stream)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, prep, min_s=args.cpu_seconds if headline else args.cpu_seconds_sub)
+    if args.host_steps > 0 and prep.tables.stride_has_i8 and (headline or name == "tiered"):
+        rec["host_tier"] = host_tier_bench(prep, args, stream, med)
+    del prep
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="ragged", choices=sorted(DESCRIPTIONS),
+                    help="headline workload (default: the largest single-GPU one, ragged)")
+    ap.add_argument("--configs", default="tiny,llama8b,tiered,tiered4,radix",
+                    help="comma-separated workloads measured after the headline, each a sub-record ('' = none)")
+    ap.add_argument("--chunk-bf", type=int, default=None, help="bf16 rows per plan item (default per workload)")
+    ap.add_argument("--chunk-i8", type=int, default=None, help="INT8 rows per plan item (default per workload)")
+    ap.add_argument("--flush", choices=["read", "write", "none"], default="read")
+    ap.add_argument("--append-steps", type=int, default=128,
+                    help="decode steps with tg_append_kv timed on a second cache built for growth (0: skip)")
+    ap.add_argument("--host-steps", type=int, default=10,
+                    help="decode steps with the INT8 tier in pinned host memory, streamed (0: skip)")
+    ap.add_argument("--zip-reps", type=int, default=5,
+                    help="timed encode/decode passes of the lossless codec over the bf16 pool (0: skip)")
+    ap.add_argument("--group-size", type=int, default=None,
+                    help="requests per shared-prefix group item (default min(32, 128 / G) when pages are shared)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="oracle timing per headline (s)")
+    ap.add_argument("--cpu-seconds-sub", type=float, default=2.0, help="oracle timing per sub-record (s)")
+    ap.add_argument("--tune", action="store_true",
+                    help="time candidate plan item lengths on the device first and keep the fastest")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (counter calibration)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(the decode step would shard by request with no exchange)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / 5
+        print(json.dumps({"copy_bytes_each_way": n, "copies": 5, "ms_per_copy": round(dt * 1e3, 4),
+                          "GBps_read_plus_write": round(2 * n / dt / 1e9, 1)}), flush=True)
+        return
+
+    from non_uniform_paged_amd import api
+
+    torch.cuda.set_device(0)
+    t_all = time.perf_counter()
+    stream = torch.cuda.current_stream()
+    flush = None if args.flush == "none" else torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def evict(i):
+        if args.flush == "read":
+            torch.amax(flush)
+        elif args.flush == "write":
+            flush.fill_(i & 0xFF)
 
     # achievable streaming-read rate of this device (2 GiB, non-temporal
     # loads), the practical ceiling besides the 8 TB/s peak
@@ -487,77 +593,44 @@ def main():
     read_ms = float(np.median([a.elapsed_time(b) for a, b in rev]))
     read_gbps = rbuf.numel() / (read_ms * 1e-3) / 1e9
     del rbuf
+    torch.cuda.empty_cache()
 
-    # the same access pattern with no arithmetic: one stream per plan item, in
-    # plan order, each reading as many 8 KiB chunks as the item reads bytes
-    # (pages of shared runs once), chunks placed at random in a fresh buffer
-    streams = stream_read_bench(w, prep, evict, stream)
+    head = measure(args.config, args, evict, stream, read_gbps, headline=True)
+    print(f"# {args.config}: split {head['split_ms'] * 1e3:.1f} us, frac {head['roofline']['frac']}",
+          file=sys.stderr, flush=True)
+    subs = []
+    for name in [c for c in args.configs.split(",") if c and c != args.config]:
+        subs.append(measure(name, args, evict, stream, read_gbps))
+        print(f"# {name}: split {subs[-1]['split_ms'] * 1e3:.1f} us, frac {subs[-1]['roofline']['frac']}",
+              file=sys.stderr, flush=True)
 
-    # pool bytes the batch needs at the configured cluster count, one cluster
-    # and one cluster per KV-head, against the bytes it retains
-    alloc = {str(C): allocated_bytes(w, C, args.chunk_bf, args.chunk_i8)
-             for C in sorted({w.n_clusters, 1, w.Hkv})}
-    traffic = _traffic_record(args.config)
-    value = tr["effective"] / (ms * 1e-3) / 1e9
     result = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": head["effective_GBps"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
+        "ms_per_step": head["step_ms_mean"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 K/V/Q; no datasets or weights)",
-        "config": {"workload": DESCRIPTIONS[args.config], "name": args.config, "batch": w.B,
-                   "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "clusters": w.n_clusters,
-                   "page": w.page_size, "chunk_bf": args.chunk_bf, "chunk_i8": args.chunk_i8,
-                   "plan_items": prep.tables.n_items, "group_items": prep.tables.n_gitems,
-                   "group_size": prep.group_size, "retained_head_rows": tr["head_rows"],
-                   "chunks_tuned": None if tuned is None else [[a, b, round(c, 1)] for a, b, c in tuned[:5]],
-                   "parallelism": "single GPU"},
-        "hbm_frac_roofline_bytes": round(tr["roofline"] / (med * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "effective_bytes": tr["effective"],
-        "roofline_bytes": tr["roofline"],
-        "steps_per_s": round(1e3 / med, 2),
-        "median_ms": round(med, 5),
-        "p10_ms": round(float(np.percentile(step_ms, 10)), 5),
-        "p90_ms": round(float(np.percentile(step_ms, 90)), 5),
-        "split_ms": round(split_ms, 5),
-        "merge_ms": round(float(merge_ms_all.mean()), 5),
-        "kernel_timing": "split, read-ceiling and stream-read kernels: HIP events recorded at each kernel's own "
-                         "start and end (hipExtLaunchKernel); merge_ms: split end to an event after the merge",
+        "config": dict(workload=head["workload"], name=head["name"], parallelism="single GPU", **head["config"]),
+        "hbm_frac_roofline_bytes": head["step_frac_roofline_bytes"],
+        "kernel_timing": "split and read kernels: HIP events recorded at each kernel's own start and end "
+                         "(hipExtLaunchKernel); merge_ms: split end to an event after the merge; steps: event "
+                         "pairs around each tg_decode_attn call",
         "cache_eviction_between_steps": args.flush,
-        "wall_s_timed_region": round(wall, 4),
-        "prepare_s": round(t_prep, 2),
         "device": _device_record(torch),
         "read_ceiling_GBps": round(read_gbps, 1),
-        "split_frac_of_read_ceiling": round(achieved / read_gbps, 4),
-        "stream_read": dict(streams, split_time_frac=round(streams["ms"] / split_ms, 4)),
-        "fragmentation": {"retained_bytes": tr["kv_roofline"], "allocated_bytes_by_clusters": alloc,
-                          "ratio_by_clusters": {k: round(v / tr["kv_roofline"], 4) for k, v in alloc.items()}},
-        "roofline": {
-            "kernel": "split_bf16_kernel" if not prep.tables.stride_has_i8 else "split_tiered_kernel",
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": split_bytes,
-        },
     }
-    if args.append_steps > 0 and w.paths is None:
-        result["append"] = append_bench(w, args, evict, stream)
-    if args.zip_reps > 0:
-        result["codec"] = codec_bench(prep, args, stream)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, prep)
-    if args.host_steps > 0 and prep.tables.stride_has_i8:
-        result["host_tier"] = host_tier_bench(prep, args, stream, med)
+    for k, v in head.items():
+        if k not in ("name", "workload", "config") and k not in result:
+            result[k] = v
+    result["configs"] = subs
+    result["bench_wall_s"] = round(time.perf_counter() - t_all, 1)
     print(json.dumps(result), flush=True)
 
 
