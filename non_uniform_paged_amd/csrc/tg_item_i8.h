@@ -59,10 +59,38 @@ __device__ __forceinline__ u32x2_t codes_to_f16(uint32_t w) {
 // 1024 + u = 1032 + q4); one in bits 4..7 sits in mantissa bits 4..7 of fp16
 // 64 (value 64 + u = 72 + q4); a byte shift brings nibbles 2, 3, 6, 7 to
 // those places.  Words 0 and 2 are offset by 1032, words 1 and 3 by 72.
+// (x & mask) | base as one instruction.  gfx9 VOP3 encodings take no
+// literal, so the compiler otherwise spends an AND and an OR (each with a
+// literal) on it; here the mask comes in a scalar register and the base in a
+// vector register (one scalar operand: the constant-bus limit).
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t base) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(base));
+  return r;
+}
+
 __device__ __forceinline__ u32x4_t nibbles_to_f16(uint32_t x) {
   const uint32_t y = x >> 8;
-  return u32x4_t{(x & 0x000F000Fu) | 0x64006400u, (x & 0x00F000F0u) | 0x54005400u,
-                 (y & 0x000F000Fu) | 0x64006400u, (y & 0x00F000F0u) | 0x54005400u};
+  return u32x4_t{and_or(x, 0x000F000Fu, 0x64006400u), and_or(x, 0x00F000F0u, 0x54005400u),
+                 and_or(y, 0x000F000Fu, 0x64006400u), and_or(y, 0x00F000F0u, 0x54005400u)};
+}
+
+// The same 8 codes with every nibble in mantissa bits 6..9 of fp16 16, so
+// that each value is 16 + u = 24 + q4 (word k again nibbles k and k + 4).
+// Used for K: the scores subtract 24 * sum_c q'_c from sum_c (24 + q4) q'_c,
+// and the small offset keeps that difference to within a few units of fp32
+// rounding of the score itself at any score scale (the 1032 offset of the
+// cheaper form cost ~8 bits there).
+constexpr uint32_t kF16x2_24 = 0x4E004E00u;  // two fp16 24.0
+__device__ __forceinline__ u32x4_t nibbles_to_f16_k(uint32_t x) {
+  constexpr uint32_t kMask = 0x03C003C0u, kBase = 0x4C004C00u;  // mantissa bits 6..9 of fp16 16.0
+  return u32x4_t{and_or(x << 6, kMask, kBase), and_or(x << 2, kMask, kBase), and_or(x >> 2, kMask, kBase),
+                 and_or(x >> 6, kMask, kBase)};
+}
+
+// x of the lane 8 places on inside its 16-lane row (DPP row_ror:8)
+__device__ __forceinline__ float ror8_in_row(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
 }
 
 __device__ __forceinline__ float half_lo(uint32_t w) {
@@ -74,9 +102,9 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
 
 // BITS = 4: the INT4 page (include/tg.h): per 16-row group one 16-byte load
 // per lane holds all d = 128 channels of K (and one all of V) as nibbles;
-// values 1032 + q4 or 72 + q4 (by operand word, nibbles_to_f16) take the
-// place of 1152 + q8, the constant tiles carry the same per-word offsets,
-// and the rest is unchanged.
+// K values 24 + q4 (nibbles_to_f16_k) and V values 1032 + q4 or 72 + q4 (by
+// operand word, nibbles_to_f16) take the place of 1152 + q8, the constant
+// tiles carry the same offsets, and the rest is unchanged.
 template <int D, int G, bool QF32, int DEPTH, bool STREAM, int BITS>
 __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0, int t1, int slot,
                                         int hs, const TG_GLOBAL int32_t* bt_row, gptr pool,
@@ -84,10 +112,12 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
   static_assert(BITS == 8 || (BITS == 4 && D == 128), "INT4 pages are laid out for d = 128");
   constexpr int NL = BITS == 8 ? D / 64 : 1;  // 1 KiB loads per 16-row group (K codes, V codes)
   constexpr int CODE_BYTES = kQBlock * D * BITS / 8;  // K (or V) codes of one head's block
-  // INT8: q' and the weights P enter the matrix cores as fp16 high + low
-  // parts (~22 significant bits).  INT4: one fp16 part each (11 bits, far
-  // finer than the 4-bit codes they multiply), half the matrix-core work.
-  constexpr bool TWO = BITS == 8;
+  // q' = q * s_K enters the matrix cores as fp16 high + low parts (~22
+  // significant bits): a score's error then stays a small fraction of the
+  // score at any score scale.  The weights P: two parts for INT8, one for
+  // INT4 (P <= 2^kSlack, so one fp16 part bounds the relative error of every
+  // weight by 2^-11 whatever the scores; the sum l takes the rounded weights).
+  constexpr bool TWO = BITS == 8;  // two-part P
   // INT4: two 16-row groups form one 32-row step (one reference max, K = 32
   // products for P V), with DEPTH groups in the register pipeline, one pair
   // ahead.  (For INT8 the pair step measured slower: its two-part operands
@@ -103,11 +133,20 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
   const int lg = lane & 15;
   const int lj = lane >> 4;
   const bool has = lg < G;
+  // INT4 (PACKQ): the two fp16 parts of q' share one score tile, the high
+  // part of head g in column g and the low part in column g + 8 (G <= 8), so
+  // that one matrix-core product per step gives both; a rotation by 8 lanes
+  // inside each 16-lane row then adds column g + 8 to column g (and g to
+  // g + 8, a copy of head g that is never written out).
+  constexpr bool PACKQ = BITS == 4;
+  static_assert(!PACKQ || G <= 8, "packed q parts need 2G <= 16 columns");
+  const int qhead = PACKQ ? (lg & 7) : lg;   // head whose q this lane holds
+  const bool hasq = qhead < G;
 
-  // q of head lg, channels 32 s + 8 lj + e
+  // q of head qhead, channels 32 s + 8 lj + e
   float qf[NK][8];
   {
-    const int64_t row = static_cast<int64_t>(r) * a.n_q_heads + h * G + (has ? lg : 0);
+    const int64_t row = static_cast<int64_t>(r) * a.n_q_heads + h * G + (hasq ? qhead : 0);
 #pragma unroll
     for (int s = 0; s < NK; ++s) {
       if constexpr (QF32) {
@@ -115,15 +154,15 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
         const u32x4_t x1 = ldv16(a.q + (row * D + 32 * s + 8 * lj + 4) * 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          qf[s][e] = has ? __uint_as_float(x0[e]) : 0.f;
-          qf[s][e + 4] = has ? __uint_as_float(x1[e]) : 0.f;
+          qf[s][e] = hasq ? __uint_as_float(x0[e]) : 0.f;
+          qf[s][e + 4] = hasq ? __uint_as_float(x1[e]) : 0.f;
         }
       } else {
         const u32x4_t x = ldv16(a.q + (row * D + 32 * s + 8 * lj) * 2);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          qf[s][2 * e] = has ? __uint_as_float(x[e] << 16) : 0.f;
-          qf[s][2 * e + 1] = has ? __uint_as_float(x[e] & 0xffff0000u) : 0.f;
+          qf[s][2 * e] = hasq ? __uint_as_float(x[e] << 16) : 0.f;
+          qf[s][2 * e + 1] = hasq ? __uint_as_float(x[e] & 0xffff0000u) : 0.f;
         }
       }
     }
@@ -140,7 +179,8 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
   // of the operand words (K: words 0-3 of a step; V: the two words of a tile)
   constexpr uint32_t kOffA = BITS == 8 ? kF16x2_1152 : kF16x2_1032;
   constexpr uint32_t kOffB = BITS == 8 ? kF16x2_1152 : kF16x2_72;
-  const u32x4_t c1152x8 = {kOffA, kOffB, kOffA, kOffB};
+  constexpr uint32_t kOffK = BITS == 8 ? kF16x2_1152 : kF16x2_24;  // K operands (nibbles_to_f16_k)
+  const u32x4_t c1152x8 = {kOffK, kOffK, kOffK, kOffK};
   const u32x2_t c1152x4 = {kOffA, kOffB};
   const int b0 = t0 / kQBlock;
   const int nb = (t1 - t0) / kQBlock;
@@ -187,15 +227,20 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
         for (int e = 0; e < 4; ++e) {
           qop[0][s][e] = hi[2 * e] | (hi[2 * e + 1] << 16);
           qop[1][s][e] = lo[2 * e] | (lo[2 * e + 1] << 16);
+          if constexpr (PACKQ) {  // columns 8.. take the low parts
+            if (lg >= 8) qop[0][s][e] = qop[1][s][e];
+          }
         }
       }
       f32x4_t qb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NK; ++s) {
         qb = mfma_f16_k32(c1152x8, qop[0][s], qb);
-        if constexpr (TWO) qb = mfma_f16_k32(c1152x8, qop[1][s], qb);
+        if constexpr (!PACKQ) qb = mfma_f16_k32(c1152x8, qop[1][s], qb);
       }
-      const float qk_bias = qb[0];  // 1152 * sum_c Q'[lg][c], the same in every row
+      // offset * sum_c Q'[lg][c] (with PACKQ: of this column's part), the same
+      // in every row
+      const float qk_bias = qb[0];
 
       f32x4_t accb[NT];
 #pragma unroll
@@ -227,12 +272,12 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
             A0 = u32x4_t{c00[0], c00[1], c01[0], c01[1]};
             A1 = u32x4_t{c10[0], c10[1], c11[0], c11[1]};
           } else {
-            A0 = nibbles_to_f16(kc[u0][0][s]);
-            A1 = nibbles_to_f16(kc[u1][0][s]);
+            A0 = nibbles_to_f16_k(kc[u0][0][s]);
+            A1 = nibbles_to_f16_k(kc[u1][0][s]);
           }
           s0 = mfma_f16_k32(A0, qop[0][s], s0);
           s1 = mfma_f16_k32(A1, qop[0][s], s1);
-          if constexpr (TWO) {
+          if constexpr (!PACKQ) {
             s0 = mfma_f16_k32(A0, qop[1][s], s0);
             s1 = mfma_f16_k32(A1, qop[1][s], s1);
           }
@@ -240,8 +285,13 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
         float sc[8];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          sc[rr] = (s0[rr] - qk_bias) * a.scale_log2;
-          sc[4 + rr] = (s1[rr] - qk_bias) * a.scale_log2;
+          float d0 = s0[rr] - qk_bias, d1 = s1[rr] - qk_bias;
+          if constexpr (PACKQ) {  // + the other part, 8 lanes on in the row
+            d0 += ror8_in_row(d0);
+            d1 += ror8_in_row(d1);
+          }
+          sc[rr] = d0 * a.scale_log2;
+          sc[4 + rr] = d1 * a.scale_log2;
         }
         float pm = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
         pm = xor32_max(xor16_max(pm));
@@ -314,10 +364,10 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
             const u32x2_t c1 = codes_to_f16(x[(s % 2) * 2 + 1]);
             A = u32x4_t{c0[0], c0[1], c1[0], c1[1]};
           } else {
-            A = nibbles_to_f16(kc[u][0][s]);  // channels 32 s + 8 lj + e, e < 8
+            A = nibbles_to_f16_k(kc[u][0][s]);  // channels 32 s + 8 lj + e, e < 8
           }
           sacc = mfma_f16_k32(A, qop[0][s], sacc);
-          if constexpr (TWO) sacc = mfma_f16_k32(A, qop[1][s], sacc);
+          sacc = mfma_f16_k32(A, qop[1][s], sacc);
         }
         float sc[4];
 #pragma unroll

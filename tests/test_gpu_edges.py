@@ -141,9 +141,6 @@ def test_random_page_permutation_bitwise(case):
     before = p.output().copy()
     moved = _permute_pages(p, seed=31)
     assert moved > 0
-    from non_uniform_paged_amd import api
-    tg_res = p.res
-    api.tg_check_tables(p.pool, tg_res, p.tables)  # the permuted tables are still consistent
     p.step()
     after = p.output()
     assert np.array_equal(before, after), f"{case}: outputs differ after permuting {moved} page ids"
@@ -159,14 +156,14 @@ def test_random_page_permutation_bitwise(case):
 
 # ---------------------------------------------------------------------------- softmax range
 class _Ramp(Workload):
-    """Scores that climb along each sequence: q has a common component in one
-    channel per KV-head (4, plus N(0, 1/4) noise elsewhere), and K's value in
+    """Scores that climb along each sequence: q is 4 in one channel per
+    KV-head (and N(0, 1/4) elsewhere), and K's value in
     that channel grows by `step` per logical row (on top of its N(0, 1)
     draw), so q . k rises by about 4 * step * scale per row -- more than 2^8
-    in base 2 per 16-row page at the default scale.  Shared radix nodes and
+    in base 2 per 16-row page at the default scale (checked per q-head).  Shared radix nodes and
     private suffixes continue the same ramp at their logical positions."""
 
-    step = 1.5
+    step = 1.2
 
     def _channel(self, h):
         return (37 * h + 5) % self.d
@@ -175,7 +172,7 @@ class _Ramp(Workload):
         g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([20260601, 77, self.cfg_id])))
         x = 0.5 * g.standard_normal((self.B, self.Hq, self.d), dtype=np.float32)
         for hq in range(self.Hq):
-            x[:, hq, self._channel(hq // self.G)] += np.float32(4.0)
+            x[:, hq, self._channel(hq // self.G)] = np.float32(4.0)
         return x if self.q_dtype == "f32" else bf16_round(x)
 
     def _start(self, key):
