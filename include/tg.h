@@ -452,8 +452,10 @@ int tg_merge_partials(const float* workspace, int32_t n_slots, int32_t n_pairs, 
  *   args.work  the plan reordered by tg_stream_order (device copy);
  *   chunk_off  host [B + 1] from tg_stream_order
  *   staging    device, 256-byte aligned, >= tg_stream_staging_bytes bytes
- * Calls must not overlap in time (one copy stream per process).  Errors as
- * tg_decode_attn; TG_EINVAL on a bad chunk_off or staging size. */
+ * The library creates one copy stream and its events per device, on the
+ * device's first call, and keeps them until the process ends: calls on one
+ * device must not overlap in time; calls on different devices may.  Errors
+ * as tg_decode_attn; TG_EINVAL on a bad chunk_off or staging size. */
 size_t tg_stream_staging_bytes(const tg_cache* cache, const tg_tables* tables);
 int tg_decode_streamed(const tg_cache* cache, const tg_tables* tables, const tg_decode_args* args,
                        const int32_t* chunk_off, void* staging, size_t staging_bytes, void* stream);

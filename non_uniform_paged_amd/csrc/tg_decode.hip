@@ -11,6 +11,8 @@
 #include <cmath>
 #include <algorithm>
 #include <cstdint>
+#include <map>
+#include <mutex>
 #include <vector>
 
 #include "tg_device.h"
@@ -287,13 +289,22 @@ size_t slot_layout(const tg_cache* c, const tg_tables* t, size_t* off /*[C]*/) {
   return at;
 }
 
+// The copy stream and events of the streamed decode, one set per device,
+// created on a device's first call and kept until the process ends.  Calls on
+// one device must not overlap in time (they share the set); calls on
+// different devices may.
 struct StreamState {
   hipStream_t copy = nullptr;
   std::vector<hipEvent_t> events;
 };
 
 int stream_state(int32_t n_events, StreamState** out) {
-  static StreamState state;  // one device per process; calls must not overlap
+  static std::mutex mu;
+  static std::map<int, StreamState> states;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TG_EDEVICE;
+  std::lock_guard<std::mutex> lock(mu);
+  StreamState& state = states[dev];
   if (state.copy == nullptr &&
       hipStreamCreateWithFlags(&state.copy, hipStreamNonBlocking) != hipSuccess)
     return TG_EDEVICE;
