@@ -411,6 +411,21 @@ typedef struct tg_decode_args {
 
 int tg_decode_attn(const tg_cache* cache, const tg_decode_args* args, void* stream);
 
+/* tg_decode_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the partials go to a fixed device array of the library instead of
+ * args->workspace (ignored, as is args->workspace_bytes).  The array holds
+ * TG_NOALLOC_SCRATCH_BYTES on each device the library runs on, from the
+ * device's first call until the process ends; the call itself allocates
+ * nothing.  Every call on one device shares that device's array, so calls
+ * that overlap in time on one device (on different streams) race; calls on
+ * one stream are ordered.  Nothing in the array needs to start at zero.
+ * TG_EOVERFLOW when tg_decode_workspace_bytes(n_slots, G, d) exceeds
+ * TG_NOALLOC_SCRATCH_BYTES (nothing is launched); otherwise the errors of
+ * tg_decode_attn, and TG_EDEVICE if the array's address cannot be taken. */
+#define TG_NOALLOC_SCRATCH_BYTES (32u << 20)
+int tg_decode_attn_noalloc(const tg_cache* cache, const tg_decode_args* args, void* stream);
+
 /* Split stage alone: writes the partials of every plan item into
  * `workspace` (layout above) without merging them; `out` is not used.
  * tg_decode_attn == tg_decode_split followed by tg_merge_partials over the

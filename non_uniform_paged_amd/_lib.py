@@ -27,6 +27,7 @@ TG_TIER_BF16 = 1
 TG_GROUP_WIDTH = 32
 TG_BENCH_READ_BLOCKS = 4096
 TG_MAX_CLUSTERS = 16
+TG_NOALLOC_SCRATCH_BYTES = 32 << 20
 TG_Q_F32 = 0
 TG_Q_BF16 = 1
 
@@ -110,6 +111,7 @@ SIGNATURES = {
     "tg_decode_workspace_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
     "tg_decode_attn": (ctypes.c_int, [POINTER(Cache), POINTER(DecodeArgs), c_void_p]),
     "tg_decode_split": (ctypes.c_int, [POINTER(Cache), POINTER(DecodeArgs), c_void_p]),
+    "tg_decode_attn_noalloc": (ctypes.c_int, [POINTER(Cache), POINTER(DecodeArgs), c_void_p]),
     "tg_merge_partials": (ctypes.c_int, [c_void_p, c_int32, c_int32, c_int32, c_int32, c_void_p,
                                          c_void_p, c_void_p]),
     "tg_decode_split_timed": (ctypes.c_int, [POINTER(Cache), POINTER(DecodeArgs), c_void_p, c_void_p, c_void_p]),

@@ -18,7 +18,8 @@ __all__ = [
     "TGError", "TG_TIER_I8", "TG_TIER_BF16", "TG_Q_F32", "TG_Q_BF16", "TG_GROUP_WIDTH",
     "Reservation", "Share", "Pool", "Tables", "DeviceCache",
     "tg_reserve", "tg_size_tables", "tg_build_tables", "tg_release", "tg_check_tables",
-    "tg_write_kv", "tg_decode_workspace_bytes", "tg_decode_attn", "tg_decode_split", "tg_decode_split_timed",
+    "tg_write_kv", "tg_decode_workspace_bytes", "tg_decode_attn", "tg_decode_attn_noalloc", "tg_decode_split",
+    "tg_decode_split_timed",
     "tg_merge_partials", "tg_bench_read", "tg_bench_streams", "TG_BENCH_READ_BLOCKS", "tg_append_kv",
     "tg_stream_order", "tg_stream_staging_bytes", "tg_decode_streamed",
     "tg_zip_bound", "tg_zip_workspace_bytes", "tg_zip_encode", "tg_zip_decode", "zip_compressed_bytes",
@@ -341,7 +342,8 @@ def _decode_args(cache, q, out, workspace, n_q_heads, sm_scale, work=None):
     _dev(q, "q", rows * q.element_size())
     if out is not None:
         _dev(out, "out", rows * 4, (torch.float32,))
-    _dev(workspace, "workspace")
+    if workspace is not None:
+        _dev(workspace, "workspace")
     _dev(cache.work if work is None else work, "work", int(cache.n_items) * 24, (torch.int32,))
     a = L.DecodeArgs()
     a.n_q_heads = int(n_q_heads)
@@ -354,7 +356,7 @@ def _decode_args(cache, q, out, workspace, n_q_heads, sm_scale, work=None):
     a.n_gitems = int(cache.n_gitems)
     a.n_slots = int(cache.n_slots)
     a.workspace = _ptr(workspace)
-    a.workspace_bytes = int(workspace.numel() * workspace.element_size())
+    a.workspace_bytes = 0 if workspace is None else int(workspace.numel() * workspace.element_size())
     a.out = _ptr(out)
     a.sm_scale = float(sm_scale)
     return a
@@ -369,6 +371,16 @@ def tg_decode_attn(cache: DeviceCache, q, out, workspace, n_q_heads: int, sm_sca
     a = _decode_args(cache, q, out, workspace, n_q_heads, sm_scale)
     check(lib().tg_decode_attn(ctypes.byref(cache.struct), ctypes.byref(a), _stream_ptr(stream)),
           "tg_decode_attn")
+
+
+def tg_decode_attn_noalloc(cache: DeviceCache, q, out, n_q_heads: int, sm_scale: float = 0.0,
+                           stream=None) -> None:
+    """tg_decode_attn with the partials in the library's fixed device array
+    (no workspace argument, nothing allocated by the call); TGError
+    TG_EOVERFLOW when the plan's partials exceed TG_NOALLOC_SCRATCH_BYTES."""
+    a = _decode_args(cache, q, out, None, n_q_heads, sm_scale)
+    check(lib().tg_decode_attn_noalloc(ctypes.byref(cache.struct), ctypes.byref(a), _stream_ptr(stream)),
+          "tg_decode_attn_noalloc")
 
 
 def tg_decode_split(cache: DeviceCache, q, workspace, n_q_heads: int, sm_scale: float = 0.0,

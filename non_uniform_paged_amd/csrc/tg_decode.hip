@@ -389,12 +389,50 @@ extern "C" int tg_decode_streamed(const tg_cache* c, const tg_tables* t, const t
   return e == hipSuccess ? TG_OK : TG_EDEVICE;
 }
 
+extern "C" int tg_decode_attn(const tg_cache* c, const tg_decode_args* a, void* stream) {
+  return decode_split(c, a, stream, true);
+}
+
+// ---------------------------------------------------------------- decode without allocation
+// Partials of tg_decode_attn_noalloc: a fixed device array of the library.
+// Each device the library runs on holds its own copy until the process ends.
+// Host code never passes `scratch` itself to a kernel (in host code the name
+// is a stand-in, not a device address): it takes the address that
+// hipGetSymbolAddress gives on each device, once per device.
+static __device__ __align__(256) char scratch[TG_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+int scratch_address(void** out) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;  // device -> its copy of `scratch`
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return TG_EDEVICE;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return TG_EDEVICE;
+    it = addr.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return TG_OK;
+}
 
 }  // namespace
 
-extern "C" int tg_decode_attn(const tg_cache* c, const tg_decode_args* a, void* stream) {
-  return decode_split(c, a, stream, true);
+extern "C" int tg_decode_attn_noalloc(const tg_cache* c, const tg_decode_args* a, void* stream) {
+  if (!c || !a || c->n_kv_heads < 1 || a->n_q_heads < 1 || a->n_q_heads % c->n_kv_heads || a->n_slots < 0)
+    return TG_EINVAL;
+  const size_t need = tg_decode_workspace_bytes(a->n_slots, a->n_q_heads / c->n_kv_heads, c->head_dim);
+  if (need > TG_NOALLOC_SCRATCH_BYTES) return TG_EOVERFLOW;
+  void* ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st) return st;
+  tg_decode_args b = *a;
+  b.workspace = static_cast<float*>(ws);
+  b.workspace_bytes = TG_NOALLOC_SCRATCH_BYTES;
+  return decode_split(c, &b, stream, true);
 }
 
 extern "C" int tg_decode_split(const tg_cache* c, const tg_decode_args* a, void* stream) {

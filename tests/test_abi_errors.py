@@ -182,3 +182,17 @@ def test_pool_create_checks():
     assert create(128, 16, 64, 8, n_c=(ctypes.c_int32 * 1)(0)) == L.TG_EINVAL
     assert create(128, 16, 64, 8, pi=neg) == L.TG_EINVAL
     assert create(1 << 30, 16, 64, 8, pb=(ctypes.c_int64 * 1)(1 << 40)) == L.TG_EOVERFLOW
+
+
+def test_noalloc_refuses_oversized_partials_before_any_launch():
+    """tg_decode_attn_noalloc checks the partials' size against its fixed
+    array on the host: more slots than fit give TG_EOVERFLOW, malformed head
+    counts TG_EINVAL, without touching the device."""
+    lib = L.lib()
+    assert lib.tg_decode_attn_noalloc(None, None, None) == L.TG_EINVAL
+    c = _cache()
+    a = _args(n_q_heads=4)
+    a.n_slots = L.TG_NOALLOC_SCRATCH_BYTES // (2 * 130 * 4) + 1  # G = 2, d = 128
+    assert lib.tg_decode_attn_noalloc(ctypes.byref(c), ctypes.byref(a), None) == L.TG_EOVERFLOW
+    a.n_q_heads = 3  # not a multiple of the KV-heads
+    assert lib.tg_decode_attn_noalloc(ctypes.byref(c), ctypes.byref(a), None) == L.TG_EINVAL
