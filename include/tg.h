@@ -198,7 +198,8 @@ int32_t tg_pool_refcount(const tg_pool* pool, int32_t c, int32_t tier, int64_t p
  *           each (r, h) are cut into runs of one radix node; requests whose
  *           run has the same (node, first row, pages, n_i8) are taken in
  *           ascending r, group_size at a time, and each group's rows are
- *           split as above (chunk_bf) from the run's first row into group items
+ *           split as above (chunk_group, or chunk_bf when it is 0) from the
+ *           run's first row into group items
  *           {-1 - k, h, bf16, t0, t1, -1}: one pass over those pages for up
  *           to group_size requests.  gitems[k] lists its members as
  *           TG_GROUP_WIDTH (r, slot) pairs, padded with (-1, -1).  Group items
@@ -238,6 +239,8 @@ typedef struct tg_plan_opts {
                          pages, so 128 / G or less is one pass) */
   int32_t gen_tokens; /* >= 0: rows each (r, h) may still gain by tg_append_kv
                          (see growth below); 0 with `share` only */
+  int32_t chunk_group; /* group item length in rows, a multiple of page_size;
+                          0: chunk_bf */
 } tg_plan_opts;
 
 typedef struct tg_table_sizes {

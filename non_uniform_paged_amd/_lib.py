@@ -54,7 +54,7 @@ class ShareDesc(ctypes.Structure):
 
 class PlanOpts(ctypes.Structure):
     _fields_ = [("chunk_bf", c_int32), ("chunk_i8", c_int32), ("lpt", c_int32), ("group_size", c_int32),
-                ("gen_tokens", c_int32)]
+                ("gen_tokens", c_int32), ("chunk_group", c_int32)]
 
 
 class TableSizes(ctypes.Structure):

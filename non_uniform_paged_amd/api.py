@@ -134,8 +134,9 @@ class Pool:
 
 def tg_size_tables(res: Reservation, page_size: int, quant_block: int, share: Optional[Share] = None,
                    chunk_bf: int = 1024, chunk_i8: int = 1024, lpt: bool = True,
-                   group_size: int = 0, gen_tokens: int = 0) -> dict:
-    opts = L.PlanOpts(int(chunk_bf), int(chunk_i8), int(bool(lpt)), int(group_size), int(gen_tokens))
+                   group_size: int = 0, gen_tokens: int = 0, chunk_group: int = 0) -> dict:
+    opts = L.PlanOpts(int(chunk_bf), int(chunk_i8), int(bool(lpt)), int(group_size), int(gen_tokens),
+                      int(chunk_group))
     sz = L.TableSizes()
     check(lib().tg_size_tables(ctypes.byref(res.struct), int(page_size), int(quant_block),
                                _share_ptr(share), ctypes.byref(opts), ctypes.byref(sz)), "tg_size_tables")
@@ -194,12 +195,13 @@ class Tables:
 
 def tg_build_tables(pool: Pool, res: Reservation, share: Optional[Share] = None, chunk_bf: int = 1024,
                     chunk_i8: int = 1024, lpt: bool = True, group_size: int = 0,
-                    gen_tokens: int = 0) -> Tables:
+                    gen_tokens: int = 0, chunk_group: int = 0) -> Tables:
     sizes = tg_size_tables(res, pool.page_size, pool.quant_block, share, chunk_bf, chunk_i8, lpt, group_size,
-                           gen_tokens)
+                           gen_tokens, chunk_group)
     t = Tables(res, sizes)
     t.gen_tokens = int(gen_tokens)
-    opts = L.PlanOpts(int(chunk_bf), int(chunk_i8), int(bool(lpt)), int(group_size), int(gen_tokens))
+    opts = L.PlanOpts(int(chunk_bf), int(chunk_i8), int(bool(lpt)), int(group_size), int(gen_tokens),
+                      int(chunk_group))
     check(lib().tg_build_tables(pool.handle, ctypes.byref(res.struct), _share_ptr(share),
                                 ctypes.byref(opts), ctypes.byref(t.struct)), "tg_build_tables")
     t.sizes = sizes

@@ -380,6 +380,7 @@ int check_opts(const tg_plan_opts* o, int32_t ps, int32_t qb) {
   if (o->chunk_bf < ps || o->chunk_bf % ps || o->chunk_i8 < qb || o->chunk_i8 % qb) return TG_EINVAL;
   if (o->group_size < 0 || o->group_size > TG_GROUP_WIDTH) return TG_EINVAL;
   if (o->gen_tokens < 0) return TG_EINVAL;
+  if (o->chunk_group < 0 || o->chunk_group % ps) return TG_EINVAL;
   return TG_OK;
 }
 
@@ -543,7 +544,8 @@ int make_plan(const tg_reservation* res, const tg_reservation* live, const Geome
         const int64_t lo = grp.ja * g.ps, hi = (grp.ja + grp.id.npages) * g.ps;
         for (size_t k = 0; k < grp.members.size(); k += o->group_size) {
           const size_t e = std::min(grp.members.size(), k + size_t(o->group_size));
-          split_range(lo, hi, hi, g.ps, o->chunk_bf, [&](int64_t t0, int64_t t1) {
+          split_range(lo, hi, hi, g.ps, o->chunk_group > 0 ? o->chunk_group : o->chunk_bf,
+                      [&](int64_t t0, int64_t t1) {
             gi.push_back(GItem{h, t0, t1, std::vector<int32_t>(grp.members.begin() + k, grp.members.begin() + e)});
           });
         }

@@ -66,7 +66,8 @@ R-group  (only with a group size > 1 and radix paths) the leading shared bf16
          pages of each (r, h) are cut into runs with the same radix node;
          requests whose run has the same (node, first row, page count, INT8
          rows) are taken in ascending r, group_size at a time, and each group's
-         rows are chunked from the run's first row into group items (listed
+         rows are chunked as in R-plan, with chunk_group rows (chunk_bf when
+         chunk_group is 0), from the run's first row into group items (listed
          first: per h, runs in order of first appearance, groups, chunks).  A
          request's own bf16 items then start after its shared rows.  Slots: per
          (r, h) in natural order, its group memberships (in group-item order)
@@ -446,7 +447,7 @@ def lpt_weight(tier: int, quant_block: int, old_bits: int) -> int:
 
 def plan(res: Reservation, chunk_bf: int, chunk_i8: int, lpt: bool, group_size: int = 0,
          page_size: int = 16, quant_block: int = 64, n_fixed=None, paths=None, node_len=None,
-         old_bits: int = 8, live=None):
+         old_bits: int = 8, live=None, chunk_group: int = 0):
     """Split plan, partial CSR and group-item member table (R-plan, R-group).
 
     Returns (work, part_off, gitems).  A work item is (r, h, tier, t0, t1,
@@ -479,7 +480,7 @@ def plan(res: Reservation, chunk_bf: int, chunk_i8: int, lpt: bool, group_size: 
                 lo, hi = ja * page_size, (ja + ident[2]) * page_size
                 for k in range(0, len(mem), group_size):
                     grp = mem[k:k + group_size]
-                    for t0, t1 in split_range(lo, hi, page_size, chunk_bf):
+                    for t0, t1 in split_range(lo, hi, page_size, chunk_group or chunk_bf):
                         gitems_members.append(grp)
                         gitem_rows.append((h, t0, t1))
     # slots in natural (r, h) order: group memberships first, then own items
@@ -517,7 +518,7 @@ def plan(res: Reservation, chunk_bf: int, chunk_i8: int, lpt: bool, group_size: 
 def build_tables(pool: Pool, res: Reservation, page_size: int, quant_block: int,
                  chunk_bf: int, chunk_i8: int, lpt: bool,
                  n_fixed=None, paths=None, node_len=None, group_size: int = 0,
-                 gen_tokens: int = 0, old_bits: int = 8) -> Tables:
+                 gen_tokens: int = 0, old_bits: int = 8, chunk_group: int = 0) -> Tables:
     """Allocate pages and emit block tables, lengths and the plan (R-alloc,
     R-page, R-plan, R-group).  With gen_tokens > 0 pages and plan cover the
     capacity for that many appended rows (R-step); lengths stay the live ones
@@ -527,6 +528,8 @@ def build_tables(pool: Pool, res: Reservation, page_size: int, quant_block: int,
         raise OracleError("EINVAL", "chunk sizes")
     if not 0 <= group_size <= GROUP_WIDTH:
         raise OracleError("EINVAL", "group size")
+    if chunk_group < 0 or chunk_group % page_size:
+        raise OracleError("EINVAL", "group chunk")
     if gen_tokens < 0 or (gen_tokens > 0 and paths is not None):
         raise OracleError("EINVAL", "growth")
     B = len(res.L)
@@ -543,7 +546,7 @@ def build_tables(pool: Pool, res: Reservation, page_size: int, quant_block: int,
     nf = [0] * B if n_fixed is None else list(n_fixed)
     work, part_off, gitems = plan(res, chunk_bf, chunk_i8, lpt, group_size, page_size, quant_block,
                                   nf, paths, node_len, old_bits,
-                                  live if gen_tokens > 0 else None)
+                                  live if gen_tokens > 0 else None, chunk_group)
     t = Tables(bt, stride, lens, work, part_off, pages)
     t.gitems = gitems
     t.ring = [[len(pages[r][c][TIER_BF]) for c in range(C)] for r in range(B)]

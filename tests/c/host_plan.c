@@ -55,7 +55,7 @@ int main(void) {
   CHECK(same(n_bf, want_budget, B * H) && same(n_i8, want_zero, B * H));
   CHECK(same(coh, want_coh, H) && same(sic, want_sic, H) && same(csize, want_csize, C));
 
-  const tg_plan_opts opts = {32, 64, 0, 0, 0};
+  const tg_plan_opts opts = {32, 64, 0, 0, 0, 0};
   tg_table_sizes sz;
   CHECK(tg_size_tables(&res, 16, 64, NULL, &opts, &sz) == TG_OK);
   CHECK(sz.n_items == 5 && sz.n_gitems == 0 && sz.n_slots == 5);

@@ -59,20 +59,22 @@ def _gitems_of(t_o):
     return np.array(t_o.gitems, dtype=np.int32).reshape(-1, 32, 2)
 
 
-def _tables_parity(w, chunk_bf=512, chunk_i8=1024, lpt=True, slack=3, group_size=0, gen=0):
+def _tables_parity(w, chunk_bf=512, chunk_i8=1024, lpt=True, slack=3, group_size=0, gen=0, chunk_group=0):
     res_o, res_g = _both(w)
     _compare_reservation(res_o, res_g)
     share, sh_o = _share(w)
     need_bf, need_i8 = P.pages_needed(P.capacity(res_o, gen), w.page_size, w.quant_block, *sh_o)
-    sizes = tg.tg_size_tables(res_g, w.page_size, w.quant_block, share, chunk_bf, chunk_i8, lpt, group_size, gen)
+    sizes = tg.tg_size_tables(res_g, w.page_size, w.quant_block, share, chunk_bf, chunk_i8, lpt, group_size, gen,
+                              chunk_group)
     assert [row[1] for row in sizes["pages_needed"]] == need_bf
     assert [row[0] for row in sizes["pages_needed"]] == need_i8
     pool_g = tg.Pool(res_g.cluster_size, w.d, w.page_size, w.quant_block,
                      [x + slack for x in need_bf], [x + slack for x in need_i8], old_bits=w.old_bits)
     pool_o = P.Pool([x + slack for x in need_bf], [x + slack for x in need_i8])
-    t_g = tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt, group_size, gen)
+    t_g = tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt, group_size, gen, chunk_group)
     t_o = P.build_tables(pool_o, res_o, w.page_size, w.quant_block, chunk_bf, chunk_i8, lpt, *sh_o,
-                         **({"group_size": group_size} if sh_o else {"gen_tokens": gen}), old_bits=w.old_bits)
+                         **({"group_size": group_size} if sh_o else {"gen_tokens": gen}), old_bits=w.old_bits,
+                         chunk_group=chunk_group)
     for c in range(w.n_clusters):
         for t in range(2):
             assert t_g.stride[c][t] == t_o.stride[c][t]
@@ -110,6 +112,16 @@ def test_full_size_configs_bit_exact(name, gs):
             cap = pool_g.capacity(c, t)
             for pid in range(0, cap, max(1, cap // 97)):
                 assert pool_g.refcount(c, t, pid) == pool_o.refcount(c, t, pid)
+
+
+@pytest.mark.parametrize("chunk_bf,chunk_group", [(256, 1008), (128, 0), (768, 512)])
+def test_radix_group_chunk_bit_exact(chunk_bf, chunk_group):
+    """Group items cut with their own length (chunk_group) while the
+    requests' own items use chunk_bf, at full radix size."""
+    w = make_workload("radix")
+    res_o, res_g, pool_o, pool_g, t_o, t_g = _tables_parity(w, chunk_bf=chunk_bf, group_size=32,
+                                                           chunk_group=chunk_group)
+    assert t_g.n_gitems > 0
 
 
 def test_release_and_reallocation_bit_exact():
@@ -166,6 +178,7 @@ def test_randomised_small_cases_bit_exact():
         chunk_i8 = qb * rnd.randint(1, 3)
         lpt = rnd.random() < 0.5
         gs = rnd.choice([0, 1, 2, 3, 16, 32])
+        cg = ps * rnd.randint(1, 8) if rnd.random() < 0.5 else 0
         gen = 0 if use_share else rnd.choice([0, 0, 1, 70, 300])
         grp = {"group_size": gs} if use_share else {"gen_tokens": gen}
         need_bf, need_i8 = P.pages_needed(P.capacity(res_o, gen), ps, qb, *sh_o)
@@ -177,17 +190,18 @@ def test_randomised_small_cases_bit_exact():
         pool_g = tg.Pool(res_g.cluster_size, 16, ps, qb, cap_bf, cap_i8, old_bits=bits)
         pool_o = P.Pool(cap_bf, cap_i8)
         try:
-            t_o = P.build_tables(pool_o, res_o, ps, qb, chunk_bf, chunk_i8, lpt, *sh_o, **grp, old_bits=bits)
+            t_o = P.build_tables(pool_o, res_o, ps, qb, chunk_bf, chunk_i8, lpt, *sh_o, **grp, old_bits=bits,
+                                 chunk_group=cg)
         except P.OracleError as e:
             assert e.code == "ENOMEM"
             with pytest.raises(tg.TGError) as ge:
-                tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt, gs, gen)
+                tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt, gs, gen, cg)
             assert ge.value.name == "TG_ENOMEM"
             for c in range(C):
                 for t in range(2):
                     assert pool_g.free_pages(c, t) == pool_g.capacity(c, t)
             continue
-        t_g = tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt, gs, gen)
+        t_g = tg.tg_build_tables(pool_g, res_g, share, chunk_bf, chunk_i8, lpt, gs, gen, cg)
         assert np.array_equal(t_g.ring, np.array(t_o.ring, dtype=np.int32)), case
         for c in range(C):
             for t in range(2):

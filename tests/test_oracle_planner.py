@@ -528,3 +528,35 @@ def test_growth_tables_cover_capacity_and_keep_live_lengths():
     with pytest.raises(P.OracleError):
         P.build_tables(P.Pool([100], [0]), res, w.page_size, w.quant_block, 256, 512, True,
                        [0, 0], [[0], [0]], [0], gen_tokens=T)
+
+
+def test_hand_worked_group_chunk():
+    """Group items cut with their own length (chunk_group), worked by hand.
+    Three requests share one radix node of 40 rows (pages of 4 rows: one run
+    of 10 shared pages per request), H = 1, own rows 5, 9 and 3; groups of 2.
+    chunk_group 16 rows = 4 pages: k = ceil(10 / 4) = 3 items per group,
+    starting at pages floor(i * 10 / 3) = 0, 3, 6, i.e. rows [0,12) [12,24)
+    [24,40); groups {0, 1} then {2}.  Own items with chunk_bf 8 rows = 2
+    pages: r0 rows 40..45 (2 pages, 1 item), r1 40..49 (3 pages: 2 items
+    starting at pages 0 and floor(3/2) = 1, i.e. 40..44, 44..49), r2 40..43.
+    Slots per request: its three memberships, then its own items."""
+    n_comp = [5, 9, 3]
+    res = P.reserve([0], 1_000_000, 1_000_000, 1, 1_000_000, 8, n_comp, [40, 40, 40], None)
+    pool = P.Pool([60], [0])
+    t = P.build_tables(pool, res, 4, 8, 8, 8, False, [40, 40, 40], [[0], [0], [0]], [40], group_size=2,
+                       chunk_group=16)
+    assert [list(w) for w in t.work] == [
+        [-1, 0, 1, 0, 12, -1], [-2, 0, 1, 12, 24, -1], [-3, 0, 1, 24, 40, -1],
+        [-4, 0, 1, 0, 12, -1], [-5, 0, 1, 12, 24, -1], [-6, 0, 1, 24, 40, -1],
+        [0, 0, 1, 40, 45, 3], [1, 0, 1, 40, 44, 7], [1, 0, 1, 44, 49, 8], [2, 0, 1, 40, 43, 12]]
+    assert t.part_off == [0, 4, 9, 13]
+    pad = [(-1, -1)] * 30
+    assert t.gitems == [[(0, 0), (1, 4)] + pad, [(0, 1), (1, 5)] + pad, [(0, 2), (1, 6)] + pad,
+                        [(2, 9)] + [(-1, -1)] * 31, [(2, 10)] + [(-1, -1)] * 31, [(2, 11)] + [(-1, -1)] * 31]
+    # chunk_group 0 takes chunk_bf for the group items too: 5 items per group
+    pool2 = P.Pool([60], [0])
+    t2 = P.build_tables(pool2, res, 4, 8, 8, 8, False, [40, 40, 40], [[0], [0], [0]], [40], group_size=2)
+    assert [tuple(w[3:5]) for w in t2.work if w[0] < 0][:5] == [(0, 8), (8, 16), (16, 24), (24, 32), (32, 40)]
+    with pytest.raises(P.OracleError):
+        P.build_tables(P.Pool([60], [0]), res, 4, 8, 8, 8, False, [40, 40, 40], [[0], [0], [0]], [40],
+                       group_size=2, chunk_group=6)
