@@ -51,13 +51,14 @@ class Prepared:
 
     def __init__(self, w, chunk_bf: int = 1024, chunk_i8: int = 1024, lpt: bool = True,
                  slack_pages: int = 0, shift_pages: int = 0, device: str = "cuda",
-                 group_size: Optional[int] = None, gen_tokens: int = 0):
+                 group_size: Optional[int] = None, gen_tokens: int = 0, chunk_group: int = 0):
         """``group_size`` None: group shared-prefix pages for as many requests
         as a workgroup's four wavefronts score at once (two 16-column tiles
         each: 128 / G, at most 32) when the batch shares a radix prefix, else
         no groups.  ``gen_tokens`` > 0 reserves room for that
         many appended rows per (r, h) and stages them (the continuation of
-        each sequence) on the device for ``append``."""
+        each sequence) on the device for ``append``.  ``chunk_group`` cuts
+        group items with their own length (0: chunk_bf)."""
         import torch
 
         self.w = w
@@ -69,8 +70,9 @@ class Prepared:
             group_size = min(128 // G, api.TG_GROUP_WIDTH) if self.share is not None else 0
         self.group_size = group_size
         self.gen_tokens = gen_tokens
+        self.chunk_group = chunk_group
         sizes = api.tg_size_tables(self.res, w.page_size, w.quant_block, self.share, chunk_bf, chunk_i8, lpt,
-                                   group_size, gen_tokens)
+                                   group_size, gen_tokens, chunk_group)
         need = sizes["pages_needed"]
         C = self.res.C
         extra = slack_pages + shift_pages
@@ -87,7 +89,7 @@ class Prepared:
                 fillers.append(api.tg_build_tables(self.pool, filler, None, w.page_size * 4, w.quant_block * 4,
                                                    False))
         self.tables = api.tg_build_tables(self.pool, self.res, self.share, chunk_bf, chunk_i8, lpt, group_size,
-                                          gen_tokens)
+                                          gen_tokens, chunk_group)
         self.chunks = (chunk_bf, chunk_i8)
         for ftab in fillers:
             api.tg_release(self.pool, ftab, 0)
@@ -132,7 +134,7 @@ class Prepared:
                         [self.pool.capacity(c, api.TG_TIER_BF16) for c in range(C)],
                         [self.pool.capacity(c, api.TG_TIER_I8) for c in range(C)], getattr(w, "old_bits", 8))
         t = api.tg_build_tables(pool, self.res, self.share, chunk_bf, chunk_i8, lpt, self.group_size,
-                                self.gen_tokens)
+                                self.gen_tokens, self.chunk_group)
         for c in range(C):
             for tier in range(2):
                 if not np.array_equal(t.bt[c][tier], self.tables.bt[c][tier]):
