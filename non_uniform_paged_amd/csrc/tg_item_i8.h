@@ -34,7 +34,10 @@
 // (64g + l)*4 + s, nibble ((e&1)<<2) | (e>>1); V codes (at +32d) of lane l
 // (channel l%16 of tile n, rows 16g + 4(l/16) + i) are word (64g + l)*4 + n/2,
 // nibble ((i&1)<<2) | ((n&1)<<1) | (i>>1); scales at +64d (K) and +66d (V).
-// Five bit operations turn a word of 8 codes into four fp16 operand words.
+// A word of 8 codes becomes four fp16 operand words with one and-or each
+// (and a shift per K word, one per two V words): K as 24 + q4, V as 1032 + q4
+// or 72 + q4 by word.  q' goes in as two fp16 parts packed into one score
+// tile (columns g and g + 8); the weights P as one fp16 part.
 
 #include <cmath>
 
