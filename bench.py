@@ -34,6 +34,11 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+# device pool layouts (include/tg.h), as (INT8 pools, bf16 pools) head-major
+# flags; "auto" is the runner's measured choice (bf16 pools head-major when
+# the cache has no quantised tier, all else page-major)
+LAYOUTS = {"auto": None, "page-major": (False, False), "head-major": (True, True),
+           "bf16-head-major": (False, True)}
 METRIC = "effective KV GB/s (and % of HBM peak) in ragged-paged decode attention"
 DESCRIPTIONS = {
     "tiny": "tiny: 2 requests, 4/2 heads, d 64, ctx 256, budgets in {32..256}, 2 clusters",
@@ -133,7 +138,8 @@ def append_bench(w, args, evict, stream):
     from non_uniform_paged_amd.runner import Prepared
 
     K = args.append_steps
-    gp = Prepared(w, chunk_bf=args.chunk_bf, chunk_i8=args.chunk_i8, gen_tokens=K)
+    gp = Prepared(w, chunk_bf=args.chunk_bf, chunk_i8=args.chunk_i8, gen_tokens=K,
+                  head_major=LAYOUTS[args.layout])
     lens0 = gp.live_lengths().copy()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     for k in range(K):
@@ -168,6 +174,13 @@ def append_bench(w, args, evict, stream):
     del gp
     torch.cuda.empty_cache()
     return out
+
+
+def _layout_name(prep) -> str:
+    """Layout of the prepared cache's pools, by tier."""
+    hm = prep.cache.head_major
+    return {(False, False): "page-major", (True, True): "head-major",
+            (False, True): "bf16-head-major", (True, False): "int8-head-major"}[hm]
 
 
 def host_tier_bench(prep, args, stream, resident_ms):
@@ -394,7 +407,8 @@ def measure(name, args, evict, stream, read_gbps=None, headline=False):
     chunk_bf = args.chunk_bf if (headline and args.chunk_bf) else PLAN_CHUNKS[name][0]
     chunk_i8 = args.chunk_i8 if (headline and args.chunk_i8) else PLAN_CHUNKS[name][1]
     t_prep = time.perf_counter()
-    prep = Prepared(w, chunk_bf=chunk_bf, chunk_i8=chunk_i8, group_size=args.group_size if headline else None)
+    prep = Prepared(w, chunk_bf=chunk_bf, chunk_i8=chunk_i8, group_size=args.group_size if headline else None,
+                    head_major=LAYOUTS[args.layout])
     t_prep = time.perf_counter() - t_prep
     G = w.Hq // w.Hkv
     tuned = None
@@ -461,7 +475,8 @@ def measure(name, args, evict, stream, read_gbps=None, headline=False):
         "name": name,
         "workload": DESCRIPTIONS[name],
         "config": {"batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.d, "clusters": w.n_clusters,
-                   "page": w.page_size, "chunk_bf": chunk_bf, "chunk_i8": chunk_i8,
+                   "page": w.page_size, "pool_layout": _layout_name(prep), "chunk_bf": chunk_bf,
+                   "chunk_i8": chunk_i8,
                    "plan_items": prep.tables.n_items, "group_items": prep.tables.n_gitems,
                    "group_size": prep.group_size, "slots": prep.tables.n_slots,
                    "retained_head_rows": tr["head_rows"],
@@ -528,6 +543,8 @@ def main():
     ap.add_argument("--chunk-bf", type=int, default=None, help="bf16 rows per plan item (default per workload)")
     ap.add_argument("--chunk-i8", type=int, default=None, help="INT8 rows per plan item (default per workload)")
     ap.add_argument("--flush", choices=["read", "write", "none"], default="read")
+    ap.add_argument("--layout", choices=sorted(LAYOUTS), default="auto",
+                    help="device pool layout (include/tg.h); outputs are identical")
     ap.add_argument("--append-steps", type=int, default=128,
                     help="decode steps with tg_append_kv timed on a second cache built for growth (0: skip)")
     ap.add_argument("--host-steps", type=int, default=10,

@@ -332,7 +332,23 @@ typedef struct tg_cache {
                                                 (zero at admission; updated by tg_append_kv) */
   int32_t recent_ppm;                        /* tier rule of the reservation (tg_append_kv) */
   int32_t old_bits;                          /* slow-tier codes: 8 (0 = 8) or 4 (d = 128 only) */
+  int32_t head_major[TG_MAX_CLUSTERS][2];   /* layout of pool (c, t), see below: 0 page-major,
+                                                1 head-major (0 for an INT8 pool in host memory) */
 } tg_cache;
+
+/* Pool layouts.  A page of cluster c holds one slot of head_bytes (the page
+ * layouts above) for each of the n_c heads of the cluster, so page_bytes =
+ * n_c * head_bytes and a pool of n_pages pages has n_pages * page_bytes bytes
+ * either way; the layout only decides where the slots sit:
+ *   page-major (0): page p, slot s at p * page_bytes + s * head_bytes (a
+ *                   page is contiguous);
+ *   head-major (1): slot s, page p at (s * n_pages + p) * head_bytes (the
+ *                   pages of one head slot are contiguous: a sequence's
+ *                   pages, allocated in order, read as one run per head).
+ * Page ids, tables and plans are the same for both, and so is every output
+ * bit.  tg_write_kv, tg_append_kv and tg_decode_* follow the flag of each
+ * pool; tg_decode_streamed requires page-major INT8 pools (it copies whole
+ * pages) and returns TG_EUNSUPPORTED otherwise. */
 
 /* ------------------------------------------------------------------------
  * Cache fill  (device)

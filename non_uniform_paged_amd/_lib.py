@@ -79,7 +79,8 @@ class Cache(ctypes.Structure):
                 ("stride", (c_int32 * 2) * TG_MAX_CLUSTERS),
                 ("cluster_of_head", c_void_p), ("slot_in_cluster", c_void_p), ("len", c_void_p),
                 ("n_fixed", c_void_p), ("ring", c_void_p), ("bf_base", c_void_p), ("recent_ppm", c_int32),
-                ("old_bits", c_int32)]
+                ("old_bits", c_int32),
+                ("head_major", (c_int32 * 2) * TG_MAX_CLUSTERS)]
 
 
 class DecodeArgs(ctypes.Structure):

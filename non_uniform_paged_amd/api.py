@@ -95,6 +95,7 @@ class Pool:
                  pages_bf: Sequence[int], pages_i8: Sequence[int], old_bits: int = 8):
         cs = _i32(cluster_size)
         self.C = int(cs.size)
+        self.cluster_size = cs.copy()
         self.head_dim, self.page_size, self.quant_block = int(head_dim), int(page_size), int(quant_block)
         self.old_bits = int(old_bits)
         pb = np.ascontiguousarray(pages_bf, dtype=np.int64)
@@ -246,12 +247,17 @@ def _ptr(t) -> Optional[int]:
 
 class DeviceCache:
     """Device memory of one populated cache: the (cluster, tier) pools sized
-    from ``pool`` and the uploaded tables, plus the ``tg_cache`` view."""
+    from ``pool`` and the uploaded tables, plus the ``tg_cache`` view.
+    ``head_major``: pools head-major (each head slot's pages contiguous)
+    instead of page-major, for every pool (a bool) or by tier (a pair: INT8
+    pools, bf16 pools); the same bytes, pages and outputs either way."""
 
     def __init__(self, pool: Pool, res: Reservation, tables: Tables, device="cuda",
-                 share: Optional[Share] = None):
+                 share: Optional[Share] = None, head_major=False):
         torch = _torch()
         self.device = torch.device(device)
+        hm = tuple(head_major) if isinstance(head_major, (tuple, list)) else (head_major, head_major)
+        self.head_major = (bool(hm[0]), bool(hm[1]))
         self.G_hint = None
         C = res.C
         self.pools = [[None, None] for _ in range(C)]
@@ -270,6 +276,7 @@ class DeviceCache:
                 c_s.pool[c][t] = _ptr(self.pools[c][t])
                 c_s.page_bytes[c][t] = pb
                 c_s.n_pages[c][t] = cap
+                c_s.head_major[c][t] = int(self.head_major[t])
                 c_s.bt[c][t] = _ptr(self.bt[c][t])
                 c_s.stride[c][t] = tables.stride[c][t]
         self.cluster_of_head = torch.from_numpy(res.cluster_of_head).to(self.device)
@@ -301,6 +308,14 @@ class DeviceCache:
         c_s.old_bits = pool.old_bits
         self.struct = c_s
         self.B, self.H, self.d = res.B, res.H, pool.head_dim
+
+    def slot_offset(self, c: int, t: int, page: int, slot: int, pool: "Pool") -> int:
+        """Byte offset of head slot ``slot`` of page ``page`` in pool (c, t)."""
+        pb, cap = pool.page_bytes(c, t), pool.capacity(c, t)
+        hb = pb // int(pool.cluster_size[c])
+        if self.struct.head_major[c][t]:
+            return (slot * cap + page) * hb
+        return page * pb + slot * hb
 
     def pool_bytes(self) -> int:
         return sum(int(p.numel()) for row in self.pools for p in row if p is not None)

@@ -213,12 +213,17 @@ int make_split_args(const tg_cache* c, const tg_decode_args* a, bool merge, Spli
   if (c->ring != nullptr && c->bf_base == nullptr) return TG_EINVAL;
   if (c->old_bits != 0 && c->old_bits != 8 && c->old_bits != 4) return TG_EINVAL;
   if (c->old_bits == 4 && d != 128) return TG_EUNSUPPORTED;
+  if (!layout_flags_valid(c)) return TG_EINVAL;
   SplitArgs& s = *out;
   s = SplitArgs{};
   for (int32_t cl = 0; cl < c->n_clusters; ++cl)
     for (int t = 0; t < 2; ++t) {
+      int64_t page_stride = 0, head_stride = 0;
+      pool_strides(c, cl, t, &page_stride, &head_stride);
+      if (c->stride[cl][t] > 0 && c->page_bytes[cl][t] % head_slot_bytes(c, t)) return TG_EINVAL;
       s.pool[cl][t] = (gptr)(c->pool[cl][t]);
-      s.page_bytes[cl][t] = static_cast<int32_t>(c->page_bytes[cl][t]);
+      s.page_bytes[cl][t] = static_cast<int32_t>(page_stride);
+      s.head_stride[cl][t] = head_stride;
       s.bt[cl][t] = (const TG_GLOBAL int32_t*)(c->bt[cl][t]);
       s.stride[cl][t] = c->stride[cl][t];
     }
@@ -334,6 +339,8 @@ extern "C" int tg_decode_streamed(const tg_cache* c, const tg_tables* t, const t
   if (code) return code;
   if (!t || !chunk_off || !staging) return TG_EINVAL;
   const int32_t B = c->B, d = c->head_dim;
+  for (int32_t cl = 0; cl < c->n_clusters; ++cl)
+    if (c->head_major[cl][TG_TIER_I8]) return TG_EUNSUPPORTED;  // staged pages are copied whole
   if (chunk_off[0] < 0 || chunk_off[B] != a->n_items) return TG_EINVAL;
   for (int32_t r = 0; r < B; ++r)
     if (chunk_off[r + 1] < chunk_off[r]) return TG_EINVAL;

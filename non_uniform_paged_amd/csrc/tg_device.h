@@ -8,6 +8,7 @@
 #include <cstdint>
 
 #include "tg.h"
+#include "tg_layout.h"
 
 // Every device pointer the kernels touch is kept in the global address space:
 // pointers read from a struct are otherwise generic, and flat loads also count
@@ -32,7 +33,8 @@ constexpr float kSlack = 8.f;
 
 struct SplitArgs {
   gptr pool[TG_MAX_CLUSTERS][2];
-  int32_t page_bytes[TG_MAX_CLUSTERS][2];  // < 2^31 (checked on the host)
+  int32_t page_bytes[TG_MAX_CLUSTERS][2];  // between page ids; < 2^31 (checked on the host)
+  int64_t head_stride[TG_MAX_CLUSTERS][2];  // between the head slots of one page
   const TG_GLOBAL int32_t* bt[TG_MAX_CLUSTERS][2];
   int32_t stride[TG_MAX_CLUSTERS][2];
   const TG_GLOBAL int32_t* cluster_of_head;

@@ -270,7 +270,7 @@ __device__ __forceinline__ void write_partials(const SplitArgs& a, const int (&c
 // pages form a ring: logical page p is table entry (ring_base + p) mod ring_pg.
 template <int D, int G, bool QF32, int DEPTH, bool STREAM>
 __device__ __forceinline__ void bf16_item(const SplitArgs& a, int r, int h, int t0, int t1, int slot,
-                                          const TG_GLOBAL int32_t* gm, int mbase, int hs,
+                                          const TG_GLOBAL int32_t* gm, int mbase, int64_t head_off,
                                           const TG_GLOBAL int32_t* bt_row, int ring_base, int ring_pg,
                                           gptr pool, int64_t pbytes) {
   constexpr int NK = D / 32;           // 1 KiB loads per K (and per V) block
@@ -285,7 +285,6 @@ __device__ __forceinline__ void bf16_item(const SplitArgs& a, int r, int h, int 
   u32x4_t qop[1][NQ][NK];
   load_qop<D, G, QF32, 1>(a, h, col_r, col_slot, qop);
 
-  const int64_t head_off = static_cast<int64_t>(hs) * (4 * kPage * D);
   const int lane_off = lane * 16;
   f32x4_t acc[1][NT];
 #pragma unroll
@@ -395,7 +394,7 @@ __device__ __forceinline__ void bf16_group_coop(const SplitArgs& a, const TG_GLO
   const TG_GLOBAL int32_t* bt_row = a.bt[cl][TG_TIER_BF16] + static_cast<int64_t>(r0) * a.stride[cl][TG_TIER_BF16];
   gptr pool = a.pool[cl][TG_TIER_BF16];
   const int64_t pbytes = a.page_bytes[cl][TG_TIER_BF16];
-  const int64_t head_off = static_cast<int64_t>(hs) * PAGE;
+  const int64_t head_off = static_cast<int64_t>(hs) * a.head_stride[cl][TG_TIER_BF16];
   const int p0 = t0 / kPage;
   const int np = (t1 - t0 + kPage - 1) / kPage;
 
@@ -487,6 +486,7 @@ __device__ __forceinline__ void bf16_dispatch(const SplitArgs& a, const TG_GLOBA
   }
   const int cl = uniform(a.cluster_of_head[h]);
   const int hs = uniform(a.slot_in_cluster[h]);
+  const int64_t head_off = static_cast<int64_t>(hs) * a.head_stride[cl][TG_TIER_BF16];
   const int rh = r * a.n_kv_heads + h;
   int t1c = t1;
   if (gm == nullptr) {
@@ -508,7 +508,7 @@ __device__ __forceinline__ void bf16_dispatch(const SplitArgs& a, const TG_GLOBA
   if (gm != nullptr) {
     for (int mbase = 0; mbase < TG_GROUP_WIDTH; mbase += 16 / G) {
       if (uniform(gm[2 * mbase]) < 0) break;
-      bf16_item<D, G, QF32, DEPTH, false>(a, r, h, t0, t1c, -1, gm, mbase, hs, bt_row, ring_base, ring_pg, pool,
+      bf16_item<D, G, QF32, DEPTH, false>(a, r, h, t0, t1c, -1, gm, mbase, head_off, bt_row, ring_base, ring_pg, pool,
                                           pbytes);
     }
     return;
@@ -520,10 +520,10 @@ __device__ __forceinline__ void bf16_dispatch(const SplitArgs& a, const TG_GLOBA
     shared = n_i8 + t0 + kPage <= uniform(a.n_fixed[r]);
   }
   if (shared)
-    bf16_item<D, G, QF32, DEPTH, false>(a, r, h, t0, t1c, slot, nullptr, 0, hs, bt_row, ring_base, ring_pg, pool,
+    bf16_item<D, G, QF32, DEPTH, false>(a, r, h, t0, t1c, slot, nullptr, 0, head_off, bt_row, ring_base, ring_pg, pool,
                                         pbytes);
   else
-    bf16_item<D, G, QF32, DEPTH, true>(a, r, h, t0, t1c, slot, nullptr, 0, hs, bt_row, ring_base, ring_pg, pool,
+    bf16_item<D, G, QF32, DEPTH, true>(a, r, h, t0, t1c, slot, nullptr, 0, head_off, bt_row, ring_base, ring_pg, pool,
                                        pbytes);
 }
 

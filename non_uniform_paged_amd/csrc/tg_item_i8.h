@@ -110,7 +110,7 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
 // tiles carry the same offsets, and the rest is unchanged.
 template <int D, int G, bool QF32, int DEPTH, bool STREAM, int BITS>
 __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0, int t1, int slot,
-                                        int hs, const TG_GLOBAL int32_t* bt_row, gptr pool,
+                                        int64_t head_off, const TG_GLOBAL int32_t* bt_row, gptr pool,
                                         int64_t pbytes, float* lds) {
   static_assert(BITS == 8 || (BITS == 4 && D == 128), "INT4 pages are laid out for d = 128");
   constexpr int NL = BITS == 8 ? D / 64 : 1;  // 1 KiB loads per 16-row group (K codes, V codes)
@@ -176,7 +176,6 @@ __device__ __forceinline__ void i8_item(const SplitArgs& a, int r, int h, int t0
   for (int k = 0; k < NT * 4; ++k) lds[k * 64 + lane] = 0.f;
   float m_ref = -INFINITY;
   float l_run = 0.f;
-  const int64_t head_off = static_cast<int64_t>(hs) * (2 * CODE_BYTES + 4 * D);
   const int lane_off = lane * 16;
   // constant-offset operands: 1152 for every INT8 value; for INT4 the offsets
   // of the operand words (K: words 0-3 of a step; V: the two words of a tile)
@@ -465,6 +464,7 @@ __device__ __forceinline__ void i8_dispatch(const SplitArgs& a, const TG_GLOBAL 
   }
   const int cl = uniform(a.cluster_of_head[h]);
   const int hs = uniform(a.slot_in_cluster[h]);
+  const int64_t head_off = static_cast<int64_t>(hs) * a.head_stride[cl][TG_TIER_I8];
   const TG_GLOBAL int32_t* bt_row =
       a.bt[cl][TG_TIER_I8] != nullptr ? a.bt[cl][TG_TIER_I8] + static_cast<int64_t>(r) * a.stride[cl][TG_TIER_I8]
                                       : nullptr;
@@ -473,9 +473,9 @@ __device__ __forceinline__ void i8_dispatch(const SplitArgs& a, const TG_GLOBAL 
   bool shared = false;  // an item that starts on the shared radix path reads through the caches
   if (a.n_fixed) shared = t0 + kQBlock <= uniform(a.n_fixed[r]);
   if (shared)
-    i8_item<D, G, QF32, DEPTH, false, BITS>(a, r, h, t0, t1, slot, hs, bt_row, pool, pbytes, lds);
+    i8_item<D, G, QF32, DEPTH, false, BITS>(a, r, h, t0, t1, slot, head_off, bt_row, pool, pbytes, lds);
   else
-    i8_item<D, G, QF32, DEPTH, true, BITS>(a, r, h, t0, t1, slot, hs, bt_row, pool, pbytes, lds);
+    i8_item<D, G, QF32, DEPTH, true, BITS>(a, r, h, t0, t1, slot, head_off, bt_row, pool, pbytes, lds);
 }
 
 }  // namespace tg_dev

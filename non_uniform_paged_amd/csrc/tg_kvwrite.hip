@@ -16,6 +16,7 @@
 #include <cstdint>
 
 #include "tg.h"
+#include "tg_layout.h"
 
 namespace {
 
@@ -24,7 +25,8 @@ constexpr int kQBlock = 64;
 
 struct WriteArgs {
   char* pool[TG_MAX_CLUSTERS][2];
-  int64_t page_bytes[TG_MAX_CLUSTERS][2];
+  int64_t page_bytes[TG_MAX_CLUSTERS][2];   // between page ids
+  int64_t head_stride[TG_MAX_CLUSTERS][2];  // between the head slots of a page
   const int32_t* bt[TG_MAX_CLUSTERS][2];
   int32_t stride[TG_MAX_CLUSTERS][2];
   const int32_t* cluster_of_head;
@@ -52,7 +54,7 @@ __device__ __forceinline__ void write_bf16_rows(const WriteArgs& a, int rh) {
   const uint16_t* src = a.rows + src_row * 2 * D + 8 * c8;
   const int pid = a.bt[cl][TG_TIER_BF16][static_cast<int64_t>(r) * a.stride[cl][TG_TIER_BF16] + u / kPage];
   char* head = a.pool[cl][TG_TIER_BF16] + static_cast<int64_t>(pid) * a.page_bytes[cl][TG_TIER_BF16] +
-               static_cast<int64_t>(hs) * (4 * kPage * D);
+               static_cast<int64_t>(hs) * a.head_stride[cl][TG_TIER_BF16];
   const int t = u % kPage;
   // K: channels 8c8..8c8+7 of row t are one contiguous 16-byte group
   *reinterpret_cast<uint4*>(head + (((c8 >> 2) * 64 + (c8 & 3) * 16 + t) * 16)) =
@@ -93,7 +95,7 @@ __device__ __forceinline__ void write_i8_block(const WriteArgs& a, int rh) {
   const float sf = static_cast<float>(s16);
   const int pid = a.bt[cl][TG_TIER_I8][static_cast<int64_t>(r) * a.stride[cl][TG_TIER_I8] + b];
   char* head = a.pool[cl][TG_TIER_I8] + static_cast<int64_t>(pid) * a.page_bytes[cl][TG_TIER_I8] +
-               static_cast<int64_t>(hs) * (2 * kQBlock * D + 4 * D);
+               static_cast<int64_t>(hs) * a.head_stride[cl][TG_TIER_I8];
   int8_t* codes = reinterpret_cast<int8_t*>(head + kv * kQBlock * D);
   constexpr int NL = D / 64;
   for (int t = 0; t < kQBlock; ++t) {
@@ -168,7 +170,7 @@ __device__ __forceinline__ void write_i4_block(const WriteArgs& a, int rh, int8_
   }
   const int pid = a.bt[cl][TG_TIER_I8][static_cast<int64_t>(r) * a.stride[cl][TG_TIER_I8] + b];
   char* head = a.pool[cl][TG_TIER_I8] + static_cast<int64_t>(pid) * a.page_bytes[cl][TG_TIER_I8] +
-               static_cast<int64_t>(hs) * (kQBlock * D + 4 * D);
+               static_cast<int64_t>(hs) * a.head_stride[cl][TG_TIER_I8];
   reinterpret_cast<_Float16*>(head + kQBlock * D + kv * D * 2)[ch] = s16;
   __syncthreads();
   store_i4_words<D>(codes, head);
@@ -185,7 +187,8 @@ __global__ __launch_bounds__(2 * D) void write_i4_kernel(WriteArgs a) {
 // ---------------------------------------------------------------- decode-step append
 struct AppendArgs {
   char* pool[TG_MAX_CLUSTERS][2];
-  int64_t page_bytes[TG_MAX_CLUSTERS][2];
+  int64_t page_bytes[TG_MAX_CLUSTERS][2];   // between page ids
+  int64_t head_stride[TG_MAX_CLUSTERS][2];  // between the head slots of a page
   const int32_t* bt[TG_MAX_CLUSTERS][2];
   int32_t stride[TG_MAX_CLUSTERS][2];
   const int32_t* cluster_of_head;
@@ -249,7 +252,7 @@ __global__ __launch_bounds__(2 * D) void append_kernel(AppendArgs a) {
   auto bf_head = [&](int ring_row) {
     const int pid = bt_bf[ring_row / kPage];
     return a.pool[cl][TG_TIER_BF16] + static_cast<int64_t>(pid) * a.page_bytes[cl][TG_TIER_BF16] +
-           static_cast<int64_t>(hs) * (4 * kPage * D);
+           static_cast<int64_t>(hs) * a.head_stride[cl][TG_TIER_BF16];
   };
   {
     const int pos = (base + n_bf) % ring_rows;
@@ -274,7 +277,7 @@ __global__ __launch_bounds__(2 * D) void append_kernel(AppendArgs a) {
   if (__builtin_isinf(static_cast<float>(s16))) s16 = static_cast<_Float16>(65504.0f);
   const float sf = static_cast<float>(s16);
   char* head = a.pool[cl][TG_TIER_I8] + static_cast<int64_t>(bt_i8[blk]) * a.page_bytes[cl][TG_TIER_I8] +
-               static_cast<int64_t>(hs) * (2 * CODE_BYTES + 4 * D);
+               static_cast<int64_t>(hs) * a.head_stride[cl][TG_TIER_I8];
   constexpr int NL = D / 64;
   for (int t = 0; t < kQBlock; ++t) {
     const float x = value(t);
@@ -312,12 +315,14 @@ extern "C" int tg_append_kv(const tg_cache* c, const uint16_t* rows, int32_t* st
   if (c->head_dim != 64 && c->head_dim != 128) return TG_EUNSUPPORTED;
   if (c->page_size != kPage || c->quant_block != kQBlock) return TG_EUNSUPPORTED;
   if (c->recent_ppm < 0 || c->recent_ppm > 1000000) return TG_EINVAL;
+  if (!tg_dev::layout_flags_valid(c)) return TG_EINVAL;
   AppendArgs a{};
   for (int32_t cl = 0; cl < c->n_clusters; ++cl)
     for (int t = 0; t < 2; ++t) {
       if (c->stride[cl][t] > 0 && (!c->bt[cl][t] || !c->pool[cl][t])) return TG_EINVAL;
       a.pool[cl][t] = static_cast<char*>(c->pool[cl][t]);
-      a.page_bytes[cl][t] = c->page_bytes[cl][t];
+      if (c->stride[cl][t] > 0 && c->page_bytes[cl][t] % tg_dev::head_slot_bytes(c, t)) return TG_EINVAL;
+      tg_dev::pool_strides(c, cl, t, &a.page_bytes[cl][t], &a.head_stride[cl][t]);
       a.bt[cl][t] = c->bt[cl][t];
       a.stride[cl][t] = c->stride[cl][t];
     }
@@ -354,13 +359,15 @@ extern "C" int tg_write_kv(const tg_cache* c, const uint16_t* rows, const int32_
     return TG_EINVAL;
   if (c->head_dim != 64 && c->head_dim != 128) return TG_EUNSUPPORTED;
   if (c->page_size != kPage || c->quant_block != kQBlock) return TG_EUNSUPPORTED;
+  if (!tg_dev::layout_flags_valid(c)) return TG_EINVAL;
   WriteArgs a{};
   int32_t max_bf = 0, max_i8 = 0;
   for (int32_t cl = 0; cl < c->n_clusters; ++cl)
     for (int t = 0; t < 2; ++t) {
       if (c->stride[cl][t] > 0 && (!c->bt[cl][t] || !c->pool[cl][t])) return TG_EINVAL;
       a.pool[cl][t] = static_cast<char*>(c->pool[cl][t]);
-      a.page_bytes[cl][t] = c->page_bytes[cl][t];
+      if (c->stride[cl][t] > 0 && c->page_bytes[cl][t] % tg_dev::head_slot_bytes(c, t)) return TG_EINVAL;
+      tg_dev::pool_strides(c, cl, t, &a.page_bytes[cl][t], &a.head_stride[cl][t]);
       a.bt[cl][t] = c->bt[cl][t];
       a.stride[cl][t] = c->stride[cl][t];
       if (t == TG_TIER_BF16) max_bf = c->stride[cl][t] > max_bf ? c->stride[cl][t] : max_bf;

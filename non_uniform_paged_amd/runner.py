@@ -51,14 +51,20 @@ class Prepared:
 
     def __init__(self, w, chunk_bf: int = 1024, chunk_i8: int = 1024, lpt: bool = True,
                  slack_pages: int = 0, shift_pages: int = 0, device: str = "cuda",
-                 group_size: Optional[int] = None, gen_tokens: int = 0, chunk_group: int = 0):
+                 group_size: Optional[int] = None, gen_tokens: int = 0, chunk_group: int = 0,
+                 head_major=None):
         """``group_size`` None: group shared-prefix pages for as many requests
         as a workgroup's four wavefronts score at once (two 16-column tiles
         each: 128 / G, at most 32) when the batch shares a radix prefix, else
         no groups.  ``gen_tokens`` > 0 reserves room for that
         many appended rows per (r, h) and stages them (the continuation of
         each sequence) on the device for ``append``.  ``chunk_group`` cuts
-        group items with their own length (0: chunk_bf)."""
+        group items with their own length (0: chunk_bf).  ``head_major``:
+        pool layout (include/tg.h), a bool for every pool or a pair (INT8
+        pools, bf16 pools); None chooses by measurement: bf16 pools
+        head-major when the cache has no quantised tier (faster there), every
+        other pool page-major (head-major bf16 pools beside a quantised tier
+        measured slower)."""
         import torch
 
         self.w = w
@@ -93,12 +99,11 @@ class Prepared:
         self.chunks = (chunk_bf, chunk_i8)
         for ftab in fillers:
             api.tg_release(self.pool, ftab, 0)
-        self.cache = api.DeviceCache(self.pool, self.res, self.tables, dev, self.share)
+        if head_major is None:
+            head_major = (False, int(self.res.n_i8.max()) == 0)
+        self.cache = api.DeviceCache(self.pool, self.res, self.tables, dev, self.share, head_major)
 
         rows, index, offsets = w.source_buffer(self.res.length + gen_tokens)
-        rows_t = torch.from_numpy(rows.view(np.uint16).reshape(-1).view(np.int16)).to(dev)
-        index_t = torch.from_numpy(index).to(dev)
-        off_t = torch.from_numpy(offsets).to(dev)
         self.appended = None
         if gen_tokens > 0:
             # row L0 + k of every (r, h), step-major: [T][B*H][2][d]
@@ -107,10 +112,8 @@ class Prepared:
             self.appended = torch.from_numpy(rows[src].view(np.int16)).to(dev)
             self.status = torch.zeros(1, dtype=torch.int32, device=dev)
         self.steps_appended = 0
+        self._write(rows, index, offsets)
         del rows
-        api.tg_write_kv(self.cache, rows_t, index_t, off_t)
-        torch.cuda.synchronize(dev)
-        del rows_t, index_t, off_t
 
         qn = w.q()
         if w.q_dtype == "f32":
@@ -120,6 +123,25 @@ class Prepared:
         self.out = torch.empty((w.B, w.Hq, w.d), dtype=torch.float32, device=dev)
         ws = api.tg_decode_workspace_bytes(self.tables.n_slots, G, w.d)
         self.workspace = torch.empty(max(ws // 4, 1), dtype=torch.float32, device=dev)
+
+    def _write(self, rows, index, offsets) -> None:
+        import torch
+        dev = self.cache.device
+        rows_t = torch.from_numpy(rows.view(np.uint16).reshape(-1).view(np.int16)).to(dev)
+        index_t = torch.from_numpy(index).to(dev)
+        off_t = torch.from_numpy(offsets).to(dev)
+        api.tg_write_kv(self.cache, rows_t, index_t, off_t)
+        torch.cuda.synchronize(dev)
+
+    def rewrite_zeroed(self) -> None:
+        """Zero every device pool and write the admitted rows again (bytes no
+        row reaches are then 0 rather than whatever the allocation held)."""
+        for row in self.cache.pools:
+            for pool in row:
+                if pool is not None:
+                    pool.zero_()
+        rows, index, offsets = self.w.source_buffer(self.res.length + self.gen_tokens)
+        self._write(rows, index, offsets)
 
     # ------------------------------------------------------------------ plan
     def replan(self, chunk_bf: int, chunk_i8: int, lpt: bool = True) -> None:
@@ -185,9 +207,10 @@ class Prepared:
 
     # ------------------------------------------------------------------ INT8 tier in host DRAM
     def to_host_i8(self):
-        """Move the INT8 pools to pinned host memory and prepare the streamed
-        decode (its reordered plan on the device and its staging buffer);
-        afterwards only ``step_streamed`` decodes."""
+        """Move the INT8 pools to pinned host memory (page-major: the
+        streamed decode copies whole pages) and prepare the streamed decode
+        (its reordered plan on the device and its staging buffer); afterwards
+        only ``step_streamed`` decodes."""
         import torch
         dev = self.cache.device
         self.host_pools = []
@@ -195,10 +218,14 @@ class Prepared:
             dp = self.cache.pools[c][0]
             if dp is None:
                 continue
+            if self.cache.struct.head_major[c][0]:
+                n_c, cap = int(self.res.cluster_size[c]), self.pool.capacity(c, 0)
+                dp = dp.view(n_c, cap, -1).transpose(0, 1).contiguous().view(-1)
             hp = torch.empty(dp.numel(), dtype=torch.uint8, pin_memory=True)
             hp.copy_(dp)
             self.host_pools.append(hp)
             self.cache.struct.pool[c][0] = hp.data_ptr()
+            self.cache.struct.head_major[c][0] = 0
             self.cache.pools[c][0] = None
         torch.cuda.synchronize(dev)
         work, self.chunk_off = api.tg_stream_order(self.tables)

@@ -196,3 +196,28 @@ def test_noalloc_refuses_oversized_partials_before_any_launch():
     assert lib.tg_decode_attn_noalloc(ctypes.byref(c), ctypes.byref(a), None) == L.TG_EOVERFLOW
     a.n_q_heads = 3  # not a multiple of the KV-heads
     assert lib.tg_decode_attn_noalloc(ctypes.byref(c), ctypes.byref(a), None) == L.TG_EINVAL
+
+
+def test_pool_layout_flags_are_checked():
+    """tg_cache.head_major is 0 or 1 per (cluster, tier); anything else is
+    refused by the decode, cache fill and append calls alike, and a page size
+    that is not a whole number of head slots is refused too."""
+    lib = L.lib()
+    c = _cache()
+    c.cluster_of_head = c.slot_in_cluster = c.len = FAKE.value
+    c.ring = c.bf_base = FAKE.value
+    a = _args(q=FAKE.value, out=FAKE.value, part_off=FAKE.value)
+    for bad in (2, -1):
+        c.head_major[0][1] = bad
+        assert lib.tg_decode_attn(ctypes.byref(c), ctypes.byref(a), None) == L.TG_EINVAL, bad
+        assert lib.tg_write_kv(ctypes.byref(c), FAKE, FAKE, FAKE, None) == L.TG_EINVAL, bad
+        assert lib.tg_append_kv(ctypes.byref(c), FAKE, FAKE, None) == L.TG_EINVAL, bad
+    c.head_major[0][1] = 1
+    # a bf16 page of 1.5 head slots (d 128: 8 KiB a slot)
+    c.stride[0][1] = 4
+    c.bt[0][1] = c.pool[0][1] = FAKE.value
+    c.page_bytes[0][1] = 3 * 4096
+    c.n_pages[0][1] = 8
+    assert lib.tg_decode_attn(ctypes.byref(c), ctypes.byref(a), None) == L.TG_EINVAL
+    assert lib.tg_write_kv(ctypes.byref(c), FAKE, FAKE, FAKE, None) == L.TG_EINVAL
+    assert lib.tg_append_kv(ctypes.byref(c), FAKE, FAKE, None) == L.TG_EINVAL

@@ -105,7 +105,12 @@ def _permute_pages(p, seed):
             cap, pb = p.pool.capacity(c, t), p.pool.page_bytes(c, t)
             perm = g.permutation(cap)  # page j goes to perm[j]
             new = torch.empty_like(pool)
-            new.view(cap, pb)[torch.from_numpy(perm).to(pool.device)] = pool.view(cap, pb)
+            to = torch.from_numpy(perm).to(pool.device)
+            if p.cache.struct.head_major[c][t]:  # [slot][page][head bytes]
+                n_c = int(p.res.cluster_size[c])
+                new.view(n_c, cap, -1)[:, to] = pool.view(n_c, cap, -1)
+            else:  # [page][page bytes]
+                new.view(cap, pb)[to] = pool.view(cap, pb)
             pool.copy_(new)
             del new
             bt = p.tables.bt[c][t]

@@ -52,9 +52,10 @@ def _i8_block(p, r, h, j):
     w = p.w
     d, qb = w.d, w.quant_block
     cl, s = int(p.res.cluster_of_head[h]), int(p.res.slot_in_cluster[h])
-    pb, hb = p.pool.page_bytes(cl, 0), 2 * qb * d + 4 * d
+    hb = 2 * qb * d + 4 * d
     pid = int(p.tables.bt[cl][0][r, j])
-    blk = p.cache.pools[cl][0][pid * pb + s * hb:pid * pb + (s + 1) * hb].cpu().numpy()
+    off = p.cache.slot_offset(cl, 0, pid, s, p.pool)
+    blk = p.cache.pools[cl][0][off:off + hb].cpu().numpy()
     t, c = np.arange(qb)[:, None], np.arange(d)[None, :]
     nl = d // 64
     koff = ((t >> 4) * nl + (c >> 6)) * 1024 + (((c >> 3) & 3) * 16 + (t & 15)) * 16 + ((c >> 5) & 1) * 8 + (c & 7)

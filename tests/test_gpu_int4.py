@@ -45,7 +45,8 @@ def _i4_block(p, r, h, j):
     pb, hb = p.pool.page_bytes(cl, 0), 64 * d + 4 * d
     assert pb == hb * p.res.cluster_size[cl]
     pid = int(p.tables.bt[cl][0][r, j])
-    blk = p.cache.pools[cl][0][pid * pb + s * hb:pid * pb + (s + 1) * hb].cpu().numpy()
+    off = p.cache.slot_offset(cl, 0, pid, s, p.pool)
+    blk = p.cache.pools[cl][0][off:off + hb].cpu().numpy()
     kw = blk[:32 * d].view(np.uint32)
     vw = blk[32 * d:64 * d].view(np.uint32)
     t = np.arange(64)[:, None]

@@ -173,7 +173,6 @@ def _read_i8_pages(p, r, h):
     cl = int(p.res.cluster_of_head[h])
     s = int(p.res.slot_in_cluster[h])
     n8 = int(p.res.n_i8[r, h])
-    pb = p.pool.page_bytes(cl, 0)
     hb = 2 * qb * d + 4 * d
     pool = p.cache.pools[cl][0].cpu().numpy()
     kq, vq, ks, vs = [], [], [], []
@@ -185,7 +184,7 @@ def _read_i8_pages(p, r, h):
     assert sorted(koff.ravel()) == list(range(qb * d)) and sorted(voff.ravel()) == list(range(qb * d))
     for j in range(n8 // qb):
         pid = int(p.tables.bt[cl][0][r, j])
-        base = pid * pb + s * hb
+        base = p.cache.slot_offset(cl, 0, pid, s, p.pool)
         blk = pool[base:base + hb]
         kq.append(blk[:qb * d].view(np.int8)[koff])
         vq.append(blk[qb * d:2 * qb * d].view(np.int8)[voff])
@@ -435,21 +434,27 @@ def test_custom_score_scale(scale):
         _check(p.output(), ref, pairs, w.Hq // w.Hkv, f"scale-{scale}-{w.name}")
 
 
-def test_pages_beyond_4_gib():
+@pytest.mark.parametrize("head_major", [False, True])
+def test_pages_beyond_4_gib(head_major):
     """Pages placed past byte 2^32 of their pools (bf16 and INT8 alike) give
     the same outputs, bit for bit, as the same batch in the lowest pages:
-    page addresses are formed in 64 bits on every path (~13 GB of pools)."""
+    page addresses are formed in 64 bits on every path (~13 GB of pools), in
+    either pool layout (head-major: the second head slot's pages)."""
     _need_gpu()
     w = make_workload("tiered", B=1, Hq=8, Hkv=2, ctx=("fixed", 3000), n_clusters=1)
-    a = _prep(w, chunk_bf=64, chunk_i8=192)
+    a = _prep(w, chunk_bf=64, chunk_i8=192, head_major=head_major)
     a.step()
     ga = a.output()
     del a
     shift = (1 << 32) // (2 * 8192) + 64  # bf16 pages of 2 heads x 8 KiB: past 4 GiB
-    b = _prep(w, chunk_bf=64, chunk_i8=192, shift_pages=shift)
+    b = _prep(w, chunk_bf=64, chunk_i8=192, shift_pages=shift, head_major=head_major)
     for tier in (0, 1):
         bt = b.tables.bt[0][tier]
-        assert int(bt[bt >= 0].min()) * b.pool.page_bytes(0, tier) >= 1 << 32, tier
+        lo = int(bt[bt >= 0].min())
+        if head_major:
+            assert b.cache.slot_offset(0, tier, lo, 1, b.pool) >= 1 << 32, tier
+        else:
+            assert lo * b.pool.page_bytes(0, tier) >= 1 << 32, tier
     b.step()
     assert np.array_equal(ga, b.output())
 
