@@ -122,8 +122,10 @@ int tg_reserve(const tg_budget_table* table, int32_t B, const int32_t* n_comp,
  *
  * Ragged Paging (Tangram page, "Three mechanisms", item 2): one pool per
  * (cluster, tier).  A page of cluster c holds S token slots for each of its
- * n_c heads, S = page_size (bf16) or quant_block (INT8).  Device layout of
- * one page, head slot s = slot_in_cluster at byte offset s * head_bytes:
+ * n_c heads, S = page_size (bf16) or quant_block (INT8).  Each head slot of
+ * a page (s = slot_in_cluster) is head_bytes laid out as below; where the
+ * slots sit in the pool (page-major: s * head_bytes into the page;
+ * head-major: one run of pages per slot) is tg_cache.head_major:
  *   bf16 : K block then V block, 2*S*d bytes each      head_bytes = 4*S*d
  *          (S = 16; element (row t, channel c) at byte
  *           K: ((c>>5)*64 + ((c>>3)&3)*16 + t)*16 + (c&7)*2
