@@ -348,7 +348,8 @@ typedef struct tg_cache {
  *                   pages of one head slot are contiguous: a sequence's
  *                   pages, allocated in order, read as one run per head).
  * Page ids, tables and plans are the same for both, and so is every output
- * bit.  tg_write_kv, tg_append_kv and tg_decode_* follow the flag of each
+ * bit.  (Head-major slots a large power of two apart, n_pages * head_bytes
+ * = 2^k, read measurably slower on MI355X: pad n_pages.)  tg_write_kv, tg_append_kv and tg_decode_* follow the flag of each
  * pool; tg_decode_streamed requires page-major INT8 pools (it copies whole
  * pages) and returns TG_EUNSUPPORTED otherwise. */
 

@@ -64,7 +64,8 @@ class Prepared:
         pools, bf16 pools); None chooses by measurement: bf16 pools
         head-major when the cache has no quantised tier (faster there), every
         other pool page-major (head-major bf16 pools beside a quantised tier
-        measured slower)."""
+        measured no faster, and slower when the slot stride is a power of
+        two)."""
         import torch
 
         self.w = w
