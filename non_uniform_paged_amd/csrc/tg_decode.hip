@@ -68,19 +68,23 @@ __global__ __launch_bounds__(256) void merge_kernel(const TG_GLOBAL float* __res
     }
   };
   constexpr int STEP = WPR * NG;
-  // two slots per iteration, both loaded before either is folded in
-  for (int s = s0 + w * NG + q; s < s1; s += 2 * STEP) {
-    const int64_t b0 = static_cast<int64_t>(s) * G + g;
-    const bool two = s + STEP < s1;
-    const int64_t b1 = two ? b0 + static_cast<int64_t>(STEP) * G : b0;
-    const float m0 = ws_ml[b0 * 2 + 0], l0 = ws_ml[b0 * 2 + 1];
-    const f32x4_t x00 = *(const TG_GLOBAL f32x4_t*)(ws_acc + b0 * D + 8 * c8);
-    const f32x4_t x01 = *(const TG_GLOBAL f32x4_t*)(ws_acc + b0 * D + 8 * c8 + 4);
-    const float m1 = ws_ml[b1 * 2 + 0], l1 = ws_ml[b1 * 2 + 1];
-    const f32x4_t x10 = *(const TG_GLOBAL f32x4_t*)(ws_acc + b1 * D + 8 * c8);
-    const f32x4_t x11 = *(const TG_GLOBAL f32x4_t*)(ws_acc + b1 * D + 8 * c8 + 4);
-    add(m0, l0, x00, x01);
-    if (two) add(m1, l1, x10, x11);
+  // U slots an iteration (four with many slots a pair), all loaded before
+  // any is folded in; folded in slot order
+  constexpr int U = WPR > 1 ? 4 : 2;
+  for (int s = s0 + w * NG + q; s < s1; s += U * STEP) {
+    float ms[U], ls[U];
+    f32x4_t x0[U], x1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {  // past s1: slot s again, not folded
+      const int64_t b = static_cast<int64_t>(s + u * STEP < s1 ? s + u * STEP : s) * G + g;
+      ms[u] = ws_ml[b * 2 + 0];
+      ls[u] = ws_ml[b * 2 + 1];
+      x0[u] = *(const TG_GLOBAL f32x4_t*)(ws_acc + b * D + 8 * c8);
+      x1[u] = *(const TG_GLOBAL f32x4_t*)(ws_acc + b * D + 8 * c8 + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (s + u * STEP < s1) add(ms[u], ls[u], x0[u], x1[u]);
   }
   auto fold = [&](float mo, float dno, const float* nmo) {
     const float mn = fmaxf(m, mo);
