@@ -280,3 +280,20 @@ def test_binding_signatures_follow_the_header():
             assert res is None, name
         else:
             assert res is not None and ctypes.sizeof(res) == ctypes.sizeof(want), (name, ret, res)
+
+
+def test_hand_worked_growth_plan_from_c():
+    """The library's tables for the hand-worked growth case of
+    test_oracle_planner.test_hand_worked_growth_plan: one request, L0 = 30,
+    recent 50 %, Qb 8, pages of 4 rows, room for 6 appended rows."""
+    api = tg
+    res = api.tg_reserve([0], 1_000_000, 1_000_000, 1, 500_000, 8, [30])
+    sizes = api.tg_size_tables(res, 4, 8, None, 8, 8, False, 0, 6)
+    assert [list(x) for x in sizes["pages_needed"]] == [[2, 6]]
+    pool = api.Pool(res.cluster_size, 64, 4, 8, [6], [2])
+    t = api.tg_build_tables(pool, res, None, 8, 8, False, 0, 6)
+    assert t.plan.tolist() == [[0, 0, 0, 0, 16, 0], [0, 0, 1, 0, 8, 1], [0, 0, 1, 8, 16, 2], [0, 0, 1, 16, 23, 3]]
+    assert t.part_off.tolist() == [0, 4]
+    assert t.len.reshape(-1).tolist() == [8, 22]
+    assert t.ring.tolist() == [[6]]
+    assert pool.free_pages(0, 0) == 0 and pool.free_pages(0, 1) == 0

@@ -560,3 +560,38 @@ def test_hand_worked_group_chunk():
     with pytest.raises(P.OracleError):
         P.build_tables(P.Pool([60], [0]), res, 4, 8, 8, 8, False, [40, 40, 40], [[0], [0], [0]], [40],
                        group_size=2, chunk_group=6)
+
+
+def test_hand_worked_growth_plan():
+    """A plan with room for appended rows (R-step), worked by hand.  One
+    request, H = 1, recent share 50 %, Qb 8, pages of 4 rows, L0 = 30:
+    n_bf0 = ceil(15) = 15, old 15 -> n_i8 8, n_bf 22.  Six appends:
+      L 31: n_bf0 16, old 15 -> i8 8, bf 23
+      L 32: n_bf0 16, old 16 -> i8 16: rows 8..15 age, bf 24 - 8 = 16
+      L 33..36: old 16..18 -> i8 16, bf 17, 18, 19, 20
+    Capacity: INT8 rows of the final length (16) and the most bf16 rows on
+    the way (23): 2 INT8 pages, ceil(23 / 4) = 6 bf16 pages (the ring).
+    Plan, chunk 8 rows in both tiers: INT8 [0, 16) is 2 blocks, 1 live:
+    k = max(1, ceil(1 / 1), ceil(2 / 2)) = 1 item [0, 16); bf16 [0, 23) is 6
+    pages, 6 live (22 rows): k = max(1, ceil(6 / 2), ceil(6 / 4)) = 3 items at
+    pages 0, 2, 4: [0, 8) [8, 16) [16, 23).  Live lengths stay (8, 22)."""
+    res = P.reserve([0], 1_000_000, 1_000_000, 1, 500_000, 8, [30], None, None)
+    assert (res.n_i8[0][0], res.n_bf[0][0]) == (8, 22)
+    steps, state = [], (8, 22)
+    for _ in range(6):
+        i8, bf, aged = P.append_step(state[0], state[1], 500_000, 8)
+        steps.append((i8, bf, aged))
+        state = (i8, bf)
+    assert steps == [(8, 23, False), (16, 16, True), (16, 17, False), (16, 18, False), (16, 19, False),
+                     (16, 20, False)]
+    cap = P.capacity(res, 6)
+    assert (cap.n_i8[0][0], cap.n_bf[0][0]) == (16, 23)
+    assert P.pages_needed(cap, 4, 8) == ([6], [2])
+    pool = P.Pool([6], [2])
+    t = P.build_tables(pool, res, 4, 8, 8, 8, False, gen_tokens=6)
+    assert [list(w) for w in t.work] == [[0, 0, 0, 0, 16, 0], [0, 0, 1, 0, 8, 1], [0, 0, 1, 8, 16, 2],
+                                         [0, 0, 1, 16, 23, 3]]
+    assert t.part_off == [0, 4]
+    assert t.lens[0][0] == (8, 22)
+    assert t.ring == [[6]]
+    assert pool.free_pages(0, 0) == 0 and pool.free_pages(0, 1) == 0
