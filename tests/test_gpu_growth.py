@@ -151,3 +151,49 @@ def test_append_past_capacity_is_refused_and_flagged():
         refused_any |= not grew.all()
         assert int(p.status.item()) == int(refused_any)
     assert refused_any
+
+
+def _random_growth_cases(n=24, seed=4242):
+    """Seeded random shapes, tier shares, item lengths and pool layouts, each
+    grown by a random number of appended rows within its reserved room."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        base = ["tiered", "llama8b", "tiered4"][i % 3]
+        Hkv = int(rng.choice([1, 2, 4]))
+        G = int(rng.choice([1, 2, 4, 8]))
+        d = 128 if base == "tiered4" else int(rng.choice([64, 128]))
+        lo = int(rng.integers(50, 600))
+        kw = dict(B=int(rng.integers(1, 5)), Hkv=Hkv, Hq=G * Hkv, d=d, n_clusters=int(rng.integers(1, Hkv + 1)),
+                  ctx=("uniform", lo, lo + int(rng.integers(0, 1500))),
+                  recent_ppm=int(rng.choice([100_000, 250_000, 500_000, 1_000_000])),
+                  q_dtype=str(rng.choice(["bf16", "f32"])))
+        T = int(rng.integers(1, 300))
+        k = int(rng.integers(0, T + 1))
+        hm = [(False, False), (True, True), (False, True), (True, False)][int(rng.integers(0, 4))]
+        chunks = dict(chunk_bf=int(rng.choice([16, 64, 256])), chunk_i8=int(rng.choice([64, 128, 512])))
+        cases.append((i, base, kw, T, k, hm, chunks))
+    return cases
+
+
+RANDOM_GROWTH = _random_growth_cases()
+
+
+@pytest.mark.parametrize("i,base,kw,T,k,hm,chunks", RANDOM_GROWTH, ids=[f"{c[0]}-{c[1]}" for c in RANDOM_GROWTH])
+def test_random_growth(i, base, kw, T, k, hm, chunks):
+    """k appended rows on a random shape and pool layout: live lengths exact,
+    outputs within the tolerance of the oracle at the grown length."""
+    _need_gpu()
+    from non_uniform_paged_amd.runner import Prepared
+    print(f"case {i} {base}: {kw} T={T} k={k} layout {hm} {chunks}", flush=True)
+    w = make_workload(base, **kw)
+    p = Prepared(w, gen_tokens=T, head_major=hm, **chunks)
+    for _ in range(k):
+        p.append()
+    res_k = _grown(A.reserve_for(w), k)
+    lens = p.live_lengths()
+    assert np.array_equal(lens[..., 0], np.array(res_k.n_i8))
+    assert np.array_equal(lens[..., 1], np.array(res_k.n_bf))
+    assert int(p.status.item()) == 0
+    p.step()
+    _check_outputs(p, res_k, f"case {i} after {k} appended rows")

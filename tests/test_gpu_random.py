@@ -1,7 +1,7 @@
 """GPU parity over seeded random shapes: workload kind, batch, heads, group
 size G, head size, clusters, tier split (bf16 / INT8 / INT4), q precision,
-item lengths and shared-prefix grouping drawn from one fixed seed, each case
-against the oracle over every output.  The draws stay inside the supported
+item lengths, shared-prefix grouping and pool layout drawn from fixed seeds,
+each case against the oracle over every output.  The draws stay inside the supported
 set (d in {64, 128}, G in {1, 2, 4, 8}, INT4 at d = 128)."""
 import numpy as np
 import pytest
@@ -52,9 +52,11 @@ def test_random_shape(i, kind, kw, plan):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     from non_uniform_paged_amd.runner import Prepared
-    print(f"case {i} {kind}: {kw} {plan}", flush=True)
+    # pool layout (INT8 pools, bf16 pools head-major) from a stream of its own
+    hm = [(False, False), (True, True), (False, True), (True, False)][int(np.random.default_rng(7000 + i).integers(0, 4))]
+    print(f"case {i} {kind}: {kw} {plan} layout {hm}", flush=True)
     w = make_workload(kind, **kw)
-    p = Prepared(w, **plan)
+    p = Prepared(w, head_major=hm, **plan)
     p.step()
     got = p.output()
     res_o = A.reserve_for(w)
